@@ -1,0 +1,409 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle.
+
+Each ``check_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with something the pages, a published standard, a library
+routine or exact arithmetic fixes.  ``test_oracle_pins.py`` runs them against
+the oracle; ``test_oracle_mutants.py`` runs them against oracle builds with a
+planted mistake and requires every mistake to be caught.
+
+Independent sources used here (none of them is the oracle's C code):
+  * the pages' fp2/fp3 code tables (``golden/page_code_tables.json``);
+  * the OCP MX v1.0 FP4 (E2M1) value table;
+  * torch's float8_e8m0fnu and bfloat16 casts, numpy's float16;
+  * numpy ``unpackbits`` as a second bit unpacker;
+  * exact rational arithmetic (``fractions.Fraction``) and int64 matmuls;
+  * the hand-worked blocks in ``golden/hand_worked_blocks.json``.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# OCP Microscaling Formats v1.0, FP4 E2M1 element values for codes 0..7;
+# codes 8..15 are the same magnitudes with the sign bit set.
+E2M1_TABLE = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def page_tables():
+    with open(os.path.join(GOLD, "page_code_tables.json")) as f:
+        return json.load(f)
+
+
+def hand_worked():
+    with open(os.path.join(GOLD, "hand_worked_blocks.json")) as f:
+        return json.load(f)["cases"]
+
+
+# ---------------------------------------------------------------- independent decoders
+def ref_code_values(fmt):
+    """Code -> value tables derived from the pages' printed tables."""
+    t = page_tables()
+    if fmt == "mxfp4":
+        return [E2M1_TABLE[c & 7] * (-1 if c & 8 else 1) for c in range(16)]
+    if fmt == "cb2":
+        return [v - 0.5 for v in t["fp2"]["values"]]
+    vals = [0.5 * v for v in t["fp3"]["values"]]
+    vals[4] = -3.0       # the table's second zero is the codebook's -3
+    return vals
+
+
+def ref_codes(fmt, rows, K):
+    """Unpack codes with numpy.unpackbits (little bit order): [n][K] ints."""
+    rows = np.ascontiguousarray(rows, np.uint8)
+    bits = np.unpackbits(rows, axis=-1, bitorder="little").astype(np.int64)
+    w = {"mxfp4": 4, "cb2": 2, "cb3": 3}[fmt]
+    bits = bits.reshape(rows.shape[0], -1, w)[:, :K, :]
+    return (bits * (1 << np.arange(w))).sum(axis=-1)
+
+
+def ref_e8m0(s):
+    import torch
+    t = torch.tensor(np.asarray(s, np.uint8)).view(torch.float8_e8m0fnu)
+    return t.float().double().numpy()
+
+
+def ref_fp16(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def ref_bf16(bits):
+    import torch
+    t = torch.from_numpy(np.asarray(bits, np.uint16).view(np.int16).copy()).view(torch.bfloat16)
+    return t.float().double().numpy()
+
+
+def ref_dequant(fmt, crows, srows, K):
+    """Dequantized weights [n][K] in float64 from the independent decoders."""
+    codes = ref_codes(fmt, crows, K)
+    vals = np.array(ref_code_values(fmt))[codes]
+    srows = np.ascontiguousarray(srows, np.uint8)
+    if fmt == "mxfp4":
+        sc = ref_e8m0(srows)                       # [n][K/32]
+        return vals * np.repeat(sc, 32, axis=1)
+    f16 = ref_fp16(srows.view(np.uint16))
+    per = 32 if fmt == "cb2" else 16
+    return vals * np.repeat(f16, per, axis=1)
+
+
+def ref_activations(afmt, x, xs, K):
+    if afmt == "bf16":
+        return ref_bf16(x)
+    return np.asarray(x, np.int8).astype(np.float64) * np.repeat(ref_fp16(xs), 32, axis=1)
+
+
+# ---------------------------------------------------------------- helpers
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _afmt(fmt):
+    return "bf16" if fmt == "mxfp4" else "q8"
+
+
+def _rcb(fmt, K):
+    return {"mxfp4": K // 2, "cb2": K // 4, "cb3": 3 * K // 8}[fmt]
+
+
+def _rsb(fmt, K):
+    return {"mxfp4": K // 32, "cb2": K // 16, "cb3": K // 8}[fmt]
+
+
+def _random_rows(rng, fmt, n, K, unit_scales=False):
+    codes = rng.integers(0, 256, size=(n, _rcb(fmt, K)), dtype=np.uint8)
+    if fmt == "mxfp4":
+        s = np.full((n, K // 32), 127, np.uint8) if unit_scales else \
+            rng.integers(118, 137, size=(n, K // 32), dtype=np.uint8)
+    else:
+        per = K // 32 if fmt == "cb2" else K // 16
+        f = np.ones((n, per), np.float16) if unit_scales else \
+            (np.abs(rng.standard_normal((n, per))) * 0.02).astype(np.float16)
+        s = f.view(np.uint8).reshape(n, 2 * per)
+    return codes, s
+
+
+def _random_x(rng, fmt, V, K, small_ints=False, unit_xs=False):
+    if fmt == "mxfp4":
+        import torch
+        g = rng.integers(-8, 9, size=(V, K)).astype(np.float32) if small_ints else \
+            rng.standard_normal((V, K)).astype(np.float32)
+        b = torch.from_numpy(g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        return b.copy(), None
+    q = rng.integers(-128, 128, size=(V, K), dtype=np.int16).astype(np.int8)
+    xs = np.ones((V, K // 32), np.float16) if unit_xs else \
+        (np.abs(rng.standard_normal((V, K // 32))) * 0.05 + 1e-3).astype(np.float16)
+    return q, xs.view(np.uint16)
+
+
+def _dense_one_expert(o, fmt, codes, scales, x, xs):
+    ids = np.zeros((x.shape[0], 1), np.int32)
+    y, A = o.gather(fmt, codes[None], scales[None], ids, _afmt(fmt), x, xs)
+    return y[:, 0, :], A[:, 0, :]
+
+
+# ---------------------------------------------------------------- P1-P3 scalar decoders
+def check_e2m1_table(o):
+    for c in range(16):
+        v = o.e2m1(c)
+        want = E2M1_TABLE[c & 7]
+        assert abs(v) == want, (c, v, want)
+        assert math.copysign(1.0, v) == (-1.0 if c & 8 else 1.0), ("sign", c, v)
+
+
+def check_e8m0_library(o):
+    ref = ref_e8m0(np.arange(256))
+    for s in range(256):
+        v = o.e8m0(s)
+        if math.isnan(ref[s]):
+            assert math.isnan(v), s
+        else:
+            assert v == ref[s], (s, v, ref[s])
+
+
+def check_fp16_exhaustive(o):
+    ref = ref_fp16(np.arange(65536))
+    got = np.array([o.h2d(h) for h in range(65536)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def check_bf16_exhaustive(o):
+    ref = ref_bf16(np.arange(65536))
+    got = np.array([o.bf16(b) for b in range(65536)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def check_codebooks_match_pages(o):
+    t = page_tables()
+    for fmt in ("cb2", "cb3"):
+        got = [o.code_value(fmt, c) for c in range(4 if fmt == "cb2" else 8)]
+        assert got == ref_code_values(fmt), (fmt, got)
+        want_set = sorted(t["workload_%s_set" % fmt]["values"])
+        assert sorted(got) == want_set, (fmt, sorted(got), want_set)
+
+
+# ---------------------------------------------------------------- P4 hand-worked + unpackers
+def _build_hw_case(case):
+    fmt = case["fmt"]
+    K = 32
+    crow = np.zeros(_rcb(fmt, K), np.uint8)
+    if "all" in case["codes"]:
+        crow[:] = int(case["codes"]["all"], 16)
+    else:
+        for off, hx in case["codes"].items():
+            crow[int(off)] = int(hx, 16)
+    if fmt == "mxfp4":
+        srow = np.array(case["scales"], np.uint8)
+        xv = np.zeros(K, np.float32)
+        if "all" in case["x"]:
+            xv[:] = case["x"]["all"]
+        else:
+            for i, v in case["x"].items():
+                xv[int(i)] = v
+        x = (xv.view(np.uint32) >> 16).astype(np.uint16)[None]   # exact values only
+        assert np.array_equal((x.astype(np.uint32) << 16).view(np.float32)[0], xv)
+        xs = None
+    else:
+        srow = np.array(case["scales"], np.float16).view(np.uint8)
+        q = np.zeros(K, np.int8)
+        for i, v in case["q"].items():
+            q[int(i)] = v
+        x = q[None]
+        xs = np.array(case["xs"], np.float16).view(np.uint16)[None]
+    return fmt, crow, srow, x, xs
+
+
+def check_hand_worked(o):
+    for case in hand_worked():
+        fmt, crow, srow, x, xs = _build_hw_case(case)
+        y, A = _dense_one_expert(o, fmt, crow[None], srow[None], x, xs)
+        assert y[0, 0] == case["y"], (case["name"], y[0, 0], case["y"])
+        if "S" in case:
+            S = o.block_sums(fmt, crow, x[0], 32)
+            assert list(S[:len(case["S"])]) == case["S"], (case["name"], S)
+
+
+def check_unpackers_agree(o):
+    rng = _rng(11)
+    for fmt in ("mxfp4", "cb2", "cb3"):
+        K = 256
+        codes, scales = _random_rows(rng, fmt, 8, K)
+        ref = ref_codes(fmt, codes, K)
+        for r in range(codes.shape[0]):
+            got = [o.code(fmt, codes[r], k) for k in range(K)]
+            assert got == list(ref[r]), (fmt, r)
+        want = ref_dequant(fmt, codes, scales, K)
+        for r in range(codes.shape[0]):
+            w = o.dequant_row(fmt, codes[r], scales[r], K)
+            assert np.array_equal(w, want[r]), (fmt, r)
+
+
+# ---------------------------------------------------------------- P5 brute force on K = 32
+def _frac_e2m1(c):
+    return Fraction(E2M1_TABLE[c & 7]) * (-1 if c & 8 else 1)
+
+
+def check_mxfp4_one_hot(o):
+    """Every position x every code x every scale byte in [122, 132]: one
+    nonzero weight, exact against rational arithmetic."""
+    rng = _rng(12)
+    K = 32
+    rows, expect, xs_list = [], [], []
+    x, _ = _random_x(rng, "mxfp4", 1, K)
+    xv = ref_bf16(x[0])
+    for i in range(K):
+        for c in range(16):
+            for s in range(122, 133):
+                crow = np.zeros(K // 2, np.uint8)
+                crow[i // 2] = (c << 4) if (i & 1) else c
+                rows.append((crow, np.array([s], np.uint8)))
+                expect.append(_frac_e2m1(c) * Fraction(2) ** (s - 127) * Fraction(float(xv[i])))
+    codes = np.stack([r[0] for r in rows])
+    scales = np.stack([r[1] for r in rows])
+    y, _ = _dense_one_expert(o, "mxfp4", codes, scales, x, None)
+    for n, want in enumerate(expect):
+        assert Fraction(y[0, n]) == want, (n, y[0, n], float(want))
+
+
+def check_random_blocks_exact(o):
+    """Random K=32 rows against an exact rational dot (within 2^-50 * A)."""
+    rng = _rng(13)
+    K = 32
+    for fmt in ("mxfp4", "cb2", "cb3"):
+        n = 400
+        codes, scales = _random_rows(rng, fmt, n, K)
+        x, xs = _random_x(rng, fmt, 1, K)
+        y, A = _dense_one_expert(o, fmt, codes, scales, x, xs)
+        vals = ref_code_values(fmt)
+        cds = ref_codes(fmt, codes, K)
+        if fmt == "mxfp4":
+            xv = [Fraction(float(v)) for v in ref_bf16(x[0])]
+        else:
+            d = Fraction(float(ref_fp16(xs[0])[0]))
+            xv = [Fraction(int(q)) * d for q in x[0]]
+        for r in range(n):
+            if fmt == "mxfp4":
+                sc = [Fraction(2) ** (int(scales[r, k // 32]) - 127) for k in range(K)]
+            else:
+                f16 = ref_fp16(scales[r].view(np.uint16))
+                per = 32 if fmt == "cb2" else 16
+                sc = [Fraction(float(f16[k // per])) for k in range(K)]
+            exact = sum(Fraction(vals[cds[r, k]]) * sc[k] * xv[k] for k in range(K))
+            assert abs(Fraction(y[0, r]) - exact) <= Fraction(2) ** -50 * Fraction(A[0, r]), \
+                (fmt, r, y[0, r], float(exact))
+
+
+# ---------------------------------------------------------------- P6 dot structure
+def check_block_factored(o):
+    """Literal y equals the block-factored sum_b scale_b * xs * S_b / 2 built
+    from the integer side output (per-block factorization of the dot)."""
+    rng = _rng(14)
+    for fmt in ("cb2", "cb3"):
+        K = 256
+        codes, scales = _random_rows(rng, fmt, 16, K)
+        q, xs = _random_x(rng, fmt, 1, K)
+        y, A = _dense_one_expert(o, fmt, codes, scales, q, xs)
+        f16 = ref_fp16(scales.view(np.uint16))
+        xsv = ref_fp16(xs[0])
+        bs = 32 if fmt == "cb2" else 16
+        for r in range(codes.shape[0]):
+            S = o.block_sums(fmt, codes[r], q[0], K)
+            blk = sum(float(f16[r, b]) * float(xsv[(b * bs) // 32]) * int(S[b]) / 2.0
+                      for b in range(K // bs))
+            assert abs(blk - y[0, r]) <= 1e-12 * max(A[0, r], 1e-300), (fmt, r, blk, y[0, r])
+
+
+# ---------------------------------------------------------------- P7 exact special cases
+def check_unit_scale_exact(o):
+    rng = _rng(15)
+    K = 512
+    for fmt in ("cb2", "cb3"):
+        codes, scales = _random_rows(rng, fmt, 32, K, unit_scales=True)
+        q, xs = _random_x(rng, fmt, 1, K, unit_xs=True)
+        y, _ = _dense_one_expert(o, fmt, codes, scales, q, xs)
+        v2 = (2 * np.array(ref_code_values(fmt))).astype(np.int64)[ref_codes(fmt, codes, K)]
+        want = v2 @ q[0].astype(np.int64)               # int64 matmul, exact
+        assert np.array_equal(y[0] * 2, want.astype(np.float64)), fmt
+        for r in range(codes.shape[0]):
+            S = o.block_sums(fmt, codes[r], q[0], K)
+            assert int(S.sum()) == int(want[r]), (fmt, r)
+    codes, scales = _random_rows(rng, "mxfp4", 32, K, unit_scales=True)
+    x, _ = _random_x(rng, "mxfp4", 1, K, small_ints=True)
+    y, _ = _dense_one_expert(o, "mxfp4", codes, scales, x, None)
+    vals = np.array(ref_code_values("mxfp4"))[ref_codes("mxfp4", codes, K)]
+    want = vals @ ref_bf16(x[0])
+    assert np.array_equal(y[0], want), "mxfp4 unit scale"
+
+
+# ---------------------------------------------------------------- P8 gather semantics
+def check_gather_semantics(o):
+    rng = _rng(16)
+    K, N, E = 64, 24, 6
+    for fmt in ("mxfp4", "cb2", "cb3"):
+        afmt = _afmt(fmt)
+        codes = np.stack([_random_rows(rng, fmt, N, K)[0] for _ in range(E)])
+        scales = np.stack([_random_rows(rng, fmt, N, K)[1] for _ in range(E)])
+        x, xs = _random_x(rng, fmt, 2, K)
+        # one expert == dense on that expert's matrix
+        for e in range(E):
+            yg, _ = o.gather(fmt, codes, scales, np.array([[e], [e]], np.int32), afmt, x, xs)
+            yd, _ = o.dense(fmt, codes[e], scales[e], afmt, x, xs)
+            assert np.array_equal(yg[:, 0, :], yd), (fmt, e)
+        # invalid ids give zero rows (and zero A)
+        ids = np.array([[-1, 2, E, 0], [2 ** 31 - 1, -2 ** 31, 5, 1]], np.int32)
+        y, A = o.gather(fmt, codes, scales, ids, afmt, x, xs)
+        for t in range(2):
+            for j in range(4):
+                e = ids[t, j]
+                if 0 <= e < E:
+                    yd, _ = o.dense(fmt, codes[e], scales[e], afmt, x[t:t + 1],
+                                    None if xs is None else xs[t:t + 1])
+                    assert np.array_equal(y[t, j], yd[0]), (fmt, t, j)
+                else:
+                    assert not y[t, j].any() and not A[t, j].any(), (fmt, t, j)
+        # relabelling the experts together with the ids leaves y unchanged
+        perm = rng.permutation(E)
+        inv = np.argsort(perm)
+        ids = np.array([[0, 3, 5], [1, 1, 4]], np.int32)
+        y0, _ = o.gather(fmt, codes, scales, ids, afmt, x, xs)
+        y1, _ = o.gather(fmt, codes[perm], scales[perm], inv[ids].astype(np.int32), afmt, x, xs)
+        assert np.array_equal(y0, y1), fmt
+        # y is homogeneous in x: doubling x doubles y exactly
+        if fmt == "mxfp4":
+            x2 = (x.astype(np.uint32) + (1 << 7)).astype(np.uint16)   # exponent + 1
+            xs2 = None
+        else:
+            x2 = x
+            xs2 = (xs.view(np.float16) * np.float16(2)).view(np.uint16)
+        y2, _ = o.gather(fmt, codes, scales, ids, afmt, x2, xs2)
+        assert np.array_equal(y2, 2 * y0), fmt
+        # per-slot activations that all equal the token's vector == broadcast
+        xp = np.repeat(x, 3, axis=0)
+        xsp = None if xs is None else np.repeat(xs, 3, axis=0)
+        yp, _ = o.gather(fmt, codes, scales, ids, afmt, xp, xsp, x_per_slot=True)
+        assert np.array_equal(yp, y0), fmt
+
+
+ALL_CHECKS = [
+    check_e2m1_table,
+    check_e8m0_library,
+    check_fp16_exhaustive,
+    check_bf16_exhaustive,
+    check_codebooks_match_pages,
+    check_hand_worked,
+    check_unpackers_agree,
+    check_mxfp4_one_hot,
+    check_random_blocks_exact,
+    check_block_factored,
+    check_unit_scale_exact,
+    check_gather_semantics,
+]

@@ -1,0 +1,34 @@
+"""Every planted oracle mistake must be caught by at least one pin.
+
+The mistakes are compiled into separate oracle builds (ORACLE_MUTANT=n in
+qmv_oracle.c), on the CPU only:
+  1 e2m1 sign dropped          2 nibbles swapped          3 3-bit scale of the
+  wrong half-block             4 2-bit codebook shifted   5 3-bit codes read
+  MSB-first                    6 E8M0 bias 128            7 fp16 bias off by one
+  8 out-of-range ids wrap instead of giving zero rows.
+The idea of requiring a sign-dropped decode to fail comes from mlxcel issue
+#2178, Acceptance Criteria.
+"""
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+# the cheap pins first; the exhaustive ones only run if those all passed
+ORDER = [pins.check_hand_worked, pins.check_codebooks_match_pages, pins.check_e2m1_table,
+         pins.check_e8m0_library, pins.check_unpackers_agree, pins.check_gather_semantics,
+         pins.check_unit_scale_exact, pins.check_block_factored, pins.check_fp16_exhaustive,
+         pins.check_bf16_exhaustive, pins.check_random_blocks_exact, pins.check_mxfp4_one_hot]
+
+
+@pytest.mark.parametrize("mutant", range(1, 9))
+def test_mutant_is_caught(mutant):
+    o = oracle.load(mutant)
+    caught = []
+    for check in ORDER:
+        try:
+            check(o)
+        except AssertionError:
+            caught.append(check.__name__)
+            break
+    assert caught, f"mutant {mutant} passed every pin"
