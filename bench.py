@@ -1,0 +1,317 @@
+"""Throughput of the expert-gather GEMV on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads C2,C3,...]
+                    [--no-cpu] [--no-extra]
+
+A step is one qmv_gather_moe call (expert dispatch, weight streaming, decode,
+block dots, scale epilogue, cross-lane reduction, store) on the gpt-oss-20b
+MoE decode shape: 4 of 32 MXFP4 experts, K = N = 2880, one bf16 token.
+Inputs are synthetic and seeded (module ``synth``) and already resident in
+HBM.  To measure HBM rather than the 256 MB Infinity Cache, the weights live
+in many layer copies (>= 1 GB in total) that successive calls rotate through,
+and every call draws fresh expert ids.  The K timed calls are captured once
+into a HIP graph (torch.cuda.CUDAGraph) and replayed, so host launch overhead
+is not part of the time; the time is taken with HIP events on the replay
+stream, bracketed by device synchronizations.
+
+Prints ONE JSON line.  ``value`` is effective weight GB/s (code + scale bytes
+of the experts a call reads / time per call).  ``roofline`` relates the
+kernel's algorithmic bytes (weights + activations + ids + output) per launch
+to the 8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same workload on the host's cores.  ``workloads`` lists the
+other shapes measured the same way (not the headline).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WFMT = {"mxfp4": 0, "cb2": 1, "cb3": 2}
+HEADLINE = "C2"
+METRIC = "effective weight GB/s and µs/call per expert-gather GEMV; % of HBM peak"
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def weight_bytes(wl, n_experts):
+    import synth
+    return n_experts * wl.N * (synth.row_code_bytes(wl.wfmt, wl.K) + synth.row_scale_bytes(wl.wfmt, wl.K))
+
+
+def other_bytes(wl):
+    """Activation, scale, id and output bytes of one call."""
+    V = wl.M * wl.top_k if (wl.kind == "gather" and wl.x_per_slot) else wl.M
+    xb = V * wl.K * (2 if wl.afmt == "bf16" else 1) + (0 if wl.afmt == "bf16" else V * (wl.K // 32) * 2)
+    outs = wl.M * (wl.top_k if wl.kind == "gather" else 1) * wl.N
+    ids = 4 * wl.M * wl.top_k if wl.kind == "gather" else 0
+    return xb + ids + 4 * outs
+
+
+# Rotation plan: layer copies so that between two reads of the same weights
+# more than the 256 MB Infinity Cache of other weights is read.
+ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40}
+
+
+class Prepared:
+    """Device-resident inputs of one workload plus per-call raw arguments."""
+
+    def __init__(self, name, calls, rotate=True):
+        import torch
+
+        import bit_block_quantized_amd as q
+        import synth
+        self.name = name
+        self.wl = wl = synth.WORKLOADS[name]
+        self.inp = inp = synth.make(name)
+        self.L = ROTATION[name] if rotate else 1
+        dev = torch.device("cuda")
+        c0 = torch.from_numpy(inp.codes).to(dev)
+        s0 = torch.from_numpy(inp.scales).to(dev)
+        self.codes = torch.empty((self.L,) + tuple(c0.shape), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((self.L,) + tuple(s0.shape), dtype=torch.uint8, device=dev)
+        for layer in range(self.L):
+            self.codes[layer].copy_(c0)
+            self.scales[layer].copy_(s0)
+        del c0, s0
+        if wl.afmt == "bf16":
+            self.x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+            self.xs = None
+        else:
+            self.x = torch.from_numpy(inp.x).to(dev)
+            self.xs = torch.from_numpy(inp.xs.view(np.float16)).to(dev)
+        if wl.kind == "gather":
+            if name in ("C3", "C4"):
+                ids = synth.disjoint_id_stream(wl.seed + 100, calls, wl.top_k, wl.E)
+            else:
+                ids = synth.id_stream(wl.seed + 100, calls, wl.M, wl.top_k, wl.E)
+            self.ids_host = ids
+            self.ids = torch.from_numpy(ids).to(dev)
+            n_unique = np.array([len(np.unique(i)) for i in ids])
+            self.y = torch.empty((wl.M, wl.top_k, wl.N), dtype=torch.float32, device=dev)
+        else:
+            self.ids_host = None
+            self.ids = None
+            n_unique = np.ones(calls, np.int64)
+            self.y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
+        self.calls = calls
+        self.wbytes = np.array([weight_bytes(wl, u) for u in n_unique], np.float64)
+        self.abytes = self.wbytes + other_bytes(wl)
+        self.lib = q.lib()
+        cstride = self.codes[0].numel()
+        sstride = self.scales[0].numel()
+        self.args = []
+        for i in range(calls):
+            layer = i % self.L
+            cp = self.codes.data_ptr() + layer * cstride
+            sp = self.scales.data_ptr() + layer * sstride
+            xs = None if self.xs is None else self.xs.data_ptr()
+            if wl.kind == "gather":
+                self.args.append((WFMT[wl.wfmt], cp, sp,
+                                  wl.E, self.ids.data_ptr() + i * wl.M * wl.top_k * 4, wl.M,
+                                  wl.top_k, 0 if wl.afmt == "bf16" else 1, self.x.data_ptr(), xs,
+                                  int(wl.x_per_slot), self.y.data_ptr(), wl.N, wl.K))
+            else:
+                self.args.append((WFMT[wl.wfmt], cp, sp, 0 if wl.afmt == "bf16" else 1, self.x.data_ptr(), xs,
+                                  self.y.data_ptr(), wl.M, wl.N, wl.K))
+
+    def call(self, i, stream_handle):
+        a = self.args[i]
+        if self.wl.kind == "gather":
+            s = self.lib.qmv_gather_moe(*a, ctypes.c_void_p(stream_handle))
+        else:
+            s = self.lib.qmv_dense(*a, ctypes.c_void_p(stream_handle))
+        if s != 0:
+            raise RuntimeError(f"{self.name}: status {s}")
+
+
+def time_graph(p, first, count):
+    """Capture calls [first, first+count) into one graph, replay it once
+    (untimed), then replay it timed.  Returns seconds per call."""
+    import torch
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        for i in range(first, min(first + 3, first + count)):   # eager warm-up on the stream
+            p.call(i, s.cuda_stream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(first, first + count):
+            p.call(i, h)
+    torch.cuda.synchronize()
+    g.replay()                                   # untimed replay: graph upload, warm clocks
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        torch.cuda.synchronize()
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / count
+
+
+def time_eager(p, first, count):
+    """The same calls launched one by one from Python (host-bound reference)."""
+    import torch
+    s = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(first, first + count):
+        p.call(i, s.cuda_stream)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / count
+
+
+def measure(name, steps, warmup, rotate=True):
+    p = Prepared(name, warmup + steps, rotate=rotate)
+    import torch
+    # warm-up: W untimed calls through their own graph
+    if warmup:
+        time_graph(p, 0, warmup)
+    t = time_graph(p, warmup, steps)
+    sel = slice(warmup, warmup + steps)
+    wb = float(p.wbytes[sel].mean())
+    ab = float(p.abytes[sel].mean())
+    res = {
+        "us_per_call": t * 1e6,
+        "weight_bytes_per_call": wb,
+        "algorithmic_bytes_per_call": ab,
+        "eff_weight_GBps": wb / t / 1e9,
+        "pct_hbm_peak": 100.0 * (ab / t / 1e9) / HBM_PEAK_GBS,
+        "layers_rotated": p.L,
+    }
+    te = time_eager(p, warmup, min(steps, 200))
+    res["us_per_call_eager_launch"] = te * 1e6
+    torch.cuda.synchronize()
+    return p, res
+
+
+def cpu_baseline(p, target_s=10.0):
+    """The oracle (as it stands) on whole calls of the workload, all host
+    cores (one thread per disjoint output slice), for about ``target_s``."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import oracle_call
+    import synth
+    wl = p.wl
+    cores = host_cores()
+    inp = p.inp
+    calls = 0
+    t0 = time.perf_counter()
+    wbytes = 0.0
+    while True:
+        i = calls % p.calls
+        if p.ids_host is not None:
+            inp = synth.Inputs(wl, p.inp.codes, p.inp.scales, p.ids_host[i], p.inp.x, p.inp.xs)
+        oracle_call(inp, nthreads=cores)
+        wbytes += float(p.wbytes[i])
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or calls >= 10000:
+            break
+    return {
+        "value": wbytes / el / 1e9,
+        "unit": "GB/s",
+        "us_per_call": el / calls * 1e6,
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{calls} complete {wl.name} calls (fresh ids, {wl.M} token(s), "
+                  f"K={wl.K}, N={wl.N}), fp64 C oracle, {cores} threads over disjoint outputs, "
+                  f"{el:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b",
+                    help="other shapes to measure besides the headline")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library is a single-GPU operator "
+              "(a multi-GPU deployment shards experts or rows, each GPU running the same "
+              "kernel on its share); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+
+    p, head = measure(HEADLINE, args.steps, args.warmup)
+    extra = {}
+    if not args.no_extra:
+        for name in [w for w in args.workloads.split(",") if w and w != HEADLINE]:
+            pe, r = measure(name, max(50, args.steps // 5), 10)
+            r["desc"] = pe.wl.desc
+            extra[name] = r
+            del pe
+            torch.cuda.empty_cache()
+    _, hot = measure(HEADLINE, min(args.steps, 500), 10, rotate=False)
+
+    t = head["us_per_call"] * 1e-6
+    out = {
+        "metric": METRIC,
+        "value": round(head["eff_weight_GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["us_per_call"] * 1e-3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "C2: gpt-oss-20b MoE decode expert-gather GEMV, MXFP4 (e2m1 + E8M0/32) "
+                        "x bf16 -> f32, 4 of 32 experts, 1 token, K=N=2880",
+            "E": 32, "top_k": 4, "M": 1, "N": 2880, "K": 2880,
+            "layers_rotated": head["layers_rotated"],
+            "timing": "HIP graph of the K calls, HIP events on the replay stream",
+        },
+        "us_per_call": round(head["us_per_call"], 3),
+        "pct_hbm_peak": round(head["pct_hbm_peak"], 2),
+        "us_per_call_eager_launch": round(head["us_per_call_eager_launch"], 3),
+        "hot_cache_us_per_call": round(hot["us_per_call"], 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(head["algorithmic_bytes_per_call"] / t / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["algorithmic_bytes_per_call"] / t / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "qmv::qmv_kernel<0, 32, 2, 1> (MXFP4, 32 lanes per row, 2 rows in flight)",
+            "algorithmic_bytes_per_launch": head["algorithmic_bytes_per_call"],
+        },
+        "workloads": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                      for k, v in extra.items()},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

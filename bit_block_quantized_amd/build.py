@@ -1,0 +1,56 @@
+"""Build libqmv.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m bit_block_quantized_amd.build
+
+Each translation unit (the launcher/ABI and one kernel table per weight
+format) is compiled in parallel, then linked into one shared library.  The
+library is compiled for gfx950 only.  Packed-FP32 VALU forms are switched off
+(``-packed-fp32-ops``) so the compiler never emits v_pk_{add,mul,fma}_f32.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = ["qmv.hip", "qmv_k_mxfp4.hip", "qmv_k_cb2.hip", "qmv_k_cb2s.hip", "qmv_k_cb3.hip"]
+LIB = os.path.join(HERE, "libqmv.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mcode-object-version=5",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(out: str = LIB, extra: list | None = None, verbose: bool = False) -> str:
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory(prefix="qmv_build_") as tmp:
+        def compile_one(src):
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            cmd = [HIPCC, *FLAGS, *inc, *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+            return obj
+        jobs = min(len(SOURCES), max(1, os.cpu_count() or 1))
+        with ThreadPoolExecutor(jobs) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))
+    sys.exit(0)

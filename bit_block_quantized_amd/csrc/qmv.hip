@@ -1,0 +1,203 @@
+// qmv.hip -- launcher and C ABI of libqmv.so (declared in include/qmv.h).
+//
+// The host side only validates arguments, picks a kernel instantiation from
+// the call's shape, and enqueues one launch on the caller's stream.  It never
+// allocates, synchronizes or touches device memory itself.
+#include "qmv_device.hpp"
+#include "qmv.h"
+
+#include <mutex>
+#include <stdint.h>
+
+namespace {
+
+using namespace qmv;
+
+constexpr int kMaxK = 16384;
+constexpr int kMaxM = 4;
+constexpr int kMaxTopK = 16;
+
+const void *kernel_for(int kind, int variant, int li, int ci)
+{
+    switch (kind) {
+    case kMXFP4: return kTable_mxfp4[variant][li][ci];
+    case kCB2: return kTable_cb2[variant][li][ci];
+    case kCB2S: return kTable_cb2s[variant][li][ci];
+    default: return kTable_cb3[variant][li][ci];
+    }
+}
+
+constexpr int kUnitWeights[4] = {Fmt<kMXFP4>::W, Fmt<kCB2>::W, Fmt<kCB2S>::W, Fmt<kCB3>::W};
+constexpr int kUnitXB[4] = {Fmt<kMXFP4>::XB, Fmt<kCB2>::XB, Fmt<kCB2S>::XB, Fmt<kCB3>::XB};
+constexpr int kUnitAB[4] = {Fmt<kMXFP4>::AB, Fmt<kCB2>::AB, Fmt<kCB2S>::AB, Fmt<kCB3>::AB};
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+long long row_code_bytes(int wfmt, long long K)
+{
+    return wfmt == QMV_W_MXFP4 ? K / 2 : wfmt == QMV_W_CB2 ? K / 4 : 3 * K / 8;
+}
+long long row_scale_bytes(int wfmt, long long K)
+{
+    return wfmt == QMV_W_MXFP4 ? K / 32 : wfmt == QMV_W_CB2 ? K / 16 : K / 8;
+}
+
+// Host-only argument checks (no HIP call, no pointer dereference).
+qmv_status_t validate(int wfmt, const void *codes, const void *scales, long long E,
+                      const int32_t *ids, bool gather, int M, int top_k, int afmt,
+                      const void *x, const void *xs, const float *y, int N, int K)
+{
+    if (!codes || !scales || !x || !y || (gather && !ids))
+        return QMV_EINVAL;
+    if (afmt == QMV_A_Q8B32 && !xs)
+        return QMV_EINVAL;
+    if (M <= 0 || N <= 0 || K <= 0 || E <= 0 || top_k <= 0)
+        return QMV_EINVAL;
+    if (wfmt < QMV_W_MXFP4 || wfmt > QMV_W_CB3 || afmt < QMV_A_BF16 || afmt > QMV_A_Q8B32)
+        return QMV_EUNSUPPORTED;
+    if ((wfmt == QMV_W_MXFP4) != (afmt == QMV_A_BF16))
+        return QMV_EUNSUPPORTED;
+    if (M > kMaxM || top_k > kMaxTopK || K % 32 != 0 || K > kMaxK)
+        return QMV_EUNSUPPORTED;
+    const uintptr_t calign = (wfmt == QMV_W_CB2 && K % 64 != 0) ? 8 : (wfmt == QMV_W_CB3 ? 4 : 16);
+    if (!aligned(codes, calign) || !aligned(x, 16) || !aligned(y, 4) ||
+        (wfmt != QMV_W_MXFP4 && !aligned(scales, 4)) || (xs && !aligned(xs, 4)) ||
+        (ids && !aligned(ids, 4)))
+        return QMV_EINVAL;
+    // keep every byte offset comfortably inside int64
+    const long long per_expert = (long long)N * row_code_bytes(wfmt, K);
+    if (per_expert > 0 && E > (1LL << 62) / per_expert)
+        return QMV_EUNSUPPORTED;
+    return QMV_OK;
+}
+
+// Launch shape for a row of `units` units: the (lanes per row, units per
+// lane) pair from the variant's menu that pads the row least, then needs the
+// fewest segments, then uses the most lanes per row.
+struct Shape { int li, ci, lpr, cpl; };
+
+Shape pick_shape(int variant, int units)
+{
+    Shape best = {0, 0, 0, 0};
+    long long best_key[3] = {-1, -1, -1};
+    const int ncpl = variant == 2 ? 3 : 5;
+    for (int li = 0; li < 4; ++li) {
+        const int lpr = kMenuLpr[li];
+        if (variant == 2 && lpr == 8) continue;
+        for (int ci = 0; ci < ncpl; ++ci) {
+            const int cpl = variant == 2 ? kMenuCpl2[ci] : kMenuCpl01[ci];
+            const long long seg = (long long)lpr * cpl;
+            const long long nseg = (units + seg - 1) / seg;
+            const long long key[3] = {nseg * seg, nseg, -lpr};
+            const bool better = best_key[0] < 0 || key[0] < best_key[0] ||
+                                (key[0] == best_key[0] && (key[1] < best_key[1] ||
+                                 (key[1] == best_key[1] && key[2] < best_key[2])));
+            if (better) {
+                best = {li, ci, lpr, cpl};
+                for (int k = 0; k < 3; ++k) best_key[k] = key[k];
+            }
+        }
+    }
+    return best;
+}
+
+std::once_flag g_attr_once[4][3][4][5];
+hipError_t g_attr_err[4][3][4][5];
+
+qmv_status_t launch(int wfmt, const void *codes, const void *scales, int E, const int32_t *ids,
+                    int M, int top_k, const void *x, const void *xs, int x_per_slot,
+                    float *y, int N, int K, hipStream_t stream)
+{
+    const bool gather = ids != nullptr;
+    const int kind = wfmt == QMV_W_MXFP4 ? kMXFP4 : wfmt == QMV_W_CB3 ? kCB3 : (K % 64 == 0 ? kCB2 : kCB2S);
+    const int units = K / kUnitWeights[kind];
+    const int nv_needed = !gather ? M : (x_per_slot ? (M * top_k < 4 ? M * top_k : 4) : M);
+    int variant, rt;
+    if (nv_needed == 1) { variant = 0; rt = 2; }
+    else if (gather)    { variant = 1; rt = 2; }
+    else                { variant = 2; rt = 4; }
+    const int nvmax = variant == 0 ? 1 : 4;
+    const Shape sh = pick_shape(variant, units);
+    Args a;
+    a.codes = (const uint8_t *)codes;
+    a.scales = (const uint8_t *)scales;
+    a.ids = ids;
+    a.x = (const uint8_t *)x;
+    a.xs = (const uint16_t *)xs;
+    a.y = y;
+    a.rcb = row_code_bytes(wfmt, K);
+    a.rsb = row_scale_bytes(wfmt, K);
+    a.x_vec_bytes = (wfmt == QMV_W_MXFP4) ? 2LL * K : (long long)K;
+    a.E = gather ? E : 1;
+    a.M = M;
+    a.top_k = gather ? top_k : 1;
+    a.N = N;
+    a.K = K;
+    a.units = units;
+    a.x_per_slot = gather ? x_per_slot : 0;
+    a.rows_per_tile = kWaves * (64 / sh.lpr) * rt;
+    const int vec_bytes = units * (kUnitXB[kind] + kUnitAB[kind]);
+    a.lds_vec_bytes = (vec_bytes + 15) & ~15;
+    const size_t lds = (size_t)nvmax * a.lds_vec_bytes;
+
+    const void *fn = kernel_for(kind, variant, sh.li, sh.ci);
+    // Largest dynamic LDS this kernel can ask for (K = kMaxK, all vectors).
+    std::call_once(g_attr_once[kind][variant][sh.li][sh.ci], [&] {
+        const int umax = kMaxK / kUnitWeights[kind];
+        const int vmax = (umax * (kUnitXB[kind] + kUnitAB[kind]) + 15) & ~15;
+        g_attr_err[kind][variant][sh.li][sh.ci] = hipFuncSetAttribute(
+            fn, hipFuncAttributeMaxDynamicSharedMemorySize, nvmax * vmax);
+    });
+    if (g_attr_err[kind][variant][sh.li][sh.ci] != hipSuccess)
+        return QMV_EHIP;
+
+    const dim3 grid((unsigned)((N + a.rows_per_tile - 1) / a.rows_per_tile),
+                    (unsigned)(gather ? M * top_k : 1));
+    void *kargs[] = {&a};
+    if (hipLaunchKernel(fn, grid, dim3(kThreads), kargs, lds, stream) != hipSuccess)
+        return QMV_EHIP;
+    return QMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
+                       qmv_afmt_t afmt, const void *x, const void *x_scales,
+                       float *y, int M, int N, int K, hipStream_t stream)
+{
+    const qmv_status_t s = validate(wfmt, w_codes, w_scales, 1, nullptr, false, M, 1, afmt,
+                                    x, afmt == QMV_A_Q8B32 ? x_scales : nullptr, y, N, K);
+    if (s != QMV_OK)
+        return s;
+    return launch(wfmt, w_codes, w_scales, 1, nullptr, M, 1, x,
+                  afmt == QMV_A_Q8B32 ? x_scales : nullptr, 0, y, N, K, stream);
+}
+
+qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales, int E,
+                            const int32_t *expert_ids, int M, int top_k,
+                            qmv_afmt_t afmt, const void *x, const void *x_scales,
+                            int x_per_slot, float *y, int N, int K, hipStream_t stream)
+{
+    const qmv_status_t s = validate(wfmt, w_codes, w_scales, E, expert_ids, true, M, top_k, afmt,
+                                    x, afmt == QMV_A_Q8B32 ? x_scales : nullptr, y, N, K);
+    if (s != QMV_OK)
+        return s;
+    return launch(wfmt, w_codes, w_scales, E, expert_ids, M, top_k, x,
+                  afmt == QMV_A_Q8B32 ? x_scales : nullptr, x_per_slot ? 1 : 0, y, N, K, stream);
+}
+
+const char *qmv_strerror(qmv_status_t status)
+{
+    switch (status) {
+    case QMV_OK: return "success";
+    case QMV_EINVAL: return "invalid argument (null or misaligned pointer, or a size <= 0)";
+    case QMV_EUNSUPPORTED: return "unsupported shape or format (M in [1,4], top_k in [1,16], "
+                                  "K % 32 == 0 and K <= 16384; pairs MXFP4+BF16, CB2+Q8B32, CB3+Q8B32)";
+    case QMV_EHIP: return "the HIP runtime rejected the kernel launch";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,725 @@
+// qmv_device.hpp -- gfx950 device code of the block-quantized GEMV.
+//
+// One kernel family serves every call.  A workgroup (4 wave64s) owns one
+// "work item" (an expert plus up to four activation vectors routed to it) and
+// one tile of consecutive output rows.  Inside a wave, LPR lanes share a row:
+// lane li streams the row's 16-byte-aligned "units" li, li+LPR, ... so each
+// load instruction reads LPR*unit_bytes contiguous bytes of a row, and each
+// lane keeps RT rows in flight.  All weight loads of a segment are issued
+// before any arithmetic (geo-lucebox PR #31, "issue all row loads before any
+// FMA"); activations are staged once per workgroup into LDS in a layout the
+// decode consumes directly (same page, "stage activations in LDS, coalesced +
+// swizzled"), then the lanes' partial sums of a row are combined by a fixed
+// xor butterfly, so results are bitwise reproducible.
+//
+// Units per format (one unit = what a lane decodes per load):
+//   MXFP4  32 weights: 16 B of nibbles + 1 E8M0 byte      (bf16 x, 64 B)
+//   CB2    64 weights: 16 B of 2-bit codes + 2 fp16 scales (int8 x, 64 B)
+//   CB2S   32 weights:  8 B of 2-bit codes + 1 fp16 scale  (int8 x, 32 B)
+//   CB3    32 weights: 12 B of 3-bit codes + 2 fp16 scales (int8 x, 32 B)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmv {
+
+#ifndef QMV_WAVES
+#define QMV_WAVES 4
+#endif
+constexpr int kWaves = QMV_WAVES;        // wave64s per workgroup
+constexpr int kThreads = 64 * kWaves;
+
+enum Kind : int { kMXFP4 = 0, kCB2 = 1, kCB2S = 2, kCB3 = 3 };
+
+// XB: LDS bytes of activations per unit and vector; AB: LDS bytes of
+// per-unit activation side data (scales, sums).
+template <int F> struct Fmt;
+template <> struct Fmt<kMXFP4> { static constexpr int W = 32, XB = 64, AB = 0; };
+template <> struct Fmt<kCB2>   { static constexpr int W = 64, XB = 64, AB = 16; };
+template <> struct Fmt<kCB2S>  { static constexpr int W = 32, XB = 32, AB = 8; };
+template <> struct Fmt<kCB3>   { static constexpr int W = 32, XB = 32, AB = 4; };
+
+struct Args {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const int32_t *ids;      // nullptr for a dense call
+    const uint8_t *x;
+    const uint16_t *xs;      // int8 activation scales (fp16 bits) or nullptr
+    float *y;
+    long long rcb, rsb;      // bytes per row of codes / of scales
+    long long x_vec_bytes;   // bytes per activation vector
+    int E, M, top_k, N, K;
+    int units;               // units per row
+    int x_per_slot;
+    int rows_per_tile;
+    int lds_vec_bytes;       // LDS bytes per staged activation vector
+};
+
+// ------------------------------------------------------------------ helpers
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+struct U3 { uint32_t a, b, c; };
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Shift the two 16-bit halves of v right by s_lo and s_hi (v_pk_lshrrev_b16).
+template <int S_LO, int S_HI>
+__device__ __forceinline__ uint32_t pk_shr(uint32_t v)
+{
+    u16x2 h = __builtin_bit_cast(u16x2, v);
+    const u16x2 s = {(unsigned short)S_LO, (unsigned short)S_HI};
+    return __builtin_bit_cast(uint32_t, h >> s);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t v)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t v)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(v >> 16));
+}
+
+// E8M0 byte -> float 2^(s-127), built exactly: s = 0 is the subnormal
+// 2^-127 and s = 255 is NaN.
+__device__ __forceinline__ float e8m0_f32(uint32_t s)
+{
+    uint32_t bits = s << 23;
+    bits |= (((s + 1u) & 0xFEu) == 0u) ? 0x00400000u : 0u;
+    return __uint_as_float(bits);
+}
+
+// LDS position (in 16-byte chunks) of chunk q of unit u.  The xor keeps the
+// 8 (or 16) lanes that one ds_read_b128 serves on distinct bank groups while
+// they read consecutive units -- the same trick as the query swizzle of
+// Strata PR #1661, fitted to 64- and 32-byte records.
+template <int CH> __device__ __forceinline__ int swz(int u);
+template <> __device__ __forceinline__ int swz<4>(int u) { return (((u >> 1) ^ (u >> 3)) & 1) | ((u >> 1) & 2); }
+template <> __device__ __forceinline__ int swz<2>(int u) { return ((u >> 2) ^ (u >> 3)) & 1; }
+template <int CH> __device__ __forceinline__ int chunk_pos(int u, int q) { return u * CH + (q ^ swz<CH>(u)); }
+
+// ------------------------------------------------------------------ routing
+// A work item: one expert and up to four activation vectors that read it.
+struct Item {
+    int kind;                     // 0: compute, 1: zero rows, -1: nothing to do
+    int expert;
+    int nv;
+    int vec[4];                   // activation vector index (token, or pair)
+    unsigned long long dest[4];   // output rows (pair index bits) of each vector
+};
+
+__device__ __forceinline__ int nth_set_bit(unsigned long long m, int n)
+{
+    for (int i = 0; i < n; ++i) m &= m - 1;
+    return __ffsll((long long)m) - 1;
+}
+
+// Every wave derives the same item list from the ids on its own (no LDS, no
+// barrier).  Pairs p = t*top_k + j live on lanes.  Distinct (expert, vector)
+// entries are grouped per expert in order of first appearance, four vectors
+// per item; out-of-range ids become "zero" items after the real ones.  With
+// M = 1 and broadcast activations this is one item per distinct expert, the
+// unsorted decode schedule of mlxcel issue #2178 (Current Behavior).
+__device__ Item route(const Args &a, int item_idx)
+{
+    Item it;
+    it.kind = -1;
+    it.expert = 0;
+    it.nv = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) { it.vec[m] = 0; it.dest[m] = 0ull; }
+
+    if (a.ids == nullptr) {                       // dense: one item, M vectors
+        if (item_idx == 0) {
+            it.kind = 0;
+            it.nv = a.M;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) { it.vec[m] = m; it.dest[m] = (m < a.M) ? (1ull << m) : 0ull; }
+        }
+        return it;
+    }
+
+    const int lane = threadIdx.x & 63;
+    const int P = a.M * a.top_k;
+    int e = -1;
+    if (lane < P) e = a.ids[lane];
+    const bool valid = lane < P && e >= 0 && e < a.E;
+    const int v = a.x_per_slot ? lane : lane / a.top_k;
+
+    unsigned long long same_e = 0ull, same_ev = 0ull;
+    for (int q = 0; q < P; ++q) {
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        const int vq = a.x_per_slot ? q : q / a.top_k;
+        const bool hit = valid && eq == e;
+        same_e |= hit ? (1ull << q) : 0ull;
+        same_ev |= (hit && vq == v) ? (1ull << q) : 0ull;
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const bool uniq = valid && (same_ev & below) == 0ull;
+    const unsigned long long uniq_mask = __ballot(uniq);
+    const int rank = __popcll(same_e & uniq_mask & below);
+    const bool leader = uniq && (rank & 3) == 0;
+    const unsigned long long leader_mask = __ballot(leader);
+    const unsigned long long inval_mask = __ballot(lane < P && !valid);
+    const int n_real = __popcll(leader_mask);
+    const int n_zero = __popcll(inval_mask);
+
+    if (item_idx < n_real) {
+        const int ll = nth_set_bit(leader_mask, item_idx);
+        const int e_lead = __builtin_amdgcn_readlane(e, ll);
+        const int r_lead = __builtin_amdgcn_readlane(rank, ll);
+        unsigned long long mm = __ballot(uniq && e == e_lead && rank >= r_lead && rank < r_lead + 4);
+        it.kind = 0;
+        it.expert = e_lead;
+        it.nv = __popcll(mm);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            if (m < it.nv) {
+                const int ml = __ffsll((long long)mm) - 1;
+                mm &= mm - 1ull;
+                const int vm = a.x_per_slot ? ml : ml / a.top_k;
+                it.vec[m] = vm;
+                it.dest[m] = __ballot(valid && e == e_lead && v == vm);
+            }
+        }
+    } else if (item_idx < n_real + n_zero) {
+        it.kind = 1;
+        it.dest[0] = 1ull << nth_set_bit(inval_mask, item_idx - n_real);
+    }
+    return it;
+}
+
+// ------------------------------------------------------------------ staging
+// The item's activation vectors are written into LDS in the order each
+// format's decode consumes them.  Staging is split in two so that its global
+// loads can be issued before the weight loads: xload() fetches up to kXReg
+// 16-byte chunks per thread into registers, xstore() writes them to LDS once
+// the weight loads are in flight, and xrest() moves whatever did not fit
+// (large K with several vectors) synchronously.
+constexpr int kXReg = 4;
+
+__device__ __forceinline__ int item_vec(const Item &it, int m)
+{
+    return m == 0 ? it.vec[0] : m == 1 ? it.vec[1] : m == 2 ? it.vec[2] : it.vec[3];
+}
+
+// Staging items: MXFP4 -- one 16-byte chunk of bf16; CB2/CB3 -- one 32-byte
+// block of int8 (two chunks).
+template <int F> struct XItem { static constexpr int chunks = (F == kMXFP4) ? 1 : 2; };
+
+template <int F>
+__device__ __forceinline__ int x_items_per_vec(const Args &a) { return F == kMXFP4 ? 4 * a.units : a.K / 32; }
+
+template <int F>
+__device__ __forceinline__ const uint8_t *x_item_ptr(const Args &a, const Item &it, int i)
+{
+    const int per = x_items_per_vec<F>(a);
+    const int m = i / per;
+    const int c = i - m * per;
+    return a.x + (long long)item_vec(it, m) * a.x_vec_bytes + (long long)c * (16 * XItem<F>::chunks);
+}
+
+template <int F>
+__device__ __forceinline__ void xload(const Args &a, const Item &it, uint4 (&r)[kXReg])
+{
+    constexpr int PER = kXReg / XItem<F>::chunks;          // items held per thread
+    const int T = it.nv * x_items_per_vec<F>(a);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = min((int)threadIdx.x + j * kThreads, T - 1);   // clamped: no branch
+        const uint8_t *p = x_item_ptr<F>(a, it, i);
+        r[j * XItem<F>::chunks] = *(const uint4 *)p;
+        if constexpr (XItem<F>::chunks == 2) r[j * 2 + 1] = *(const uint4 *)(p + 16);
+    }
+}
+
+// 16 int8 activations -> the 4x4 byte transpose that matches the 2-bit
+// selectors (w >> 2j) & 0x03030303: dword j holds x[j], x[4+j], x[8+j], x[12+j].
+__device__ __forceinline__ uint4 cb2_xorder(uint4 in)
+{
+    const uint32_t t0 = perm(in.y, in.x, 0x05010400u);   // x0 x4 x1 x5
+    const uint32_t t1 = perm(in.w, in.z, 0x05010400u);   // x8 x12 x9 x13
+    const uint32_t t2 = perm(in.y, in.x, 0x07030602u);   // x2 x6 x3 x7
+    const uint32_t t3 = perm(in.w, in.z, 0x07030602u);   // x10 x14 x11 x15
+    uint4 o;
+    o.x = perm(t1, t0, 0x05040100u);                      // x0 x4 x8 x12
+    o.y = perm(t1, t0, 0x07060302u);                      // x1 x5 x9 x13
+    o.z = perm(t3, t2, 0x05040100u);                      // x2 x6 x10 x14
+    o.w = perm(t3, t2, 0x07060302u);                      // x3 x7 x11 x15
+    return o;
+}
+
+// 16 int8 activations of a 3-bit half-block -> the orders of the four
+// selector dwords built in cb3_half: (0,8,1,9) (3,11,4,12) (6,14,7,15) (2,5,10,13).
+__device__ __forceinline__ uint4 cb3_xorder(uint4 in)
+{
+    uint4 o;
+    o.x = perm(in.z, in.x, 0x05010400u);                  // x0 x8 x1 x9
+    const uint32_t a = perm(in.z, in.x, 0x07030703u);     // x3 x11 . .
+    const uint32_t b = perm(in.w, in.y, 0x04000400u);     // x4 x12 . .
+    o.y = perm(b, a, 0x05040100u);                        // x3 x11 x4 x12
+    const uint32_t c = perm(in.w, in.y, 0x06020602u);     // x6 x14 . .
+    const uint32_t d = perm(in.w, in.y, 0x07030703u);     // x7 x15 . .
+    o.z = perm(d, c, 0x05040100u);                        // x6 x14 x7 x15
+    const uint32_t e = perm(in.y, in.x, 0x05050502u);     // x2 x5 . .
+    const uint32_t f = perm(in.w, in.z, 0x05050502u);     // x10 x13 . .
+    o.w = perm(f, e, 0x05040100u);                        // x2 x5 x10 x13
+    return o;
+}
+
+__device__ __forceinline__ int sum_i8x16(uint4 v)
+{
+    int s = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, 0, false);
+    s = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, s, false);
+    s = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, s, false);
+    return __builtin_amdgcn_sdot4((int)v.w, 0x01010101, s, false);
+}
+
+// Write staging item i (already in registers) to its LDS place.
+//  MXFP4: chunk c of a vector = bf16 x[8c..8c+7], stored in natural order so
+//         byte b of code dword q pairs with bf16 dword b of chunk q.
+//  CB2:   block b -> chunks 2b, 2b+1 transposed for the 2-bit selectors, and
+//         per-unit side data {0.5*xs, -3*sum(q)} per 32-block (the codebook
+//         is c - 1.5, so a block's integer sum is 2*dot(c, q) - 3*sum(q)).
+//  CB3:   block b -> its two half-blocks in the cb3_half order; side data
+//         0.5*xs per block.
+template <int F>
+__device__ __forceinline__ void xput(const Args &a, const Item &it, uint8_t *lds, int i,
+                                     uint4 lo, uint4 hi)
+{
+    const int per = x_items_per_vec<F>(a);
+    const int m = i / per;
+    const int c = i - m * per;
+    uint8_t *dst = lds + m * a.lds_vec_bytes;
+    if constexpr (F == kMXFP4) {
+        *(uint4 *)(dst + 16 * chunk_pos<4>(c >> 2, c & 3)) = lo;
+    } else {
+        constexpr int CH = Fmt<F>::XB / 16;
+        const int xbytes = a.units * Fmt<F>::XB;
+        const uint16_t xsb = a.xs[(long long)item_vec(it, m) * (a.K / 32) + c];
+        const float xsh = 0.5f * (float)__builtin_bit_cast(_Float16, xsb);
+        if constexpr (F == kCB3) {
+            *(uint4 *)(dst + 16 * chunk_pos<2>(c, 0)) = cb3_xorder(lo);
+            *(uint4 *)(dst + 16 * chunk_pos<2>(c, 1)) = cb3_xorder(hi);
+            ((float *)(dst + xbytes))[c] = xsh;
+        } else {
+            const int c0 = 2 * c, c1 = 2 * c + 1;
+            *(uint4 *)(dst + 16 * chunk_pos<CH>(c0 / CH, c0 % CH)) = cb2_xorder(lo);
+            *(uint4 *)(dst + 16 * chunk_pos<CH>(c1 / CH, c1 % CH)) = cb2_xorder(hi);
+            const int nq = -3 * (sum_i8x16(lo) + sum_i8x16(hi));
+            if constexpr (F == kCB2) {
+                float *side = (float *)(dst + xbytes + 16 * (c >> 1));
+                side[c & 1] = xsh;
+                ((int *)side)[2 + (c & 1)] = nq;
+            } else {
+                float *side = (float *)(dst + xbytes + 8 * c);
+                side[0] = xsh;
+                ((int *)side)[1] = nq;
+            }
+        }
+    }
+}
+
+template <int F>
+__device__ __forceinline__ void xstore(const Args &a, const Item &it, uint8_t *lds, const uint4 (&r)[kXReg])
+{
+    constexpr int CHK = XItem<F>::chunks;
+    constexpr int PER = kXReg / CHK;
+    const int T = it.nv * x_items_per_vec<F>(a);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = (int)threadIdx.x + j * kThreads;
+        if (i < T) xput<F>(a, it, lds, i, r[j * CHK], r[j * CHK + (CHK - 1)]);
+    }
+}
+
+// Items beyond the register budget, loaded and stored directly.  Returns
+// whether there were any (the same answer in every thread).
+template <int F>
+__device__ __forceinline__ bool xrest(const Args &a, const Item &it, uint8_t *lds)
+{
+    constexpr int PER = kXReg / XItem<F>::chunks;
+    const int T = it.nv * x_items_per_vec<F>(a);
+    if (T <= PER * kThreads) return false;
+    for (int i = PER * kThreads + (int)threadIdx.x; i < T; i += kThreads) {
+        const uint8_t *p = x_item_ptr<F>(a, it, i);
+        const uint4 lo = *(const uint4 *)p;
+        const uint4 hi = (XItem<F>::chunks == 2) ? *(const uint4 *)(p + 16) : lo;
+        xput<F>(a, it, lds, i, lo, hi);
+    }
+    return true;
+}
+
+// ------------------------------------------------------------------ units
+template <int F> struct Unit;
+template <> struct Unit<kMXFP4> { uint4 c; uint32_t s; };
+template <> struct Unit<kCB2>   { uint4 c; uint32_t s; };
+template <> struct Unit<kCB2S>  { uint2 c; uint32_t s; };
+template <> struct Unit<kCB3>   { U3 c; uint32_t s; };
+
+template <int F>
+__device__ __forceinline__ void load_unit(Unit<F> &w, const uint8_t *crow, const uint8_t *srow, int u)
+{
+    if constexpr (F == kMXFP4) {
+        w.c = *(const uint4 *)(crow + 16 * (long long)u);
+        w.s = srow[u];
+    } else if constexpr (F == kCB2) {
+        w.c = *(const uint4 *)(crow + 16 * (long long)u);
+        w.s = *(const uint32_t *)(srow + 4 * (long long)u);
+    } else if constexpr (F == kCB2S) {
+        w.c = *(const uint2 *)(crow + 8 * (long long)u);
+        w.s = *(const uint16_t *)(srow + 2 * (long long)u);
+    } else {
+        __builtin_memcpy(&w.c, __builtin_assume_aligned(crow + 12 * (long long)u, 4), 12);
+        w.s = *(const uint32_t *)(srow + 4 * (long long)u);
+    }
+}
+
+// ------------------------------------------------------------------ MAC per unit
+// Each mac_* adds the unit's contribution for RT rows and NV vectors.
+
+// MXFP4 x bf16: e2m1 -> bf16 pairs in hardware (v_cvt_scalef32_pk_bf16_fp4,
+// scale 1 so every value is exact), bf16 dot2 into two f32 chains per group,
+// then one fma with the exact E8M0 scale.
+template <int RT, int NV>
+__device__ __forceinline__ void mac_mxfp4(const Unit<kMXFP4> (&w)[RT], const uint8_t *lds,
+                                          int vec_bytes, int u, float (&acc)[RT][NV])
+{
+    uint4 xq[NV][4];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xq[v][q] = *(const uint4 *)(lds + v * vec_bytes + 16 * chunk_pos<4>(u, q));
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const uint32_t cw[4] = {w[r].c.x, w[r].c.y, w[r].c.z, w[r].c.w};
+        bf16x2 wv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            wv[4 * q + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], 1.0f, 0);
+            wv[4 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], 1.0f, 1);
+            wv[4 * q + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], 1.0f, 2);
+            wv[4 * q + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], 1.0f, 3);
+        }
+        const float sc = e8m0_f32(w[r].s);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t xd[4] = {xq[v][q].x, xq[v][q].y, xq[v][q].z, xq[v][q].w};
+                d0 = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * q + 0], __builtin_bit_cast(bf16x2, xd[0]), d0, false);
+                d1 = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * q + 1], __builtin_bit_cast(bf16x2, xd[1]), d1, false);
+                d0 = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * q + 2], __builtin_bit_cast(bf16x2, xd[2]), d0, false);
+                d1 = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * q + 3], __builtin_bit_cast(bf16x2, xd[3]), d1, false);
+            }
+            acc[r][v] = __builtin_fmaf(d0 + d1, sc, acc[r][v]);
+        }
+    }
+}
+
+// CB2 x int8: selectors (w >> 2j) & 0x03030303 hold raw codes; v_dot4 with
+// the transposed activations gives dot(c, q) exactly in int32, and the
+// block's integer sum is 2*dot + (-3*sum q).
+template <int F, int RT, int NV>
+__device__ __forceinline__ void mac_cb2(const Unit<F> (&w)[RT], const uint8_t *lds,
+                                        int vec_bytes, int xbytes, int u, float (&acc)[RT][NV])
+{
+    constexpr int NB = (F == kCB2) ? 2 : 1;      // 32-blocks per unit
+    constexpr int CH = 2 * NB;                   // 16-byte chunks per unit
+    uint4 xq[NV][CH];
+    float xsh[NV][NB];
+    int nq[NV][NB];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const uint8_t *base = lds + v * vec_bytes;
+#pragma unroll
+        for (int q = 0; q < CH; ++q)
+            xq[v][q] = *(const uint4 *)(base + 16 * chunk_pos<CH>(u, q));
+        if constexpr (NB == 2) {
+            const uint4 sd = *(const uint4 *)(base + xbytes + 16 * u);
+            xsh[v][0] = __uint_as_float(sd.x);
+            xsh[v][1] = __uint_as_float(sd.y);
+            nq[v][0] = (int)sd.z;
+            nq[v][1] = (int)sd.w;
+        } else {
+            const uint2 sd = *(const uint2 *)(base + xbytes + 8 * u);
+            xsh[v][0] = __uint_as_float(sd.x);
+            nq[v][0] = (int)sd.y;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        uint32_t cw[CH];
+        if constexpr (NB == 2) { cw[0] = w[r].c.x; cw[1] = w[r].c.y; cw[2] = w[r].c.z; cw[3] = w[r].c.w; }
+        else { cw[0] = w[r].c.x; cw[1] = w[r].c.y; }
+        uint32_t sel[CH][4];
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            sel[q][0] = cw[q] & 0x03030303u;
+            sel[q][1] = (cw[q] >> 2) & 0x03030303u;
+            sel[q][2] = (cw[q] >> 4) & 0x03030303u;
+            sel[q][3] = (cw[q] >> 6) & 0x03030303u;
+        }
+        float ws[NB];
+        ws[0] = f16_lo(w[r].s);
+        if constexpr (NB == 2) ws[1] = f16_hi(w[r].s);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint4 x0 = xq[v][2 * b], x1 = xq[v][2 * b + 1];
+                int d0 = __builtin_amdgcn_sdot4((int)sel[2 * b][0], (int)x0.x, 0, false);
+                int d1 = __builtin_amdgcn_sdot4((int)sel[2 * b + 1][0], (int)x1.x, 0, false);
+                d0 = __builtin_amdgcn_sdot4((int)sel[2 * b][1], (int)x0.y, d0, false);
+                d1 = __builtin_amdgcn_sdot4((int)sel[2 * b + 1][1], (int)x1.y, d1, false);
+                d0 = __builtin_amdgcn_sdot4((int)sel[2 * b][2], (int)x0.z, d0, false);
+                d1 = __builtin_amdgcn_sdot4((int)sel[2 * b + 1][2], (int)x1.z, d1, false);
+                d0 = __builtin_amdgcn_sdot4((int)sel[2 * b][3], (int)x0.w, d0, false);
+                d1 = __builtin_amdgcn_sdot4((int)sel[2 * b + 1][3], (int)x1.w, d1, false);
+                const int S = 2 * (d0 + d1) + nq[v][b];
+                acc[r][v] = __builtin_fmaf((float)S, ws[b] * xsh[v][b], acc[r][v]);
+            }
+        }
+    }
+}
+
+// CB3 x int8: the 16 codes of a half-block (two 24-bit triples A, B) become
+// four selector dwords with one byte permute of the code bytes, one packed
+// 16-bit shift and a mask each (straddling codes take two); a byte-permute
+// lookup of {0,1,2,4,-6,-1,-2,-4} (twice the codebook) turns selectors into
+// int8 values (lucebox-hub PR #21, Changes 'fp3' item 1: v_perm_b32 over an
+// 8-byte LUT), and v_dot4 sums them exactly per half-block.
+constexpr uint32_t kCb3LutLo = 0x04020100u;   // codes 0..3 -> 0, 1, 2, 4
+constexpr uint32_t kCb3LutHi = 0xFCFEFFFAu;   // codes 4..7 -> -6, -1, -2, -4
+
+template <int OFF>   // byte offset of triple A inside the (hi:lo) dword pair
+__device__ __forceinline__ int cb3_half(uint32_t hi, uint32_t lo, uint4 x)
+{
+    constexpr uint32_t A0 = OFF, A1 = OFF + 1, A2 = OFF + 2, B0 = OFF + 3, B1 = OFF + 4, B2 = OFF + 5;
+    const uint32_t q0 = perm(hi, lo, A0 | (B0 << 8) | (A0 << 16) | (B0 << 24));
+    const uint32_t q1 = perm(hi, lo, A1 | (B1 << 8) | (A1 << 16) | (B1 << 24));
+    const uint32_t q2 = perm(hi, lo, A2 | (B2 << 8) | (A2 << 16) | (B2 << 24));
+    const uint32_t q3 = perm(hi, lo, A0 | (A1 << 8) | (B0 << 16) | (B1 << 24));
+    const uint32_t q4 = perm(hi, lo, A1 | (A2 << 8) | (B1 << 16) | (B2 << 24));
+    const uint32_t s0 = pk_shr<0, 3>(q0) & 0x07070707u;            // codes 0 8 1 9
+    const uint32_t s1 = pk_shr<1, 4>(q1) & 0x07070707u;            // codes 3 11 4 12
+    const uint32_t s2 = pk_shr<2, 5>(q2) & 0x07070707u;            // codes 6 14 7 15
+    const uint32_t s3 = (pk_shr<6, 6>(q3) & 0x00070007u) |
+                        ((pk_shr<7, 7>(q4) & 0x00070007u) << 8);   // codes 2 5 10 13
+    int d = __builtin_amdgcn_sdot4((int)perm(kCb3LutHi, kCb3LutLo, s0), (int)x.x, 0, false);
+    d = __builtin_amdgcn_sdot4((int)perm(kCb3LutHi, kCb3LutLo, s1), (int)x.y, d, false);
+    d = __builtin_amdgcn_sdot4((int)perm(kCb3LutHi, kCb3LutLo, s2), (int)x.z, d, false);
+    return __builtin_amdgcn_sdot4((int)perm(kCb3LutHi, kCb3LutLo, s3), (int)x.w, d, false);
+}
+
+template <int RT, int NV>
+__device__ __forceinline__ void mac_cb3(const Unit<kCB3> (&w)[RT], const uint8_t *lds,
+                                        int vec_bytes, int xbytes, int u, float (&acc)[RT][NV])
+{
+    uint4 xq[NV][2];
+    float xsh[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const uint8_t *base = lds + v * vec_bytes;
+        xq[v][0] = *(const uint4 *)(base + 16 * chunk_pos<2>(u, 0));
+        xq[v][1] = *(const uint4 *)(base + 16 * chunk_pos<2>(u, 1));
+        xsh[v] = ((const float *)(base + xbytes))[u];
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const float ws0 = f16_lo(w[r].s), ws1 = f16_hi(w[r].s);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int S0 = cb3_half<0>(w[r].c.b, w[r].c.a, xq[v][0]);
+            const int S1 = cb3_half<2>(w[r].c.c, w[r].c.b, xq[v][1]);
+            const float t = __builtin_fmaf(ws1, (float)S1, ws0 * (float)S0);
+            acc[r][v] = __builtin_fmaf(t, xsh[v], acc[r][v]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ row body
+// Sum a value over the LPR lanes of a row (lane groups aligned to LPR) with a
+// fixed butterfly: DPP quad permutes and row mirrors within 16 lanes,
+// ds_swizzle across 16, readlane across 32.  After each step every lane of a
+// group holds the same bits (a + b == b + a), so the result is reproducible.
+template <int CTRL>
+__device__ __forceinline__ float dpp_step(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v = dpp_step<0xB1>(v);                          // quad_perm [1,0,3,2]
+    v = dpp_step<0x4E>(v);                          // quad_perm [2,3,0,1]
+    v = dpp_step<0x141>(v);                         // row_half_mirror
+    if constexpr (LPR >= 16) v = dpp_step<0x140>(v);  // row_mirror
+    if constexpr (LPR >= 32)
+        v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // lane ^ 16
+    if constexpr (LPR >= 64)
+        v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    return v;
+}
+
+template <int F, int LPR, int CPL, int RT>
+__device__ __forceinline__ void load_seg(Unit<F> (&w)[CPL][RT], const uint8_t *const (&crows)[RT],
+                                         const uint8_t *const (&srows)[RT], int ubase, int U)
+{
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int u = min(ubase + c * LPR, U - 1);   // past the row end: reload the last unit
+#pragma unroll
+        for (int r = 0; r < RT; ++r) load_unit<F>(w[c][r], crows[r], srows[r], u);
+    }
+}
+
+template <int F, int LPR, int CPL, int RT, int NV>
+__device__ __forceinline__ void mac_seg(const Unit<F> (&w)[CPL][RT], const Args &a, const uint8_t *lds,
+                                        int ubase, int U, float (&acc)[RT][NV])
+{
+    const int xbytes = U * Fmt<F>::XB;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int u = ubase + c * LPR;
+        if (u < U) {
+            if constexpr (F == kMXFP4) mac_mxfp4<RT, NV>(w[c], lds, a.lds_vec_bytes, u, acc);
+            else if constexpr (F == kCB3) mac_cb3<RT, NV>(w[c], lds, a.lds_vec_bytes, xbytes, u, acc);
+            else mac_cb2<F, RT, NV>(w[c], lds, a.lds_vec_bytes, xbytes, u, acc);
+        }
+    }
+}
+
+// One workgroup, one item, one tile of rows.  Order of work per lane:
+//   1. activation staging loads (registers)
+//   2. all weight loads of the first segment (CPL units x RT rows)
+//   3. activations to LDS, barrier (waits only for the staging loads)
+//   4. per unit, as its bytes arrive: decode and dot (progressive vmcnt)
+//   5. further segments when K needs them; butterfly; store.
+template <int F, int LPR, int CPL, int RT, int NV>
+__device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t *lds, int row_base)
+{
+    constexpr int SLOTS = 64 / LPR;
+    constexpr int SEG = LPR * CPL;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int slot = lane / LPR;
+    const int li = lane % LPR;
+    const int row0 = row_base + (wave * SLOTS + slot) * RT;
+    const int U = a.units;
+    const long long eoff = (long long)it.expert * a.N;
+    const uint8_t *crows[RT];
+    const uint8_t *srows[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const long long row = eoff + min(row0 + r, a.N - 1);   // rows past N: reread the last row
+        crows[r] = a.codes + row * a.rcb;
+        srows[r] = a.scales + row * a.rsb;
+    }
+
+    uint4 xr[kXReg];
+    xload<F>(a, it, xr);
+    Unit<F> w[CPL][RT];
+    load_seg<F, LPR, CPL, RT>(w, crows, srows, li, U);
+    xstore<F>(a, it, lds, xr);
+    __syncthreads();
+    if (xrest<F>(a, it, lds)) __syncthreads();
+
+    float acc[RT][NV];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[r][v] = 0.0f;
+
+    const int nseg = (U + SEG - 1) / SEG;
+    for (int seg = 0;;) {
+        mac_seg<F, LPR, CPL, RT, NV>(w, a, lds, seg * SEG + li, U, acc);
+        if (++seg >= nseg) break;
+        load_seg<F, LPR, CPL, RT>(w, crows, srows, seg * SEG + li, U);
+    }
+
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[r][v] = group_sum<LPR>(acc[r][v]);
+
+    // Lane li < RT stores row row0 + li for every vector and destination.
+    if (li < RT) {
+        const int n = row0 + li;
+        if (n < a.N) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float val = acc[0][v];
+#pragma unroll
+                for (int r = 1; r < RT; ++r) val = (li == r) ? acc[r][v] : val;
+                unsigned long long d = it.dest[v];
+                while (d) {
+                    const int p = __ffsll((long long)d) - 1;
+                    d &= d - 1ull;
+                    a.y[(long long)p * a.N + n] = val;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ kernel
+// F: format kind; LPR: lanes per row; CPL: units per lane and row in flight;
+// RT: rows per lane; NVMAX: most activation vectors one item may carry.
+template <int F, int LPR, int CPL, int RT, int NVMAX>
+__global__ __launch_bounds__(kThreads) void qmv_kernel(const Args a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const Item it = route(a, blockIdx.y);
+    if (it.kind < 0) return;
+    const int row_base = blockIdx.x * a.rows_per_tile;
+    if (it.kind == 1) {
+        const int p = __ffsll((long long)it.dest[0]) - 1;
+        const int end = min(a.N, row_base + a.rows_per_tile);
+        for (int n = row_base + threadIdx.x; n < end; n += kThreads)
+            a.y[(long long)p * a.N + n] = 0.0f;
+        return;
+    }
+    switch (it.nv) {
+    case 1: rows_body<F, LPR, CPL, RT, 1>(a, it, lds, row_base); break;
+    case 2: if constexpr (NVMAX >= 2) rows_body<F, LPR, CPL, RT, 2>(a, it, lds, row_base); break;
+    case 3: if constexpr (NVMAX >= 3) rows_body<F, LPR, CPL, RT, 3>(a, it, lds, row_base); break;
+    default: if constexpr (NVMAX >= 4) rows_body<F, LPR, CPL, RT, 4>(a, it, lds, row_base); break;
+    }
+}
+
+// Kernel menus.  Variant 0: one vector per item, 2 rows per lane.  Variant 1:
+// up to four vectors per item (gather with M > 1 or per-slot activations),
+// 2 rows per lane.  Variant 2: dense with M > 1, 4 rows per lane.
+constexpr int kMenuLpr[4] = {8, 16, 32, 64};
+constexpr int kMenuCpl01[5] = {1, 2, 3, 4, 7};
+constexpr int kMenuCpl2[3] = {1, 2, 4};
+
+// Kernel tables, one per format kind (qmv_k_*.hip): [variant][lpr][cpl].
+extern const void *const kTable_mxfp4[3][4][5];
+extern const void *const kTable_cb2[3][4][5];
+extern const void *const kTable_cb2s[3][4][5];
+extern const void *const kTable_cb3[3][4][5];
+
+}  // namespace qmv
+
+// Instantiate one format's kernel table: [variant][lpr index][cpl index].
+#define QMV_K(F, V, L, C) \
+    (const void *)&::qmv::qmv_kernel<F, L, C, (V == 2 ? 4 : 2), (V == 0 ? 1 : 4)>
+#define QMV_ROW01(F, V, L) \
+    { QMV_K(F, V, L, 1), QMV_K(F, V, L, 2), QMV_K(F, V, L, 3), QMV_K(F, V, L, 4), QMV_K(F, V, L, 7) }
+#define QMV_ROW2(F, L) \
+    { QMV_K(F, 2, L, 1), QMV_K(F, 2, L, 2), QMV_K(F, 2, L, 4), nullptr, nullptr }
+#define QMV_TABLE(F) \
+    { { QMV_ROW01(F, 0, 8), QMV_ROW01(F, 0, 16), QMV_ROW01(F, 0, 32), QMV_ROW01(F, 0, 64) }, \
+      { QMV_ROW01(F, 1, 8), QMV_ROW01(F, 1, 16), QMV_ROW01(F, 1, 32), QMV_ROW01(F, 1, 64) }, \
+      { { nullptr, nullptr, nullptr, nullptr, nullptr }, QMV_ROW2(F, 16), QMV_ROW2(F, 32), QMV_ROW2(F, 64) } }

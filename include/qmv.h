@@ -1,0 +1,133 @@
+/*
+ * qmv.h -- C ABI of libqmv.so: block-quantized GEMV for MoE expert
+ * projections on AMD Instinct MI355X (gfx950), batch 1 to 4 tokens.
+ *
+ * The library computes, for every output it is asked for,
+ *
+ *     y = sum_k  w(k) * x(k)
+ *
+ * where w is a dequantized weight (code value times its block scale) and x a
+ * dequantized activation.  The operation is the expert-gathered matrix-vector
+ * product that MoE decode spends its time in: mlxcel issue #2178 "add an
+ * mxfp4 arm to the warp-shared gather_qmv kernel for gpt-oss decode"
+ * (Problem / Background and Proposed Solution), lucebox-hub PR #21
+ * "optimize ROCMFPX fp3/fp2 MMVQ on RDNA" (Changes) and geo-lucebox PR #31
+ * "DS4 H200: rocmfp2_mix MoE matvec 3.31x" (Why this kernel).
+ *
+ * ------------------------------------------------------------------ formats
+ * Weights are row-major and planar: per expert, N rows of K weights; codes and
+ * scales are separate arrays.  A dense call has no expert dimension.
+ *
+ *   QMV_W_MXFP4  codes  uint8 [E][N][K/2]   two e2m1 nibbles per byte; weight
+ *                                            k is the low nibble of byte k/2
+ *                                            when k is even, the high nibble
+ *                                            when k is odd.
+ *                scales uint8 [E][N][K/32]  E8M0: byte s means 2^(s-127),
+ *                                            s = 255 is NaN.
+ *                (mlxcel issue #2178: w_row[k/2], group k/32, E8M0 uint8
+ *                scales.)
+ *   QMV_W_CB2    codes  uint8 [E][N][K/4]   2-bit codes, weight k in bits
+ *                                            2(k%4)..2(k%4)+1 of byte k/4;
+ *                                            code c means c - 1.5, i.e. the
+ *                                            codebook {-1.5,-0.5,0.5,1.5}.
+ *                scales fp16  [E][N][K/32]  one scale per 32 weights.
+ *   QMV_W_CB3    codes  uint8 [E][N][3K/8]  3-bit codes in one little-endian
+ *                                            bit stream per row: weight k is
+ *                                            stream bits 3k..3k+2 (bit 3k least
+ *                                            significant; stream bit b is bit
+ *                                            b%8 of byte b/8).  Code c means
+ *                                            {0,.5,1,2,-3,-.5,-1,-2}[c].
+ *                scales fp16  [E][N][K/16]  one scale per 16-weight
+ *                                            half-block.
+ *                (lucebox-hub PR #21: the fp2 {-1,0,1,2} and fp3
+ *                {0,1,2,4,0,-1,-2,-4} tables and the half-block scale split;
+ *                these codebooks are those tables minus 0.5, and times 0.5
+ *                with the second zero taken as -3.)
+ *
+ * Activations:
+ *   QMV_A_BF16   x   bf16 [V][K], x_scales unused (pass NULL).
+ *   QMV_A_Q8B32  x   int8 [V][K] with x_scales fp16 [V][K/32]: activation k
+ *                    is x[k] * x_scales[k/32] (the q8_1 blocks of lucebox-hub
+ *                    PR #21).  A 3-bit half-block uses the scale of the
+ *                    32-block that contains it.
+ * Supported pairs: (MXFP4, BF16), (CB2, Q8B32), (CB3, Q8B32).
+ *
+ * ------------------------------------------------------------- conventions
+ * Ownership: every pointer is a device pointer owned by the caller.  The
+ * library never allocates, frees, copies to the host or synchronizes; a call
+ * only enqueues kernels on `stream` and returns.  It reads only the extents
+ * above and writes only y.  It is stateless and may be called concurrently
+ * from several host threads.
+ *
+ * Alignment: codes 16 bytes (8 for CB2 when K % 64 != 0), x 16 bytes,
+ * scales, x_scales, expert ids and y 4 bytes.
+ *
+ * Limits: 1 <= M <= 4, 1 <= top_k <= 16, K % 32 == 0, 32 <= K <= 16384,
+ * N >= 1, E >= 1.
+ *
+ * Errors: arguments are checked on the host before anything is launched; on
+ * a failed check the call returns the status, launches nothing and leaves y
+ * untouched.  No check needs a device synchronization.  An expert id outside
+ * [0, E) is not an error: that (token, slot) output row is written with
+ * zeros (mlxcel issue #2178, Implementation Notes, Edge cases).
+ *
+ * Determinism: results are bitwise identical from run to run (fixed
+ * reduction order, no atomics).
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { QMV_W_MXFP4 = 0, QMV_W_CB2 = 1, QMV_W_CB3 = 2 } qmv_wfmt_t;
+typedef enum { QMV_A_BF16 = 0, QMV_A_Q8B32 = 1 } qmv_afmt_t;
+
+typedef enum {
+    QMV_OK = 0,
+    QMV_EINVAL = 1,        /* null or misaligned pointer, size <= 0 */
+    QMV_EUNSUPPORTED = 2,  /* M, top_k or K out of range; unsupported format pair */
+    QMV_EHIP = 3           /* the HIP runtime refused the launch */
+} qmv_status_t;
+
+/*
+ * Dense GEMV: y[m][n] = sum_k w(n, k) * x(m, k) for m < M, n < N.
+ *   w_codes, w_scales  one weight matrix, layouts above with E omitted
+ *   x, x_scales        M activation vectors ([M][K], [M][K/32])
+ *   y                  fp32 [M][N]
+ * This is the gather below with one expert, top_k = 1 and ids all 0.
+ */
+qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
+                       qmv_afmt_t afmt, const void *x, const void *x_scales,
+                       float *y, int M, int N, int K, hipStream_t stream);
+
+/*
+ * Expert-gathered GEMV (MoE decode):
+ *   y[t][j][n] = sum_k w(e, n, k) * x(t, j, k)     e = expert_ids[t][j]
+ *   y[t][j][n] = 0                                  if e is outside [0, E)
+ * for t < M tokens, j < top_k slots and n < N rows.
+ *   expert_ids  int32 [M][top_k] in device memory
+ *   x_per_slot  0: x is [M][K] and token t's vector feeds all its slots;
+ *               1: x is [M][top_k][K], one vector per (token, slot), as for a
+ *                  down projection whose input differs per expert.
+ *   y           fp32 [M][top_k][N]
+ * Each distinct expert's weights are streamed from memory once per call and
+ * applied to every activation vector routed to it (up to four per pass).
+ */
+qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales, int E,
+                            const int32_t *expert_ids, int M, int top_k,
+                            qmv_afmt_t afmt, const void *x, const void *x_scales,
+                            int x_per_slot, float *y, int N, int K, hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char *qmv_strerror(qmv_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

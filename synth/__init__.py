@@ -143,10 +143,11 @@ def gen_scales(rng, wfmt, E, N, K, e8m0=(122, 132)):
 
 
 def gen_ids(rng, M, top_k, E):
-    """Top-k ids: distinct within a token, independent across tokens."""
+    """Top-k ids: distinct within a token (repeats only when top_k > E),
+    independent across tokens."""
     ids = np.empty((M, top_k), np.int32)
     for t in range(M):
-        ids[t] = rng.choice(E, size=top_k, replace=False)
+        ids[t] = rng.choice(E, size=top_k, replace=top_k > E)
     return ids
 
 
