@@ -41,6 +41,35 @@ HEADLINE = "C2"
 METRIC = "effective weight GB/s and µs/call per expert-gather GEMV; % of HBM peak"
 
 
+def kernel_source_hash():
+    """sha256[:16] over the kernel sources (names and bytes, sorted)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "bit_block_quantized_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(name):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE
+    (profiles/qmv_traffic_pmc.md), or None if the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "qmv_traffic_pmc.md")
+    try:
+        with open(path) as f:
+            txt = f.read()
+    except OSError:
+        return None
+    vals = dict(line.strip().split(": ", 1) for line in txt.splitlines()
+                if line.strip().startswith("traffic_") and ": " in line)
+    if vals.get("traffic_source_sha256_16") != kernel_source_hash():
+        return None
+    v = vals.get(f"traffic_bytes_per_launch_{name}")
+    return float(v) if v else None
+
+
 def host_cores():
     try:
         return len(os.sched_getaffinity(0))
@@ -250,6 +279,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-hot", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library is a single-GPU operator "
@@ -268,7 +298,8 @@ def main():
             extra[name] = r
             del pe
             torch.cuda.empty_cache()
-    _, hot = measure(HEADLINE, min(args.steps, 500), 10, rotate=False)
+    hot = {"us_per_call": float("nan")} if args.no_hot else \
+        measure(HEADLINE, min(args.steps, 500), 10, rotate=False)[1]
 
     t = head["us_per_call"] * 1e-6
     out = {
@@ -301,8 +332,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(head["algorithmic_bytes_per_call"] / t / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "qmv::qmv_kernel<0, 32, 2, 1> (MXFP4, 32 lanes per row, 2 rows in flight)",
+            "traffic": profiled_traffic(HEADLINE),
+            "kernel": "qmv::qmv_kernel, MXFP4 one-vector gather instantiation the launcher picks for K=N=2880",
             "algorithmic_bytes_per_launch": head["algorithmic_bytes_per_call"],
         },
         "workloads": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}

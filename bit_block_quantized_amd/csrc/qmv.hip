@@ -64,40 +64,62 @@ qmv_status_t validate(int wfmt, const void *codes, const void *scales, long long
         (wfmt != QMV_W_MXFP4 && !aligned(scales, 4)) || (xs && !aligned(xs, 4)) ||
         (ids && !aligned(ids, 4)))
         return QMV_EINVAL;
-    // keep every byte offset comfortably inside int64
+    // in-expert row offsets and output indices are 32-bit on the device
     const long long per_expert = (long long)N * row_code_bytes(wfmt, K);
-    if (per_expert > 0 && E > (1LL << 62) / per_expert)
+    if (N >= (1 << 24) || per_expert >= (1LL << 31) || (long long)M * top_k * N >= (1LL << 31))
+        return QMV_EUNSUPPORTED;
+    if (E > (1LL << 62) / per_expert)
         return QMV_EUNSUPPORTED;
     return QMV_OK;
 }
 
-// Launch shape for a row of `units` units: the (lanes per row, units per
-// lane) pair from the variant's menu that pads the row least, then needs the
-// fewest segments, then uses the most lanes per row.
+// Launch shape: lanes per row (LPR) and units per lane step (CPL) from the
+// variant's menu.  Measured on MI355X over the C2..C5 shapes: the kernel is
+// fastest with 8 to 14 waves per CU in total (enough to cover memory latency,
+// few enough that per-wave set-up stays small), with few lane slots wasted on
+// the row's padding, and with as many units in flight per lane as possible.
+// So: keep shapes within 85% of the best lane efficiency, prefer total waves
+// in [8, 14] x 256 (else the nearest), then the larger CPL, then more waves.
 struct Shape { int li, ci, lpr, cpl; };
 
-Shape pick_shape(int variant, int units)
+Shape pick_shape(int variant, int units, long long rows_total, int rt)
 {
-    Shape best = {0, 0, 0, 0};
-    long long best_key[3] = {-1, -1, -1};
     const int ncpl = variant == 2 ? 3 : 5;
-    for (int li = 0; li < 4; ++li) {
-        const int lpr = kMenuLpr[li];
-        if (variant == 2 && lpr == 8) continue;
+    double best_eff = 0.0;
+    for (int li = 0; li < 4; ++li)
         for (int ci = 0; ci < ncpl; ++ci) {
+            const int lpr = kMenuLpr[li];
+            if (variant == 2 && lpr == 8) continue;
             const int cpl = variant == 2 ? kMenuCpl2[ci] : kMenuCpl01[ci];
             const long long seg = (long long)lpr * cpl;
-            const long long nseg = (units + seg - 1) / seg;
-            const long long key[3] = {nseg * seg, nseg, -lpr};
-            const bool better = best_key[0] < 0 || key[0] < best_key[0] ||
-                                (key[0] == best_key[0] && (key[1] < best_key[1] ||
-                                 (key[1] == best_key[1] && key[2] < best_key[2])));
+            const double eff = (double)units / (double)(((units + seg - 1) / seg) * seg);
+            if (eff > best_eff) best_eff = eff;
+        }
+    const long long lo = 8LL * 256, hi = 14LL * 256;
+    Shape best = {0, 0, 0, 0};
+    long long best_key[3] = {-1, -1, -1};
+    for (int li = 0; li < 4; ++li)
+        for (int ci = 0; ci < ncpl; ++ci) {
+            const int lpr = kMenuLpr[li];
+            if (variant == 2 && lpr == 8) continue;
+            const int cpl = variant == 2 ? kMenuCpl2[ci] : kMenuCpl01[ci];
+            const long long seg = (long long)lpr * cpl;
+            const double eff = (double)units / (double)(((units + seg - 1) / seg) * seg);
+            if (eff < 0.85 * best_eff) continue;
+            const long long rows_per_wave = (64 / lpr) * rt;
+            const long long waves = (rows_total + rows_per_wave - 1) / rows_per_wave;
+            const long long miss = waves < lo ? lo - waves : waves > hi ? waves - hi : 0;
+            const long long key[3] = {-miss, cpl, waves};      // larger is better
+            bool better = best_key[0] == -1 && best_key[1] == -1;
+            for (int k = 0; k < 3 && !better; ++k) {
+                if (key[k] > best_key[k]) { better = true; break; }
+                if (key[k] < best_key[k]) break;
+            }
             if (better) {
                 best = {li, ci, lpr, cpl};
                 for (int k = 0; k < 3; ++k) best_key[k] = key[k];
             }
         }
-    }
     return best;
 }
 
@@ -117,7 +139,8 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, int E, cons
     else if (gather)    { variant = 1; rt = 2; }
     else                { variant = 2; rt = 4; }
     const int nvmax = variant == 0 ? 1 : 4;
-    const Shape sh = pick_shape(variant, units);
+    const long long rows_total = (long long)N * (gather ? M * top_k : 1);
+    const Shape sh = pick_shape(variant, units, rows_total, rt);
     Args a;
     a.codes = (const uint8_t *)codes;
     a.scales = (const uint8_t *)scales;
@@ -125,9 +148,11 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, int E, cons
     a.x = (const uint8_t *)x;
     a.xs = (const uint16_t *)xs;
     a.y = y;
-    a.rcb = row_code_bytes(wfmt, K);
-    a.rsb = row_scale_bytes(wfmt, K);
-    a.x_vec_bytes = (wfmt == QMV_W_MXFP4) ? 2LL * K : (long long)K;
+    a.rcb = (int)row_code_bytes(wfmt, K);
+    a.rsb = (int)row_scale_bytes(wfmt, K);
+    a.expert_cb = (long long)N * a.rcb;
+    a.expert_sb = (long long)N * a.rsb;
+    a.x_vec_bytes = (wfmt == QMV_W_MXFP4) ? 2 * K : K;
     a.E = gather ? E : 1;
     a.M = M;
     a.top_k = gather ? top_k : 1;
@@ -135,6 +160,7 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, int E, cons
     a.K = K;
     a.units = units;
     a.x_per_slot = gather ? x_per_slot : 0;
+    a.x_early = (!gather || (M == 1 && !x_per_slot)) ? 1 : 0;
     a.rows_per_tile = kWaves * (64 / sh.lpr) * rt;
     const int vec_bytes = units * (kUnitXB[kind] + kUnitAB[kind]);
     a.lds_vec_bytes = (vec_bytes + 15) & ~15;

@@ -47,11 +47,14 @@ struct Args {
     const uint8_t *x;
     const uint16_t *xs;      // int8 activation scales (fp16 bits) or nullptr
     float *y;
-    long long rcb, rsb;      // bytes per row of codes / of scales
-    long long x_vec_bytes;   // bytes per activation vector
+    long long expert_cb;     // bytes of codes per expert (N * rcb)
+    long long expert_sb;     // bytes of scales per expert (N * rsb)
+    int rcb, rsb;            // bytes per row of codes / of scales (N * rcb < 2^31)
+    int x_vec_bytes;         // bytes per activation vector
     int E, M, top_k, N, K;
     int units;               // units per row
     int x_per_slot;
+    int x_early;             // activation vectors known before routing
     int rows_per_tile;
     int lds_vec_bytes;       // LDS bytes per staged activation vector
 };
@@ -60,7 +63,6 @@ struct Args {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-struct U3 { uint32_t a, b, c; };
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 {
@@ -103,6 +105,16 @@ template <> __device__ __forceinline__ int swz<4>(int u) { return (((u >> 1) ^ (
 template <> __device__ __forceinline__ int swz<2>(int u) { return ((u >> 2) ^ (u >> 3)) & 1; }
 template <int CH> __device__ __forceinline__ int chunk_pos(int u, int q) { return u * CH + (q ^ swz<CH>(u)); }
 
+// Chunk position of unit u0 + c * LPR.  The swizzle reads bits 1..3 of the
+// unit index only, so for LPR >= 16 a lane's units share it and the position
+// advances by a constant (an immediate LDS offset) from one unit to the next.
+template <int CH, int LPR>
+__device__ __forceinline__ int chunk_at(int u0, int c, int q)
+{
+    if constexpr (LPR >= 16) return chunk_pos<CH>(u0, q) + c * LPR * CH;
+    else return chunk_pos<CH>(u0 + c * LPR, q);
+}
+
 // ------------------------------------------------------------------ routing
 // A work item: one expert and up to four activation vectors that read it.
 struct Item {
@@ -113,10 +125,66 @@ struct Item {
     unsigned long long dest[4];   // output rows (pair index bits) of each vector
 };
 
+// Token of pair p (M <= 4 tokens of k slots each), without a division.
+__device__ __forceinline__ int token_of(int p, int k)
+{
+    return (p >= k) + (p >= 2 * k) + (p >= 3 * k);
+}
+
 __device__ __forceinline__ int nth_set_bit(unsigned long long m, int n)
 {
     for (int i = 0; i < n; ++i) m &= m - 1;
     return __ffsll((long long)m) - 1;
+}
+
+// Activation vectors of an item when they are known before routing.
+__device__ __forceinline__ Item early_item(const Args &a)
+{
+    Item it;
+    it.kind = 0;
+    it.expert = 0;
+    it.nv = a.ids == nullptr ? a.M : 1;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) { it.vec[m] = m; it.dest[m] = 0ull; }
+    return it;
+}
+
+// Routing of a one-vector kernel (dense, or a single broadcast token): the
+// items are the distinct valid experts in order of first appearance, each
+// read by activation vector 0; out-of-range ids become zero items after them.
+__device__ Item route_one(const Args &a, int item_idx)
+{
+    Item it;
+    it.kind = -1;
+    it.expert = 0;
+    it.nv = 1;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) { it.vec[m] = 0; it.dest[m] = 0ull; }
+    if (a.ids == nullptr) {
+        if (item_idx == 0) { it.kind = 0; it.dest[0] = 1ull; }
+        return it;
+    }
+    const int lane = threadIdx.x & 63;
+    const int P = a.M * a.top_k;
+    int e = -1;
+    if (lane < P) e = a.ids[lane];
+    const bool valid = lane < P && e >= 0 && e < a.E;
+    bool dup = false;
+    for (int q = 0; q < P; ++q)
+        dup = dup || (q < lane && __builtin_amdgcn_readlane(e, q) == e);
+    const unsigned long long lead = __ballot(valid && !dup);
+    const unsigned long long inval = __ballot(lane < P && !valid);
+    const int n_real = __popcll(lead);
+    if (item_idx < n_real) {
+        const int e_lead = __builtin_amdgcn_readlane(e, nth_set_bit(lead, item_idx));
+        it.kind = 0;
+        it.expert = e_lead;
+        it.dest[0] = __ballot(valid && e == e_lead);
+    } else if (item_idx < n_real + __popcll(inval)) {
+        it.kind = 1;
+        it.dest[0] = 1ull << nth_set_bit(inval, item_idx - n_real);
+    }
+    return it;
 }
 
 // Every wave derives the same item list from the ids on its own (no LDS, no
@@ -149,12 +217,12 @@ __device__ Item route(const Args &a, int item_idx)
     int e = -1;
     if (lane < P) e = a.ids[lane];
     const bool valid = lane < P && e >= 0 && e < a.E;
-    const int v = a.x_per_slot ? lane : lane / a.top_k;
+    const int v = a.x_per_slot ? lane : token_of(lane, a.top_k);
 
     unsigned long long same_e = 0ull, same_ev = 0ull;
     for (int q = 0; q < P; ++q) {
         const int eq = __builtin_amdgcn_readlane(e, q);
-        const int vq = a.x_per_slot ? q : q / a.top_k;
+        const int vq = a.x_per_slot ? q : token_of(q, a.top_k);
         const bool hit = valid && eq == e;
         same_e |= hit ? (1ull << q) : 0ull;
         same_ev |= (hit && vq == v) ? (1ull << q) : 0ull;
@@ -182,7 +250,7 @@ __device__ Item route(const Args &a, int item_idx)
             if (m < it.nv) {
                 const int ml = __ffsll((long long)mm) - 1;
                 mm &= mm - 1ull;
-                const int vm = a.x_per_slot ? ml : ml / a.top_k;
+                const int vm = a.x_per_slot ? ml : token_of(ml, a.top_k);
                 it.vec[m] = vm;
                 it.dest[m] = __ballot(valid && e == e_lead && v == vm);
             }
@@ -215,26 +283,37 @@ template <int F> struct XItem { static constexpr int chunks = (F == kMXFP4) ? 1 
 template <int F>
 __device__ __forceinline__ int x_items_per_vec(const Args &a) { return F == kMXFP4 ? 4 * a.units : a.K / 32; }
 
-template <int F>
+// Staging item i -> (vector m, item c within the vector); nv <= NVMAX <= 4.
+template <int NVMAX>
+__device__ __forceinline__ int item_m(int i, int per)
+{
+    if constexpr (NVMAX == 1) return 0;
+    else return (i >= per) + (i >= 2 * per) + (i >= 3 * per);
+}
+
+template <int F, int NVMAX>
 __device__ __forceinline__ const uint8_t *x_item_ptr(const Args &a, const Item &it, int i)
 {
     const int per = x_items_per_vec<F>(a);
-    const int m = i / per;
-    const int c = i - m * per;
-    return a.x + (long long)item_vec(it, m) * a.x_vec_bytes + (long long)c * (16 * XItem<F>::chunks);
+    const int m = item_m<NVMAX>(i, per);
+    const int c = i - __umul24(m, per);
+    return a.x + __umul24(item_vec(it, m), a.x_vec_bytes) + c * (16 * XItem<F>::chunks);
 }
 
-template <int F>
+template <int F, int NVMAX>
 __device__ __forceinline__ void xload(const Args &a, const Item &it, uint4 (&r)[kXReg])
 {
     constexpr int PER = kXReg / XItem<F>::chunks;          // items held per thread
-    const int T = it.nv * x_items_per_vec<F>(a);
+    const int T = __umul24(it.nv, x_items_per_vec<F>(a));
+    const int jn = (T + kThreads - 1) / kThreads;           // items this workgroup needs per thread
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const int i = min((int)threadIdx.x + j * kThreads, T - 1);   // clamped: no branch
-        const uint8_t *p = x_item_ptr<F>(a, it, i);
-        r[j * XItem<F>::chunks] = *(const uint4 *)p;
-        if constexpr (XItem<F>::chunks == 2) r[j * 2 + 1] = *(const uint4 *)(p + 16);
+        if (j < jn) {
+            const int i = min((int)threadIdx.x + j * kThreads, T - 1);   // clamped: no divergence
+            const uint8_t *p = x_item_ptr<F, NVMAX>(a, it, i);
+            r[j * XItem<F>::chunks] = *(const uint4 *)p;
+            if constexpr (XItem<F>::chunks == 2) r[j * 2 + 1] = *(const uint4 *)(p + 16);
+        }
     }
 }
 
@@ -288,20 +367,20 @@ __device__ __forceinline__ int sum_i8x16(uint4 v)
 //         is c - 1.5, so a block's integer sum is 2*dot(c, q) - 3*sum(q)).
 //  CB3:   block b -> its two half-blocks in the cb3_half order; side data
 //         0.5*xs per block.
-template <int F>
+template <int F, int NVMAX>
 __device__ __forceinline__ void xput(const Args &a, const Item &it, uint8_t *lds, int i,
                                      uint4 lo, uint4 hi)
 {
     const int per = x_items_per_vec<F>(a);
-    const int m = i / per;
-    const int c = i - m * per;
-    uint8_t *dst = lds + m * a.lds_vec_bytes;
+    const int m = item_m<NVMAX>(i, per);
+    const int c = i - __umul24(m, per);
+    uint8_t *dst = lds + __umul24(m, a.lds_vec_bytes);
     if constexpr (F == kMXFP4) {
         *(uint4 *)(dst + 16 * chunk_pos<4>(c >> 2, c & 3)) = lo;
     } else {
         constexpr int CH = Fmt<F>::XB / 16;
         const int xbytes = a.units * Fmt<F>::XB;
-        const uint16_t xsb = a.xs[(long long)item_vec(it, m) * (a.K / 32) + c];
+        const uint16_t xsb = a.xs[__umul24(item_vec(it, m), a.K / 32) + c];
         const float xsh = 0.5f * (float)__builtin_bit_cast(_Float16, xsb);
         if constexpr (F == kCB3) {
             *(uint4 *)(dst + 16 * chunk_pos<2>(c, 0)) = cb3_xorder(lo);
@@ -325,77 +404,106 @@ __device__ __forceinline__ void xput(const Args &a, const Item &it, uint8_t *lds
     }
 }
 
-template <int F>
+template <int F, int NVMAX>
 __device__ __forceinline__ void xstore(const Args &a, const Item &it, uint8_t *lds, const uint4 (&r)[kXReg])
 {
     constexpr int CHK = XItem<F>::chunks;
     constexpr int PER = kXReg / CHK;
-    const int T = it.nv * x_items_per_vec<F>(a);
+    const int T = __umul24(it.nv, x_items_per_vec<F>(a));
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int i = (int)threadIdx.x + j * kThreads;
-        if (i < T) xput<F>(a, it, lds, i, r[j * CHK], r[j * CHK + (CHK - 1)]);
+        if (i < T) xput<F, NVMAX>(a, it, lds, i, r[j * CHK], r[j * CHK + (CHK - 1)]);
     }
 }
 
 // Items beyond the register budget, loaded and stored directly.  Returns
 // whether there were any (the same answer in every thread).
-template <int F>
+template <int F, int NVMAX>
 __device__ __forceinline__ bool xrest(const Args &a, const Item &it, uint8_t *lds)
 {
     constexpr int PER = kXReg / XItem<F>::chunks;
-    const int T = it.nv * x_items_per_vec<F>(a);
+    const int T = __umul24(it.nv, x_items_per_vec<F>(a));
     if (T <= PER * kThreads) return false;
     for (int i = PER * kThreads + (int)threadIdx.x; i < T; i += kThreads) {
-        const uint8_t *p = x_item_ptr<F>(a, it, i);
+        const uint8_t *p = x_item_ptr<F, NVMAX>(a, it, i);
         const uint4 lo = *(const uint4 *)p;
         const uint4 hi = (XItem<F>::chunks == 2) ? *(const uint4 *)(p + 16) : lo;
-        xput<F>(a, it, lds, i, lo, hi);
+        xput<F, NVMAX>(a, it, lds, i, lo, hi);
     }
     return true;
 }
 
 // ------------------------------------------------------------------ units
-template <int F> struct Unit;
-template <> struct Unit<kMXFP4> { uint4 c; uint32_t s; };
-template <> struct Unit<kCB2>   { uint4 c; uint32_t s; };
-template <> struct Unit<kCB2S>  { uint2 c; uint32_t s; };
-template <> struct Unit<kCB3>   { U3 c; uint32_t s; };
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int F>
-__device__ __forceinline__ void load_unit(Unit<F> &w, const uint8_t *crow, const uint8_t *srow, int u)
+// Weights are read through raw buffer resources over one expert's codes (or
+// scales): the base sits in SGPRs, each lane carries a 32-bit row offset,
+// and a unit's position in the row becomes the instruction's immediate
+// offset.  A read at or past the end of the expert returns zeros without
+// touching memory, so the rows of a partial last tile need no clamping.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, long long bytes)
 {
-    if constexpr (F == kMXFP4) {
-        w.c = *(const uint4 *)(crow + 16 * (long long)u);
-        w.s = srow[u];
-    } else if constexpr (F == kCB2) {
-        w.c = *(const uint4 *)(crow + 16 * (long long)u);
-        w.s = *(const uint32_t *)(srow + 4 * (long long)u);
-    } else if constexpr (F == kCB2S) {
-        w.c = *(const uint2 *)(crow + 8 * (long long)u);
-        w.s = *(const uint16_t *)(srow + 2 * (long long)u);
-    } else {
-        __builtin_memcpy(&w.c, __builtin_assume_aligned(crow + 12 * (long long)u, 4), 12);
-        w.s = *(const uint32_t *)(srow + 4 * (long long)u);
-    }
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
+
+template <int F> struct Unit;
+template <> struct Unit<kMXFP4> { u32x4 c; uint32_t s; static constexpr int CB = 16, SB = 1; };
+template <> struct Unit<kCB2>   { u32x4 c; uint32_t s; static constexpr int CB = 16, SB = 4; };
+template <> struct Unit<kCB2S>  { u32x2 c; uint32_t s; static constexpr int CB = 8, SB = 2; };
+template <> struct Unit<kCB3>   { u32x3 c; uint32_t s; static constexpr int CB = 12, SB = 4; };
 
 // ------------------------------------------------------------------ MAC per unit
 // Each mac_* adds the unit's contribution for RT rows and NV vectors.
 
-// MXFP4 x bf16: e2m1 -> bf16 pairs in hardware (v_cvt_scalef32_pk_bf16_fp4,
-// scale 1 so every value is exact), bf16 dot2 into two f32 chains per group,
-// then one fma with the exact E8M0 scale.
-template <int RT, int NV>
+// MXFP4 x bf16.  Fast path (every E8M0 byte of the unit in [2, 252], so
+// e2m1 * 2^(s-127) is an exact bf16 normal): v_cvt_scalef32_pk_bf16_fp4
+// decodes two nibbles and applies the scale in one instruction, and
+// v_dot2c_f32_bf16 accumulates straight into the row's f32 sum.  Otherwise
+// (scale bytes 0, 1, 253..255 anywhere in the wave): decode unscaled, dot the
+// group, then one fma with the exactly built 2^(s-127) (subnormal at 0, NaN
+// at 255).
+template <int LPR, int RT, int NV>
 __device__ __forceinline__ void mac_mxfp4(const Unit<kMXFP4> (&w)[RT], const uint8_t *lds,
-                                          int vec_bytes, int u, float (&acc)[RT][NV])
+                                          int vec_bytes, int u0, int cu, bool fast,
+                                          float (&acc)[RT][NV])
 {
     uint4 xq[NV][4];
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            xq[v][q] = *(const uint4 *)(lds + v * vec_bytes + 16 * chunk_pos<4>(u, q));
+            xq[v][q] = *(const uint4 *)(lds + v * vec_bytes + 16 * chunk_at<4, LPR>(u0, cu, q));
+    if (fast) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const uint32_t cw[4] = {w[r].c.x, w[r].c.y, w[r].c.z, w[r].c.w};
+            const float sc = __uint_as_float(w[r].s << 23);
+            bf16x2 wv[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wv[4 * q + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], sc, 0);
+                wv[4 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], sc, 1);
+                wv[4 * q + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], sc, 2);
+                wv[4 * q + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], sc, 3);
+            }
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float s = acc[r][v];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t xd[4] = {xq[v][q].x, xq[v][q].y, xq[v][q].z, xq[v][q].w};
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        s = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * q + b], __builtin_bit_cast(bf16x2, xd[b]), s, false);
+                }
+                acc[r][v] = s;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         const uint32_t cw[4] = {w[r].c.x, w[r].c.y, w[r].c.z, w[r].c.w};
@@ -427,10 +535,11 @@ __device__ __forceinline__ void mac_mxfp4(const Unit<kMXFP4> (&w)[RT], const uin
 // CB2 x int8: selectors (w >> 2j) & 0x03030303 hold raw codes; v_dot4 with
 // the transposed activations gives dot(c, q) exactly in int32, and the
 // block's integer sum is 2*dot + (-3*sum q).
-template <int F, int RT, int NV>
+template <int F, int LPR, int RT, int NV>
 __device__ __forceinline__ void mac_cb2(const Unit<F> (&w)[RT], const uint8_t *lds,
-                                        int vec_bytes, int xbytes, int u, float (&acc)[RT][NV])
+                                        int vec_bytes, int xbytes, int u0, int cu, float (&acc)[RT][NV])
 {
+    const int u = u0 + cu * LPR;
     constexpr int NB = (F == kCB2) ? 2 : 1;      // 32-blocks per unit
     constexpr int CH = 2 * NB;                   // 16-byte chunks per unit
     uint4 xq[NV][CH];
@@ -441,7 +550,7 @@ __device__ __forceinline__ void mac_cb2(const Unit<F> (&w)[RT], const uint8_t *l
         const uint8_t *base = lds + v * vec_bytes;
 #pragma unroll
         for (int q = 0; q < CH; ++q)
-            xq[v][q] = *(const uint4 *)(base + 16 * chunk_pos<CH>(u, q));
+            xq[v][q] = *(const uint4 *)(base + 16 * chunk_at<CH, LPR>(u0, cu, q));
         if constexpr (NB == 2) {
             const uint4 sd = *(const uint4 *)(base + xbytes + 16 * u);
             xsh[v][0] = __uint_as_float(sd.x);
@@ -519,17 +628,18 @@ __device__ __forceinline__ int cb3_half(uint32_t hi, uint32_t lo, uint4 x)
     return __builtin_amdgcn_sdot4((int)perm(kCb3LutHi, kCb3LutLo, s3), (int)x.w, d, false);
 }
 
-template <int RT, int NV>
+template <int LPR, int RT, int NV>
 __device__ __forceinline__ void mac_cb3(const Unit<kCB3> (&w)[RT], const uint8_t *lds,
-                                        int vec_bytes, int xbytes, int u, float (&acc)[RT][NV])
+                                        int vec_bytes, int xbytes, int u0, int cu, float (&acc)[RT][NV])
 {
+    const int u = u0 + cu * LPR;
     uint4 xq[NV][2];
     float xsh[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const uint8_t *base = lds + v * vec_bytes;
-        xq[v][0] = *(const uint4 *)(base + 16 * chunk_pos<2>(u, 0));
-        xq[v][1] = *(const uint4 *)(base + 16 * chunk_pos<2>(u, 1));
+        xq[v][0] = *(const uint4 *)(base + 16 * chunk_at<2, LPR>(u0, cu, 0));
+        xq[v][1] = *(const uint4 *)(base + 16 * chunk_at<2, LPR>(u0, cu, 1));
         xsh[v] = ((const float *)(base + xbytes))[u];
     }
 #pragma unroll
@@ -537,8 +647,8 @@ __device__ __forceinline__ void mac_cb3(const Unit<kCB3> (&w)[RT], const uint8_t
         const float ws0 = f16_lo(w[r].s), ws1 = f16_hi(w[r].s);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const int S0 = cb3_half<0>(w[r].c.b, w[r].c.a, xq[v][0]);
-            const int S1 = cb3_half<2>(w[r].c.c, w[r].c.b, xq[v][1]);
+            const int S0 = cb3_half<0>(w[r].c.y, w[r].c.x, xq[v][0]);
+            const int S1 = cb3_half<2>(w[r].c.z, w[r].c.y, xq[v][1]);
             const float t = __builtin_fmaf(ws1, (float)S1, ws0 * (float)S0);
             acc[r][v] = __builtin_fmaf(t, xsh[v], acc[r][v]);
         }
@@ -571,30 +681,88 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
-template <int F, int LPR, int CPL, int RT>
-__device__ __forceinline__ void load_seg(Unit<F> (&w)[CPL][RT], const uint8_t *const (&crows)[RT],
-                                         const uint8_t *const (&srows)[RT], int ubase, int U)
+// Code bytes are read exactly once per call, in whole cache lines per wave
+// instruction, so they are streamed with the non-temporal cache policy (aux
+// bit 1, "nt"): on MI355X this lifts a cold 17 MB gather read from about 3.9
+// to 4.4 TB/s.  Scale loads touch only part of a line per instruction and
+// the next unit step reads the rest, so they keep the default policy.
+constexpr int kStream = 2;
+
+template <int F>
+__device__ __forceinline__ uint32_t load_scale(__amdgpu_buffer_rsrc_t rs, uint32_t os)
 {
+    if constexpr (F == kMXFP4) return __builtin_amdgcn_raw_buffer_load_b8(rs, os, 0, 0);
+    else if constexpr (F == kCB2S) return __builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
+}
+
+template <int F>
+__device__ __forceinline__ void load_codes(Unit<F> &w, __amdgpu_buffer_rsrc_t rc, uint32_t oc)
+{
+    if constexpr (F == kMXFP4 || F == kCB2) w.c = __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, kStream);
+    else if constexpr (F == kCB2S) w.c = __builtin_amdgcn_raw_buffer_load_b64(rc, oc, 0, kStream);
+    else w.c = __builtin_amdgcn_raw_buffer_load_b96(rc, oc, 0, kStream);
+}
+
+// Loads of one segment: every scale first (1/17 to 1/4 of the bytes), then
+// the codes of unit steps c (all RT rows of step c) on demand.
+// Offsets are relative to the lane's first unit (oc/os include li * bytes);
+// a unit past the row end is redirected to the row's last unit, which another
+// lane of the same instruction reads anyway, so it costs no extra traffic.
+template <int F, int LPR, int CPL, int RT>
+__device__ __forceinline__ void load_scales(Unit<F> (&w)[CPL][RT], __amdgpu_buffer_rsrc_t rs,
+                                            const uint32_t (&os)[RT], int seg_unit, int li, int U)
+{
+    constexpr int SB = Unit<F>::SB;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        const int u = min(ubase + c * LPR, U - 1);   // past the row end: reload the last unit
+        const int du = min(seg_unit + c * LPR, U - 1 - li);
 #pragma unroll
-        for (int r = 0; r < RT; ++r) load_unit<F>(w[c][r], crows[r], srows[r], u);
+        for (int r = 0; r < RT; ++r) w[c][r].s = load_scale<F>(rs, os[r] + du * SB);
     }
 }
 
-template <int F, int LPR, int CPL, int RT, int NV>
-__device__ __forceinline__ void mac_seg(const Unit<F> (&w)[CPL][RT], const Args &a, const uint8_t *lds,
-                                        int ubase, int U, float (&acc)[RT][NV])
+template <int F, int LPR, int CPL, int RT>
+__device__ __forceinline__ void load_step(Unit<F> (&w)[CPL][RT], __amdgpu_buffer_rsrc_t rc,
+                                          const uint32_t (&oc)[RT], int seg_unit, int li, int U, int c)
 {
+    constexpr int CB = Unit<F>::CB;
+    const int du = min(seg_unit + c * LPR, U - 1 - li);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) load_codes<F>(w[c][r], rc, oc[r] + du * CB);
+}
+
+// Unit steps whose code loads are in flight ahead of the step being computed.
+// Vector-memory loads of a wave complete in issue order, so issuing a whole
+// row segment at once would make every step wait for the slowest request;
+// a short lead lets decode follow the data as it streams in.
+#ifndef QMV_LEAD
+#define QMV_LEAD 1
+#endif
+template <int CPL> struct Lead { static constexpr int v = (QMV_LEAD > 0 && QMV_LEAD < CPL) ? QMV_LEAD : CPL; };
+
+template <int F, int LPR, int CPL, int RT, int NV>
+__device__ __forceinline__ void mac_seg(Unit<F> (&w)[CPL][RT], const Args &a, const uint8_t *lds,
+                                        __amdgpu_buffer_rsrc_t rc, const uint32_t (&oc)[RT],
+                                        int seg_unit, int u0, int U, float (&acc)[RT][NV])
+{
+    constexpr int LEAD = Lead<CPL>::v;
     const int xbytes = U * Fmt<F>::XB;
+    bool fast = true;              // MXFP4: every scale byte of the segment in [2, 252]
+    if constexpr (F == kMXFP4) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int r = 0; r < RT; ++r) fast = fast && (w[c][r].s - 2u) <= 250u;
+        fast = __all(fast);
+    }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        const int u = ubase + c * LPR;
-        if (u < U) {
-            if constexpr (F == kMXFP4) mac_mxfp4<RT, NV>(w[c], lds, a.lds_vec_bytes, u, acc);
-            else if constexpr (F == kCB3) mac_cb3<RT, NV>(w[c], lds, a.lds_vec_bytes, xbytes, u, acc);
-            else mac_cb2<F, RT, NV>(w[c], lds, a.lds_vec_bytes, xbytes, u, acc);
+        if (c + LEAD < CPL) load_step<F, LPR, CPL, RT>(w, rc, oc, seg_unit, u0 - seg_unit, U, c + LEAD);
+        if (u0 + c * LPR < U) {
+            if constexpr (F == kMXFP4) mac_mxfp4<LPR, RT, NV>(w[c], lds, a.lds_vec_bytes, u0, c, fast, acc);
+            else if constexpr (F == kCB3) mac_cb3<LPR, RT, NV>(w[c], lds, a.lds_vec_bytes, xbytes, u0, c, acc);
+            else mac_cb2<F, LPR, RT, NV>(w[c], lds, a.lds_vec_bytes, xbytes, u0, c, acc);
         }
     }
 }
@@ -605,8 +773,9 @@ __device__ __forceinline__ void mac_seg(const Unit<F> (&w)[CPL][RT], const Args 
 //   3. activations to LDS, barrier (waits only for the staging loads)
 //   4. per unit, as its bytes arrive: decode and dot (progressive vmcnt)
 //   5. further segments when K needs them; butterfly; store.
-template <int F, int LPR, int CPL, int RT, int NV>
-__device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t *lds, int row_base)
+template <int F, int LPR, int CPL, int RT, int NV, int NVMAX>
+__device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t *lds, int row_base,
+                                          uint4 (&xr)[kXReg])
 {
     constexpr int SLOTS = 64 / LPR;
     constexpr int SEG = LPR * CPL;
@@ -616,23 +785,24 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
     const int li = lane % LPR;
     const int row0 = row_base + (wave * SLOTS + slot) * RT;
     const int U = a.units;
-    const long long eoff = (long long)it.expert * a.N;
-    const uint8_t *crows[RT];
-    const uint8_t *srows[RT];
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (long long)it.expert * a.expert_cb, a.expert_cb);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.scales + (long long)it.expert * a.expert_sb, a.expert_sb);
+    uint32_t oc[RT], os[RT];           // rows past N land past the expert's end: zeros
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-        const long long row = eoff + min(row0 + r, a.N - 1);   // rows past N: reread the last row
-        crows[r] = a.codes + row * a.rcb;
-        srows[r] = a.scales + row * a.rsb;
+        const int n = row0 + r;
+        oc[r] = (uint32_t)__umul24(n, a.rcb) + li * Unit<F>::CB;
+        os[r] = (uint32_t)__umul24(n, a.rsb) + li * Unit<F>::SB;
     }
 
-    uint4 xr[kXReg];
-    xload<F>(a, it, xr);
+    if (!a.x_early) xload<F, NVMAX>(a, it, xr);
     Unit<F> w[CPL][RT];
-    load_seg<F, LPR, CPL, RT>(w, crows, srows, li, U);
-    xstore<F>(a, it, lds, xr);
+    load_scales<F, LPR, CPL, RT>(w, rs, os, 0, li, U);
+#pragma unroll
+    for (int c = 0; c < Lead<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, 0, li, U, c);
+    xstore<F, NVMAX>(a, it, lds, xr);
     __syncthreads();
-    if (xrest<F>(a, it, lds)) __syncthreads();
+    if (xrest<F, NVMAX>(a, it, lds)) __syncthreads();
 
     float acc[RT][NV];
 #pragma unroll
@@ -642,9 +812,11 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
 
     const int nseg = (U + SEG - 1) / SEG;
     for (int seg = 0;;) {
-        mac_seg<F, LPR, CPL, RT, NV>(w, a, lds, seg * SEG + li, U, acc);
+        mac_seg<F, LPR, CPL, RT, NV>(w, a, lds, rc, oc, seg * SEG, seg * SEG + li, U, acc);
         if (++seg >= nseg) break;
-        load_seg<F, LPR, CPL, RT>(w, crows, srows, seg * SEG + li, U);
+        load_scales<F, LPR, CPL, RT>(w, rs, os, seg * SEG, li, U);
+#pragma unroll
+        for (int c = 0; c < Lead<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, seg * SEG, li, U, c);
     }
 
 #pragma unroll
@@ -665,7 +837,7 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
                 while (d) {
                     const int p = __ffsll((long long)d) - 1;
                     d &= d - 1ull;
-                    a.y[(long long)p * a.N + n] = val;
+                    a.y[p * a.N + n] = val;                     // M * top_k * N < 2^31
                 }
             }
         }
@@ -679,21 +851,29 @@ template <int F, int LPR, int CPL, int RT, int NVMAX>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const Item it = route(a, blockIdx.y);
+    uint4 xr[kXReg];
+    if (a.x_early) xload<F, NVMAX>(a, early_item(a), xr);   // in flight while the ids arrive
+    Item it;
+    if constexpr (NVMAX == 1) it = route_one(a, blockIdx.y);
+    else it = route(a, blockIdx.y);
     if (it.kind < 0) return;
     const int row_base = blockIdx.x * a.rows_per_tile;
     if (it.kind == 1) {
         const int p = __ffsll((long long)it.dest[0]) - 1;
         const int end = min(a.N, row_base + a.rows_per_tile);
         for (int n = row_base + threadIdx.x; n < end; n += kThreads)
-            a.y[(long long)p * a.N + n] = 0.0f;
+            a.y[p * a.N + n] = 0.0f;
         return;
     }
-    switch (it.nv) {
-    case 1: rows_body<F, LPR, CPL, RT, 1>(a, it, lds, row_base); break;
-    case 2: if constexpr (NVMAX >= 2) rows_body<F, LPR, CPL, RT, 2>(a, it, lds, row_base); break;
-    case 3: if constexpr (NVMAX >= 3) rows_body<F, LPR, CPL, RT, 3>(a, it, lds, row_base); break;
-    default: if constexpr (NVMAX >= 4) rows_body<F, LPR, CPL, RT, 4>(a, it, lds, row_base); break;
+    if constexpr (NVMAX == 1) {
+        rows_body<F, LPR, CPL, RT, 1, 1>(a, it, lds, row_base, xr);
+    } else {
+        switch (it.nv) {
+        case 1: rows_body<F, LPR, CPL, RT, 1, NVMAX>(a, it, lds, row_base, xr); break;
+        case 2: rows_body<F, LPR, CPL, RT, 2, NVMAX>(a, it, lds, row_base, xr); break;
+        case 3: rows_body<F, LPR, CPL, RT, 3, NVMAX>(a, it, lds, row_base, xr); break;
+        default: rows_body<F, LPR, CPL, RT, 4, NVMAX>(a, it, lds, row_base, xr); break;
+        }
     }
 }
 
@@ -714,12 +894,13 @@ extern const void *const kTable_cb3[3][4][5];
 
 // Instantiate one format's kernel table: [variant][lpr index][cpl index].
 #define QMV_K(F, V, L, C) \
-    (const void *)&::qmv::qmv_kernel<F, L, C, (V == 2 ? 4 : 2), (V == 0 ? 1 : 4)>
+    (const void *)&::qmv::qmv_kernel<F, L, C, ((V) == 2 ? 4 : 2), ((V) == 0 ? 1 : 4)>
 #define QMV_ROW01(F, V, L) \
     { QMV_K(F, V, L, 1), QMV_K(F, V, L, 2), QMV_K(F, V, L, 3), QMV_K(F, V, L, 4), QMV_K(F, V, L, 7) }
-#define QMV_ROW2(F, L) \
-    { QMV_K(F, 2, L, 1), QMV_K(F, 2, L, 2), QMV_K(F, 2, L, 4), nullptr, nullptr }
+#define QMV_ROW2(F, V, L) \
+    { QMV_K(F, V, L, 1), QMV_K(F, V, L, 2), QMV_K(F, V, L, 4), nullptr, nullptr }
+#define QMV_NOROW { nullptr, nullptr, nullptr, nullptr, nullptr }
 #define QMV_TABLE(F) \
     { { QMV_ROW01(F, 0, 8), QMV_ROW01(F, 0, 16), QMV_ROW01(F, 0, 32), QMV_ROW01(F, 0, 64) }, \
       { QMV_ROW01(F, 1, 8), QMV_ROW01(F, 1, 16), QMV_ROW01(F, 1, 32), QMV_ROW01(F, 1, 64) }, \
-      { { nullptr, nullptr, nullptr, nullptr, nullptr }, QMV_ROW2(F, 16), QMV_ROW2(F, 32), QMV_ROW2(F, 64) } }
+      { QMV_NOROW, QMV_ROW2(F, 2, 16), QMV_ROW2(F, 2, 32), QMV_ROW2(F, 2, 64) } }
