@@ -220,3 +220,28 @@ def test_rejects_misaligned_and_leaves_y():
     assert e.value.status == 2
     torch.cuda.synchronize()
     assert (y == 3.0).all()
+
+
+def test_graph_replays_match_eager():
+    """Calls captured in a HIP graph give the eager results on every replay,
+    with eager work and synchronizations between the replays."""
+    cases = [synth.make(synth.WORKLOADS[n].scaled(**SMALL[n])) for n in ("C2", "C3", "C4", "C5a")]
+    devs = [to_dev(inp) for inp in cases]
+    eager = [gpu_call(inp, dev).clone() for inp, dev in zip(cases, devs)]
+    outs = [torch.empty_like(e) for e in eager]
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for inp, dev, out in zip(cases, devs, outs):
+            gpu_call(inp, dev, y=out, stream=torch.cuda.current_stream())
+    for rep in range(4):
+        for out in outs:
+            out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, out in zip(eager, outs):
+            assert torch.equal(e.view(torch.int32), out.view(torch.int32)), rep
+        gpu_call(cases[0], devs[0])          # eager work between replays
+        torch.cuda.synchronize()
