@@ -77,6 +77,9 @@ def _bind(lib):
                                       _L, _L, _P, _P]
     lib.oracle_qmv_dense.restype = _I
     lib.oracle_qmv_dense.argtypes = [_I, _P, _P, _I, _P, _P, _L, _L, _L, _P, _P]
+    lib.oracle_qmv_gather_swiglu_sel.restype = _I
+    lib.oracle_qmv_gather_swiglu_sel.argtypes = [_I, _P, _P, _P, _P, _L, _P, _L, _L, _I, _P, _P,
+                                                 _L, _L, _P, _L, _P, _P, _P, _P, _P]
     lib.oracle_mutant_id.restype = _I
     lib.oracle_mutant_id.argtypes = []
     return lib
@@ -200,6 +203,31 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return y, A
+
+    def gather_swiglu(self, wfmt, gcodes, gscales, ucodes, uscales, ids, afmt, x, xs=None,
+                      outs=None):
+        """Fused gate/up + SwiGLU; returns (y, g, u, Ag, Au) in fp64, shaped
+        [M][top_k][N] (or flat over ``outs``)."""
+        gcodes, gscales = _c(gcodes, np.uint8), _c(gscales, np.uint8)
+        ucodes, uscales = _c(ucodes, np.uint8), _c(uscales, np.uint8)
+        ids = _c(ids, np.int32)
+        E, N = gcodes.shape[0], gcodes.shape[1]
+        M, top_k = ids.shape
+        x = self._xarr(afmt, x)
+        K = x.shape[-1]
+        xs = _c(xs, np.uint16)
+        shape = (M, top_k, N)
+        sel = np.arange(M * top_k * N, dtype=np.int64) if outs is None else _c(outs, np.int64)
+        res = [np.empty(sel.shape[0], np.float64) for _ in range(5)]
+        rc = self.lib.oracle_qmv_gather_swiglu_sel(
+            WFMT.get(wfmt, wfmt), _ptr(gcodes), _ptr(gscales), _ptr(ucodes), _ptr(uscales), E,
+            _ptr(ids), M, top_k, AFMT.get(afmt, afmt), _ptr(x), _ptr(xs), N, K, _ptr(sel),
+            sel.shape[0], *[_ptr(r) for r in res])
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        if outs is None:
+            res = [r.reshape(shape) for r in res]
+        return tuple(res)
 
     def dense(self, wfmt, codes, scales, afmt, x, xs=None):
         """Dense GEMV; codes [N][row_code_bytes]; returns (y, A) shaped [M][N]."""

@@ -44,7 +44,14 @@
  *    per 16-weight half-block; an int8 activation carries one fp16 scale per
  *    32 and a half-block uses the scale of the 32-block that contains it.
  *
- * Build: plain C99, gcc -O2, no SIMD intrinsics (oracle/build.py).
+ * Fused gate/up (oracle_qmv_gather_swiglu_sel): the pages name one matvec
+ * kernel for an MoE layer's gate and up expert projections (geo-lucebox PR
+ * "DS4 H200: rocmfp2_mix MoE matvec", the per-kernel table and "Why this
+ * kernel") but not the activation between them.  Reading taken: the SwiGLU
+ * of Shazeer, "GLU Variants Improve Transformer" (2020), silu(g) * u with
+ * silu(g) = g / (1 + e^-g), no clamp and no bias.
+ *
+ * Build: plain C99, gcc -O2, no SIMD intrinsics (build() in oracle/__init__.py).
  *
  * Compile-time ORACLE_MUTANT=<n> plants one deliberate mistake so the tests
  * can show that the pins catch it; the default build plants none.
@@ -389,6 +396,44 @@ int oracle_qmv_dense(int wfmt, const uint8_t *codes, const uint8_t *scales,
                     x_vector(afmt, x, m, K), xsrow, K,
                     &y[(size_t)m * N + n], &A[(size_t)m * N + n]);
         }
+    return 0;
+}
+
+/*
+ * Fused gate/up projection with the SwiGLU activation (Shazeer, "GLU Variants
+ * Improve Transformer", 2020): for each selected output o of y[M][top_k][N],
+ *     g = gather output of the gate weights,  u = gather output of the up weights
+ *     y = silu(g) * u,   silu(g) = g / (1 + e^-g),
+ * with the token's activation vector (x[M][K]) and the gather's rules for
+ * expert ids (an id outside [0, E) gives g = u = y = 0).  Also returns g, u and
+ * their sum |w x| scales Ag, Au.  Any of g, u, Ag, Au may be NULL.
+ */
+int oracle_qmv_gather_swiglu_sel(int wfmt, const uint8_t *gcodes, const uint8_t *gscales,
+                                 const uint8_t *ucodes, const uint8_t *uscales, long E,
+                                 const int32_t *ids, long M, long top_k,
+                                 int afmt, const void *x, const uint16_t *xs,
+                                 long N, long K, const int64_t *outs, long n_outs,
+                                 double *y, double *g, double *u, double *Ag, double *Au)
+{
+    for (long i = 0; i < n_outs; i++) {
+        double gi, ui, ag, au;
+        if (oracle_qmv_gather_sel(wfmt, gcodes, gscales, E, ids, M, top_k, afmt, x, xs, 0,
+                                  N, K, &outs[i], 1, &gi, &ag) != 0 ||
+            oracle_qmv_gather_sel(wfmt, ucodes, uscales, E, ids, M, top_k, afmt, x, xs, 0,
+                                  N, K, &outs[i], 1, &ui, &au) != 0)
+            return -1;
+#if ORACLE_MUTANT == 9
+        y[i] = ui / (1.0 + exp(-ui)) * gi;
+#elif ORACLE_MUTANT == 10
+        y[i] = ui / (1.0 + exp(-gi));
+#else
+        y[i] = gi / (1.0 + exp(-gi)) * ui;
+#endif
+        if (g) g[i] = gi;
+        if (u) u[i] = ui;
+        if (Ag) Ag[i] = ag;
+        if (Au) Au[i] = au;
+    }
     return 0;
 }
 

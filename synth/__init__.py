@@ -94,6 +94,22 @@ WORKLOADS = {
                     desc="dense MXFP4 GEMV, M=4, K=N=7168"),
 }
 
+# Fused gate/up projections (two weight tensors of one shape, SwiGLU between
+# them): the gpt-oss-20b and DeepSeek-shaped MoE gate/up matrices.
+GATE_UP_WORKLOADS = {
+    "C2gu": Workload("C2gu", "gate_up", "mxfp4", M=1, N=2880, K=2880, seed=6, E=32, top_k=4,
+                     e8m0=(115, 120),
+                     desc="gpt-oss-20b MoE decode gate+up with SwiGLU, 4 of 32 experts, "
+                          "K=N=2880, MXFP4"),
+    "C3gu": Workload("C3gu", "gate_up", "cb2", M=1, N=2048, K=7168, seed=7, E=256, top_k=4,
+                     desc="DeepSeek-shaped 2-bit MoE gate+up with SwiGLU, 4 of 256, K=7168, "
+                          "N=2048"),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name] if name in WORKLOADS else GATE_UP_WORKLOADS[name]
+
 
 @dataclass
 class Inputs:
@@ -177,6 +193,34 @@ def make(name_or_wl, seed: int | None = None, experts: int | None = None) -> Inp
     if wl.kind == "dense":
         codes, scales = codes[0], scales[0]
     return Inputs(wl, codes, scales, ids, x, xs)
+
+
+@dataclass
+class GateUpInputs:
+    """Host arrays of one fused gate/up call (broadcast token activations)."""
+    wl: Workload
+    gcodes: np.ndarray
+    gscales: np.ndarray
+    ucodes: np.ndarray
+    uscales: np.ndarray
+    ids: np.ndarray
+    x: np.ndarray
+    xs: np.ndarray | None
+
+
+def make_gate_up(wl, seed: int | None = None) -> GateUpInputs:
+    """Gate and up weights of the same shape and recipe, drawn in the order
+    gate codes -> gate scales -> up codes -> up scales -> ids -> activations."""
+    if isinstance(wl, str):
+        wl = workload(wl)
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    gc = gen_codes(rng, wl.wfmt, wl.E, wl.N, wl.K)
+    gs = gen_scales(rng, wl.wfmt, wl.E, wl.N, wl.K, wl.e8m0)
+    uc = gen_codes(rng, wl.wfmt, wl.E, wl.N, wl.K)
+    us = gen_scales(rng, wl.wfmt, wl.E, wl.N, wl.K, wl.e8m0)
+    ids = gen_ids(rng, wl.M, wl.top_k, wl.E)
+    x, xs = gen_activations(rng, wl.afmt, wl.M, wl.K)
+    return GateUpInputs(wl, gc, gs, uc, us, ids, x, xs)
 
 
 def id_stream(seed: int, calls: int, M: int, top_k: int, E: int) -> np.ndarray:

@@ -393,6 +393,51 @@ def check_gather_semantics(o):
         assert np.array_equal(yp, y0), fmt
 
 
+# ---------------------------------------------------------------- P9 fused gate/up SwiGLU
+def check_swiglu(o):
+    """silu(g) * u against scipy's logistic function, on g and u from the
+    (separately pinned) gather; gate and up must not be interchangeable."""
+    from scipy.special import expit
+    rng = _rng(17)
+    K, N, E = 64, 16, 5
+    for fmt in ("mxfp4", "cb2", "cb3"):
+        afmt = _afmt(fmt)
+        gc = np.stack([_random_rows(rng, fmt, N, K)[0] for _ in range(E)])
+        gs = np.stack([_random_rows(rng, fmt, N, K)[1] for _ in range(E)])
+        uc = np.stack([_random_rows(rng, fmt, N, K)[0] for _ in range(E)])
+        us = np.stack([_random_rows(rng, fmt, N, K)[1] for _ in range(E)])
+        x, xs = _random_x(rng, fmt, 2, K)
+        if fmt == "mxfp4":
+            # make the gate pre-activations span silu's range, well past +-10
+            gs = np.full_like(gs, 130)
+        ids = np.array([[0, 4, E], [3, -1, 4]], np.int32)
+        y, g, u, Ag, Au = o.gather_swiglu(fmt, gc, gs, uc, us, ids, afmt, x, xs)
+        g2, Ag2 = o.gather(fmt, gc, gs, ids, afmt, x, xs)
+        u2, Au2 = o.gather(fmt, uc, us, ids, afmt, x, xs)
+        assert np.array_equal(g, g2) and np.array_equal(u, u2), fmt
+        assert np.array_equal(Ag, Ag2) and np.array_equal(Au, Au2), fmt
+        want = g * expit(g) * u
+        assert np.allclose(y, want, rtol=1e-14, atol=1e-300), fmt
+        valid = (ids >= 0) & (ids < E)
+        assert not y[~valid].any(), fmt
+        assert (np.abs(g[valid]) > 0).all(), fmt
+        if fmt == "mxfp4":
+            assert np.abs(g).max() > 10, "gate range too narrow to test saturation"
+        # an all-zero gate weight gives g = 0 and silu(0) = 0 whatever u is
+        zc = np.zeros_like(gc)
+        if fmt == "cb2":    # 2-bit codes have no zero: take a zero scale instead
+            zs = np.zeros_like(gs)
+        else:
+            zs = gs
+            if fmt == "cb3":
+                zc = np.zeros_like(gc)          # code 0 means 0 in the 3-bit book
+        yz, gz, _, _, _ = o.gather_swiglu(fmt, zc, zs, uc, us, ids, afmt, x, xs)
+        assert not gz.any() and not yz.any(), fmt
+        # gate and up are not symmetric: swapping them changes y
+        ysw, _, _, _, _ = o.gather_swiglu(fmt, uc, us, gc, gs, ids, afmt, x, xs)
+        assert not np.array_equal(ysw[valid], y[valid]), fmt
+
+
 ALL_CHECKS = [
     check_e2m1_table,
     check_e8m0_library,
@@ -406,4 +451,5 @@ ALL_CHECKS = [
     check_block_factored,
     check_unit_scale_exact,
     check_gather_semantics,
+    check_swiglu,
 ]
