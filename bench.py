@@ -19,7 +19,8 @@ of the experts a call reads / time per call).  ``roofline`` relates the
 kernel's algorithmic bytes (weights + activations + ids + output) per launch
 to the 8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same workload on the host's cores.  ``workloads`` lists the
-other shapes measured the same way (not the headline).
+other shapes measured the same way (not the headline), among them the fused
+gate/up + SwiGLU calls (qmv_gather_moe_swiglu) C2gu and C3gu.
 """
 from __future__ import annotations
 
@@ -86,14 +87,15 @@ def other_bytes(wl):
     """Activation, scale, id and output bytes of one call."""
     V = wl.M * wl.top_k if (wl.kind == "gather" and wl.x_per_slot) else wl.M
     xb = V * wl.K * (2 if wl.afmt == "bf16" else 1) + (0 if wl.afmt == "bf16" else V * (wl.K // 32) * 2)
-    outs = wl.M * (wl.top_k if wl.kind == "gather" else 1) * wl.N
-    ids = 4 * wl.M * wl.top_k if wl.kind == "gather" else 0
+    routed = wl.kind in ("gather", "gate_up")
+    outs = wl.M * (wl.top_k if routed else 1) * wl.N
+    ids = 4 * wl.M * wl.top_k if routed else 0
     return xb + ids + 4 * outs
 
 
 # Rotation plan: layer copies so that between two reads of the same weights
 # more than the 256 MB Infinity Cache of other weights is read.
-ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40}
+ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40, "C2gu": 4, "C3gu": 1}
 
 
 class Prepared:
@@ -105,26 +107,32 @@ class Prepared:
         import bit_block_quantized_amd as q
         import synth
         self.name = name
-        self.wl = wl = synth.WORKLOADS[name]
-        self.inp = inp = synth.make(name)
+        self.wl = wl = synth.workload(name)
+        gate_up = wl.kind == "gate_up"
+        self.inp = inp = synth.make_gate_up(wl) if gate_up else synth.make(name)
         self.L = ROTATION[name] if rotate else 1
         dev = torch.device("cuda")
-        c0 = torch.from_numpy(inp.codes).to(dev)
-        s0 = torch.from_numpy(inp.scales).to(dev)
-        self.codes = torch.empty((self.L,) + tuple(c0.shape), dtype=torch.uint8, device=dev)
-        self.scales = torch.empty((self.L,) + tuple(s0.shape), dtype=torch.uint8, device=dev)
-        for layer in range(self.L):
-            self.codes[layer].copy_(c0)
-            self.scales[layer].copy_(s0)
-        del c0, s0
+
+        def layers(a):
+            a0 = torch.from_numpy(a).to(dev)
+            t = torch.empty((self.L,) + tuple(a0.shape), dtype=torch.uint8, device=dev)
+            for layer in range(self.L):
+                t[layer].copy_(a0)
+            return t
+
+        if gate_up:
+            self.codes, self.scales = layers(inp.gcodes), layers(inp.gscales)
+            self.codes2, self.scales2 = layers(inp.ucodes), layers(inp.uscales)
+        else:
+            self.codes, self.scales = layers(inp.codes), layers(inp.scales)
         if wl.afmt == "bf16":
             self.x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
             self.xs = None
         else:
             self.x = torch.from_numpy(inp.x).to(dev)
             self.xs = torch.from_numpy(inp.xs.view(np.float16)).to(dev)
-        if wl.kind == "gather":
-            if name in ("C3", "C4"):
+        if wl.kind in ("gather", "gate_up"):
+            if name in ("C3", "C4", "C3gu"):
                 ids = synth.disjoint_id_stream(wl.seed + 100, calls, wl.top_k, wl.E)
             else:
                 ids = synth.id_stream(wl.seed + 100, calls, wl.M, wl.top_k, wl.E)
@@ -139,6 +147,8 @@ class Prepared:
             self.y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
         self.calls = calls
         self.wbytes = np.array([weight_bytes(wl, u) for u in n_unique], np.float64)
+        if gate_up:
+            self.wbytes *= 2
         self.abytes = self.wbytes + other_bytes(wl)
         self.lib = q.lib()
         cstride = self.codes[0].numel()
@@ -149,18 +159,26 @@ class Prepared:
             cp = self.codes.data_ptr() + layer * cstride
             sp = self.scales.data_ptr() + layer * sstride
             xs = None if self.xs is None else self.xs.data_ptr()
-            if wl.kind == "gather":
-                self.args.append((WFMT[wl.wfmt], cp, sp,
-                                  wl.E, self.ids.data_ptr() + i * wl.M * wl.top_k * 4, wl.M,
-                                  wl.top_k, 0 if wl.afmt == "bf16" else 1, self.x.data_ptr(), xs,
-                                  int(wl.x_per_slot), self.y.data_ptr(), wl.N, wl.K))
+            idp = None if self.ids is None else self.ids.data_ptr() + i * wl.M * wl.top_k * 4
+            afmt = 0 if wl.afmt == "bf16" else 1
+            if gate_up:
+                self.args.append((WFMT[wl.wfmt], cp, sp, self.codes2.data_ptr() + layer * cstride,
+                                  self.scales2.data_ptr() + layer * sstride, wl.E, idp, wl.M,
+                                  wl.top_k, afmt, self.x.data_ptr(), xs, self.y.data_ptr(), wl.N,
+                                  wl.K))
+            elif wl.kind == "gather":
+                self.args.append((WFMT[wl.wfmt], cp, sp, wl.E, idp, wl.M, wl.top_k, afmt,
+                                  self.x.data_ptr(), xs, int(wl.x_per_slot), self.y.data_ptr(),
+                                  wl.N, wl.K))
             else:
-                self.args.append((WFMT[wl.wfmt], cp, sp, 0 if wl.afmt == "bf16" else 1, self.x.data_ptr(), xs,
+                self.args.append((WFMT[wl.wfmt], cp, sp, afmt, self.x.data_ptr(), xs,
                                   self.y.data_ptr(), wl.M, wl.N, wl.K))
 
     def call(self, i, stream_handle):
         a = self.args[i]
-        if self.wl.kind == "gather":
+        if self.wl.kind == "gate_up":
+            s = self.lib.qmv_gather_moe_swiglu(*a, ctypes.c_void_p(stream_handle))
+        elif self.wl.kind == "gather":
             s = self.lib.qmv_gather_moe(*a, ctypes.c_void_p(stream_handle))
         else:
             s = self.lib.qmv_dense(*a, ctypes.c_void_p(stream_handle))
@@ -274,7 +292,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b",
+    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu",
                     help="other shapes to measure besides the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")

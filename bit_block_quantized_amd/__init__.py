@@ -24,7 +24,7 @@ import os
 
 import torch  # noqa: F401  -- loads the HIP runtime that libqmv.so binds to
 
-__all__ = ["qmv_dense", "qmv_gather_moe", "qmv_strerror", "lib", "LIB_PATH",
+__all__ = ["qmv_dense", "qmv_gather_moe", "qmv_gather_moe_swiglu", "qmv_strerror", "lib", "LIB_PATH",
            "W_MXFP4", "W_CB2", "W_CB3", "A_BF16", "A_Q8B32", "QmvError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
@@ -59,6 +59,8 @@ def lib():
     L.qmv_dense.argtypes = [I, P, P, I, P, P, P, I, I, I, P]
     L.qmv_gather_moe.restype = I
     L.qmv_gather_moe.argtypes = [I, P, P, I, P, I, I, I, P, P, I, P, I, I, P]
+    L.qmv_gather_moe_swiglu.restype = I
+    L.qmv_gather_moe_swiglu.argtypes = [I, P, P, P, P, I, P, I, I, I, P, P, P, I, I, P]
     L.qmv_strerror.restype = ctypes.c_char_p
     L.qmv_strerror.argtypes = [I]
     _lib = L
@@ -146,5 +148,32 @@ def qmv_gather_moe(wfmt, w_codes, w_scales, expert_ids, x, x_scales=None, x_per_
                              _dev_ptr(x_scales, "x_scales", (torch.float16,), dev),
                              int(bool(x_per_slot)),
                              _dev_ptr(y, "y", (torch.float32,), dev), N, K, _stream(dev, stream))
+    _check(s)
+    return y
+
+
+def qmv_gather_moe_swiglu(wfmt, gate_codes, gate_scales, up_codes, up_scales, expert_ids, x,
+                          x_scales=None, y=None, stream=None):
+    """Fused gate/up projection with SwiGLU: y = silu(gate x) * (up x);
+    returns y (float32 [M][top_k][N]).  ``x`` is the tokens' [M][K]."""
+    w = _wfmt(wfmt)
+    dev = gate_codes.device
+    if dev.type != "cuda":
+        raise ValueError("qmv_gather_moe_swiglu runs on the GPU only; pass device tensors")
+    E, N = gate_codes.shape[0], gate_codes.shape[1]
+    M, top_k = expert_ids.shape
+    K = x.shape[-1]
+    if y is None:
+        y = torch.empty((M, top_k, N), dtype=torch.float32, device=dev)
+    a = _AFMT_OF.get(w, A_BF16)
+    xd = (torch.bfloat16,) if a == A_BF16 else (torch.int8,)
+    s = lib().qmv_gather_moe_swiglu(
+        w, _dev_ptr(gate_codes, "gate_codes", (torch.uint8,), dev),
+        _dev_ptr(gate_scales, "gate_scales", _SCALE_DT, dev),
+        _dev_ptr(up_codes, "up_codes", (torch.uint8,), dev),
+        _dev_ptr(up_scales, "up_scales", _SCALE_DT, dev), E,
+        _dev_ptr(expert_ids, "expert_ids", (torch.int32,), dev), M, top_k, a,
+        _dev_ptr(x, "x", xd, dev), _dev_ptr(x_scales, "x_scales", (torch.float16,), dev),
+        _dev_ptr(y, "y", (torch.float32,), dev), N, K, _stream(dev, stream))
     _check(s)
     return y

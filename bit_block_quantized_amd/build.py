@@ -25,7 +25,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mcode-object-version=5",
+    "-mcode-object-version=5", "-fvisibility=hidden",
     "-Wall", "-Wno-unused-function",
 ]
 

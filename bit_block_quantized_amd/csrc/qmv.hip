@@ -17,8 +17,16 @@ constexpr int kMaxK = 16384;
 constexpr int kMaxM = 4;
 constexpr int kMaxTopK = 16;
 
-const void *kernel_for(int kind, int variant, int li, int ci)
+const void *kernel_for(int kind, int variant, int li, int ci, bool gate_up)
 {
+    if (gate_up) {
+        switch (kind) {
+        case kMXFP4: return kTableGU_mxfp4[variant][li][ci];
+        case kCB2: return kTableGU_cb2[variant][li][ci];
+        case kCB2S: return kTableGU_cb2s[variant][li][ci];
+        default: return kTableGU_cb3[variant][li][ci];
+        }
+    }
     switch (kind) {
     case kMXFP4: return kTable_mxfp4[variant][li][ci];
     case kCB2: return kTable_cb2[variant][li][ci];
@@ -123,14 +131,18 @@ Shape pick_shape(int variant, int units, long long rows_total, int rt)
     return best;
 }
 
-std::once_flag g_attr_once[4][3][4][5];
-hipError_t g_attr_err[4][3][4][5];
+std::once_flag g_attr_once[2][4][3][4][5];
+hipError_t g_attr_err[2][4][3][4][5];
 
-qmv_status_t launch(int wfmt, const void *codes, const void *scales, int E, const int32_t *ids,
+// codes2/scales2 non-null selects the gate/up mode: codes/scales are the gate
+// projection, codes2/scales2 the up projection, y = swiglu(gate x, up x).
+qmv_status_t launch(int wfmt, const void *codes, const void *scales, const void *codes2,
+                    const void *scales2, int E, const int32_t *ids,
                     int M, int top_k, const void *x, const void *xs, int x_per_slot,
                     float *y, int N, int K, hipStream_t stream)
 {
     const bool gather = ids != nullptr;
+    const bool gate_up = codes2 != nullptr;
     const int kind = wfmt == QMV_W_MXFP4 ? kMXFP4 : wfmt == QMV_W_CB3 ? kCB3 : (K % 64 == 0 ? kCB2 : kCB2S);
     const int units = K / kUnitWeights[kind];
     const int nv_needed = !gather ? M : (x_per_slot ? (M * top_k < 4 ? M * top_k : 4) : M);
@@ -139,11 +151,13 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, int E, cons
     else if (gather)    { variant = 1; rt = 2; }
     else                { variant = 2; rt = 4; }
     const int nvmax = variant == 0 ? 1 : 4;
-    const long long rows_total = (long long)N * (gather ? M * top_k : 1);
+    const long long rows_total = (long long)N * (gather ? M * top_k : 1) * (gate_up ? 2 : 1);
     const Shape sh = pick_shape(variant, units, rows_total, rt);
     Args a;
     a.codes = (const uint8_t *)codes;
     a.scales = (const uint8_t *)scales;
+    a.codes2 = (const uint8_t *)codes2;
+    a.scales2 = (const uint8_t *)scales2;
     a.ids = ids;
     a.x = (const uint8_t *)x;
     a.xs = (const uint16_t *)xs;
@@ -161,20 +175,20 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, int E, cons
     a.units = units;
     a.x_per_slot = gather ? x_per_slot : 0;
     a.x_early = (!gather || (M == 1 && !x_per_slot)) ? 1 : 0;
-    a.rows_per_tile = kWaves * (64 / sh.lpr) * rt;
+    a.rows_per_tile = kWaves * (64 / sh.lpr) * (gate_up ? 1 : rt);
     const int vec_bytes = units * (kUnitXB[kind] + kUnitAB[kind]);
     a.lds_vec_bytes = (vec_bytes + 15) & ~15;
     const size_t lds = (size_t)nvmax * a.lds_vec_bytes;
 
-    const void *fn = kernel_for(kind, variant, sh.li, sh.ci);
+    const void *fn = kernel_for(kind, variant, sh.li, sh.ci, gate_up);
     // Largest dynamic LDS this kernel can ask for (K = kMaxK, all vectors).
-    std::call_once(g_attr_once[kind][variant][sh.li][sh.ci], [&] {
+    std::call_once(g_attr_once[gate_up][kind][variant][sh.li][sh.ci], [&] {
         const int umax = kMaxK / kUnitWeights[kind];
         const int vmax = (umax * (kUnitXB[kind] + kUnitAB[kind]) + 15) & ~15;
-        g_attr_err[kind][variant][sh.li][sh.ci] = hipFuncSetAttribute(
+        g_attr_err[gate_up][kind][variant][sh.li][sh.ci] = hipFuncSetAttribute(
             fn, hipFuncAttributeMaxDynamicSharedMemorySize, nvmax * vmax);
     });
-    if (g_attr_err[kind][variant][sh.li][sh.ci] != hipSuccess)
+    if (g_attr_err[gate_up][kind][variant][sh.li][sh.ci] != hipSuccess)
         return QMV_EHIP;
 
     const dim3 grid((unsigned)((N + a.rows_per_tile - 1) / a.rows_per_tile),
@@ -189,7 +203,9 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, int E, cons
 
 extern "C" {
 
-qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
+#define QMV_API __attribute__((visibility("default")))
+
+QMV_API qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
                        qmv_afmt_t afmt, const void *x, const void *x_scales,
                        float *y, int M, int N, int K, hipStream_t stream)
 {
@@ -197,11 +213,11 @@ qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scale
                                     x, afmt == QMV_A_Q8B32 ? x_scales : nullptr, y, N, K);
     if (s != QMV_OK)
         return s;
-    return launch(wfmt, w_codes, w_scales, 1, nullptr, M, 1, x,
+    return launch(wfmt, w_codes, w_scales, nullptr, nullptr, 1, nullptr, M, 1, x,
                   afmt == QMV_A_Q8B32 ? x_scales : nullptr, 0, y, N, K, stream);
 }
 
-qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales, int E,
+QMV_API qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales, int E,
                             const int32_t *expert_ids, int M, int top_k,
                             qmv_afmt_t afmt, const void *x, const void *x_scales,
                             int x_per_slot, float *y, int N, int K, hipStream_t stream)
@@ -210,11 +226,29 @@ qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const void *w_
                                     x, afmt == QMV_A_Q8B32 ? x_scales : nullptr, y, N, K);
     if (s != QMV_OK)
         return s;
-    return launch(wfmt, w_codes, w_scales, E, expert_ids, M, top_k, x,
+    return launch(wfmt, w_codes, w_scales, nullptr, nullptr, E, expert_ids, M, top_k, x,
                   afmt == QMV_A_Q8B32 ? x_scales : nullptr, x_per_slot ? 1 : 0, y, N, K, stream);
 }
 
-const char *qmv_strerror(qmv_status_t status)
+QMV_API qmv_status_t qmv_gather_moe_swiglu(qmv_wfmt_t wfmt, const void *gate_codes, const void *gate_scales,
+                                   const void *up_codes, const void *up_scales, int E,
+                                   const int32_t *expert_ids, int M, int top_k,
+                                   qmv_afmt_t afmt, const void *x, const void *x_scales,
+                                   float *y, int N, int K, hipStream_t stream)
+{
+    const void *xs = afmt == QMV_A_Q8B32 ? x_scales : nullptr;
+    qmv_status_t s = validate(wfmt, gate_codes, gate_scales, E, expert_ids, true, M, top_k, afmt,
+                              x, xs, y, N, K);
+    if (s != QMV_OK)
+        return s;
+    s = validate(wfmt, up_codes, up_scales, E, expert_ids, true, M, top_k, afmt, x, xs, y, N, K);
+    if (s != QMV_OK)
+        return s;
+    return launch(wfmt, gate_codes, gate_scales, up_codes, up_scales, E, expert_ids, M, top_k, x,
+                  xs, 0, y, N, K, stream);
+}
+
+QMV_API const char *qmv_strerror(qmv_status_t status)
 {
     switch (status) {
     case QMV_OK: return "success";

@@ -5,12 +5,13 @@
 // one tile of consecutive output rows.  Inside a wave, LPR lanes share a row:
 // lane li streams the row's 16-byte-aligned "units" li, li+LPR, ... so each
 // load instruction reads LPR*unit_bytes contiguous bytes of a row, and each
-// lane keeps RT rows in flight.  All weight loads of a segment are issued
-// before any arithmetic (geo-lucebox PR #31, "issue all row loads before any
-// FMA"); activations are staged once per workgroup into LDS in a layout the
-// decode consumes directly (same page, "stage activations in LDS, coalesced +
-// swizzled"), then the lanes' partial sums of a row are combined by a fixed
-// xor butterfly, so results are bitwise reproducible.
+// lane keeps RT rows in flight.  Weight loads run ahead of the arithmetic that
+// consumes them (geo-lucebox PR #31 "DS4 H200: rocmfp2_mix MoE matvec", the
+// commit table: hoisting row loads above the FMAs was one of its steps);
+// activations are staged once per workgroup into swizzled LDS in the layout
+// each decode consumes (the same table's LDS staging step), and the lanes'
+// partial sums of a row are combined by a fixed butterfly, so results are
+// bitwise reproducible.
 //
 // Units per format (one unit = what a lane decodes per load):
 //   MXFP4  32 weights: 16 B of nibbles + 1 E8M0 byte      (bf16 x, 64 B)
@@ -43,6 +44,8 @@ template <> struct Fmt<kCB3>   { static constexpr int W = 32, XB = 32, AB = 4; }
 struct Args {
     const uint8_t *codes;
     const uint8_t *scales;
+    const uint8_t *codes2;   // gate/up mode: the up projection (codes is the gate)
+    const uint8_t *scales2;
     const int32_t *ids;      // nullptr for a dense call
     const uint8_t *x;
     const uint16_t *xs;      // int8 activation scales (fp16 bits) or nullptr
@@ -710,7 +713,7 @@ __device__ __forceinline__ void load_codes(Unit<F> &w, __amdgpu_buffer_rsrc_t rc
 // a unit past the row end is redirected to the row's last unit, which another
 // lane of the same instruction reads anyway, so it costs no extra traffic.
 template <int F, int LPR, int CPL, int RT>
-__device__ __forceinline__ void load_scales(Unit<F> (&w)[CPL][RT], __amdgpu_buffer_rsrc_t rs,
+__device__ __forceinline__ void load_scales(Unit<F> (&w)[CPL][RT], const __amdgpu_buffer_rsrc_t (&rs)[RT],
                                             const uint32_t (&os)[RT], int seg_unit, int li, int U)
 {
     constexpr int SB = Unit<F>::SB;
@@ -718,18 +721,18 @@ __device__ __forceinline__ void load_scales(Unit<F> (&w)[CPL][RT], __amdgpu_buff
     for (int c = 0; c < CPL; ++c) {
         const int du = min(seg_unit + c * LPR, U - 1 - li);
 #pragma unroll
-        for (int r = 0; r < RT; ++r) w[c][r].s = load_scale<F>(rs, os[r] + du * SB);
+        for (int r = 0; r < RT; ++r) w[c][r].s = load_scale<F>(rs[r], os[r] + du * SB);
     }
 }
 
 template <int F, int LPR, int CPL, int RT>
-__device__ __forceinline__ void load_step(Unit<F> (&w)[CPL][RT], __amdgpu_buffer_rsrc_t rc,
+__device__ __forceinline__ void load_step(Unit<F> (&w)[CPL][RT], const __amdgpu_buffer_rsrc_t (&rc)[RT],
                                           const uint32_t (&oc)[RT], int seg_unit, int li, int U, int c)
 {
     constexpr int CB = Unit<F>::CB;
     const int du = min(seg_unit + c * LPR, U - 1 - li);
 #pragma unroll
-    for (int r = 0; r < RT; ++r) load_codes<F>(w[c][r], rc, oc[r] + du * CB);
+    for (int r = 0; r < RT; ++r) load_codes<F>(w[c][r], rc[r], oc[r] + du * CB);
 }
 
 // Unit steps whose code loads are in flight ahead of the step being computed.
@@ -743,7 +746,7 @@ template <int CPL> struct Lead { static constexpr int v = (QMV_LEAD > 0 && QMV_L
 
 template <int F, int LPR, int CPL, int RT, int NV>
 __device__ __forceinline__ void mac_seg(Unit<F> (&w)[CPL][RT], const Args &a, const uint8_t *lds,
-                                        __amdgpu_buffer_rsrc_t rc, const uint32_t (&oc)[RT],
+                                        const __amdgpu_buffer_rsrc_t (&rc)[RT], const uint32_t (&oc)[RT],
                                         int seg_unit, int u0, int U, float (&acc)[RT][NV])
 {
     constexpr int LEAD = Lead<CPL>::v;
@@ -767,30 +770,44 @@ __device__ __forceinline__ void mac_seg(Unit<F> (&w)[CPL][RT], const Args &a, co
     }
 }
 
+// y = silu(g) * u with silu(g) = g / (1 + e^-g), in f32 (SwiGLU, the gated
+// activation between an MoE expert's gate/up and down projections).
+__device__ __forceinline__ float swiglu(float g, float u)
+{
+    return g / (1.0f + __expf(-g)) * u;
+}
+
 // One workgroup, one item, one tile of rows.  Order of work per lane:
 //   1. activation staging loads (registers)
-//   2. all weight loads of the first segment (CPL units x RT rows)
+//   2. all scale loads, then code loads one unit step ahead (load_step)
 //   3. activations to LDS, barrier (waits only for the staging loads)
 //   4. per unit, as its bytes arrive: decode and dot (progressive vmcnt)
 //   5. further segments when K needs them; butterfly; store.
-template <int F, int LPR, int CPL, int RT, int NV, int NVMAX>
+// MODE 0: the lane's RT rows are RT consecutive output rows.  MODE 1 (gate/up,
+// RT == 2): the lane's two rows are row n of the gate and row n of the up
+// projection, and the store writes swiglu(gate, up).
+template <int F, int LPR, int CPL, int RT, int NV, int NVMAX, int MODE>
 __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t *lds, int row_base,
                                           uint4 (&xr)[kXReg])
 {
+    static_assert(MODE == 0 || RT == 2, "gate/up rows come in pairs");
     constexpr int SLOTS = 64 / LPR;
     constexpr int SEG = LPR * CPL;
+    constexpr int NROW = MODE == 0 ? RT : 1;                  // output rows per lane
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int slot = lane / LPR;
     const int li = lane % LPR;
-    const int row0 = row_base + (wave * SLOTS + slot) * RT;
+    const int row0 = row_base + (wave * SLOTS + slot) * NROW;
     const int U = a.units;
-    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (long long)it.expert * a.expert_cb, a.expert_cb);
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.scales + (long long)it.expert * a.expert_sb, a.expert_sb);
+    __amdgpu_buffer_rsrc_t rc[RT], rs[RT];
     uint32_t oc[RT], os[RT];           // rows past N land past the expert's end: zeros
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-        const int n = row0 + r;
+        const bool up = MODE == 1 && r == 1;
+        rc[r] = buffer_rsrc((up ? a.codes2 : a.codes) + (long long)it.expert * a.expert_cb, a.expert_cb);
+        rs[r] = buffer_rsrc((up ? a.scales2 : a.scales) + (long long)it.expert * a.expert_sb, a.expert_sb);
+        const int n = row0 + (MODE == 0 ? r : 0);
         oc[r] = (uint32_t)__umul24(n, a.rcb) + li * Unit<F>::CB;
         os[r] = (uint32_t)__umul24(n, a.rsb) + li * Unit<F>::SB;
     }
@@ -824,15 +841,20 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
 #pragma unroll
         for (int v = 0; v < NV; ++v) acc[r][v] = group_sum<LPR>(acc[r][v]);
 
-    // Lane li < RT stores row row0 + li for every vector and destination.
-    if (li < RT) {
+    // Lane li < NROW stores row row0 + li for every vector and destination.
+    if (li < NROW) {
         const int n = row0 + li;
         if (n < a.N) {
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                float val = acc[0][v];
+                float val;
+                if constexpr (MODE == 1) {
+                    val = swiglu(acc[0][v], acc[1][v]);
+                } else {
+                    val = acc[0][v];
 #pragma unroll
-                for (int r = 1; r < RT; ++r) val = (li == r) ? acc[r][v] : val;
+                    for (int r = 1; r < RT; ++r) val = (li == r) ? acc[r][v] : val;
+                }
                 unsigned long long d = it.dest[v];
                 while (d) {
                     const int p = __ffsll((long long)d) - 1;
@@ -847,7 +869,7 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
 // ------------------------------------------------------------------ kernel
 // F: format kind; LPR: lanes per row; CPL: units per lane and row in flight;
 // RT: rows per lane; NVMAX: most activation vectors one item may carry.
-template <int F, int LPR, int CPL, int RT, int NVMAX>
+template <int F, int LPR, int CPL, int RT, int NVMAX, int MODE>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -866,13 +888,13 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const Args a)
         return;
     }
     if constexpr (NVMAX == 1) {
-        rows_body<F, LPR, CPL, RT, 1, 1>(a, it, lds, row_base, xr);
+        rows_body<F, LPR, CPL, RT, 1, 1, MODE>(a, it, lds, row_base, xr);
     } else {
         switch (it.nv) {
-        case 1: rows_body<F, LPR, CPL, RT, 1, NVMAX>(a, it, lds, row_base, xr); break;
-        case 2: rows_body<F, LPR, CPL, RT, 2, NVMAX>(a, it, lds, row_base, xr); break;
-        case 3: rows_body<F, LPR, CPL, RT, 3, NVMAX>(a, it, lds, row_base, xr); break;
-        default: rows_body<F, LPR, CPL, RT, 4, NVMAX>(a, it, lds, row_base, xr); break;
+        case 1: rows_body<F, LPR, CPL, RT, 1, NVMAX, MODE>(a, it, lds, row_base, xr); break;
+        case 2: rows_body<F, LPR, CPL, RT, 2, NVMAX, MODE>(a, it, lds, row_base, xr); break;
+        case 3: rows_body<F, LPR, CPL, RT, 3, NVMAX, MODE>(a, it, lds, row_base, xr); break;
+        default: rows_body<F, LPR, CPL, RT, 4, NVMAX, MODE>(a, it, lds, row_base, xr); break;
         }
     }
 }
@@ -889,18 +911,26 @@ extern const void *const kTable_mxfp4[3][4][5];
 extern const void *const kTable_cb2[3][4][5];
 extern const void *const kTable_cb2s[3][4][5];
 extern const void *const kTable_cb3[3][4][5];
+// Gate/up (SwiGLU) kernels: [variant 0 or 1][lpr][cpl].
+extern const void *const kTableGU_mxfp4[2][4][5];
+extern const void *const kTableGU_cb2[2][4][5];
+extern const void *const kTableGU_cb2s[2][4][5];
+extern const void *const kTableGU_cb3[2][4][5];
 
 }  // namespace qmv
 
-// Instantiate one format's kernel table: [variant][lpr index][cpl index].
-#define QMV_K(F, V, L, C) \
-    (const void *)&::qmv::qmv_kernel<F, L, C, ((V) == 2 ? 4 : 2), ((V) == 0 ? 1 : 4)>
-#define QMV_ROW01(F, V, L) \
-    { QMV_K(F, V, L, 1), QMV_K(F, V, L, 2), QMV_K(F, V, L, 3), QMV_K(F, V, L, 4), QMV_K(F, V, L, 7) }
+// Instantiate one format's kernel tables: [variant][lpr index][cpl index].
+#define QMV_K(F, V, L, C, MODE) \
+    (const void *)&::qmv::qmv_kernel<F, L, C, ((V) == 2 ? 4 : 2), ((V) == 0 ? 1 : 4), MODE>
+#define QMV_ROW01(F, V, L, MODE) \
+    { QMV_K(F, V, L, 1, MODE), QMV_K(F, V, L, 2, MODE), QMV_K(F, V, L, 3, MODE), QMV_K(F, V, L, 4, MODE), QMV_K(F, V, L, 7, MODE) }
 #define QMV_ROW2(F, V, L) \
-    { QMV_K(F, V, L, 1), QMV_K(F, V, L, 2), QMV_K(F, V, L, 4), nullptr, nullptr }
+    { QMV_K(F, V, L, 1, 0), QMV_K(F, V, L, 2, 0), QMV_K(F, V, L, 4, 0), nullptr, nullptr }
 #define QMV_NOROW { nullptr, nullptr, nullptr, nullptr, nullptr }
 #define QMV_TABLE(F) \
-    { { QMV_ROW01(F, 0, 8), QMV_ROW01(F, 0, 16), QMV_ROW01(F, 0, 32), QMV_ROW01(F, 0, 64) }, \
-      { QMV_ROW01(F, 1, 8), QMV_ROW01(F, 1, 16), QMV_ROW01(F, 1, 32), QMV_ROW01(F, 1, 64) }, \
+    { { QMV_ROW01(F, 0, 8, 0), QMV_ROW01(F, 0, 16, 0), QMV_ROW01(F, 0, 32, 0), QMV_ROW01(F, 0, 64, 0) }, \
+      { QMV_ROW01(F, 1, 8, 0), QMV_ROW01(F, 1, 16, 0), QMV_ROW01(F, 1, 32, 0), QMV_ROW01(F, 1, 64, 0) }, \
       { QMV_NOROW, QMV_ROW2(F, 2, 16), QMV_ROW2(F, 2, 32), QMV_ROW2(F, 2, 64) } }
+#define QMV_TABLE_GU(F) \
+    { { QMV_ROW01(F, 0, 8, 1), QMV_ROW01(F, 0, 16, 1), QMV_ROW01(F, 0, 32, 1), QMV_ROW01(F, 0, 64, 1) }, \
+      { QMV_ROW01(F, 1, 8, 1), QMV_ROW01(F, 1, 16, 1), QMV_ROW01(F, 1, 32, 1), QMV_ROW01(F, 1, 64, 1) } }

@@ -5,4 +5,6 @@
 namespace qmv {
 extern const void *const kTable_cb2s[3][4][5];
 const void *const kTable_cb2s[3][4][5] = QMV_TABLE(kCB2S);
+extern const void *const kTableGU_cb2s[2][4][5];
+const void *const kTableGU_cb2s[2][4][5] = QMV_TABLE_GU(kCB2S);
 }  // namespace qmv

@@ -5,4 +5,6 @@
 namespace qmv {
 extern const void *const kTable_cb3[3][4][5];
 const void *const kTable_cb3[3][4][5] = QMV_TABLE(kCB3);
+extern const void *const kTableGU_cb3[2][4][5];
+const void *const kTableGU_cb3[2][4][5] = QMV_TABLE_GU(kCB3);
 }  // namespace qmv

@@ -123,6 +123,25 @@ qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const void *w_
                             qmv_afmt_t afmt, const void *x, const void *x_scales,
                             int x_per_slot, float *y, int N, int K, hipStream_t stream);
 
+/*
+ * Fused gate/up expert projection with the SwiGLU activation:
+ *   y[t][j][n] = silu(g) * u,   silu(g) = g / (1 + e^-g),
+ *   g = sum_k w_gate(e, n, k) * x(t, k),   u = sum_k w_up(e, n, k) * x(t, k)
+ * with e = expert_ids[t][j] (0 where e is outside [0, E)).  Both projections
+ * use the weight format and layout above ([E][N][...] each) and the token's
+ * activation vector x[M][K]; y is fp32 [M][top_k][N].  One launch streams both
+ * weight tensors of the routed experts -- the gate and up expert projections
+ * that geo-lucebox PR #31 "DS4 H200: rocmfp2_mix MoE matvec" (Why this kernel)
+ * computes in one matvec kernel -- and hands the down projection its input
+ * directly.  Arguments, limits and errors as qmv_gather_moe; silu is
+ * evaluated in fp32.
+ */
+qmv_status_t qmv_gather_moe_swiglu(qmv_wfmt_t wfmt, const void *gate_codes, const void *gate_scales,
+                                   const void *up_codes, const void *up_scales, int E,
+                                   const int32_t *expert_ids, int M, int top_k,
+                                   qmv_afmt_t afmt, const void *x, const void *x_scales,
+                                   float *y, int N, int K, hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char *qmv_strerror(qmv_status_t status);
 

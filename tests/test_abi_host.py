@@ -33,7 +33,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["qmv_dense", "qmv_gather_moe", "qmv_strerror"]
+    assert declared_functions() == ["qmv_dense", "qmv_gather_moe", "qmv_gather_moe_swiglu",
+                                    "qmv_strerror"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -113,3 +114,19 @@ def test_product_path_never_imports_the_oracle():
                 with open(os.path.join(dirpath, f)) as fh:
                     src = fh.read()
                 assert "oracle" not in src.replace("oracle-", ""), os.path.join(dirpath, f)
+
+
+def swiglu(L, wfmt=W_MXFP4, gc=FAKE, gs=FAKE, uc=FAKE, us=FAKE, E=32, ids=FAKE, M=1, top_k=4,
+           afmt=A_BF16, x=FAKE, xs=None, y=FAKE, N=2880, K=2880):
+    return L.qmv_gather_moe_swiglu(wfmt, gc, gs, uc, us, E, ids, M, top_k, afmt, x, xs, y, N, K,
+                                   None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(uc=None), EINVAL), (dict(us=None), EINVAL), (dict(gc=None), EINVAL),
+    (dict(uc=FAKE + 8), EINVAL), (dict(ids=None), EINVAL), (dict(M=5), EUNSUP),
+    (dict(K=100), EUNSUP), (dict(wfmt=W_CB2), EUNSUP),
+    (dict(wfmt=W_CB3, afmt=A_Q8, xs=FAKE, us=FAKE + 2), EINVAL),
+])
+def test_swiglu_validation(L, kw, want):
+    assert swiglu(L, **kw) == want
