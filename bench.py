@@ -17,8 +17,13 @@ stream, bracketed by device synchronizations.
 Prints ONE JSON line.  ``value`` is effective weight GB/s (code + scale bytes
 of the experts a call reads / time per call).  ``roofline`` relates the
 kernel's algorithmic bytes (weights + activations + ids + output) per launch
-to the 8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same workload on the host's cores.  ``workloads`` lists the
+to the 8 TB/s HBM peak.  ``stream_ceiling`` times a read-only probe kernel
+over exactly the same code and scale bytes (no decode, no ids), so the GEMV's
+time can also be read against what the memory system delivers for that
+transfer.  Each workload also gets a hot-cache time (the same buffers every
+call, so the Infinity Cache serves them).  ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload on all host cores, and
+``cpu_baseline_1thread`` on one.  ``workloads`` lists the
 other shapes measured the same way (not the headline), among them the fused
 gate/up + SwiGLU calls (qmv_gather_moe_swiglu) C2gu and C3gu.
 """
@@ -99,7 +104,13 @@ ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40, "C2gu": 4,
 
 
 class Prepared:
-    """Device-resident inputs of one workload plus per-call raw arguments."""
+    """Device-resident inputs of one workload plus per-call raw arguments.
+
+    ``args[i]`` addresses layer copy i % L (cold: the weights rotate through
+    more than the Infinity Cache holds); ``args_hot[i]`` always addresses copy
+    0 (hot: the same buffers every call).  ``regions[i]`` lists the (address,
+    bytes) ranges of codes and scales call i must read, for the stream probe.
+    """
 
     def __init__(self, name, calls, rotate=True):
         import torch
@@ -120,62 +131,66 @@ class Prepared:
                 t[layer].copy_(a0)
             return t
 
-        if gate_up:
-            self.codes, self.scales = layers(inp.gcodes), layers(inp.gscales)
-            self.codes2, self.scales2 = layers(inp.ucodes), layers(inp.uscales)
-        else:
-            self.codes, self.scales = layers(inp.codes), layers(inp.scales)
+        tensors = [(inp.gcodes, inp.gscales), (inp.ucodes, inp.uscales)] if gate_up else \
+            [(inp.codes, inp.scales)]
+        self.w = [(layers(c), layers(sc)) for c, sc in tensors]
         if wl.afmt == "bf16":
             self.x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
             self.xs = None
         else:
             self.x = torch.from_numpy(inp.x).to(dev)
             self.xs = torch.from_numpy(inp.xs.view(np.float16)).to(dev)
-        if wl.kind in ("gather", "gate_up"):
+        routed = wl.kind in ("gather", "gate_up")
+        if routed:
             if name in ("C3", "C4", "C3gu"):
                 ids = synth.disjoint_id_stream(wl.seed + 100, calls, wl.top_k, wl.E)
             else:
                 ids = synth.id_stream(wl.seed + 100, calls, wl.M, wl.top_k, wl.E)
             self.ids_host = ids
             self.ids = torch.from_numpy(ids).to(dev)
-            n_unique = np.array([len(np.unique(i)) for i in ids])
+            experts = [np.unique(i) for i in ids]
             self.y = torch.empty((wl.M, wl.top_k, wl.N), dtype=torch.float32, device=dev)
         else:
             self.ids_host = None
             self.ids = None
-            n_unique = np.ones(calls, np.int64)
+            experts = [np.zeros(1, np.int64) for _ in range(calls)]
             self.y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
         self.calls = calls
-        self.wbytes = np.array([weight_bytes(wl, u) for u in n_unique], np.float64)
-        if gate_up:
-            self.wbytes *= 2
+        n_unique = np.array([len(e) for e in experts])
+        self.wbytes = np.array([weight_bytes(wl, u) for u in n_unique], np.float64) * len(self.w)
         self.abytes = self.wbytes + other_bytes(wl)
         self.lib = q.lib()
-        cstride = self.codes[0].numel()
-        sstride = self.scales[0].numel()
-        self.args = []
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        rcb = synth.row_code_bytes(wl.wfmt, wl.K) * wl.N
+        rsb = synth.row_scale_bytes(wl.wfmt, wl.K) * wl.N
+        afmt = 0 if wl.afmt == "bf16" else 1
+        xs = None if self.xs is None else self.xs.data_ptr()
+        self.args, self.args_hot, self.regions = [], [], []
         for i in range(calls):
-            layer = i % self.L
-            cp = self.codes.data_ptr() + layer * cstride
-            sp = self.scales.data_ptr() + layer * sstride
-            xs = None if self.xs is None else self.xs.data_ptr()
-            idp = None if self.ids is None else self.ids.data_ptr() + i * wl.M * wl.top_k * 4
-            afmt = 0 if wl.afmt == "bf16" else 1
-            if gate_up:
-                self.args.append((WFMT[wl.wfmt], cp, sp, self.codes2.data_ptr() + layer * cstride,
-                                  self.scales2.data_ptr() + layer * sstride, wl.E, idp, wl.M,
-                                  wl.top_k, afmt, self.x.data_ptr(), xs, self.y.data_ptr(), wl.N,
-                                  wl.K))
-            elif wl.kind == "gather":
-                self.args.append((WFMT[wl.wfmt], cp, sp, wl.E, idp, wl.M, wl.top_k, afmt,
-                                  self.x.data_ptr(), xs, int(wl.x_per_slot), self.y.data_ptr(),
-                                  wl.N, wl.K))
-            else:
-                self.args.append((WFMT[wl.wfmt], cp, sp, afmt, self.x.data_ptr(), xs,
-                                  self.y.data_ptr(), wl.M, wl.N, wl.K))
+            for hot in (False, True):
+                layer = 0 if hot else i % self.L
+                wp = [(c.data_ptr() + layer * c[0].numel(), sc.data_ptr() + layer * sc[0].numel())
+                      for c, sc in self.w]
+                idp = None if self.ids is None else self.ids.data_ptr() + i * wl.M * wl.top_k * 4
+                if gate_up:
+                    a = (WFMT[wl.wfmt], wp[0][0], wp[0][1], wp[1][0], wp[1][1], wl.E, idp, wl.M,
+                         wl.top_k, afmt, self.x.data_ptr(), xs, self.y.data_ptr(), wl.N, wl.K)
+                elif routed:
+                    a = (WFMT[wl.wfmt], wp[0][0], wp[0][1], wl.E, idp, wl.M, wl.top_k, afmt,
+                         self.x.data_ptr(), xs, int(wl.x_per_slot), self.y.data_ptr(), wl.N, wl.K)
+                else:
+                    a = (WFMT[wl.wfmt], wp[0][0], wp[0][1], afmt, self.x.data_ptr(), xs,
+                         self.y.data_ptr(), wl.M, wl.N, wl.K)
+                (self.args_hot if hot else self.args).append(a)
+                if not hot:
+                    reg = [(cp + int(e) * rcb, rcb) for cp, _ in wp for e in experts[i]] + \
+                          [(sp + int(e) * rsb, rsb) for _, sp in wp for e in experts[i]]
+                    n = len(reg)
+                    self.regions.append((n, (ctypes.c_void_p * n)(*[r[0] for r in reg]),
+                                         (ctypes.c_longlong * n)(*[r[1] for r in reg])))
 
-    def call(self, i, stream_handle):
-        a = self.args[i]
+    def call(self, i, stream_handle, hot=False):
+        a = (self.args_hot if hot else self.args)[i]
         if self.wl.kind == "gate_up":
             s = self.lib.qmv_gather_moe_swiglu(*a, ctypes.c_void_p(stream_handle))
         elif self.wl.kind == "gather":
@@ -185,21 +200,28 @@ class Prepared:
         if s != 0:
             raise RuntimeError(f"{self.name}: status {s}")
 
+    def probe(self, i, stream_handle, variant):
+        n, ptrs, sizes = self.regions[i]
+        s = self.lib.qmv_probe_stream_read(n, ptrs, sizes, variant, self.sink.data_ptr(),
+                                           ctypes.c_void_p(stream_handle))
+        if s != 0:
+            raise RuntimeError(f"{self.name}: probe status {s}")
 
-def time_graph(p, first, count):
-    """Capture calls [first, first+count) into one graph, replay it once
-    (untimed), then replay it timed.  Returns seconds per call."""
+
+def time_graph(fn, first, count):
+    """Capture fn(i, stream) for i in [first, first+count) into one graph,
+    replay it once (untimed), then replay it timed.  Returns seconds per call."""
     import torch
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         for i in range(first, min(first + 3, first + count)):   # eager warm-up on the stream
-            p.call(i, s.cuda_stream)
+            fn(i, s.cuda_stream)
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=s):
         h = torch.cuda.current_stream().cuda_stream
         for i in range(first, first + count):
-            p.call(i, h)
+            fn(i, h)
     torch.cuda.synchronize()
     g.replay()                                   # untimed replay: graph upload, warm clocks
     torch.cuda.synchronize()
@@ -229,13 +251,26 @@ def time_eager(p, first, count):
     return e0.elapsed_time(e1) * 1e-3 / count
 
 
-def measure(name, steps, warmup, rotate=True):
-    p = Prepared(name, warmup + steps, rotate=rotate)
+def stream_ceiling(p, first, count):
+    """Best time per call over the probe's launch shapes for reading exactly
+    the bytes of calls [first, first+count): the practical read ceiling."""
+    import bit_block_quantized_amd as q
+    best = None
+    for v in range(q.PROBE_VARIANTS):
+        t = time_graph(lambda i, h: p.probe(i, h, v), first, count)
+        if best is None or t < best[0]:
+            best = (t, v)
+    return best
+
+
+def measure(name, steps, warmup, hot=True):
+    """Cold (rotated) timing of the workload, then the stream ceiling for the
+    same calls, the hot-cache timing and the eager-launch timing."""
     import torch
-    # warm-up: W untimed calls through their own graph
+    p = Prepared(name, warmup + steps)
     if warmup:
-        time_graph(p, 0, warmup)
-    t = time_graph(p, warmup, steps)
+        time_graph(p.call, 0, warmup)
+    t = time_graph(p.call, warmup, steps)
     sel = slice(warmup, warmup + steps)
     wb = float(p.wbytes[sel].mean())
     ab = float(p.abytes[sel].mean())
@@ -247,29 +282,53 @@ def measure(name, steps, warmup, rotate=True):
         "pct_hbm_peak": 100.0 * (ab / t / 1e9) / HBM_PEAK_GBS,
         "layers_rotated": p.L,
     }
+    ts, v = stream_ceiling(p, warmup, min(steps, 500))
+    wcode = float(p.wbytes[warmup:warmup + min(steps, 500)].mean())
+    res["stream_ceiling_us_per_call"] = ts * 1e6
+    res["stream_ceiling_GBps"] = wcode / ts / 1e9
+    res["pct_of_stream_ceiling"] = 100.0 * ts / t
+    res["stream_probe_variant"] = v
+    if hot:
+        th = time_graph(lambda i, h: p.call(i, h, hot=True), warmup, min(steps, 500))
+        res["hot_us_per_call"] = th * 1e6
     te = time_eager(p, warmup, min(steps, 200))
     res["us_per_call_eager_launch"] = te * 1e6
     torch.cuda.synchronize()
     return p, res
 
 
-def cpu_baseline(p, target_s=10.0):
-    """The oracle (as it stands) on whole calls of the workload, all host
-    cores (one thread per disjoint output slice), for about ``target_s``."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(p, target_s=10.0, threads=None):
+    """The oracle (as it stands) on whole calls of the workload, ``threads``
+    host threads (default: all cores) over disjoint output slices, for about
+    ``target_s`` seconds; the rate and the median time per call."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gpu_util import oracle_call
     import synth
     wl = p.wl
-    cores = host_cores()
-    inp = p.inp
+    cores = threads or host_cores()
     calls = 0
     t0 = time.perf_counter()
     wbytes = 0.0
+    per_call = []
     while True:
         i = calls % p.calls
+        inp = p.inp
         if p.ids_host is not None:
             inp = synth.Inputs(wl, p.inp.codes, p.inp.scales, p.ids_host[i], p.inp.x, p.inp.xs)
+        t1 = time.perf_counter()
         oracle_call(inp, nthreads=cores)
+        per_call.append(time.perf_counter() - t1)
         wbytes += float(p.wbytes[i])
         calls += 1
         el = time.perf_counter() - t0
@@ -279,12 +338,32 @@ def cpu_baseline(p, target_s=10.0):
         "value": wbytes / el / 1e9,
         "unit": "GB/s",
         "us_per_call": el / calls * 1e6,
+        "us_per_call_median": float(np.median(per_call)) * 1e6,
         "cores": cores,
         "kind": "oracle",
+        "cpu": cpu_model(),
         "sample": f"{calls} complete {wl.name} calls (fresh ids, {wl.M} token(s), "
-                  f"K={wl.K}, N={wl.N}), fp64 C oracle, {cores} threads over disjoint outputs, "
+                  f"K={wl.K}, N={wl.N}), fp64 C oracle, {cores} thread(s) over disjoint outputs, "
                   f"{el:.1f} s wall",
     }
+
+
+def gpu_clocks():
+    """Shader and memory clock levels from sysfs (plain file reads; the level
+    in use is marked '*'), or None where the driver does not expose them."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for kind in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev, kind)) as f:
+                    levels = [ln.strip() for ln in f if ln.strip()]
+            except OSError:
+                continue
+            cur = [ln for ln in levels if ln.endswith("*")]
+            out[f"{os.path.basename(os.path.dirname(dev))}:{kind}"] = \
+                (cur[0] if cur else None, levels[-1] if levels else None)
+    return out or None
 
 
 def main():
@@ -307,17 +386,15 @@ def main():
     import torch
     torch.cuda.set_device(0)
 
-    p, head = measure(HEADLINE, args.steps, args.warmup)
+    p, head = measure(HEADLINE, args.steps, args.warmup, hot=not args.no_hot)
     extra = {}
     if not args.no_extra:
         for name in [w for w in args.workloads.split(",") if w and w != HEADLINE]:
-            pe, r = measure(name, max(50, args.steps // 5), 10)
+            pe, r = measure(name, max(50, args.steps // 5), 10, hot=not args.no_hot)
             r["desc"] = pe.wl.desc
             extra[name] = r
             del pe
             torch.cuda.empty_cache()
-    hot = {"us_per_call": float("nan")} if args.no_hot else \
-        measure(HEADLINE, min(args.steps, 500), 10, rotate=False)[1]
 
     t = head["us_per_call"] * 1e-6
     out = {
@@ -343,7 +420,15 @@ def main():
         "us_per_call": round(head["us_per_call"], 3),
         "pct_hbm_peak": round(head["pct_hbm_peak"], 2),
         "us_per_call_eager_launch": round(head["us_per_call_eager_launch"], 3),
-        "hot_cache_us_per_call": round(hot["us_per_call"], 3),
+        "hot_cache_us_per_call": round(head.get("hot_us_per_call", float("nan")), 3),
+        "stream_ceiling": {
+            "us_per_call": round(head["stream_ceiling_us_per_call"], 3),
+            "weight_GBps": round(head["stream_ceiling_GBps"], 2),
+            "pct_of_ceiling": round(head["pct_of_stream_ceiling"], 2),
+            "what": "qmv_probe_stream_read over exactly the code and scale bytes of the same "
+                    "calls (16-byte non-temporal buffer loads, no decode, no ids), best of "
+                    "its launch shapes, timed the same way",
+        },
         "roofline": {
             "bound": "hbm",
             "achieved": round(head["algorithmic_bytes_per_call"] / t / 1e9, 2),
@@ -359,6 +444,8 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+        out["cpu_baseline_1thread"] = cpu_baseline(p, args.cpu_seconds / 2, threads=1)
+    out["gpu_clocks"] = gpu_clocks()
     print(json.dumps(out), flush=True)
 
 

@@ -24,7 +24,8 @@ import os
 
 import torch  # noqa: F401  -- loads the HIP runtime that libqmv.so binds to
 
-__all__ = ["qmv_dense", "qmv_gather_moe", "qmv_gather_moe_swiglu", "qmv_strerror", "lib", "LIB_PATH",
+__all__ = ["qmv_dense", "qmv_gather_moe", "qmv_gather_moe_swiglu", "qmv_strerror",
+           "qmv_probe_stream_read", "lib", "LIB_PATH",
            "W_MXFP4", "W_CB2", "W_CB3", "A_BF16", "A_Q8B32", "QmvError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
@@ -61,6 +62,8 @@ def lib():
     L.qmv_gather_moe.argtypes = [I, P, P, I, P, I, I, I, P, P, I, P, I, I, P]
     L.qmv_gather_moe_swiglu.restype = I
     L.qmv_gather_moe_swiglu.argtypes = [I, P, P, P, P, I, P, I, I, I, P, P, P, I, I, P]
+    L.qmv_probe_stream_read.restype = I
+    L.qmv_probe_stream_read.argtypes = [I, P, P, I, P, P]
     L.qmv_strerror.restype = ctypes.c_char_p
     L.qmv_strerror.argtypes = [I]
     _lib = L
@@ -177,3 +180,18 @@ def qmv_gather_moe_swiglu(wfmt, gate_codes, gate_scales, up_codes, up_scales, ex
         _dev_ptr(y, "y", (torch.float32,), dev), N, K, _stream(dev, stream))
     _check(s)
     return y
+
+
+PROBE_VARIANTS = 6
+
+
+def qmv_probe_stream_read(regions, variant, sink, stream=None):
+    """Read-only streaming probe (include/qmv_probe.h): ``regions`` is a list
+    of (device address, bytes); ``sink`` a 1-element int32 device tensor."""
+    n = len(regions)
+    ptrs = (ctypes.c_void_p * n)(*[int(p) for p, _ in regions])
+    sizes = (ctypes.c_longlong * n)(*[int(b) for _, b in regions])
+    dev = sink.device
+    _check(lib().qmv_probe_stream_read(n, ptrs, sizes, int(variant),
+                                       _dev_ptr(sink, "sink", (torch.int32,), dev),
+                                       _stream(dev, stream)))

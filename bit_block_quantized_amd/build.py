@@ -18,7 +18,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["qmv.hip", "qmv_k_mxfp4.hip", "qmv_k_cb2.hip", "qmv_k_cb2s.hip", "qmv_k_cb3.hip"]
+SOURCES = ["qmv.hip", "qmv_k_mxfp4.hip", "qmv_k_cb2.hip", "qmv_k_cb2s.hip", "qmv_k_cb3.hip",
+           "qmv_probe.hip"]
 LIB = os.path.join(HERE, "libqmv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -118,6 +118,18 @@ __device__ __forceinline__ int chunk_at(int u0, int c, int q)
     else return chunk_pos<CH>(u0 + c * LPR, q);
 }
 
+// One 16-byte LDS read as a single vector load.  Reading through a HIP
+// uint4 lets the compiler split the struct into per-field loads and rebuild
+// them as ds_read_b96 + ds_read_b32, whose 4-byte part hits only a quarter
+// of the banks at a 16-byte lane stride; a native vector load stays one
+// ds_read_b128.
+__device__ __forceinline__ uint4 lds_read16(const uint8_t *p)
+{
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = *(const v4u *)__builtin_assume_aligned(p, 16);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ------------------------------------------------------------------ routing
 // A work item: one expert and up to four activation vectors that read it.
 struct Item {
@@ -478,7 +490,7 @@ __device__ __forceinline__ void mac_mxfp4(const Unit<kMXFP4> (&w)[RT], const uin
     for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            xq[v][q] = *(const uint4 *)(lds + v * vec_bytes + 16 * chunk_at<4, LPR>(u0, cu, q));
+            xq[v][q] = lds_read16(lds + v * vec_bytes + 16 * chunk_at<4, LPR>(u0, cu, q));
     if (fast) {
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
@@ -553,9 +565,9 @@ __device__ __forceinline__ void mac_cb2(const Unit<F> (&w)[RT], const uint8_t *l
         const uint8_t *base = lds + v * vec_bytes;
 #pragma unroll
         for (int q = 0; q < CH; ++q)
-            xq[v][q] = *(const uint4 *)(base + 16 * chunk_at<CH, LPR>(u0, cu, q));
+            xq[v][q] = lds_read16(base + 16 * chunk_at<CH, LPR>(u0, cu, q));
         if constexpr (NB == 2) {
-            const uint4 sd = *(const uint4 *)(base + xbytes + 16 * u);
+            const uint4 sd = lds_read16(base + xbytes + 16 * u);
             xsh[v][0] = __uint_as_float(sd.x);
             xsh[v][1] = __uint_as_float(sd.y);
             nq[v][0] = (int)sd.z;
@@ -641,8 +653,8 @@ __device__ __forceinline__ void mac_cb3(const Unit<kCB3> (&w)[RT], const uint8_t
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const uint8_t *base = lds + v * vec_bytes;
-        xq[v][0] = *(const uint4 *)(base + 16 * chunk_at<2, LPR>(u0, cu, 0));
-        xq[v][1] = *(const uint4 *)(base + 16 * chunk_at<2, LPR>(u0, cu, 1));
+        xq[v][0] = lds_read16(base + 16 * chunk_at<2, LPR>(u0, cu, 0));
+        xq[v][1] = lds_read16(base + 16 * chunk_at<2, LPR>(u0, cu, 1));
         xsh[v] = ((const float *)(base + xbytes))[u];
     }
 #pragma unroll

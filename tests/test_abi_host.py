@@ -25,24 +25,36 @@ def L():
     return q.lib()
 
 
-def declared_functions():
-    with open(os.path.join(ROOT, "include", "qmv.h")) as f:
-        src = f.read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(qmv_[a-z_]+)\s*\(", src)))
+def declared_functions(header=None):
+    """qmv_* functions declared in one header, or in every include/*.h."""
+    inc = os.path.join(ROOT, "include")
+    names = [header] if header else sorted(f for f in os.listdir(inc) if f.endswith(".h"))
+    found = set()
+    for h in names:
+        with open(os.path.join(inc, h)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        found |= set(re.findall(r"\b(qmv_[a-z_]+)\s*\(", src))
+    return sorted(found)
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["qmv_dense", "qmv_gather_moe", "qmv_gather_moe_swiglu",
-                                    "qmv_strerror"]
+    assert declared_functions("qmv.h") == ["qmv_dense", "qmv_gather_moe",
+                                           "qmv_gather_moe_swiglu", "qmv_strerror"]
+    assert declared_functions("qmv_probe.h") == ["qmv_probe_stream_read"]
 
 
 def test_library_exports_every_declared_symbol(L):
-    for name in declared_functions():
+    declared = declared_functions()
+    assert len(declared) == 5
+    for name in declared:
         assert hasattr(L, name), name
     out = os.popen(f"nm -D --defined-only {ROOT}/bit_block_quantized_amd/libqmv.so").read()
-    for name in declared_functions():
+    for name in declared:
         assert re.search(rf"\bT {name}\b", out), name
+    # nothing but the declared entry points is exported as a function
+    exported = set(re.findall(r"\bT (\S+)", out))
+    assert exported == set(declared), sorted(exported - set(declared))
 
 
 def test_strerror_covers_every_status(L):
@@ -130,3 +142,19 @@ def swiglu(L, wfmt=W_MXFP4, gc=FAKE, gs=FAKE, uc=FAKE, us=FAKE, E=32, ids=FAKE, 
 ])
 def test_swiglu_validation(L, kw, want):
     assert swiglu(L, **kw) == want
+
+
+def probe(L, n=1, ptrs=(FAKE,), sizes=(4096,), variant=0, sink=FAKE):
+    P = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    B = (ctypes.c_longlong * max(1, len(sizes)))(*sizes)
+    return L.qmv_probe_stream_read(n, P, B, variant, sink, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(n=0), EUNSUP), (dict(n=65), EUNSUP), (dict(variant=6), EUNSUP),
+    (dict(variant=-1), EUNSUP), (dict(ptrs=(FAKE + 8,)), EINVAL), (dict(ptrs=(0,)), EINVAL),
+    (dict(sizes=(0,)), EINVAL), (dict(sizes=(2 ** 31,)), EINVAL), (dict(sink=None), EINVAL),
+    (dict(sink=FAKE + 2), EINVAL),
+])
+def test_probe_validation(L, kw, want):
+    assert probe(L, **kw) == want
