@@ -18,8 +18,13 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["qmv.hip", "qmv_k_mxfp4.hip", "qmv_k_cb2.hip", "qmv_k_cb2s.hip", "qmv_k_cb3.hip",
-           "qmv_probe.hip"]
+KERNEL_SOURCES = ["qmv_k_mxfp4.hip", "qmv_k_cb2.hip", "qmv_k_cb2s.hip", "qmv_k_cb3.hip"]
+# (source, extra flags, object): the launcher, the probe, and every kernel
+# table twice -- 4 and 8 wave64s per workgroup, in namespaces qmv / qmv_w8.
+UNITS = ([("qmv.hip", [], "qmv.o"), ("qmv_probe.hip", [], "qmv_probe.o")] +
+         [(k, [], k.replace(".hip", ".o")) for k in KERNEL_SOURCES] +
+         [(k, ["-DQMV_WAVES=8", "-DQMV_NS=qmv_w8"], k.replace(".hip", "_w8.o")) for k in KERNEL_SOURCES])
+SOURCES = [u[0] for u in UNITS]
 LIB = os.path.join(HERE, "libqmv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -34,16 +39,18 @@ FLAGS = [
 def build(out: str = LIB, extra: list | None = None, verbose: bool = False) -> str:
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     with tempfile.TemporaryDirectory(prefix="qmv_build_") as tmp:
-        def compile_one(src):
-            obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [HIPCC, *FLAGS, *inc, *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
+        def compile_one(unit):
+            src, defs, objname = unit
+            obj = os.path.join(tmp, objname)
+            cmd = [HIPCC, *FLAGS, *inc, *defs, *(extra or []), "-c", os.path.join(CSRC, src),
+                   "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             subprocess.run(cmd, check=True)
             return obj
-        jobs = min(len(SOURCES), max(1, os.cpu_count() or 1))
+        jobs = min(len(UNITS), max(1, os.cpu_count() or 1))
         with ThreadPoolExecutor(jobs) as ex:
-            objs = list(ex.map(compile_one, SOURCES))
+            objs = list(ex.map(compile_one, UNITS))
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -9,16 +9,46 @@
 #include <mutex>
 #include <stdint.h>
 
+// The same kernel tables built with 8 wave64s per workgroup (qmv_device.hpp).
+namespace qmv_w8 {
+extern const void *const kTable_mxfp4[3][4][5];
+extern const void *const kTable_cb2[3][4][5];
+extern const void *const kTable_cb2s[3][4][5];
+extern const void *const kTable_cb3[3][4][5];
+extern const void *const kTableGU_mxfp4[2][4][5];
+extern const void *const kTableGU_cb2[2][4][5];
+extern const void *const kTableGU_cb2s[2][4][5];
+extern const void *const kTableGU_cb3[2][4][5];
+}  // namespace qmv_w8
+
 namespace {
 
 using namespace qmv;
+
+constexpr int kWaveMenu[2] = {4, 8};     // wave64s per workgroup: qmv, qmv_w8
 
 constexpr int kMaxK = 16384;
 constexpr int kMaxM = 4;
 constexpr int kMaxTopK = 16;
 
-const void *kernel_for(int kind, int variant, int li, int ci, bool gate_up)
+const void *kernel_for(int wi, int kind, int variant, int li, int ci, bool gate_up)
 {
+    if (wi == 1) {
+        if (gate_up) {
+            switch (kind) {
+            case kMXFP4: return qmv_w8::kTableGU_mxfp4[variant][li][ci];
+            case kCB2: return qmv_w8::kTableGU_cb2[variant][li][ci];
+            case kCB2S: return qmv_w8::kTableGU_cb2s[variant][li][ci];
+            default: return qmv_w8::kTableGU_cb3[variant][li][ci];
+            }
+        }
+        switch (kind) {
+        case kMXFP4: return qmv_w8::kTable_mxfp4[variant][li][ci];
+        case kCB2: return qmv_w8::kTable_cb2[variant][li][ci];
+        case kCB2S: return qmv_w8::kTable_cb2s[variant][li][ci];
+        default: return qmv_w8::kTable_cb3[variant][li][ci];
+        }
+    }
     if (gate_up) {
         switch (kind) {
         case kMXFP4: return kTableGU_mxfp4[variant][li][ci];
@@ -131,8 +161,43 @@ Shape pick_shape(int variant, int units, long long rows_total, int rt)
     return best;
 }
 
-std::once_flag g_attr_once[2][4][3][4][5];
-hipError_t g_attr_err[2][4][3][4][5];
+// Launch shapes measured best on MI355X for the MoE expert shapes this library
+// is tuned on (sweeps of every menu shape at 4 and 8 waves per workgroup, HBM-
+// resident weights rotated past the Infinity Cache).  Other shapes use
+// pick_shape() with 4 waves.  An entry matches on format kind, variant,
+// gate/up mode, K, N and the number of (token, slot) pairs.
+struct Tuned { int kind, variant, gate_up, K, N, pairs, waves, lpr, cpl; };
+constexpr Tuned kTuned[] = {
+    {kMXFP4, 0, 0, 2880, 2880, 4, 4, 32, 3},     // gpt-oss-20b expert projection
+    {kMXFP4, 0, 1, 2880, 2880, 4, 4, 32, 3},     // gpt-oss-20b gate+up, SwiGLU
+    {kCB2,   0, 0, 7168, 2048, 4, 4, 64, 2},     // DeepSeek-shaped 2-bit gate/up
+    {kCB2,   0, 1, 7168, 2048, 4, 4, 16, 7},     // ... fused gate+up, SwiGLU
+    {kCB3,   1, 0, 2048, 7168, 4, 8, 16, 2},     // DeepSeek-shaped 3-bit down
+    {kMXFP4, 1, 0, 7168, 2048, 16, 4, 8, 7},     // 4 tokens x top-4 of 256
+    {kMXFP4, 2, 0, 7168, 7168, 1, 8, 64, 4},     // dense, 4 tokens
+};
+
+bool tuned_shape(int kind, int variant, bool gate_up, int K, int N, int pairs, int &wi, Shape &sh)
+{
+    for (const Tuned &t : kTuned) {
+        if (t.kind != kind || t.variant != variant || t.gate_up != (gate_up ? 1 : 0) || t.K != K ||
+            t.N != N || t.pairs != pairs)
+            continue;
+        wi = t.waves == 8 ? 1 : 0;
+        const int ncpl = variant == 2 ? 3 : 5;
+        for (int li = 0; li < 4; ++li)
+            for (int ci = 0; ci < ncpl; ++ci)
+                if (kMenuLpr[li] == t.lpr &&
+                    (variant == 2 ? kMenuCpl2[ci] : kMenuCpl01[ci]) == t.cpl) {
+                    sh = {li, ci, t.lpr, t.cpl};
+                    return true;
+                }
+    }
+    return false;
+}
+
+std::once_flag g_attr_once[2][2][4][3][4][5];
+hipError_t g_attr_err[2][2][4][3][4][5];
 
 // codes2/scales2 non-null selects the gate/up mode: codes/scales are the gate
 // projection, codes2/scales2 the up projection, y = swiglu(gate x, up x).
@@ -152,7 +217,10 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, const void 
     else                { variant = 2; rt = 4; }
     const int nvmax = variant == 0 ? 1 : 4;
     const long long rows_total = (long long)N * (gather ? M * top_k : 1) * (gate_up ? 2 : 1);
-    const Shape sh = pick_shape(variant, units, rows_total, rt);
+    Shape sh;
+    int wi = 0;
+    if (!tuned_shape(kind, variant, gate_up, K, N, gather ? M * top_k : 1, wi, sh))
+        sh = pick_shape(variant, units, rows_total, rt);
     Args a;
     a.codes = (const uint8_t *)codes;
     a.scales = (const uint8_t *)scales;
@@ -175,26 +243,27 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, const void 
     a.units = units;
     a.x_per_slot = gather ? x_per_slot : 0;
     a.x_early = (!gather || (M == 1 && !x_per_slot)) ? 1 : 0;
-    a.rows_per_tile = kWaves * (64 / sh.lpr) * (gate_up ? 1 : rt);
+    const int waves = kWaveMenu[wi];
+    a.rows_per_tile = waves * (64 / sh.lpr) * (gate_up ? 1 : rt);
     const int vec_bytes = units * (kUnitXB[kind] + kUnitAB[kind]);
     a.lds_vec_bytes = (vec_bytes + 15) & ~15;
     const size_t lds = (size_t)nvmax * a.lds_vec_bytes;
 
-    const void *fn = kernel_for(kind, variant, sh.li, sh.ci, gate_up);
+    const void *fn = kernel_for(wi, kind, variant, sh.li, sh.ci, gate_up);
     // Largest dynamic LDS this kernel can ask for (K = kMaxK, all vectors).
-    std::call_once(g_attr_once[gate_up][kind][variant][sh.li][sh.ci], [&] {
+    std::call_once(g_attr_once[wi][gate_up][kind][variant][sh.li][sh.ci], [&] {
         const int umax = kMaxK / kUnitWeights[kind];
         const int vmax = (umax * (kUnitXB[kind] + kUnitAB[kind]) + 15) & ~15;
-        g_attr_err[gate_up][kind][variant][sh.li][sh.ci] = hipFuncSetAttribute(
+        g_attr_err[wi][gate_up][kind][variant][sh.li][sh.ci] = hipFuncSetAttribute(
             fn, hipFuncAttributeMaxDynamicSharedMemorySize, nvmax * vmax);
     });
-    if (g_attr_err[gate_up][kind][variant][sh.li][sh.ci] != hipSuccess)
+    if (g_attr_err[wi][gate_up][kind][variant][sh.li][sh.ci] != hipSuccess)
         return QMV_EHIP;
 
     const dim3 grid((unsigned)((N + a.rows_per_tile - 1) / a.rows_per_tile),
                     (unsigned)(gather ? M * top_k : 1));
     void *kargs[] = {&a};
-    if (hipLaunchKernel(fn, grid, dim3(kThreads), kargs, lds, stream) != hipSuccess)
+    if (hipLaunchKernel(fn, grid, dim3(64 * waves), kargs, lds, stream) != hipSuccess)
         return QMV_EHIP;
     return QMV_OK;
 }

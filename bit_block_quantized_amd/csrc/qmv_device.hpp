@@ -23,7 +23,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace qmv {
+// The kernels are instantiated twice, with 4 and with 8 wave64s per
+// workgroup (a larger workgroup stages the activations once for twice the
+// rows); QMV_NS keeps the two sets of names apart.
+#ifndef QMV_NS
+#define QMV_NS qmv
+#endif
+
+namespace QMV_NS {
 
 #ifndef QMV_WAVES
 #define QMV_WAVES 4
@@ -929,11 +936,11 @@ extern const void *const kTableGU_cb2[2][4][5];
 extern const void *const kTableGU_cb2s[2][4][5];
 extern const void *const kTableGU_cb3[2][4][5];
 
-}  // namespace qmv
+}  // namespace QMV_NS
 
 // Instantiate one format's kernel tables: [variant][lpr index][cpl index].
 #define QMV_K(F, V, L, C, MODE) \
-    (const void *)&::qmv::qmv_kernel<F, L, C, ((V) == 2 ? 4 : 2), ((V) == 0 ? 1 : 4), MODE>
+    (const void *)&::QMV_NS::qmv_kernel<F, L, C, ((V) == 2 ? 4 : 2), ((V) == 0 ? 1 : 4), MODE>
 #define QMV_ROW01(F, V, L, MODE) \
     { QMV_K(F, V, L, 1, MODE), QMV_K(F, V, L, 2, MODE), QMV_K(F, V, L, 3, MODE), QMV_K(F, V, L, 4, MODE), QMV_K(F, V, L, 7, MODE) }
 #define QMV_ROW2(F, V, L) \

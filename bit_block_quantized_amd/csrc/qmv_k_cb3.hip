@@ -1,10 +1,11 @@
 // qmv_k_cb3.hip -- kernel instantiations for one weight format (split into
-// one translation unit per format so the build runs in parallel).
+// one translation unit per format so the build runs in parallel; built once
+// per workgroup size, see QMV_NS in qmv_device.hpp).
 #include "qmv_device.hpp"
 
-namespace qmv {
+namespace QMV_NS {
 extern const void *const kTable_cb3[3][4][5];
 const void *const kTable_cb3[3][4][5] = QMV_TABLE(kCB3);
 extern const void *const kTableGU_cb3[2][4][5];
 const void *const kTableGU_cb3[2][4][5] = QMV_TABLE_GU(kCB3);
-}  // namespace qmv
+}  // namespace QMV_NS

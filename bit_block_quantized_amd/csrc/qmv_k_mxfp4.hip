@@ -1,10 +1,11 @@
 // qmv_k_mxfp4.hip -- kernel instantiations for one weight format (split into
-// one translation unit per format so the build runs in parallel).
+// one translation unit per format so the build runs in parallel; built once
+// per workgroup size, see QMV_NS in qmv_device.hpp).
 #include "qmv_device.hpp"
 
-namespace qmv {
+namespace QMV_NS {
 extern const void *const kTable_mxfp4[3][4][5];
 const void *const kTable_mxfp4[3][4][5] = QMV_TABLE(kMXFP4);
 extern const void *const kTableGU_mxfp4[2][4][5];
 const void *const kTableGU_mxfp4[2][4][5] = QMV_TABLE_GU(kMXFP4);
-}  // namespace qmv
+}  // namespace QMV_NS
