@@ -80,6 +80,9 @@ def _bind(lib):
     lib.oracle_qmv_gather_swiglu_sel.restype = _I
     lib.oracle_qmv_gather_swiglu_sel.argtypes = [_I, _P, _P, _P, _P, _L, _P, _L, _L, _I, _P, _P,
                                                  _L, _L, _P, _L, _P, _P, _P, _P, _P]
+    lib.oracle_qmv_combine_sel.restype = _I
+    lib.oracle_qmv_combine_sel.argtypes = [_I, _P, _P, _L, _P, _P, _L, _L, _I, _P, _P, _I,
+                                           _L, _L, _P, _L, _P, _P]
     lib.oracle_mutant_id.restype = _I
     lib.oracle_mutant_id.argtypes = []
     return lib
@@ -228,6 +231,32 @@ class Oracle:
         if outs is None:
             res = [r.reshape(shape) for r in res]
         return tuple(res)
+
+    def combine(self, wfmt, codes, scales, ids, weights, afmt, x, xs=None, x_per_slot=True,
+                outs=None):
+        """Down projection with the router-weighted combine; returns (y, A) in
+        fp64 shaped [M][N] (or flat over ``outs``, indices t * N + n)."""
+        codes, scales = _c(codes, np.uint8), _c(scales, np.uint8)
+        ids = _c(ids, np.int32)
+        weights = _c(weights, np.float32)
+        E, N = codes.shape[0], codes.shape[1]
+        M, top_k = ids.shape
+        assert weights.shape == ids.shape
+        x = self._xarr(afmt, x)
+        K = x.shape[-1]
+        xs = _c(xs, np.uint16)
+        sel = np.arange(M * N, dtype=np.int64) if outs is None else _c(outs, np.int64)
+        y = np.empty(sel.shape[0], np.float64)
+        A = np.empty_like(y)
+        rc = self.lib.oracle_qmv_combine_sel(
+            WFMT.get(wfmt, wfmt), _ptr(codes), _ptr(scales), E, _ptr(ids), _ptr(weights), M,
+            top_k, AFMT.get(afmt, afmt), _ptr(x), _ptr(xs), int(bool(x_per_slot)), N, K,
+            _ptr(sel), sel.shape[0], _ptr(y), _ptr(A))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        if outs is None:
+            return y.reshape(M, N), A.reshape(M, N)
+        return y, A
 
     def dense(self, wfmt, codes, scales, afmt, x, xs=None):
         """Dense GEMV; codes [N][row_code_bytes]; returns (y, A) shaped [M][N]."""

@@ -437,4 +437,47 @@ int oracle_qmv_gather_swiglu_sel(int wfmt, const uint8_t *gcodes, const uint8_t 
     return 0;
 }
 
+/*
+ * Down projection with the router-weighted top-k combine: for token t and row n
+ *     y[t][n] = sum_j  w[t][j] * g(t, j, n)
+ * where g is the gather output of slot j (zero for an expert id outside
+ * [0, E)) and w[t][j] the router's fp32 weight of that slot.  Also returns
+ * A[t][n] = sum_j |w[t][j]| * A_gather(t, j, n), the tolerance scale.
+ * Outputs are selected by flat index o = t * N + n.
+ */
+int oracle_qmv_combine_sel(int wfmt, const uint8_t *codes, const uint8_t *scales, long E,
+                           const int32_t *ids, const float *w, long M, long top_k,
+                           int afmt, const void *x, const uint16_t *xs, int x_per_slot,
+                           long N, long K, const int64_t *outs, long n_outs,
+                           double *y, double *A)
+{
+    for (long i = 0; i < n_outs; i++) {
+        long t = (long)(outs[i] / N), n = (long)(outs[i] % N);
+        if (t < 0 || t >= M)
+            return -1;
+        double acc = 0.0, acc_a = 0.0;
+#if ORACLE_MUTANT == 12
+        for (long j = 0; j + 1 < top_k; j++) {       /* mutant: last slot dropped */
+#else
+        for (long j = 0; j < top_k; j++) {
+#endif
+            int64_t o = (int64_t)(t * top_k + j) * N + n;
+            double g, a;
+            if (oracle_qmv_gather_sel(wfmt, codes, scales, E, ids, M, top_k, afmt, x, xs,
+                                      x_per_slot, N, K, &o, 1, &g, &a) != 0)
+                return -1;
+#if ORACLE_MUTANT == 11
+            double wj = (double)w[t * top_k + (j + 1) % top_k];   /* mutant: weights shifted */
+#else
+            double wj = (double)w[t * top_k + j];
+#endif
+            acc += wj * g;
+            acc_a += fabs(wj) * a;
+        }
+        y[i] = acc;
+        if (A) A[i] = acc_a;
+    }
+    return 0;
+}
+
 int oracle_mutant_id(void) { return ORACLE_MUTANT; }

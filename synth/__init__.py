@@ -107,8 +107,25 @@ GATE_UP_WORKLOADS = {
 }
 
 
+# Down projections with the router-weighted top-k combine (one activation
+# vector per (token, slot), y[M][N]).
+COMBINE_WORKLOADS = {
+    "C4c": Workload("C4c", "combine", "cb3", M=1, N=7168, K=2048, seed=8, E=256, top_k=4,
+                    x_per_slot=True,
+                    desc="3-bit MoE down-proj, 4 of 256, K=2048, N=7168, per-slot int8 x, "
+                         "router-weighted combine"),
+    "C2c": Workload("C2c", "combine", "mxfp4", M=1, N=2880, K=2880, seed=9, E=32, top_k=4,
+                    x_per_slot=True,
+                    desc="gpt-oss-20b MoE down-proj, 4 of 32, K=N=2880, MXFP4, per-slot bf16 x, "
+                         "router-weighted combine"),
+}
+
+
 def workload(name: str) -> Workload:
-    return WORKLOADS[name] if name in WORKLOADS else GATE_UP_WORKLOADS[name]
+    for table in (WORKLOADS, GATE_UP_WORKLOADS, COMBINE_WORKLOADS):
+        if name in table:
+            return table[name]
+    raise KeyError(name)
 
 
 @dataclass
@@ -184,15 +201,27 @@ def make(name_or_wl, seed: int | None = None, experts: int | None = None) -> Inp
     if experts is not None:
         wl = wl.scaled(E=experts)
     rng = np.random.default_rng(wl.seed if seed is None else seed)
-    E = wl.E if wl.kind == "gather" else 1
+    routed = wl.kind in ("gather", "combine")
+    E = wl.E if routed else 1
     codes = gen_codes(rng, wl.wfmt, E, wl.N, wl.K)
     scales = gen_scales(rng, wl.wfmt, E, wl.N, wl.K, wl.e8m0)
-    ids = gen_ids(rng, wl.M, wl.top_k, E) if wl.kind == "gather" else None
-    V = wl.M * wl.top_k if (wl.kind == "gather" and wl.x_per_slot) else wl.M
+    ids = gen_ids(rng, wl.M, wl.top_k, E) if routed else None
+    V = wl.M * wl.top_k if (routed and wl.x_per_slot) else wl.M
     x, xs = gen_activations(rng, wl.afmt, V, wl.K)
     if wl.kind == "dense":
         codes, scales = codes[0], scales[0]
-    return Inputs(wl, codes, scales, ids, x, xs)
+    inp = Inputs(wl, codes, scales, ids, x, xs)
+    if wl.kind == "combine":
+        inp.extra["weights"] = gen_route_weights(rng, wl.M, wl.top_k)
+    return inp
+
+
+def gen_route_weights(rng, M, top_k):
+    """Router weights of the selected slots: softmax of N(0,1) logits over each
+    token's top_k slots, fp32 [M][top_k] (positive, summing to 1)."""
+    z = rng.standard_normal((M, top_k))
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
 @dataclass

@@ -438,6 +438,53 @@ def check_swiglu(o):
         assert not np.array_equal(ysw[valid], y[valid]), fmt
 
 
+# ---------------------------------------------------------------- P10 router-weighted combine
+def check_combine(o):
+    """The combine against facts that do not restate its sum: a one-hot weight
+    picks one slot's gather row exactly; scaling every weight by a power of two
+    scales y exactly; slots reordered together with their weights give the same
+    y (to rounding); an out-of-range id adds nothing; two slots of one expert
+    equal one slot with the summed weight."""
+    rng = _rng(18)
+    K, N, E, M, top_k = 64, 12, 5, 2, 4
+    for fmt in ("mxfp4", "cb2", "cb3"):
+        afmt = _afmt(fmt)
+        codes = np.stack([_random_rows(rng, fmt, N, K)[0] for _ in range(E)])
+        scales = np.stack([_random_rows(rng, fmt, N, K)[1] for _ in range(E)])
+        x, xs = _random_x(rng, fmt, M * top_k, K)            # one vector per (token, slot)
+        ids = np.array([[0, 3, 1, 4], [2, 2, 0, 1]], np.int32)
+        w = rng.uniform(0.05, 1.0, size=(M, top_k)).astype(np.float32)
+        y, A = o.combine(fmt, codes, scales, ids, w, afmt, x, xs)
+        g, Ag = o.gather(fmt, codes, scales, ids, afmt, x, xs, x_per_slot=True)
+        for t in range(M):
+            for j in range(top_k):
+                oh = np.zeros_like(w)
+                oh[t, j] = 1.0
+                y1, _ = o.combine(fmt, codes, scales, ids, oh, afmt, x, xs)
+                assert np.array_equal(y1[t], g[t, j]), (fmt, t, j)
+        y4, A4 = o.combine(fmt, codes, scales, ids, 4 * w, afmt, x, xs)
+        assert np.array_equal(y4, 4 * y) and np.allclose(A4, 4 * A, rtol=1e-15), fmt
+        perm = np.array([2, 0, 3, 1])
+        xp = x.reshape(M, top_k, -1)[:, perm].reshape(M * top_k, -1)
+        xsp = None if xs is None else xs.reshape(M, top_k, -1)[:, perm].reshape(M * top_k, -1)
+        yp, _ = o.combine(fmt, codes, scales, ids[:, perm], w[:, perm], afmt, xp, xsp)
+        assert np.allclose(yp, y, rtol=1e-12, atol=1e-12 * A.max()), fmt
+        bad = ids.copy()
+        bad[0, 1] = E
+        yb, Ab = o.combine(fmt, codes, scales, bad, w, afmt, x, xs)
+        assert np.allclose(yb[0], y[0] - w[0, 1] * g[0, 1], rtol=1e-12, atol=1e-12 * A.max()), fmt
+        assert np.array_equal(yb[1], y[1]), fmt
+        # token 1 has expert 2 in slots 0 and 1: with broadcast activations the two
+        # slots are one slot of summed weight
+        xb, xsb = _random_x(rng, fmt, M, K)
+        w2 = w.copy()
+        w2[1, 0], w2[1, 1] = 0.25, 0.5
+        yd, _ = o.combine(fmt, codes, scales, ids, w2, afmt, xb, xsb, x_per_slot=False)
+        gb, _ = o.gather(fmt, codes, scales, ids, afmt, xb, xsb)
+        want = 0.75 * gb[1, 0] + w2[1, 2] * gb[1, 2] + w2[1, 3] * gb[1, 3]
+        assert np.allclose(yd[1], want, rtol=1e-12, atol=1e-12 * np.abs(gb).max()), fmt
+
+
 ALL_CHECKS = [
     check_e2m1_table,
     check_e8m0_library,
@@ -452,4 +499,5 @@ ALL_CHECKS = [
     check_unit_scale_exact,
     check_gather_semantics,
     check_swiglu,
+    check_combine,
 ]
