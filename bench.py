@@ -25,7 +25,9 @@ call, so the Infinity Cache serves them).  ``cpu_baseline`` times the CPU
 oracle on a bounded sample of the same workload on all host cores, and
 ``cpu_baseline_1thread`` on one.  ``workloads`` lists the
 other shapes measured the same way (not the headline), among them the fused
-gate/up + SwiGLU calls (qmv_gather_moe_swiglu) C2gu and C3gu.
+gate/up + SwiGLU calls (qmv_gather_moe_swiglu) C2gu and C3gu and the down
+projections with the router-weighted combine (qmv_gather_moe_combine) C4c and
+C2c.
 """
 from __future__ import annotations
 
@@ -90,17 +92,19 @@ def weight_bytes(wl, n_experts):
 
 def other_bytes(wl):
     """Activation, scale, id and output bytes of one call."""
-    V = wl.M * wl.top_k if (wl.kind == "gather" and wl.x_per_slot) else wl.M
+    V = wl.M * wl.top_k if (wl.kind in ("gather", "combine") and wl.x_per_slot) else wl.M
     xb = V * wl.K * (2 if wl.afmt == "bf16" else 1) + (0 if wl.afmt == "bf16" else V * (wl.K // 32) * 2)
-    routed = wl.kind in ("gather", "gate_up")
-    outs = wl.M * (wl.top_k if routed else 1) * wl.N
+    routed = wl.kind in ("gather", "gate_up", "combine")
+    outs = wl.M * (wl.top_k if wl.kind in ("gather", "gate_up") else 1) * wl.N
     ids = 4 * wl.M * wl.top_k if routed else 0
-    return xb + ids + 4 * outs
+    route_w = 4 * wl.M * wl.top_k if wl.kind == "combine" else 0
+    return xb + ids + route_w + 4 * outs
 
 
 # Rotation plan: layer copies so that between two reads of the same weights
 # more than the 256 MB Infinity Cache of other weights is read.
-ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40, "C2gu": 4, "C3gu": 1}
+ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40, "C2gu": 4, "C3gu": 1,
+            "C4c": 2, "C2c": 32}
 
 
 class Prepared:
@@ -120,7 +124,7 @@ class Prepared:
         self.name = name
         self.wl = wl = synth.workload(name)
         gate_up = wl.kind == "gate_up"
-        self.inp = inp = synth.make_gate_up(wl) if gate_up else synth.make(name)
+        self.inp = inp = synth.make_gate_up(wl) if gate_up else synth.make(wl)
         self.L = ROTATION[name] if rotate else 1
         dev = torch.device("cuda")
 
@@ -140,16 +144,19 @@ class Prepared:
         else:
             self.x = torch.from_numpy(inp.x).to(dev)
             self.xs = torch.from_numpy(inp.xs.view(np.float16)).to(dev)
-        routed = wl.kind in ("gather", "gate_up")
+        routed = wl.kind in ("gather", "gate_up", "combine")
+        combine = wl.kind == "combine"
+        self.rw = torch.from_numpy(inp.extra["weights"]).to(dev) if combine else None
         if routed:
-            if name in ("C3", "C4", "C3gu"):
+            if name in ("C3", "C4", "C3gu", "C4c"):
                 ids = synth.disjoint_id_stream(wl.seed + 100, calls, wl.top_k, wl.E)
             else:
                 ids = synth.id_stream(wl.seed + 100, calls, wl.M, wl.top_k, wl.E)
             self.ids_host = ids
             self.ids = torch.from_numpy(ids).to(dev)
             experts = [np.unique(i) for i in ids]
-            self.y = torch.empty((wl.M, wl.top_k, wl.N), dtype=torch.float32, device=dev)
+            self.y = torch.empty((wl.M, wl.N) if combine else (wl.M, wl.top_k, wl.N),
+                                 dtype=torch.float32, device=dev)
         else:
             self.ids_host = None
             self.ids = None
@@ -175,6 +182,10 @@ class Prepared:
                 if gate_up:
                     a = (WFMT[wl.wfmt], wp[0][0], wp[0][1], wp[1][0], wp[1][1], wl.E, idp, wl.M,
                          wl.top_k, afmt, self.x.data_ptr(), xs, self.y.data_ptr(), wl.N, wl.K)
+                elif combine:
+                    a = (WFMT[wl.wfmt], wp[0][0], wp[0][1], wl.E, idp, self.rw.data_ptr(), wl.M,
+                         wl.top_k, afmt, self.x.data_ptr(), xs, int(wl.x_per_slot),
+                         self.y.data_ptr(), wl.N, wl.K)
                 elif routed:
                     a = (WFMT[wl.wfmt], wp[0][0], wp[0][1], wl.E, idp, wl.M, wl.top_k, afmt,
                          self.x.data_ptr(), xs, int(wl.x_per_slot), self.y.data_ptr(), wl.N, wl.K)
@@ -195,6 +206,8 @@ class Prepared:
             s = self.lib.qmv_gather_moe_swiglu(*a, ctypes.c_void_p(stream_handle))
         elif self.wl.kind == "gather":
             s = self.lib.qmv_gather_moe(*a, ctypes.c_void_p(stream_handle))
+        elif self.wl.kind == "combine":
+            s = self.lib.qmv_gather_moe_combine(*a, ctypes.c_void_p(stream_handle))
         else:
             s = self.lib.qmv_dense(*a, ctypes.c_void_p(stream_handle))
         if s != 0:
@@ -371,7 +384,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu",
+    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c",
                     help="other shapes to measure besides the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")

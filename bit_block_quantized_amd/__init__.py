@@ -24,7 +24,8 @@ import os
 
 import torch  # noqa: F401  -- loads the HIP runtime that libqmv.so binds to
 
-__all__ = ["qmv_dense", "qmv_gather_moe", "qmv_gather_moe_swiglu", "qmv_strerror",
+__all__ = ["qmv_dense", "qmv_gather_moe", "qmv_gather_moe_swiglu", "qmv_gather_moe_combine",
+           "qmv_strerror",
            "qmv_probe_stream_read", "lib", "LIB_PATH",
            "W_MXFP4", "W_CB2", "W_CB3", "A_BF16", "A_Q8B32", "QmvError"]
 
@@ -62,6 +63,8 @@ def lib():
     L.qmv_gather_moe.argtypes = [I, P, P, I, P, I, I, I, P, P, I, P, I, I, P]
     L.qmv_gather_moe_swiglu.restype = I
     L.qmv_gather_moe_swiglu.argtypes = [I, P, P, P, P, I, P, I, I, I, P, P, P, I, I, P]
+    L.qmv_gather_moe_combine.restype = I
+    L.qmv_gather_moe_combine.argtypes = [I, P, P, I, P, P, I, I, I, P, P, I, P, I, I, P]
     L.qmv_probe_stream_read.restype = I
     L.qmv_probe_stream_read.argtypes = [I, P, P, I, P, P]
     L.qmv_strerror.restype = ctypes.c_char_p
@@ -178,6 +181,36 @@ def qmv_gather_moe_swiglu(wfmt, gate_codes, gate_scales, up_codes, up_scales, ex
         _dev_ptr(expert_ids, "expert_ids", (torch.int32,), dev), M, top_k, a,
         _dev_ptr(x, "x", xd, dev), _dev_ptr(x_scales, "x_scales", (torch.float16,), dev),
         _dev_ptr(y, "y", (torch.float32,), dev), N, K, _stream(dev, stream))
+    _check(s)
+    return y
+
+
+def qmv_gather_moe_combine(wfmt, w_codes, w_scales, expert_ids, route_weights, x, x_scales=None,
+                           x_per_slot=True, y=None, stream=None):
+    """Down projection with the router-weighted top-k combine:
+    y[t][n] = sum_j route_weights[t][j] * (w(ids[t][j]) . x(t, j)); returns y
+    (float32 [M][N]).  ``x`` is [M][top_k][K] (``x_per_slot=True``) or [M][K]."""
+    w = _wfmt(wfmt)
+    dev = w_codes.device
+    if dev.type != "cuda":
+        raise ValueError("qmv_gather_moe_combine runs on the GPU only; pass device tensors")
+    E, N = w_codes.shape[0], w_codes.shape[1]
+    M, top_k = expert_ids.shape
+    if tuple(route_weights.shape) != (M, top_k):
+        raise ValueError(f"route_weights has shape {tuple(route_weights.shape)}, expected {(M, top_k)}")
+    K = x.shape[-1]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    a = _AFMT_OF.get(w, A_BF16)
+    xd = (torch.bfloat16,) if a == A_BF16 else (torch.int8,)
+    s = lib().qmv_gather_moe_combine(
+        w, _dev_ptr(w_codes, "w_codes", (torch.uint8,), dev),
+        _dev_ptr(w_scales, "w_scales", _SCALE_DT, dev), E,
+        _dev_ptr(expert_ids, "expert_ids", (torch.int32,), dev),
+        _dev_ptr(route_weights, "route_weights", (torch.float32,), dev), M, top_k, a,
+        _dev_ptr(x, "x", xd, dev), _dev_ptr(x_scales, "x_scales", (torch.float16,), dev),
+        int(bool(x_per_slot)), _dev_ptr(y, "y", (torch.float32,), dev), N, K,
+        _stream(dev, stream))
     _check(s)
     return y
 

@@ -19,6 +19,10 @@ extern const void *const kTableGU_mxfp4[2][4][5];
 extern const void *const kTableGU_cb2[2][4][5];
 extern const void *const kTableGU_cb2s[2][4][5];
 extern const void *const kTableGU_cb3[2][4][5];
+extern const void *const kTableCB_mxfp4[4][3];
+extern const void *const kTableCB_cb2[4][3];
+extern const void *const kTableCB_cb2s[4][3];
+extern const void *const kTableCB_cb3[4][3];
 }  // namespace qmv_w8
 
 namespace {
@@ -62,6 +66,24 @@ const void *kernel_for(int wi, int kind, int variant, int li, int ci, bool gate_
     case kCB2: return kTable_cb2[variant][li][ci];
     case kCB2S: return kTable_cb2s[variant][li][ci];
     default: return kTable_cb3[variant][li][ci];
+    }
+}
+
+const void *combine_kernel_for(int wi, int kind, int li, int ci)
+{
+    if (wi == 1) {
+        switch (kind) {
+        case kMXFP4: return qmv_w8::kTableCB_mxfp4[li][ci];
+        case kCB2: return qmv_w8::kTableCB_cb2[li][ci];
+        case kCB2S: return qmv_w8::kTableCB_cb2s[li][ci];
+        default: return qmv_w8::kTableCB_cb3[li][ci];
+        }
+    }
+    switch (kind) {
+    case kMXFP4: return kTableCB_mxfp4[li][ci];
+    case kCB2: return kTableCB_cb2[li][ci];
+    case kCB2S: return kTableCB_cb2s[li][ci];
+    default: return kTableCB_cb3[li][ci];
     }
 }
 
@@ -120,15 +142,18 @@ qmv_status_t validate(int wfmt, const void *codes, const void *scales, long long
 // in [8, 14] x 256 (else the nearest), then the larger CPL, then more waves.
 struct Shape { int li, ci, lpr, cpl; };
 
+// Variant 3 is the combine kernel: CPL menu {1, 2, 4}, every LPR.
 Shape pick_shape(int variant, int units, long long rows_total, int rt)
 {
-    const int ncpl = variant == 2 ? 3 : 5;
+    const bool small_cpl = variant >= 2;
+    const bool no_lpr8 = variant == 2;
+    const int ncpl = small_cpl ? 3 : 5;
     double best_eff = 0.0;
     for (int li = 0; li < 4; ++li)
         for (int ci = 0; ci < ncpl; ++ci) {
             const int lpr = kMenuLpr[li];
-            if (variant == 2 && lpr == 8) continue;
-            const int cpl = variant == 2 ? kMenuCpl2[ci] : kMenuCpl01[ci];
+            if (no_lpr8 && lpr == 8) continue;
+            const int cpl = small_cpl ? kMenuCpl2[ci] : kMenuCpl01[ci];
             const long long seg = (long long)lpr * cpl;
             const double eff = (double)units / (double)(((units + seg - 1) / seg) * seg);
             if (eff > best_eff) best_eff = eff;
@@ -139,8 +164,8 @@ Shape pick_shape(int variant, int units, long long rows_total, int rt)
     for (int li = 0; li < 4; ++li)
         for (int ci = 0; ci < ncpl; ++ci) {
             const int lpr = kMenuLpr[li];
-            if (variant == 2 && lpr == 8) continue;
-            const int cpl = variant == 2 ? kMenuCpl2[ci] : kMenuCpl01[ci];
+            if (no_lpr8 && lpr == 8) continue;
+            const int cpl = small_cpl ? kMenuCpl2[ci] : kMenuCpl01[ci];
             const long long seg = (long long)lpr * cpl;
             const double eff = (double)units / (double)(((units + seg - 1) / seg) * seg);
             if (eff < 0.85 * best_eff) continue;
@@ -164,7 +189,8 @@ Shape pick_shape(int variant, int units, long long rows_total, int rt)
 // Launch shapes measured best on MI355X for the MoE expert shapes this library
 // is tuned on (sweeps of every menu shape at 4 and 8 waves per workgroup, HBM-
 // resident weights rotated past the Infinity Cache).  Other shapes use
-// pick_shape() with 4 waves.  An entry matches on format kind, variant,
+// pick_shape() with 4 waves (8 for the combine kernel, whose tuned shapes
+// all prefer it).  An entry matches on format kind, variant (3: combine),
 // gate/up mode, K, N and the number of (token, slot) pairs.
 struct Tuned { int kind, variant, gate_up, K, N, pairs, waves, lpr, cpl; };
 constexpr Tuned kTuned[] = {
@@ -175,6 +201,8 @@ constexpr Tuned kTuned[] = {
     {kCB3,   1, 0, 2048, 7168, 4, 8, 16, 2},     // DeepSeek-shaped 3-bit down
     {kMXFP4, 1, 0, 7168, 2048, 16, 4, 8, 7},     // 4 tokens x top-4 of 256
     {kMXFP4, 2, 0, 7168, 7168, 1, 8, 64, 4},     // dense, 4 tokens
+    {kCB3,   3, 0, 2048, 7168, 4, 8, 32, 1},     // 3-bit down + router-weighted combine
+    {kMXFP4, 3, 0, 2880, 2880, 4, 8, 32, 2},     // gpt-oss down + router-weighted combine
 };
 
 bool tuned_shape(int kind, int variant, bool gate_up, int K, int N, int pairs, int &wi, Shape &sh)
@@ -184,11 +212,11 @@ bool tuned_shape(int kind, int variant, bool gate_up, int K, int N, int pairs, i
             t.N != N || t.pairs != pairs)
             continue;
         wi = t.waves == 8 ? 1 : 0;
-        const int ncpl = variant == 2 ? 3 : 5;
+        const int ncpl = variant >= 2 ? 3 : 5;
         for (int li = 0; li < 4; ++li)
             for (int ci = 0; ci < ncpl; ++ci)
                 if (kMenuLpr[li] == t.lpr &&
-                    (variant == 2 ? kMenuCpl2[ci] : kMenuCpl01[ci]) == t.cpl) {
+                    (variant >= 2 ? kMenuCpl2[ci] : kMenuCpl01[ci]) == t.cpl) {
                     sh = {li, ci, t.lpr, t.cpl};
                     return true;
                 }
@@ -198,6 +226,47 @@ bool tuned_shape(int kind, int variant, bool gate_up, int K, int N, int pairs, i
 
 std::once_flag g_attr_once[2][2][4][3][4][5];
 hipError_t g_attr_err[2][2][4][3][4][5];
+std::once_flag g_cattr_once[2][4][4][3];
+hipError_t g_cattr_err[2][4][4][3];
+
+// Arguments common to every kernel of a call (Args in qmv_device.hpp).
+Args base_args(int wfmt, int kind, const void *codes, const void *scales, int E,
+               const int32_t *ids, int M, int top_k, const void *x, const void *xs,
+               int x_per_slot, float *y, int N, int K)
+{
+    Args a;
+    a.codes = (const uint8_t *)codes;
+    a.scales = (const uint8_t *)scales;
+    a.codes2 = nullptr;
+    a.scales2 = nullptr;
+    a.ids = ids;
+    a.route_w = nullptr;
+    a.x = (const uint8_t *)x;
+    a.xs = (const uint16_t *)xs;
+    a.y = y;
+    a.rcb = (int)row_code_bytes(wfmt, K);
+    a.rsb = (int)row_scale_bytes(wfmt, K);
+    a.expert_cb = (long long)N * a.rcb;
+    a.expert_sb = (long long)N * a.rsb;
+    a.x_vec_bytes = (wfmt == QMV_W_MXFP4) ? 2 * K : K;
+    a.E = E;
+    a.M = M;
+    a.top_k = top_k;
+    a.N = N;
+    a.K = K;
+    a.units = K / kUnitWeights[kind];
+    a.x_per_slot = x_per_slot;
+    a.x_early = 0;
+    a.rows_per_tile = 0;
+    const int vec_bytes = a.units * (kUnitXB[kind] + kUnitAB[kind]);
+    a.lds_vec_bytes = (vec_bytes + 15) & ~15;
+    return a;
+}
+
+int kind_of(int wfmt, int K)
+{
+    return wfmt == QMV_W_MXFP4 ? kMXFP4 : wfmt == QMV_W_CB3 ? kCB3 : (K % 64 == 0 ? kCB2 : kCB2S);
+}
 
 // codes2/scales2 non-null selects the gate/up mode: codes/scales are the gate
 // projection, codes2/scales2 the up projection, y = swiglu(gate x, up x).
@@ -208,7 +277,7 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, const void 
 {
     const bool gather = ids != nullptr;
     const bool gate_up = codes2 != nullptr;
-    const int kind = wfmt == QMV_W_MXFP4 ? kMXFP4 : wfmt == QMV_W_CB3 ? kCB3 : (K % 64 == 0 ? kCB2 : kCB2S);
+    const int kind = kind_of(wfmt, K);
     const int units = K / kUnitWeights[kind];
     const int nv_needed = !gather ? M : (x_per_slot ? (M * top_k < 4 ? M * top_k : 4) : M);
     int variant, rt;
@@ -221,32 +290,13 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, const void 
     int wi = 0;
     if (!tuned_shape(kind, variant, gate_up, K, N, gather ? M * top_k : 1, wi, sh))
         sh = pick_shape(variant, units, rows_total, rt);
-    Args a;
-    a.codes = (const uint8_t *)codes;
-    a.scales = (const uint8_t *)scales;
+    Args a = base_args(wfmt, kind, codes, scales, gather ? E : 1, ids, M, gather ? top_k : 1, x, xs,
+                       gather ? x_per_slot : 0, y, N, K);
     a.codes2 = (const uint8_t *)codes2;
     a.scales2 = (const uint8_t *)scales2;
-    a.ids = ids;
-    a.x = (const uint8_t *)x;
-    a.xs = (const uint16_t *)xs;
-    a.y = y;
-    a.rcb = (int)row_code_bytes(wfmt, K);
-    a.rsb = (int)row_scale_bytes(wfmt, K);
-    a.expert_cb = (long long)N * a.rcb;
-    a.expert_sb = (long long)N * a.rsb;
-    a.x_vec_bytes = (wfmt == QMV_W_MXFP4) ? 2 * K : K;
-    a.E = gather ? E : 1;
-    a.M = M;
-    a.top_k = gather ? top_k : 1;
-    a.N = N;
-    a.K = K;
-    a.units = units;
-    a.x_per_slot = gather ? x_per_slot : 0;
     a.x_early = (!gather || (M == 1 && !x_per_slot)) ? 1 : 0;
     const int waves = kWaveMenu[wi];
     a.rows_per_tile = waves * (64 / sh.lpr) * (gate_up ? 1 : rt);
-    const int vec_bytes = units * (kUnitXB[kind] + kUnitAB[kind]);
-    a.lds_vec_bytes = (vec_bytes + 15) & ~15;
     const size_t lds = (size_t)nvmax * a.lds_vec_bytes;
 
     const void *fn = kernel_for(wi, kind, variant, sh.li, sh.ci, gate_up);
@@ -262,6 +312,43 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, const void 
 
     const dim3 grid((unsigned)((N + a.rows_per_tile - 1) / a.rows_per_tile),
                     (unsigned)(gather ? M * top_k : 1));
+    void *kargs[] = {&a};
+    if (hipLaunchKernel(fn, grid, dim3(64 * waves), kargs, lds, stream) != hipSuccess)
+        return QMV_EHIP;
+    return QMV_OK;
+}
+
+// Down projection with the router-weighted combine: one launch, grid (row
+// tiles, tokens); each lane carries row n of four of the token's slots.
+qmv_status_t launch_combine(int wfmt, const void *codes, const void *scales, int E,
+                            const int32_t *ids, const float *route_w, int M, int top_k,
+                            const void *x, const void *xs, int x_per_slot, float *y, int N, int K,
+                            hipStream_t stream)
+{
+    const int kind = kind_of(wfmt, K);
+    Args a = base_args(wfmt, kind, codes, scales, E, ids, M, top_k, x, xs, x_per_slot, y, N, K);
+    a.route_w = route_w;
+    a.x_early = 1;
+    Shape sh;
+    int wi = 1;
+    constexpr int RT = 4;
+    if (!tuned_shape(kind, 3, false, K, N, M * top_k, wi, sh))
+        sh = pick_shape(3, a.units, (long long)N * M * RT, RT);
+    const int waves = kWaveMenu[wi];
+    a.rows_per_tile = waves * (64 / sh.lpr);
+    const int nv = x_per_slot ? (top_k < 4 ? top_k : 4) : 1;
+    const size_t lds = (size_t)nv * a.lds_vec_bytes;
+
+    const void *fn = combine_kernel_for(wi, kind, sh.li, sh.ci);
+    std::call_once(g_cattr_once[wi][kind][sh.li][sh.ci], [&] {
+        const int umax = kMaxK / kUnitWeights[kind];
+        const int vmax = (umax * (kUnitXB[kind] + kUnitAB[kind]) + 15) & ~15;
+        g_cattr_err[wi][kind][sh.li][sh.ci] = hipFuncSetAttribute(
+            fn, hipFuncAttributeMaxDynamicSharedMemorySize, 4 * vmax);
+    });
+    if (g_cattr_err[wi][kind][sh.li][sh.ci] != hipSuccess)
+        return QMV_EHIP;
+    const dim3 grid((unsigned)((N + a.rows_per_tile - 1) / a.rows_per_tile), (unsigned)M);
     void *kargs[] = {&a};
     if (hipLaunchKernel(fn, grid, dim3(64 * waves), kargs, lds, stream) != hipSuccess)
         return QMV_EHIP;
@@ -315,6 +402,23 @@ QMV_API qmv_status_t qmv_gather_moe_swiglu(qmv_wfmt_t wfmt, const void *gate_cod
         return s;
     return launch(wfmt, gate_codes, gate_scales, up_codes, up_scales, E, expert_ids, M, top_k, x,
                   xs, 0, y, N, K, stream);
+}
+
+QMV_API qmv_status_t qmv_gather_moe_combine(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
+                                    int E, const int32_t *expert_ids, const float *route_weights,
+                                    int M, int top_k, qmv_afmt_t afmt, const void *x,
+                                    const void *x_scales, int x_per_slot, float *y, int N, int K,
+                                    hipStream_t stream)
+{
+    const void *xs = afmt == QMV_A_Q8B32 ? x_scales : nullptr;
+    const qmv_status_t s = validate(wfmt, w_codes, w_scales, E, expert_ids, true, M, top_k, afmt,
+                                    x, xs, y, N, K);
+    if (s != QMV_OK)
+        return s;
+    if (!route_weights || !aligned(route_weights, 4))
+        return QMV_EINVAL;
+    return launch_combine(wfmt, w_codes, w_scales, E, expert_ids, route_weights, M, top_k, x, xs,
+                          x_per_slot ? 1 : 0, y, N, K, stream);
 }
 
 QMV_API const char *qmv_strerror(qmv_status_t status)

@@ -54,6 +54,7 @@ struct Args {
     const uint8_t *codes2;   // gate/up mode: the up projection (codes is the gate)
     const uint8_t *scales2;
     const int32_t *ids;      // nullptr for a dense call
+    const float *route_w;    // combine mode: router weights fp32 [M][top_k]
     const uint8_t *x;
     const uint16_t *xs;      // int8 activation scales (fp16 bits) or nullptr
     float *y;
@@ -918,6 +919,152 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const Args a)
     }
 }
 
+// ------------------------------------------------------------------ combine
+// Down projection with the router-weighted top-k combine:
+//     y[t][n] = sum_j  w[t][j] * g(t, j, n),   g = the gather output of slot j
+// (zero for an expert id outside [0, E)).  A workgroup owns token t
+// (blockIdx.y) and a tile of rows; each lane keeps row n of up to four of the
+// token's slots in flight at once (the four slots' experts are four buffer
+// resources), so the slots' dot products of a row end in the same lane group
+// and the weighted sum is formed in registers, in slot order, with no second
+// pass over memory and no atomics.  Slots beyond the fourth are taken four at
+// a time by the same workgroup.  The activation vector of slot j is x[t][j]
+// (or x[t] for every slot when x_per_slot == 0), known before the ids arrive,
+// so its staging loads are issued first.
+constexpr int kCombineRT = 4;        // slots per pass
+
+__device__ __forceinline__ Item combine_item(const Args &a, int t, int g)
+{
+    Item it;
+    it.kind = 0;
+    it.expert = 0;
+    it.nv = a.x_per_slot ? min(4, a.top_k - 4 * g) : 1;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        it.vec[m] = a.x_per_slot ? t * a.top_k + 4 * g + m : t;
+        it.dest[m] = 0ull;
+    }
+    return it;
+}
+
+// One unit step of the combine: row r (slot 4g + r) is dotted with its own
+// staged vector (vo[r] bytes into LDS) only; rows of invalid slots are
+// skipped (wave-uniform) and keep a zero sum.
+template <int F, int LPR, int CPL, int RT>
+__device__ __forceinline__ void mac_seg_diag(Unit<F> (&w)[CPL][RT], const Args &a, const uint8_t *lds,
+                                             const __amdgpu_buffer_rsrc_t (&rc)[RT], const uint32_t (&oc)[RT],
+                                             const int (&vo)[RT], const bool (&valid)[RT],
+                                             int seg_unit, int u0, int U, float (&acc)[RT])
+{
+    constexpr int LEAD = Lead<CPL>::v;
+    const int xbytes = U * Fmt<F>::XB;
+    bool fast = true;
+    if constexpr (F == kMXFP4) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int r = 0; r < RT; ++r) fast = fast && (!valid[r] || (w[c][r].s - 2u) <= 250u);
+        fast = __all(fast);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        if (c + LEAD < CPL) load_step<F, LPR, CPL, RT>(w, rc, oc, seg_unit, u0 - seg_unit, U, c + LEAD);
+        if (u0 + c * LPR < U) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                if (!valid[r]) continue;
+                const Unit<F>(&w1)[1] = *reinterpret_cast<const Unit<F>(*)[1]>(&w[c][r]);
+                float(&a1)[1][1] = *reinterpret_cast<float(*)[1][1]>(&acc[r]);
+                const uint8_t *l = lds + vo[r];
+                if constexpr (F == kMXFP4) mac_mxfp4<LPR, 1, 1>(w1, l, 0, u0, c, fast, a1);
+                else if constexpr (F == kCB3) mac_cb3<LPR, 1, 1>(w1, l, 0, xbytes, u0, c, a1);
+                else mac_cb2<F, LPR, 1, 1>(w1, l, 0, xbytes, u0, c, a1);
+            }
+        }
+    }
+}
+
+template <int F, int LPR, int CPL>
+__global__ __launch_bounds__(kThreads) void qmv_combine_kernel(const Args a)
+{
+    constexpr int RT = kCombineRT;
+    constexpr int SLOTS = 64 / LPR;
+    constexpr int SEG = LPR * CPL;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int t = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int li = lane % LPR;
+    const int n = blockIdx.x * a.rows_per_tile + wave * SLOTS + lane / LPR;
+    const int U = a.units;
+    const int ngroups = (a.top_k + RT - 1) / RT;
+
+    Item it = combine_item(a, t, 0);
+    uint4 xr[kXReg];
+    xload<F, 4>(a, it, xr);                        // in flight while the ids arrive
+    int e_l = -1;
+    float w_l = 0.0f;
+    if (lane < a.top_k) {
+        e_l = a.ids[t * a.top_k + lane];
+        w_l = a.route_w[t * a.top_k + lane];
+    }
+
+    float y = 0.0f;
+    for (int g = 0; g < ngroups; ++g) {
+        __amdgpu_buffer_rsrc_t rc[RT], rs[RT];
+        uint32_t oc[RT], os[RT];
+        bool valid[RT];
+        int vo[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int j = RT * g + r;
+            const int e = __builtin_amdgcn_readlane(e_l, j);          // lane j < 16 < 64
+            valid[r] = j < a.top_k && e >= 0 && e < a.E;
+            const long long eo = valid[r] ? (long long)e : 0ll;      // invalid: empty resource, reads 0
+            rc[r] = buffer_rsrc(a.codes + eo * a.expert_cb, valid[r] ? a.expert_cb : 0);
+            rs[r] = buffer_rsrc(a.scales + eo * a.expert_sb, valid[r] ? a.expert_sb : 0);
+            oc[r] = (uint32_t)__umul24(n, a.rcb) + li * Unit<F>::CB;
+            os[r] = (uint32_t)__umul24(n, a.rsb) + li * Unit<F>::SB;
+            vo[r] = a.x_per_slot ? r * a.lds_vec_bytes : 0;
+        }
+        const bool restage = g > 0 && a.x_per_slot;
+        if (restage) {
+            it = combine_item(a, t, g);
+            xload<F, 4>(a, it, xr);
+        }
+        Unit<F> w[CPL][RT];
+        load_scales<F, LPR, CPL, RT>(w, rs, os, 0, li, U);
+#pragma unroll
+        for (int c = 0; c < Lead<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, 0, li, U, c);
+        if (g == 0 || restage) {
+            if (restage) __syncthreads();          // every wave is done with the last group's vectors
+            xstore<F, 4>(a, it, lds, xr);
+            __syncthreads();
+            if (xrest<F, 4>(a, it, lds)) __syncthreads();
+        }
+
+        float acc[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] = 0.0f;
+        const int nseg = (U + SEG - 1) / SEG;
+        for (int seg = 0;;) {
+            mac_seg_diag<F, LPR, CPL, RT>(w, a, lds, rc, oc, vo, valid, seg * SEG, seg * SEG + li, U, acc);
+            if (++seg >= nseg) break;
+            load_scales<F, LPR, CPL, RT>(w, rs, os, seg * SEG, li, U);
+#pragma unroll
+            for (int c = 0; c < Lead<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, seg * SEG, li, U, c);
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int j = RT * g + r;
+            const float s = group_sum<LPR>(acc[r]);
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), j));
+            if (j < a.top_k) y = __builtin_fmaf(wj, valid[r] ? s : 0.0f, y);
+        }
+    }
+    if (li == 0 && n < a.N) a.y[t * a.N + n] = y;      // M * N < 2^31
+}
+
 // Kernel menus.  Variant 0: one vector per item, 2 rows per lane.  Variant 1:
 // up to four vectors per item (gather with M > 1 or per-slot activations),
 // 2 rows per lane.  Variant 2: dense with M > 1, 4 rows per lane.
@@ -935,6 +1082,11 @@ extern const void *const kTableGU_mxfp4[2][4][5];
 extern const void *const kTableGU_cb2[2][4][5];
 extern const void *const kTableGU_cb2s[2][4][5];
 extern const void *const kTableGU_cb3[2][4][5];
+// Combine kernels: [lpr][cpl in {1, 2, 4}].
+extern const void *const kTableCB_mxfp4[4][3];
+extern const void *const kTableCB_cb2[4][3];
+extern const void *const kTableCB_cb2s[4][3];
+extern const void *const kTableCB_cb3[4][3];
 
 }  // namespace QMV_NS
 
@@ -950,6 +1102,9 @@ extern const void *const kTableGU_cb3[2][4][5];
     { { QMV_ROW01(F, 0, 8, 0), QMV_ROW01(F, 0, 16, 0), QMV_ROW01(F, 0, 32, 0), QMV_ROW01(F, 0, 64, 0) }, \
       { QMV_ROW01(F, 1, 8, 0), QMV_ROW01(F, 1, 16, 0), QMV_ROW01(F, 1, 32, 0), QMV_ROW01(F, 1, 64, 0) }, \
       { QMV_NOROW, QMV_ROW2(F, 2, 16), QMV_ROW2(F, 2, 32), QMV_ROW2(F, 2, 64) } }
+#define QMV_KC(F, L, C) (const void *)&::QMV_NS::qmv_combine_kernel<F, L, C>
+#define QMV_ROWC(F, L) { QMV_KC(F, L, 1), QMV_KC(F, L, 2), QMV_KC(F, L, 4) }
+#define QMV_TABLE_CB(F) { QMV_ROWC(F, 8), QMV_ROWC(F, 16), QMV_ROWC(F, 32), QMV_ROWC(F, 64) }
 #define QMV_TABLE_GU(F) \
     { { QMV_ROW01(F, 0, 8, 1), QMV_ROW01(F, 0, 16, 1), QMV_ROW01(F, 0, 32, 1), QMV_ROW01(F, 0, 64, 1) }, \
       { QMV_ROW01(F, 1, 8, 1), QMV_ROW01(F, 1, 16, 1), QMV_ROW01(F, 1, 32, 1), QMV_ROW01(F, 1, 64, 1) } }

@@ -142,6 +142,33 @@ qmv_status_t qmv_gather_moe_swiglu(qmv_wfmt_t wfmt, const void *gate_codes, cons
                                    qmv_afmt_t afmt, const void *x, const void *x_scales,
                                    float *y, int N, int K, hipStream_t stream);
 
+/*
+ * Down (expert output) projection with the router-weighted top-k combine:
+ *   y[t][n] = sum_j  route_weights[t][j] * g(t, j, n)      for t < M, n < N
+ *   g(t, j, n) = sum_k w(e, n, k) * x(t, j, k),  e = expert_ids[t][j]
+ *   g(t, j, n) = 0                               if e is outside [0, E)
+ * The per-slot gather above followed by the weighted sum over each token's
+ * slots, in one launch: the result an MoE layer adds to the residual stream.
+ * The pages count gate, up and down expert calls per decoded token (mlxcel
+ * issue #2178, Problem / Background) and time the down projection's 3-bit
+ * matvec on its own (lucebox-hub PR #21, Summary); the combine is the
+ * standard top-k mixture sum that consumes it.
+ *   route_weights  fp32 [M][top_k] in device memory (4-byte aligned)
+ *   x_per_slot     1: x is [M][top_k][K], the activated gate/up output of
+ *                     each (token, slot) -- the usual down-projection input;
+ *                  0: x is [M][K] for every slot of a token.
+ *   y              fp32 [M][N], overwritten (not accumulated into).
+ * The slots of a token are summed in slot order; results are bitwise
+ * reproducible.  An out-of-range id contributes route_weights[t][j] * 0.
+ * Weights, scales and activations, limits and errors as qmv_gather_moe;
+ * a null or misaligned route_weights is QMV_EINVAL.
+ */
+qmv_status_t qmv_gather_moe_combine(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
+                                    int E, const int32_t *expert_ids, const float *route_weights,
+                                    int M, int top_k, qmv_afmt_t afmt, const void *x,
+                                    const void *x_scales, int x_per_slot, float *y, int N, int K,
+                                    hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char *qmv_strerror(qmv_status_t status);
 

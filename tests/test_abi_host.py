@@ -40,13 +40,14 @@ def declared_functions(header=None):
 
 def test_header_declares_the_boundary():
     assert declared_functions("qmv.h") == ["qmv_dense", "qmv_gather_moe",
-                                           "qmv_gather_moe_swiglu", "qmv_strerror"]
+                                           "qmv_gather_moe_combine", "qmv_gather_moe_swiglu",
+                                           "qmv_strerror"]
     assert declared_functions("qmv_probe.h") == ["qmv_probe_stream_read"]
 
 
 def test_library_exports_every_declared_symbol(L):
     declared = declared_functions()
-    assert len(declared) == 5
+    assert len(declared) == 6
     for name in declared:
         assert hasattr(L, name), name
     out = os.popen(f"nm -D --defined-only {ROOT}/bit_block_quantized_amd/libqmv.so").read()
@@ -142,6 +143,23 @@ def swiglu(L, wfmt=W_MXFP4, gc=FAKE, gs=FAKE, uc=FAKE, us=FAKE, E=32, ids=FAKE, 
 ])
 def test_swiglu_validation(L, kw, want):
     assert swiglu(L, **kw) == want
+
+
+def combine(L, wfmt=W_CB3, codes=FAKE, scales=FAKE, E=256, ids=FAKE, rw=FAKE, M=1, top_k=4,
+            afmt=A_Q8, x=FAKE, xs=FAKE, per_slot=1, y=FAKE, N=7168, K=2048):
+    return L.qmv_gather_moe_combine(wfmt, codes, scales, E, ids, rw, M, top_k, afmt, x, xs,
+                                    per_slot, y, N, K, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rw=None), EINVAL), (dict(rw=FAKE + 2), EINVAL), (dict(ids=None), EINVAL),
+    (dict(codes=None), EINVAL), (dict(y=FAKE + 1), EINVAL), (dict(xs=None), EINVAL),
+    (dict(M=5), EUNSUP), (dict(top_k=17), EUNSUP), (dict(top_k=0), EINVAL),
+    (dict(K=2048 + 16), EUNSUP), (dict(afmt=A_BF16, xs=None), EUNSUP),
+    (dict(wfmt=W_MXFP4), EUNSUP), (dict(E=0), EINVAL),
+])
+def test_combine_validation(L, kw, want):
+    assert combine(L, **kw) == want
 
 
 def probe(L, n=1, ptrs=(FAKE,), sizes=(4096,), variant=0, sink=FAKE):
