@@ -83,6 +83,10 @@ def _bind(lib):
     lib.oracle_qmv_combine_sel.restype = _I
     lib.oracle_qmv_combine_sel.argtypes = [_I, _P, _P, _L, _P, _P, _L, _L, _I, _P, _P, _I,
                                            _L, _L, _P, _L, _P, _P]
+    lib.oracle_f2h.restype = ctypes.c_uint
+    lib.oracle_f2h.argtypes = [ctypes.c_float]
+    lib.oracle_quantize_q8.restype = _I
+    lib.oracle_quantize_q8.argtypes = [_P, _L, _L, _P, _P]
     lib.oracle_mutant_id.restype = _I
     lib.oracle_mutant_id.argtypes = []
     return lib
@@ -257,6 +261,20 @@ class Oracle:
         if outs is None:
             return y.reshape(M, N), A.reshape(M, N)
         return y, A
+
+    def quantize_q8(self, x_bf16_bits):
+        """bf16 activations (uint16 bit patterns [V][K]) -> (int8 q [V][K],
+        fp16 scale bits uint16 [V][K/32]) by the oracle's q8 quantizer."""
+        x = _c(x_bf16_bits, np.uint16)
+        squeeze = x.ndim == 1
+        if squeeze:
+            x = x[None]
+        V, K = x.shape
+        q = np.empty((V, K), np.int8)
+        d = np.empty((V, K // 32), np.uint16)
+        if self.lib.oracle_quantize_q8(_ptr(x), V, K, _ptr(q), _ptr(d)) != 0:
+            raise ValueError("K must be a multiple of 32")
+        return (q[0], d[0]) if squeeze else (q, d)
 
     def dense(self, wfmt, codes, scales, afmt, x, xs=None):
         """Dense GEMV; codes [N][row_code_bytes]; returns (y, A) shaped [M][N]."""

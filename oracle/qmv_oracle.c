@@ -480,4 +480,93 @@ int oracle_qmv_combine_sel(int wfmt, const uint8_t *codes, const uint8_t *scales
     return 0;
 }
 
+/* ------------------------------------------------- activation quantizer */
+
+/*
+ * binary32 -> IEEE-754 binary16 bit pattern, rounded to nearest, ties to
+ * even (subnormals kept, overflow to Inf, NaN to a quiet NaN).  Written out
+ * in double arithmetic, where every step below is exact: scale the magnitude
+ * to units of the target's last place, round to an integer with nearbyint
+ * (the default rounding mode rounds halves to even), and let a mantissa that
+ * rounds up to 2^10 carry into the exponent field.
+ */
+unsigned oracle_f2h(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    unsigned sign = (u >> 31) ? 0x8000u : 0u;
+    if (isnan(f))
+        return sign | 0x7E00u;
+    double a = fabs((double)f);
+    if (a >= 65520.0)                       /* halfway above 65504 and beyond: Inf */
+        return sign | 0x7C00u;
+    if (a < ldexp(1.0, -14)) {              /* subnormal range: units of 2^-24 */
+        double m = nearbyint(a * ldexp(1.0, 24));
+        return sign | (unsigned)m;          /* m == 1024 encodes 2^-14 exactly */
+    }
+    int ex;
+    frexp(a, &ex);                          /* a = fr * 2^ex, fr in [0.5, 1) */
+    int e = ex - 1;                         /* a in [2^e, 2^(e+1)) */
+    double m = nearbyint((ldexp(a, -e) - 1.0) * 1024.0);
+    if (m >= 1024.0) {
+        m = 0.0;
+        e += 1;
+    }
+    return sign | (unsigned)((e + 15) << 10) | (unsigned)m;
+}
+
+/*
+ * Activation quantizer: bf16 activations -> int8 with one fp16 scale per 32,
+ * the q8_1 activation blocks that the integer dot products consume
+ * (lucebox-hub PR "optimize ROCMFPX fp3/fp2 MMVQ on RDNA", the MMVQ path;
+ * geo-lucebox PR "DS4 H200: rocmfp2_mix MoE matvec", "What is now hot",
+ * where quantize_q8_1 runs as its own launch before every matvec).  The
+ * pages name the step but print no formula; reading taken, in fp32 (the
+ * precision the integer decision is made in on both sides):
+ *     amax = max_i |x_i|                     (exact)
+ *     d    = amax / 127                      (fp32, nearest even)
+ *     d16  = binary16(d)                     (nearest even; the stored scale)
+ *     r    = 1 / float(d16)  in fp32, or 0 when d16 is zero or infinite
+ *     q_i  = clamp(rint(x_i * r), -127, 127) (x_i * r in fp32; rint ties to even)
+ * Activations must be finite.  q: int8 [V][K]; d16: fp16 bits [V][K/32].
+ */
+int oracle_quantize_q8(const uint16_t *xb, long V, long K, int8_t *q, uint16_t *d16)
+{
+    if (K % 32 != 0)
+        return -1;
+    for (long v = 0; v < V; v++)
+        for (long b = 0; b < K / 32; b++) {
+            const uint16_t *xs = xb + v * K + b * 32;
+            float x[32];
+            float amax = 0.0f;
+            for (int i = 0; i < 32; i++) {
+                uint32_t u = (uint32_t)xs[i] << 16;
+                memcpy(&x[i], &u, sizeof u);
+                float a = fabsf(x[i]);
+                if (a > amax)
+                    amax = a;
+            }
+            float d = amax / 127.0f;
+            unsigned h = oracle_f2h(d);
+            float dd = (float)oracle_h2d(h);
+#if ORACLE_MUTANT == 14
+            dd = d;                             /* mutant: unrounded scale used for q */
+#endif
+            float r = (dd > 0.0f && !isinf(dd)) ? 1.0f / dd : 0.0f;
+            for (int i = 0; i < 32; i++) {
+                float t = x[i] * r;
+#if ORACLE_MUTANT == 13
+                float qi = roundf(t);           /* mutant: ties away from zero */
+#else
+                float qi = rintf(t);
+#endif
+                if (qi > 127.0f) qi = 127.0f;
+                if (qi < -127.0f) qi = -127.0f;
+                q[v * K + b * 32 + i] = (int8_t)qi;
+            }
+            d16[v * (K / 32) + b] = (uint16_t)h;
+        }
+    return 0;
+}
+
 int oracle_mutant_id(void) { return ORACLE_MUTANT; }

@@ -12,7 +12,8 @@ Independent sources used here (none of them is the oracle's C code):
   * torch's float8_e8m0fnu and bfloat16 casts, numpy's float16;
   * numpy ``unpackbits`` as a second bit unpacker;
   * exact rational arithmetic (``fractions.Fraction``) and int64 matmuls;
-  * the hand-worked blocks in ``golden/hand_worked_blocks.json``.
+  * the hand-worked blocks in ``golden/hand_worked_blocks.json`` and the
+    hand-quantized activation blocks in ``golden/q8_quantizer_blocks.json``.
 """
 from __future__ import annotations
 
@@ -485,6 +486,77 @@ def check_combine(o):
         assert np.allclose(yd[1], want, rtol=1e-12, atol=1e-12 * np.abs(gb).max()), fmt
 
 
+# ---------------------------------------------------------------- P11 activation quantizer
+def check_f2h_library(o):
+    """The oracle's binary16 encoder against numpy's float32 -> float16 cast
+    (round to nearest even): every bf16 value, random float32 bit patterns,
+    and the exact midpoints between neighbouring fp16 values."""
+    rng = _rng(31)
+    bf = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    rnd = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    h = np.arange(0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mid = ((h[:-1] + h[1:]) / 2).astype(np.float32)            # exact in fp32
+    near = np.concatenate([np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1e9))])
+    vals = np.concatenate([bf, rnd, mid, -mid, near, -near]).astype(np.float32)
+    vals = vals[~np.isnan(vals)]
+    with np.errstate(over="ignore"):
+        want = vals.astype(np.float16).view(np.uint16)
+    got = np.array([o.lib.oracle_f2h(float(v)) for v in vals], np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (vals[bad[0]], hex(got[bad[0]]), hex(want[bad[0]]))
+
+
+def q8_blocks_golden():
+    with open(os.path.join(GOLD, "q8_quantizer_blocks.json")) as f:
+        return json.load(f)["cases"]
+
+
+def check_q8_hand_worked(o):
+    """The quantizer against blocks quantized by hand (ties to even, the
+    rounded fp16 scale, clipping, zero and underflowing scales)."""
+    for case in q8_blocks_golden():
+        x = np.zeros(32, np.float32)
+        for i, v in case["x"].items():
+            x[int(i)] = v
+        bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), x), case["name"]
+        q, d = o.quantize_q8(bits[None])
+        want = np.zeros(32, np.int64)
+        for i, v in case["q"].items():
+            want[int(i)] = v
+        assert np.array_equal(q[0].astype(np.int64), want), (case["name"], q[0])
+        assert int(d[0, 0]) == int(case["d16"], 16), (case["name"], hex(int(d[0, 0])))
+
+
+def check_q8_invariants(o):
+    """Random blocks over twenty decades of magnitude: |q| <= 127; where the
+    fp16 scale d16 is normal, the largest |x| maps to +-127 and every q is
+    within 1/2 (plus fp32 rounding of x * r) of x / d16; signs are kept;
+    d16 is numpy's float16 rounding of the fp32 amax / 127."""
+    rng = _rng(32)
+    V, K = 64, 32 * 40
+    for sigma in [1e-12, 1e-8, 1e-6, 1e-4, 1e-2, 1.0, 1e2, 1e4]:
+        g = (rng.standard_normal((V, K)) * sigma).astype(np.float32)
+        bits = (g.view(np.uint32) >> 16).astype(np.uint16)        # truncate to bf16
+        x = (bits.astype(np.uint32) << 16).view(np.float32).reshape(V, K // 32, 32)
+        q, d = o.quantize_q8(bits)
+        q = q.reshape(V, K // 32, 32).astype(np.int64)
+        amax = np.abs(x).max(axis=2)
+        assert np.array_equal(d, (amax / np.float32(127)).astype(np.float16).view(np.uint16))
+        d16 = d.view(np.float16).astype(np.float64)[..., None]
+        assert (np.abs(q) <= 127).all()
+        assert ((q == 0) | (np.sign(q) == np.sign(x))).all()
+        normal = (d16 >= 2.0 ** -14)[..., 0]
+        if normal.any():
+            t = x.astype(np.float64)[normal] / d16[normal]
+            assert (np.abs(q[normal] - t) <= 0.5 + 1e-6 * np.abs(t)).all(), sigma
+            am = np.abs(x[normal]).argmax(axis=1)
+            top = np.take_along_axis(q[normal], am[:, None], axis=1)[:, 0]
+            assert (np.abs(top) == 127).all(), sigma
+        zero = (d16 == 0)[..., 0]
+        assert (q[zero] == 0).all()
+
+
 ALL_CHECKS = [
     check_e2m1_table,
     check_e8m0_library,
@@ -500,4 +572,7 @@ ALL_CHECKS = [
     check_gather_semantics,
     check_swiglu,
     check_combine,
+    check_f2h_library,
+    check_q8_hand_worked,
+    check_q8_invariants,
 ]
