@@ -27,7 +27,8 @@ oracle on a bounded sample of the same workload on all host cores, and
 other shapes measured the same way (not the headline), among them the fused
 gate/up + SwiGLU calls (qmv_gather_moe_swiglu) C2gu and C3gu and the down
 projections with the router-weighted combine (qmv_gather_moe_combine) C4c and
-C2c.
+C2c, and the 2-bit and 3-bit gathers fed bf16 activations that the kernel
+quantizes while staging them, C3q and C4q.
 """
 from __future__ import annotations
 
@@ -93,7 +94,8 @@ def weight_bytes(wl, n_experts):
 def other_bytes(wl):
     """Activation, scale, id and output bytes of one call."""
     V = wl.M * wl.top_k if (wl.kind in ("gather", "combine") and wl.x_per_slot) else wl.M
-    xb = V * wl.K * (2 if wl.afmt == "bf16" else 1) + (0 if wl.afmt == "bf16" else V * (wl.K // 32) * 2)
+    bf = wl.afmt in ("bf16", "bf16q8")
+    xb = V * wl.K * (2 if bf else 1) + (0 if bf else V * (wl.K // 32) * 2)
     routed = wl.kind in ("gather", "gate_up", "combine")
     outs = wl.M * (wl.top_k if wl.kind in ("gather", "gate_up") else 1) * wl.N
     ids = 4 * wl.M * wl.top_k if routed else 0
@@ -104,7 +106,7 @@ def other_bytes(wl):
 # Rotation plan: layer copies so that between two reads of the same weights
 # more than the 256 MB Infinity Cache of other weights is read.
 ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40, "C2gu": 4, "C3gu": 1,
-            "C4c": 2, "C2c": 32}
+            "C4c": 2, "C2c": 32, "C3q": 2, "C4q": 2}
 
 
 class Prepared:
@@ -138,7 +140,7 @@ class Prepared:
         tensors = [(inp.gcodes, inp.gscales), (inp.ucodes, inp.uscales)] if gate_up else \
             [(inp.codes, inp.scales)]
         self.w = [(layers(c), layers(sc)) for c, sc in tensors]
-        if wl.afmt == "bf16":
+        if wl.afmt in ("bf16", "bf16q8"):
             self.x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
             self.xs = None
         else:
@@ -148,7 +150,7 @@ class Prepared:
         combine = wl.kind == "combine"
         self.rw = torch.from_numpy(inp.extra["weights"]).to(dev) if combine else None
         if routed:
-            if name in ("C3", "C4", "C3gu", "C4c"):
+            if name in ("C3", "C4", "C3gu", "C4c", "C3q", "C4q"):
                 ids = synth.disjoint_id_stream(wl.seed + 100, calls, wl.top_k, wl.E)
             else:
                 ids = synth.id_stream(wl.seed + 100, calls, wl.M, wl.top_k, wl.E)
@@ -170,7 +172,7 @@ class Prepared:
         self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
         rcb = synth.row_code_bytes(wl.wfmt, wl.K) * wl.N
         rsb = synth.row_scale_bytes(wl.wfmt, wl.K) * wl.N
-        afmt = 0 if wl.afmt == "bf16" else 1
+        afmt = {"bf16": 0, "q8": 1, "bf16q8": 2}[wl.afmt]
         xs = None if self.xs is None else self.xs.data_ptr()
         self.args, self.args_hot, self.regions = [], [], []
         for i in range(calls):
@@ -384,7 +386,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c",
+    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c,C3q,C4q",
                     help="other shapes to measure besides the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")

@@ -16,6 +16,8 @@ Layouts (C-contiguous device tensors, see include/qmv.h):
     ids     int32 [M][top_k]
     x       bfloat16 [M][K] / int8 [M][K]; per-slot: [M][top_k][K]
     x_scales float16 [...][K/32] for int8 activations
+bf16 activations with 2-bit or 3-bit weights (x_scales None) are quantized
+to int8 per 32 inside the kernel (QMV_A_BF16_Q8).
 """
 from __future__ import annotations
 
@@ -27,12 +29,12 @@ import torch  # noqa: F401  -- loads the HIP runtime that libqmv.so binds to
 __all__ = ["qmv_dense", "qmv_gather_moe", "qmv_gather_moe_swiglu", "qmv_gather_moe_combine",
            "qmv_strerror",
            "qmv_probe_stream_read", "lib", "LIB_PATH",
-           "W_MXFP4", "W_CB2", "W_CB3", "A_BF16", "A_Q8B32", "QmvError"]
+           "W_MXFP4", "W_CB2", "W_CB3", "A_BF16", "A_Q8B32", "A_BF16_Q8", "QmvError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
 
 W_MXFP4, W_CB2, W_CB3 = 0, 1, 2
-A_BF16, A_Q8B32 = 0, 1
+A_BF16, A_Q8B32, A_BF16_Q8 = 0, 1, 2
 _WFMT = {"mxfp4": W_MXFP4, "cb2": W_CB2, "cb3": W_CB3}
 _AFMT_OF = {W_MXFP4: A_BF16, W_CB2: A_Q8B32, W_CB3: A_Q8B32}
 STATUS = {0: "QMV_OK", 1: "QMV_EINVAL", 2: "QMV_EUNSUPPORTED", 3: "QMV_EHIP"}
@@ -109,6 +111,16 @@ def _check(status):
 _SCALE_DT = (torch.uint8, torch.float16)
 
 
+def _afmt(w, x):
+    """Activation format from the weight format and x's dtype: MXFP4 takes
+    bf16; 2-/3-bit weights take int8 (+ scales) or bf16 (quantized in-kernel)."""
+    if w == W_MXFP4:
+        return A_BF16, (torch.bfloat16,)
+    if isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16:
+        return A_BF16_Q8, (torch.bfloat16,)
+    return A_Q8B32, (torch.int8,)
+
+
 def qmv_dense(wfmt, w_codes, w_scales, x, x_scales=None, y=None, stream=None):
     """Dense GEMV: y[m][n] = sum_k w(n,k) x(m,k); returns y (float32 [M][N])."""
     w = _wfmt(wfmt)
@@ -119,8 +131,7 @@ def qmv_dense(wfmt, w_codes, w_scales, x, x_scales=None, y=None, stream=None):
     N = w_codes.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    a = _AFMT_OF.get(w, A_BF16)
-    xd = (torch.bfloat16,) if a == A_BF16 else (torch.int8,)
+    a, xd = _afmt(w, x)
     s = lib().qmv_dense(w, _dev_ptr(w_codes, "w_codes", (torch.uint8,), dev),
                         _dev_ptr(w_scales, "w_scales", _SCALE_DT, dev), a,
                         _dev_ptr(x, "x", xd, dev),
@@ -145,8 +156,7 @@ def qmv_gather_moe(wfmt, w_codes, w_scales, expert_ids, x, x_scales=None, x_per_
     K = x.shape[-1]
     if y is None:
         y = torch.empty((M, top_k, N), dtype=torch.float32, device=dev)
-    a = _AFMT_OF.get(w, A_BF16)
-    xd = (torch.bfloat16,) if a == A_BF16 else (torch.int8,)
+    a, xd = _afmt(w, x)
     s = lib().qmv_gather_moe(w, _dev_ptr(w_codes, "w_codes", (torch.uint8,), dev),
                              _dev_ptr(w_scales, "w_scales", _SCALE_DT, dev), E,
                              _dev_ptr(expert_ids, "expert_ids", (torch.int32,), dev), M, top_k, a,
@@ -171,8 +181,7 @@ def qmv_gather_moe_swiglu(wfmt, gate_codes, gate_scales, up_codes, up_scales, ex
     K = x.shape[-1]
     if y is None:
         y = torch.empty((M, top_k, N), dtype=torch.float32, device=dev)
-    a = _AFMT_OF.get(w, A_BF16)
-    xd = (torch.bfloat16,) if a == A_BF16 else (torch.int8,)
+    a, xd = _afmt(w, x)
     s = lib().qmv_gather_moe_swiglu(
         w, _dev_ptr(gate_codes, "gate_codes", (torch.uint8,), dev),
         _dev_ptr(gate_scales, "gate_scales", _SCALE_DT, dev),
@@ -201,8 +210,7 @@ def qmv_gather_moe_combine(wfmt, w_codes, w_scales, expert_ids, route_weights, x
     K = x.shape[-1]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    a = _AFMT_OF.get(w, A_BF16)
-    xd = (torch.bfloat16,) if a == A_BF16 else (torch.int8,)
+    a, xd = _afmt(w, x)
     s = lib().qmv_gather_moe_combine(
         w, _dev_ptr(w_codes, "w_codes", (torch.uint8,), dev),
         _dev_ptr(w_scales, "w_scales", _SCALE_DT, dev), E,

@@ -23,6 +23,15 @@ extern const void *const kTableCB_mxfp4[4][3];
 extern const void *const kTableCB_cb2[4][3];
 extern const void *const kTableCB_cb2s[4][3];
 extern const void *const kTableCB_cb3[4][3];
+extern const void *const kTableQ_cb2[3][4][5];
+extern const void *const kTableQ_cb2s[3][4][5];
+extern const void *const kTableQ_cb3[3][4][5];
+extern const void *const kTableQGU_cb2[2][4][5];
+extern const void *const kTableQGU_cb2s[2][4][5];
+extern const void *const kTableQGU_cb3[2][4][5];
+extern const void *const kTableQCB_cb2[4][3];
+extern const void *const kTableQCB_cb2s[4][3];
+extern const void *const kTableQCB_cb3[4][3];
 }  // namespace qmv_w8
 
 namespace {
@@ -35,8 +44,41 @@ constexpr int kMaxK = 16384;
 constexpr int kMaxM = 4;
 constexpr int kMaxTopK = 16;
 
-const void *kernel_for(int wi, int kind, int variant, int li, int ci, bool gate_up)
+// Kernels for bf16 activations quantized in staging (2-bit and 3-bit weights).
+const void *kernel_for_q8(int wi, int kind, int variant, int li, int ci, bool gate_up)
 {
+    if (wi == 1) {
+        if (gate_up) {
+            switch (kind) {
+            case kCB2: return qmv_w8::kTableQGU_cb2[variant][li][ci];
+            case kCB2S: return qmv_w8::kTableQGU_cb2s[variant][li][ci];
+            default: return qmv_w8::kTableQGU_cb3[variant][li][ci];
+            }
+        }
+        switch (kind) {
+        case kCB2: return qmv_w8::kTableQ_cb2[variant][li][ci];
+        case kCB2S: return qmv_w8::kTableQ_cb2s[variant][li][ci];
+        default: return qmv_w8::kTableQ_cb3[variant][li][ci];
+        }
+    }
+    if (gate_up) {
+        switch (kind) {
+        case kCB2: return kTableQGU_cb2[variant][li][ci];
+        case kCB2S: return kTableQGU_cb2s[variant][li][ci];
+        default: return kTableQGU_cb3[variant][li][ci];
+        }
+    }
+    switch (kind) {
+    case kCB2: return kTableQ_cb2[variant][li][ci];
+    case kCB2S: return kTableQ_cb2s[variant][li][ci];
+    default: return kTableQ_cb3[variant][li][ci];
+    }
+}
+
+const void *kernel_for(int wi, int kind, int variant, int li, int ci, bool gate_up, bool q8)
+{
+    if (q8)
+        return kernel_for_q8(wi, kind, variant, li, ci, gate_up);
     if (wi == 1) {
         if (gate_up) {
             switch (kind) {
@@ -69,8 +111,22 @@ const void *kernel_for(int wi, int kind, int variant, int li, int ci, bool gate_
     }
 }
 
-const void *combine_kernel_for(int wi, int kind, int li, int ci)
+const void *combine_kernel_for(int wi, int kind, int li, int ci, bool q8)
 {
+    if (q8) {
+        if (wi == 1) {
+            switch (kind) {
+            case kCB2: return qmv_w8::kTableQCB_cb2[li][ci];
+            case kCB2S: return qmv_w8::kTableQCB_cb2s[li][ci];
+            default: return qmv_w8::kTableQCB_cb3[li][ci];
+            }
+        }
+        switch (kind) {
+        case kCB2: return kTableQCB_cb2[li][ci];
+        case kCB2S: return kTableQCB_cb2s[li][ci];
+        default: return kTableQCB_cb3[li][ci];
+        }
+    }
     if (wi == 1) {
         switch (kind) {
         case kMXFP4: return qmv_w8::kTableCB_mxfp4[li][ci];
@@ -113,8 +169,9 @@ qmv_status_t validate(int wfmt, const void *codes, const void *scales, long long
         return QMV_EINVAL;
     if (M <= 0 || N <= 0 || K <= 0 || E <= 0 || top_k <= 0)
         return QMV_EINVAL;
-    if (wfmt < QMV_W_MXFP4 || wfmt > QMV_W_CB3 || afmt < QMV_A_BF16 || afmt > QMV_A_Q8B32)
+    if (wfmt < QMV_W_MXFP4 || wfmt > QMV_W_CB3 || afmt < QMV_A_BF16 || afmt > QMV_A_BF16_Q8)
         return QMV_EUNSUPPORTED;
+    // pairs: (MXFP4, BF16), (CB2 or CB3, Q8B32), (CB2 or CB3, BF16_Q8)
     if ((wfmt == QMV_W_MXFP4) != (afmt == QMV_A_BF16))
         return QMV_EUNSUPPORTED;
     if (M > kMaxM || top_k > kMaxTopK || K % 32 != 0 || K > kMaxK)
@@ -189,10 +246,12 @@ Shape pick_shape(int variant, int units, long long rows_total, int rt)
 // Launch shapes measured best on MI355X for the MoE expert shapes this library
 // is tuned on (sweeps of every menu shape at 4 and 8 waves per workgroup, HBM-
 // resident weights rotated past the Infinity Cache).  Other shapes use
-// pick_shape() with 4 waves (8 for the combine kernel, whose tuned shapes
-// all prefer it).  An entry matches on format kind, variant (3: combine),
+// pick_shape() with 4 waves (8 for the combine kernel and for bf16
+// activations quantized in staging, whose tuned shapes all prefer it: each
+// workgroup quantizes the whole activation vector, so fewer, larger
+// workgroups repeat that less).  An entry matches on format kind, variant (3: combine),
 // gate/up mode, K, N and the number of (token, slot) pairs.
-struct Tuned { int kind, variant, gate_up, K, N, pairs, waves, lpr, cpl; };
+struct Tuned { int kind, variant, gate_up, K, N, pairs, waves, lpr, cpl, q8 = 0; };
 constexpr Tuned kTuned[] = {
     {kMXFP4, 0, 0, 2880, 2880, 4, 4, 32, 3},     // gpt-oss-20b expert projection
     {kMXFP4, 0, 1, 2880, 2880, 4, 4, 32, 3},     // gpt-oss-20b gate+up, SwiGLU
@@ -203,13 +262,18 @@ constexpr Tuned kTuned[] = {
     {kMXFP4, 2, 0, 7168, 7168, 1, 8, 64, 4},     // dense, 4 tokens
     {kCB3,   3, 0, 2048, 7168, 4, 8, 32, 1},     // 3-bit down + router-weighted combine
     {kMXFP4, 3, 0, 2880, 2880, 4, 8, 32, 2},     // gpt-oss down + router-weighted combine
+    // bf16 activations quantized in staging: larger workgroups quantize the
+    // activation vector fewer times over (C3 7.10 -> 6.48 us, C4 10.04 -> 9.17 us)
+    {kCB2,   0, 0, 7168, 2048, 4, 8, 32, 4, 1},  // 2-bit gate/up, bf16 x
+    {kCB3,   1, 0, 2048, 7168, 4, 8, 16, 4, 1},  // 3-bit down, per-slot bf16 x
 };
 
-bool tuned_shape(int kind, int variant, bool gate_up, int K, int N, int pairs, int &wi, Shape &sh)
+bool tuned_shape(int kind, int variant, bool gate_up, bool q8, int K, int N, int pairs, int &wi,
+                 Shape &sh)
 {
     for (const Tuned &t : kTuned) {
         if (t.kind != kind || t.variant != variant || t.gate_up != (gate_up ? 1 : 0) || t.K != K ||
-            t.N != N || t.pairs != pairs)
+            t.N != N || t.pairs != pairs || t.q8 != (q8 ? 1 : 0))
             continue;
         wi = t.waves == 8 ? 1 : 0;
         const int ncpl = variant >= 2 ? 3 : 5;
@@ -224,13 +288,13 @@ bool tuned_shape(int kind, int variant, bool gate_up, int K, int N, int pairs, i
     return false;
 }
 
-std::once_flag g_attr_once[2][2][4][3][4][5];
-hipError_t g_attr_err[2][2][4][3][4][5];
-std::once_flag g_cattr_once[2][4][4][3];
-hipError_t g_cattr_err[2][4][4][3];
+std::once_flag g_attr_once[2][2][2][4][3][4][5];        // [q8][waves][gate_up][kind][variant][lpr][cpl]
+hipError_t g_attr_err[2][2][2][4][3][4][5];
+std::once_flag g_cattr_once[2][2][4][4][3];             // [q8][waves][kind][lpr][cpl]
+hipError_t g_cattr_err[2][2][4][4][3];
 
 // Arguments common to every kernel of a call (Args in qmv_device.hpp).
-Args base_args(int wfmt, int kind, const void *codes, const void *scales, int E,
+Args base_args(int wfmt, int afmt, int kind, const void *codes, const void *scales, int E,
                const int32_t *ids, int M, int top_k, const void *x, const void *xs,
                int x_per_slot, float *y, int N, int K)
 {
@@ -248,7 +312,7 @@ Args base_args(int wfmt, int kind, const void *codes, const void *scales, int E,
     a.rsb = (int)row_scale_bytes(wfmt, K);
     a.expert_cb = (long long)N * a.rcb;
     a.expert_sb = (long long)N * a.rsb;
-    a.x_vec_bytes = (wfmt == QMV_W_MXFP4) ? 2 * K : K;
+    a.x_vec_bytes = (afmt == QMV_A_Q8B32) ? K : 2 * K;      // int8, or bf16
     a.E = E;
     a.M = M;
     a.top_k = top_k;
@@ -270,7 +334,7 @@ int kind_of(int wfmt, int K)
 
 // codes2/scales2 non-null selects the gate/up mode: codes/scales are the gate
 // projection, codes2/scales2 the up projection, y = swiglu(gate x, up x).
-qmv_status_t launch(int wfmt, const void *codes, const void *scales, const void *codes2,
+qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, const void *codes2,
                     const void *scales2, int E, const int32_t *ids,
                     int M, int top_k, const void *x, const void *xs, int x_per_slot,
                     float *y, int N, int K, hipStream_t stream)
@@ -287,10 +351,11 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, const void 
     const int nvmax = variant == 0 ? 1 : 4;
     const long long rows_total = (long long)N * (gather ? M * top_k : 1) * (gate_up ? 2 : 1);
     Shape sh;
-    int wi = 0;
-    if (!tuned_shape(kind, variant, gate_up, K, N, gather ? M * top_k : 1, wi, sh))
+    const bool q8 = afmt == QMV_A_BF16_Q8;
+    int wi = q8 ? 1 : 0;
+    if (!tuned_shape(kind, variant, gate_up, q8, K, N, gather ? M * top_k : 1, wi, sh))
         sh = pick_shape(variant, units, rows_total, rt);
-    Args a = base_args(wfmt, kind, codes, scales, gather ? E : 1, ids, M, gather ? top_k : 1, x, xs,
+    Args a = base_args(wfmt, afmt, kind, codes, scales, gather ? E : 1, ids, M, gather ? top_k : 1, x, xs,
                        gather ? x_per_slot : 0, y, N, K);
     a.codes2 = (const uint8_t *)codes2;
     a.scales2 = (const uint8_t *)scales2;
@@ -299,15 +364,15 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, const void 
     a.rows_per_tile = waves * (64 / sh.lpr) * (gate_up ? 1 : rt);
     const size_t lds = (size_t)nvmax * a.lds_vec_bytes;
 
-    const void *fn = kernel_for(wi, kind, variant, sh.li, sh.ci, gate_up);
+    const void *fn = kernel_for(wi, kind, variant, sh.li, sh.ci, gate_up, q8);
     // Largest dynamic LDS this kernel can ask for (K = kMaxK, all vectors).
-    std::call_once(g_attr_once[wi][gate_up][kind][variant][sh.li][sh.ci], [&] {
+    std::call_once(g_attr_once[q8][wi][gate_up][kind][variant][sh.li][sh.ci], [&] {
         const int umax = kMaxK / kUnitWeights[kind];
         const int vmax = (umax * (kUnitXB[kind] + kUnitAB[kind]) + 15) & ~15;
-        g_attr_err[wi][gate_up][kind][variant][sh.li][sh.ci] = hipFuncSetAttribute(
+        g_attr_err[q8][wi][gate_up][kind][variant][sh.li][sh.ci] = hipFuncSetAttribute(
             fn, hipFuncAttributeMaxDynamicSharedMemorySize, nvmax * vmax);
     });
-    if (g_attr_err[wi][gate_up][kind][variant][sh.li][sh.ci] != hipSuccess)
+    if (g_attr_err[q8][wi][gate_up][kind][variant][sh.li][sh.ci] != hipSuccess)
         return QMV_EHIP;
 
     const dim3 grid((unsigned)((N + a.rows_per_tile - 1) / a.rows_per_tile),
@@ -320,33 +385,34 @@ qmv_status_t launch(int wfmt, const void *codes, const void *scales, const void 
 
 // Down projection with the router-weighted combine: one launch, grid (row
 // tiles, tokens); each lane carries row n of four of the token's slots.
-qmv_status_t launch_combine(int wfmt, const void *codes, const void *scales, int E,
+qmv_status_t launch_combine(int wfmt, int afmt, const void *codes, const void *scales, int E,
                             const int32_t *ids, const float *route_w, int M, int top_k,
                             const void *x, const void *xs, int x_per_slot, float *y, int N, int K,
                             hipStream_t stream)
 {
     const int kind = kind_of(wfmt, K);
-    Args a = base_args(wfmt, kind, codes, scales, E, ids, M, top_k, x, xs, x_per_slot, y, N, K);
+    Args a = base_args(wfmt, afmt, kind, codes, scales, E, ids, M, top_k, x, xs, x_per_slot, y, N, K);
     a.route_w = route_w;
     a.x_early = 1;
     Shape sh;
     int wi = 1;
     constexpr int RT = 4;
-    if (!tuned_shape(kind, 3, false, K, N, M * top_k, wi, sh))
+    const bool q8 = afmt == QMV_A_BF16_Q8;
+    if (!tuned_shape(kind, 3, false, q8, K, N, M * top_k, wi, sh))
         sh = pick_shape(3, a.units, (long long)N * M * RT, RT);
     const int waves = kWaveMenu[wi];
     a.rows_per_tile = waves * (64 / sh.lpr);
     const int nv = x_per_slot ? (top_k < 4 ? top_k : 4) : 1;
     const size_t lds = (size_t)nv * a.lds_vec_bytes;
 
-    const void *fn = combine_kernel_for(wi, kind, sh.li, sh.ci);
-    std::call_once(g_cattr_once[wi][kind][sh.li][sh.ci], [&] {
+    const void *fn = combine_kernel_for(wi, kind, sh.li, sh.ci, q8);
+    std::call_once(g_cattr_once[q8][wi][kind][sh.li][sh.ci], [&] {
         const int umax = kMaxK / kUnitWeights[kind];
         const int vmax = (umax * (kUnitXB[kind] + kUnitAB[kind]) + 15) & ~15;
-        g_cattr_err[wi][kind][sh.li][sh.ci] = hipFuncSetAttribute(
+        g_cattr_err[q8][wi][kind][sh.li][sh.ci] = hipFuncSetAttribute(
             fn, hipFuncAttributeMaxDynamicSharedMemorySize, 4 * vmax);
     });
-    if (g_cattr_err[wi][kind][sh.li][sh.ci] != hipSuccess)
+    if (g_cattr_err[q8][wi][kind][sh.li][sh.ci] != hipSuccess)
         return QMV_EHIP;
     const dim3 grid((unsigned)((N + a.rows_per_tile - 1) / a.rows_per_tile), (unsigned)M);
     void *kargs[] = {&a};
@@ -369,7 +435,7 @@ QMV_API qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void 
                                     x, afmt == QMV_A_Q8B32 ? x_scales : nullptr, y, N, K);
     if (s != QMV_OK)
         return s;
-    return launch(wfmt, w_codes, w_scales, nullptr, nullptr, 1, nullptr, M, 1, x,
+    return launch(wfmt, afmt, w_codes, w_scales, nullptr, nullptr, 1, nullptr, M, 1, x,
                   afmt == QMV_A_Q8B32 ? x_scales : nullptr, 0, y, N, K, stream);
 }
 
@@ -382,7 +448,7 @@ QMV_API qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const 
                                     x, afmt == QMV_A_Q8B32 ? x_scales : nullptr, y, N, K);
     if (s != QMV_OK)
         return s;
-    return launch(wfmt, w_codes, w_scales, nullptr, nullptr, E, expert_ids, M, top_k, x,
+    return launch(wfmt, afmt, w_codes, w_scales, nullptr, nullptr, E, expert_ids, M, top_k, x,
                   afmt == QMV_A_Q8B32 ? x_scales : nullptr, x_per_slot ? 1 : 0, y, N, K, stream);
 }
 
@@ -400,7 +466,7 @@ QMV_API qmv_status_t qmv_gather_moe_swiglu(qmv_wfmt_t wfmt, const void *gate_cod
     s = validate(wfmt, up_codes, up_scales, E, expert_ids, true, M, top_k, afmt, x, xs, y, N, K);
     if (s != QMV_OK)
         return s;
-    return launch(wfmt, gate_codes, gate_scales, up_codes, up_scales, E, expert_ids, M, top_k, x,
+    return launch(wfmt, afmt, gate_codes, gate_scales, up_codes, up_scales, E, expert_ids, M, top_k, x,
                   xs, 0, y, N, K, stream);
 }
 
@@ -417,7 +483,7 @@ QMV_API qmv_status_t qmv_gather_moe_combine(qmv_wfmt_t wfmt, const void *w_codes
         return s;
     if (!route_weights || !aligned(route_weights, 4))
         return QMV_EINVAL;
-    return launch_combine(wfmt, w_codes, w_scales, E, expert_ids, route_weights, M, top_k, x, xs,
+    return launch_combine(wfmt, afmt, w_codes, w_scales, E, expert_ids, route_weights, M, top_k, x, xs,
                           x_per_slot ? 1 : 0, y, N, K, stream);
 }
 
@@ -427,7 +493,8 @@ QMV_API const char *qmv_strerror(qmv_status_t status)
     case QMV_OK: return "success";
     case QMV_EINVAL: return "invalid argument (null or misaligned pointer, or a size <= 0)";
     case QMV_EUNSUPPORTED: return "unsupported shape or format (M in [1,4], top_k in [1,16], "
-                                  "K % 32 == 0 and K <= 16384; pairs MXFP4+BF16, CB2+Q8B32, CB3+Q8B32)";
+                                  "K % 32 == 0 and K <= 16384; pairs MXFP4+BF16, CB2/CB3+Q8B32, "
+                                  "CB2/CB3+BF16_Q8)";
     case QMV_EHIP: return "the HIP runtime rejected the kernel launch";
     }
     return "unknown status";

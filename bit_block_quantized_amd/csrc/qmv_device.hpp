@@ -13,6 +13,11 @@
 // partial sums of a row are combined by a fixed butterfly, so results are
 // bitwise reproducible.
 //
+// The 2-bit and 3-bit kernels are also built with Q = true: activations then
+// arrive as bf16 and each staging thread quantizes one 32-block to int8 plus
+// an fp16 scale on its way into LDS (quant_q8_block); everything after the
+// staging is the int8 kernel unchanged.
+//
 // Units per format (one unit = what a lane decodes per load):
 //   MXFP4  32 weights: 16 B of nibbles + 1 E8M0 byte      (bf16 x, 64 B)
 //   CB2    64 weights: 16 B of 2-bit codes + 2 fp16 scales (int8 x, 64 B)
@@ -314,18 +319,26 @@ __device__ __forceinline__ int item_m(int i, int per)
     else return (i >= per) + (i >= 2 * per) + (i >= 3 * per);
 }
 
-template <int F, int NVMAX>
+// Staging item i's bytes in global memory: Q items are 64-byte bf16 blocks.
+template <int F, int NVMAX, bool Q>
 __device__ __forceinline__ const uint8_t *x_item_ptr(const Args &a, const Item &it, int i)
 {
     const int per = x_items_per_vec<F>(a);
     const int m = item_m<NVMAX>(i, per);
     const int c = i - __umul24(m, per);
-    return a.x + __umul24(item_vec(it, m), a.x_vec_bytes) + c * (16 * XItem<F>::chunks);
+    return a.x + __umul24(item_vec(it, m), a.x_vec_bytes) + c * (Q ? 64 : 16 * XItem<F>::chunks);
 }
 
-template <int F, int NVMAX>
+template <int F, int NVMAX, bool Q>
 __device__ __forceinline__ void xload(const Args &a, const Item &it, uint4 (&r)[kXReg])
 {
+    if constexpr (Q) {                                      // one bf16 block per thread
+        const int T = __umul24(it.nv, x_items_per_vec<F>(a));
+        const uint8_t *p = x_item_ptr<F, NVMAX, true>(a, it, min((int)threadIdx.x, T - 1));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = *(const uint4 *)(p + 16 * q);
+        return;
+    }
     constexpr int PER = kXReg / XItem<F>::chunks;          // items held per thread
     const int T = __umul24(it.nv, x_items_per_vec<F>(a));
     const int jn = (T + kThreads - 1) / kThreads;           // items this workgroup needs per thread
@@ -333,7 +346,7 @@ __device__ __forceinline__ void xload(const Args &a, const Item &it, uint4 (&r)[
     for (int j = 0; j < PER; ++j) {
         if (j < jn) {
             const int i = min((int)threadIdx.x + j * kThreads, T - 1);   // clamped: no divergence
-            const uint8_t *p = x_item_ptr<F, NVMAX>(a, it, i);
+            const uint8_t *p = x_item_ptr<F, NVMAX, false>(a, it, i);
             r[j * XItem<F>::chunks] = *(const uint4 *)p;
             if constexpr (XItem<F>::chunks == 2) r[j * 2 + 1] = *(const uint4 *)(p + 16);
         }
@@ -391,8 +404,8 @@ __device__ __forceinline__ int sum_i8x16(uint4 v)
 //  CB3:   block b -> its two half-blocks in the cb3_half order; side data
 //         0.5*xs per block.
 template <int F, int NVMAX>
-__device__ __forceinline__ void xput(const Args &a, const Item &it, uint8_t *lds, int i,
-                                     uint4 lo, uint4 hi)
+__device__ __forceinline__ void xput_blk(const Args &a, const Item &it, uint8_t *lds, int i,
+                                         uint4 lo, uint4 hi, uint32_t xsb)
 {
     const int per = x_items_per_vec<F>(a);
     const int m = item_m<NVMAX>(i, per);
@@ -403,8 +416,7 @@ __device__ __forceinline__ void xput(const Args &a, const Item &it, uint8_t *lds
     } else {
         constexpr int CH = Fmt<F>::XB / 16;
         const int xbytes = a.units * Fmt<F>::XB;
-        const uint16_t xsb = a.xs[__umul24(item_vec(it, m), a.K / 32) + c];
-        const float xsh = 0.5f * (float)__builtin_bit_cast(_Float16, xsb);
+        const float xsh = 0.5f * (float)__builtin_bit_cast(_Float16, (uint16_t)xsb);
         if constexpr (F == kCB3) {
             *(uint4 *)(dst + 16 * chunk_pos<2>(c, 0)) = cb3_xorder(lo);
             *(uint4 *)(dst + 16 * chunk_pos<2>(c, 1)) = cb3_xorder(hi);
@@ -428,8 +440,71 @@ __device__ __forceinline__ void xput(const Args &a, const Item &it, uint8_t *lds
 }
 
 template <int F, int NVMAX>
+__device__ __forceinline__ void xput(const Args &a, const Item &it, uint8_t *lds, int i,
+                                     uint4 lo, uint4 hi)
+{
+    uint32_t xsb = 0;
+    if constexpr (F != kMXFP4) {
+        const int per = x_items_per_vec<F>(a);
+        const int m = item_m<NVMAX>(i, per);
+        xsb = a.xs[__umul24(item_vec(it, m), a.K / 32) + (i - __umul24(m, per))];
+    }
+    xput_blk<F, NVMAX>(a, it, lds, i, lo, hi, xsb);
+}
+
+// bf16 activations of one 32-block -> 32 int8 (lo, hi) and the fp16 scale
+// bits, all in fp32: d = amax / 127, d16 = fp16(d) (nearest even), then
+// q = clamp(rint(x * (1 / d16)), -127, 127) with ties to even, and q = 0
+// where d16 is 0 or infinite.  This is the q8 activation block that the
+// pages quantize in a launch of its own before every integer matvec
+// (geo-lucebox PR #31, "What is now hot": quantize_q8_1); here each staging
+// thread quantizes one block on its way into LDS, so there is no separate
+// launch and no int8 copy of x in memory.  Division and reciprocal are the
+// IEEE (correctly rounded) ones.
+__device__ __forceinline__ uint32_t quant_q8_block(const uint4 (&c)[4], uint4 &lo, uint4 &hi)
+{
+    const uint32_t w[16] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w,
+                            c[2].x, c[2].y, c[2].z, c[2].w, c[3].x, c[3].y, c[3].z, c[3].w};
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+    }
+    const float d = amax / 127.0f;
+    const _Float16 h = (_Float16)d;
+    const float dd = (float)h;
+    const float r = (dd > 0.0f && dd < __builtin_inff()) ? 1.0f / dd : 0.0f;
+    uint32_t qd[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float t = fminf(fmaxf(__builtin_rintf(v[4 * j + b] * r), -127.0f), 127.0f);
+            packed |= ((uint32_t)(int)t & 0xFFu) << (8 * b);
+        }
+        qd[j] = packed;
+    }
+    lo = make_uint4(qd[0], qd[1], qd[2], qd[3]);
+    hi = make_uint4(qd[4], qd[5], qd[6], qd[7]);
+    return (uint32_t)__builtin_bit_cast(unsigned short, h);
+}
+
+template <int F, int NVMAX, bool Q>
 __device__ __forceinline__ void xstore(const Args &a, const Item &it, uint8_t *lds, const uint4 (&r)[kXReg])
 {
+    if constexpr (Q) {
+        const int i = (int)threadIdx.x;
+        if (i < __umul24(it.nv, x_items_per_vec<F>(a))) {
+            uint4 lo, hi;
+            const uint32_t xsb = quant_q8_block(r, lo, hi);
+            xput_blk<F, NVMAX>(a, it, lds, i, lo, hi, xsb);
+        }
+        return;
+    }
     constexpr int CHK = XItem<F>::chunks;
     constexpr int PER = kXReg / CHK;
     const int T = __umul24(it.nv, x_items_per_vec<F>(a));
@@ -442,14 +517,28 @@ __device__ __forceinline__ void xstore(const Args &a, const Item &it, uint8_t *l
 
 // Items beyond the register budget, loaded and stored directly.  Returns
 // whether there were any (the same answer in every thread).
-template <int F, int NVMAX>
+template <int F, int NVMAX, bool Q>
 __device__ __forceinline__ bool xrest(const Args &a, const Item &it, uint8_t *lds)
 {
+    if constexpr (Q) {
+        const int T = __umul24(it.nv, x_items_per_vec<F>(a));
+        if (T <= kThreads) return false;
+        for (int i = kThreads + (int)threadIdx.x; i < T; i += kThreads) {
+            const uint8_t *p = x_item_ptr<F, NVMAX, true>(a, it, i);
+            uint4 c[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c[q] = *(const uint4 *)(p + 16 * q);
+            uint4 lo, hi;
+            const uint32_t xsb = quant_q8_block(c, lo, hi);
+            xput_blk<F, NVMAX>(a, it, lds, i, lo, hi, xsb);
+        }
+        return true;
+    }
     constexpr int PER = kXReg / XItem<F>::chunks;
     const int T = __umul24(it.nv, x_items_per_vec<F>(a));
     if (T <= PER * kThreads) return false;
     for (int i = PER * kThreads + (int)threadIdx.x; i < T; i += kThreads) {
-        const uint8_t *p = x_item_ptr<F, NVMAX>(a, it, i);
+        const uint8_t *p = x_item_ptr<F, NVMAX, false>(a, it, i);
         const uint4 lo = *(const uint4 *)p;
         const uint4 hi = (XItem<F>::chunks == 2) ? *(const uint4 *)(p + 16) : lo;
         xput<F, NVMAX>(a, it, lds, i, lo, hi);
@@ -806,7 +895,7 @@ __device__ __forceinline__ float swiglu(float g, float u)
 // MODE 0: the lane's RT rows are RT consecutive output rows.  MODE 1 (gate/up,
 // RT == 2): the lane's two rows are row n of the gate and row n of the up
 // projection, and the store writes swiglu(gate, up).
-template <int F, int LPR, int CPL, int RT, int NV, int NVMAX, int MODE>
+template <int F, int LPR, int CPL, int RT, int NV, int NVMAX, int MODE, bool Q>
 __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t *lds, int row_base,
                                           uint4 (&xr)[kXReg])
 {
@@ -832,14 +921,14 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
         os[r] = (uint32_t)__umul24(n, a.rsb) + li * Unit<F>::SB;
     }
 
-    if (!a.x_early) xload<F, NVMAX>(a, it, xr);
+    if (!a.x_early) xload<F, NVMAX, Q>(a, it, xr);
     Unit<F> w[CPL][RT];
     load_scales<F, LPR, CPL, RT>(w, rs, os, 0, li, U);
 #pragma unroll
     for (int c = 0; c < Lead<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, 0, li, U, c);
-    xstore<F, NVMAX>(a, it, lds, xr);
+    xstore<F, NVMAX, Q>(a, it, lds, xr);
     __syncthreads();
-    if (xrest<F, NVMAX>(a, it, lds)) __syncthreads();
+    if (xrest<F, NVMAX, Q>(a, it, lds)) __syncthreads();
 
     float acc[RT][NV];
 #pragma unroll
@@ -888,13 +977,14 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
 
 // ------------------------------------------------------------------ kernel
 // F: format kind; LPR: lanes per row; CPL: units per lane and row in flight;
-// RT: rows per lane; NVMAX: most activation vectors one item may carry.
-template <int F, int LPR, int CPL, int RT, int NVMAX, int MODE>
+// RT: rows per lane; NVMAX: most activation vectors one item may carry;
+// Q: bf16 activations quantized to int8 blocks while staged.
+template <int F, int LPR, int CPL, int RT, int NVMAX, int MODE, bool Q>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     uint4 xr[kXReg];
-    if (a.x_early) xload<F, NVMAX>(a, early_item(a), xr);   // in flight while the ids arrive
+    if (a.x_early) xload<F, NVMAX, Q>(a, early_item(a), xr);   // in flight while the ids arrive
     Item it;
     if constexpr (NVMAX == 1) it = route_one(a, blockIdx.y);
     else it = route(a, blockIdx.y);
@@ -908,13 +998,13 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const Args a)
         return;
     }
     if constexpr (NVMAX == 1) {
-        rows_body<F, LPR, CPL, RT, 1, 1, MODE>(a, it, lds, row_base, xr);
+        rows_body<F, LPR, CPL, RT, 1, 1, MODE, Q>(a, it, lds, row_base, xr);
     } else {
         switch (it.nv) {
-        case 1: rows_body<F, LPR, CPL, RT, 1, NVMAX, MODE>(a, it, lds, row_base, xr); break;
-        case 2: rows_body<F, LPR, CPL, RT, 2, NVMAX, MODE>(a, it, lds, row_base, xr); break;
-        case 3: rows_body<F, LPR, CPL, RT, 3, NVMAX, MODE>(a, it, lds, row_base, xr); break;
-        default: rows_body<F, LPR, CPL, RT, 4, NVMAX, MODE>(a, it, lds, row_base, xr); break;
+        case 1: rows_body<F, LPR, CPL, RT, 1, NVMAX, MODE, Q>(a, it, lds, row_base, xr); break;
+        case 2: rows_body<F, LPR, CPL, RT, 2, NVMAX, MODE, Q>(a, it, lds, row_base, xr); break;
+        case 3: rows_body<F, LPR, CPL, RT, 3, NVMAX, MODE, Q>(a, it, lds, row_base, xr); break;
+        default: rows_body<F, LPR, CPL, RT, 4, NVMAX, MODE, Q>(a, it, lds, row_base, xr); break;
         }
     }
 }
@@ -984,7 +1074,7 @@ __device__ __forceinline__ void mac_seg_diag(Unit<F> (&w)[CPL][RT], const Args &
     }
 }
 
-template <int F, int LPR, int CPL>
+template <int F, int LPR, int CPL, bool Q>
 __global__ __launch_bounds__(kThreads) void qmv_combine_kernel(const Args a)
 {
     constexpr int RT = kCombineRT;
@@ -1001,7 +1091,7 @@ __global__ __launch_bounds__(kThreads) void qmv_combine_kernel(const Args a)
 
     Item it = combine_item(a, t, 0);
     uint4 xr[kXReg];
-    xload<F, 4>(a, it, xr);                        // in flight while the ids arrive
+    xload<F, 4, Q>(a, it, xr);                     // in flight while the ids arrive
     int e_l = -1;
     float w_l = 0.0f;
     if (lane < a.top_k) {
@@ -1030,7 +1120,7 @@ __global__ __launch_bounds__(kThreads) void qmv_combine_kernel(const Args a)
         const bool restage = g > 0 && a.x_per_slot;
         if (restage) {
             it = combine_item(a, t, g);
-            xload<F, 4>(a, it, xr);
+            xload<F, 4, Q>(a, it, xr);
         }
         Unit<F> w[CPL][RT];
         load_scales<F, LPR, CPL, RT>(w, rs, os, 0, li, U);
@@ -1038,9 +1128,9 @@ __global__ __launch_bounds__(kThreads) void qmv_combine_kernel(const Args a)
         for (int c = 0; c < Lead<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, 0, li, U, c);
         if (g == 0 || restage) {
             if (restage) __syncthreads();          // every wave is done with the last group's vectors
-            xstore<F, 4>(a, it, lds, xr);
+            xstore<F, 4, Q>(a, it, lds, xr);
             __syncthreads();
-            if (xrest<F, 4>(a, it, lds)) __syncthreads();
+            if (xrest<F, 4, Q>(a, it, lds)) __syncthreads();
         }
 
         float acc[RT];
@@ -1087,24 +1177,36 @@ extern const void *const kTableCB_mxfp4[4][3];
 extern const void *const kTableCB_cb2[4][3];
 extern const void *const kTableCB_cb2s[4][3];
 extern const void *const kTableCB_cb3[4][3];
+// The same for bf16 activations quantized in staging (2-bit and 3-bit only).
+extern const void *const kTableQ_cb2[3][4][5];
+extern const void *const kTableQ_cb2s[3][4][5];
+extern const void *const kTableQ_cb3[3][4][5];
+extern const void *const kTableQGU_cb2[2][4][5];
+extern const void *const kTableQGU_cb2s[2][4][5];
+extern const void *const kTableQGU_cb3[2][4][5];
+extern const void *const kTableQCB_cb2[4][3];
+extern const void *const kTableQCB_cb2s[4][3];
+extern const void *const kTableQCB_cb3[4][3];
 
 }  // namespace QMV_NS
 
-// Instantiate one format's kernel tables: [variant][lpr index][cpl index].
-#define QMV_K(F, V, L, C, MODE) \
-    (const void *)&::QMV_NS::qmv_kernel<F, L, C, ((V) == 2 ? 4 : 2), ((V) == 0 ? 1 : 4), MODE>
-#define QMV_ROW01(F, V, L, MODE) \
-    { QMV_K(F, V, L, 1, MODE), QMV_K(F, V, L, 2, MODE), QMV_K(F, V, L, 3, MODE), QMV_K(F, V, L, 4, MODE), QMV_K(F, V, L, 7, MODE) }
-#define QMV_ROW2(F, V, L) \
-    { QMV_K(F, V, L, 1, 0), QMV_K(F, V, L, 2, 0), QMV_K(F, V, L, 4, 0), nullptr, nullptr }
+// Instantiate one format's kernel tables: [variant][lpr index][cpl index];
+// Q selects bf16 activations quantized in staging.
+#define QMV_K(F, V, L, C, MODE, Q) \
+    (const void *)&::QMV_NS::qmv_kernel<F, L, C, ((V) == 2 ? 4 : 2), ((V) == 0 ? 1 : 4), MODE, Q>
+#define QMV_ROW01(F, V, L, MODE, Q) \
+    { QMV_K(F, V, L, 1, MODE, Q), QMV_K(F, V, L, 2, MODE, Q), QMV_K(F, V, L, 3, MODE, Q), \
+      QMV_K(F, V, L, 4, MODE, Q), QMV_K(F, V, L, 7, MODE, Q) }
+#define QMV_ROW2(F, V, L, Q) \
+    { QMV_K(F, V, L, 1, 0, Q), QMV_K(F, V, L, 2, 0, Q), QMV_K(F, V, L, 4, 0, Q), nullptr, nullptr }
 #define QMV_NOROW { nullptr, nullptr, nullptr, nullptr, nullptr }
-#define QMV_TABLE(F) \
-    { { QMV_ROW01(F, 0, 8, 0), QMV_ROW01(F, 0, 16, 0), QMV_ROW01(F, 0, 32, 0), QMV_ROW01(F, 0, 64, 0) }, \
-      { QMV_ROW01(F, 1, 8, 0), QMV_ROW01(F, 1, 16, 0), QMV_ROW01(F, 1, 32, 0), QMV_ROW01(F, 1, 64, 0) }, \
-      { QMV_NOROW, QMV_ROW2(F, 2, 16), QMV_ROW2(F, 2, 32), QMV_ROW2(F, 2, 64) } }
-#define QMV_KC(F, L, C) (const void *)&::QMV_NS::qmv_combine_kernel<F, L, C>
-#define QMV_ROWC(F, L) { QMV_KC(F, L, 1), QMV_KC(F, L, 2), QMV_KC(F, L, 4) }
-#define QMV_TABLE_CB(F) { QMV_ROWC(F, 8), QMV_ROWC(F, 16), QMV_ROWC(F, 32), QMV_ROWC(F, 64) }
-#define QMV_TABLE_GU(F) \
-    { { QMV_ROW01(F, 0, 8, 1), QMV_ROW01(F, 0, 16, 1), QMV_ROW01(F, 0, 32, 1), QMV_ROW01(F, 0, 64, 1) }, \
-      { QMV_ROW01(F, 1, 8, 1), QMV_ROW01(F, 1, 16, 1), QMV_ROW01(F, 1, 32, 1), QMV_ROW01(F, 1, 64, 1) } }
+#define QMV_TABLE(F, Q) \
+    { { QMV_ROW01(F, 0, 8, 0, Q), QMV_ROW01(F, 0, 16, 0, Q), QMV_ROW01(F, 0, 32, 0, Q), QMV_ROW01(F, 0, 64, 0, Q) }, \
+      { QMV_ROW01(F, 1, 8, 0, Q), QMV_ROW01(F, 1, 16, 0, Q), QMV_ROW01(F, 1, 32, 0, Q), QMV_ROW01(F, 1, 64, 0, Q) }, \
+      { QMV_NOROW, QMV_ROW2(F, 2, 16, Q), QMV_ROW2(F, 2, 32, Q), QMV_ROW2(F, 2, 64, Q) } }
+#define QMV_KC(F, L, C, Q) (const void *)&::QMV_NS::qmv_combine_kernel<F, L, C, Q>
+#define QMV_ROWC(F, L, Q) { QMV_KC(F, L, 1, Q), QMV_KC(F, L, 2, Q), QMV_KC(F, L, 4, Q) }
+#define QMV_TABLE_CB(F, Q) { QMV_ROWC(F, 8, Q), QMV_ROWC(F, 16, Q), QMV_ROWC(F, 32, Q), QMV_ROWC(F, 64, Q) }
+#define QMV_TABLE_GU(F, Q) \
+    { { QMV_ROW01(F, 0, 8, 1, Q), QMV_ROW01(F, 0, 16, 1, Q), QMV_ROW01(F, 0, 32, 1, Q), QMV_ROW01(F, 0, 64, 1, Q) }, \
+      { QMV_ROW01(F, 1, 8, 1, Q), QMV_ROW01(F, 1, 16, 1, Q), QMV_ROW01(F, 1, 32, 1, Q), QMV_ROW01(F, 1, 64, 1, Q) } }

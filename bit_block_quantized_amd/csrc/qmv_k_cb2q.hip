@@ -1,0 +1,14 @@
+// qmv_k_cb2q.hip -- kernel instantiations for one weight format fed bf16
+// activations that are quantized to int8 blocks while staged (one
+// translation unit per format so the build runs in parallel; built once per
+// workgroup size, see QMV_NS in qmv_device.hpp).
+#include "qmv_device.hpp"
+
+namespace QMV_NS {
+extern const void *const kTableQ_cb2[3][4][5];
+const void *const kTableQ_cb2[3][4][5] = QMV_TABLE(kCB2, true);
+extern const void *const kTableQGU_cb2[2][4][5];
+const void *const kTableQGU_cb2[2][4][5] = QMV_TABLE_GU(kCB2, true);
+extern const void *const kTableQCB_cb2[4][3];
+const void *const kTableQCB_cb2[4][3] = QMV_TABLE_CB(kCB2, true);
+}  // namespace QMV_NS

@@ -50,7 +50,19 @@
  *                    is x[k] * x_scales[k/32] (the q8_1 blocks of lucebox-hub
  *                    PR #21).  A 3-bit half-block uses the scale of the
  *                    32-block that contains it.
- * Supported pairs: (MXFP4, BF16), (CB2, Q8B32), (CB3, Q8B32).
+ *   QMV_A_BF16_Q8 x  bf16 [V][K], x_scales unused (pass NULL): the kernel
+ *                    quantizes each 32-block of x to the Q8B32 form while
+ *                    staging it and then computes exactly as for Q8B32 --
+ *                    the separate activation-quantize launch of the pages
+ *                    (geo-lucebox PR #31, "What is now hot": quantize_q8_1)
+ *                    folded into the matvec.  Per block, in fp32:
+ *                      d   = max_k |x[k]| / 127,
+ *                      d16 = d rounded to fp16 (nearest even), the scale;
+ *                      q[k] = clamp(rint(x[k] * (1 / d16)), -127, 127),
+ *                            ties to even; q = 0 where d16 is 0 or Inf.
+ *                    Activations must be finite.
+ * Supported pairs: (MXFP4, BF16), (CB2, Q8B32), (CB3, Q8B32), (CB2, BF16_Q8),
+ * (CB3, BF16_Q8).
  *
  * ------------------------------------------------------------- conventions
  * Ownership: every pointer is a device pointer owned by the caller.  The
@@ -85,7 +97,7 @@ extern "C" {
 #endif
 
 typedef enum { QMV_W_MXFP4 = 0, QMV_W_CB2 = 1, QMV_W_CB3 = 2 } qmv_wfmt_t;
-typedef enum { QMV_A_BF16 = 0, QMV_A_Q8B32 = 1 } qmv_afmt_t;
+typedef enum { QMV_A_BF16 = 0, QMV_A_Q8B32 = 1, QMV_A_BF16_Q8 = 2 } qmv_afmt_t;
 
 typedef enum {
     QMV_OK = 0,

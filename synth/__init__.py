@@ -67,9 +67,12 @@ class Workload:
     e8m0: tuple = (122, 132)
     ids: str = "distinct"     # distinct within a token; overlaps across tokens allowed
     desc: str = ""
+    x_bf16: bool = False      # 2-/3-bit weights fed bf16 activations (quantized in the kernel)
 
     @property
     def afmt(self) -> str:
+        if self.x_bf16 and self.wfmt != "mxfp4":
+            return "bf16q8"
         return afmt_of(self.wfmt)
 
     def scaled(self, **kw) -> "Workload":
@@ -121,8 +124,20 @@ COMBINE_WORKLOADS = {
 }
 
 
+# The 2-bit and 3-bit gathers fed bf16 activations, which the kernel quantizes
+# to int8 per 32 while staging them (no separate quantize launch).
+QUANT_WORKLOADS = {
+    "C3q": WORKLOADS["C3"].scaled(name="C3q", x_bf16=True, seed=10,
+                                  desc="DeepSeek-shaped 2-bit MoE gate/up gather, 4 of 256, "
+                                       "K=7168, N=2048, bf16 x quantized in the kernel"),
+    "C4q": WORKLOADS["C4"].scaled(name="C4q", x_bf16=True, seed=11,
+                                  desc="3-bit MoE down-proj gather, 4 of 256, K=2048, N=7168, "
+                                       "per-slot bf16 x quantized in the kernel"),
+}
+
+
 def workload(name: str) -> Workload:
-    for table in (WORKLOADS, GATE_UP_WORKLOADS, COMBINE_WORKLOADS):
+    for table in (WORKLOADS, GATE_UP_WORKLOADS, COMBINE_WORKLOADS, QUANT_WORKLOADS):
         if name in table:
             return table[name]
     raise KeyError(name)
@@ -186,7 +201,7 @@ def gen_ids(rng, M, top_k, E):
 
 def gen_activations(rng, afmt, V, K):
     g = rng.standard_normal(size=(V, K), dtype=np.float32)
-    if afmt == "bf16":
+    if afmt in ("bf16", "bf16q8"):
         return bf16_bits(g), None
     return q8_blocks(g)
 

@@ -27,7 +27,7 @@ def to_dev(inp, device="cuda"):
     d["codes"] = torch.from_numpy(np.ascontiguousarray(inp.codes)).to(device)
     d["scales"] = torch.from_numpy(np.ascontiguousarray(inp.scales)).to(device)
     d["ids"] = None if inp.ids is None else torch.from_numpy(np.ascontiguousarray(inp.ids)).to(device)
-    if inp.wl.afmt == "bf16":
+    if inp.wl.afmt in ("bf16", "bf16q8"):
         d["x"] = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).to(device).view(torch.bfloat16)
         d["xs"] = None
     else:
@@ -69,8 +69,13 @@ def oracle_call(inp, outs=None, nthreads=None):
     n = nthreads or threads()
     parts = np.array_split(sel, max(1, min(n, len(sel) // 64 + 1)))
 
+    afmt, x, xs = wl.afmt, inp.x, inp.xs
+    if afmt == "bf16q8":                 # the oracle's quantizer, then the int8 definition
+        x, xs = o.quantize_q8(np.asarray(x).reshape(-1, wl.K))
+        afmt = "q8"
+
     def run(p):
-        return o.gather(wl.wfmt, codes, scales, ids, wl.afmt, inp.x, inp.xs,
+        return o.gather(wl.wfmt, codes, scales, ids, afmt, x, xs,
                         x_per_slot=wl.x_per_slot, outs=p)
 
     with ThreadPoolExecutor(len(parts)) as ex:

@@ -81,7 +81,9 @@ def gather(L, wfmt=W_MXFP4, codes=FAKE, scales=FAKE, E=32, ids=FAKE, M=1, top_k=
     (dict(y=None), EINVAL), (dict(M=0), EINVAL), (dict(N=0), EINVAL), (dict(K=0), EINVAL),
     (dict(N=-5), EINVAL), (dict(M=5), EUNSUP), (dict(K=48), EUNSUP), (dict(K=16416), EUNSUP),
     (dict(afmt=A_Q8, xs=FAKE), EUNSUP), (dict(wfmt=W_CB2), EUNSUP), (dict(wfmt=7), EUNSUP),
-    (dict(afmt=3), EUNSUP), (dict(codes=FAKE + 8), EINVAL), (dict(x=FAKE + 2), EINVAL),
+    (dict(afmt=3), EUNSUP), (dict(afmt=2), EUNSUP), (dict(codes=FAKE + 8), EINVAL),
+    (dict(x=FAKE + 2), EINVAL), (dict(wfmt=W_CB2, afmt=2, x=FAKE + 8), EINVAL),
+    (dict(wfmt=W_CB3, afmt=2, x=FAKE, codes=FAKE + 2), EINVAL),
     (dict(y=FAKE + 2), EINVAL),
 ])
 def test_dense_validation(L, kw, want):
