@@ -170,19 +170,59 @@ def test_combine_bf16_quantized_in_kernel(wfmt):
     assert_parity(y_b, yr, A, f"combine {wfmt}")
 
 
+def _exact_sum_bf16_x(seed, V, K):
+    """bf16 x whose every 32-block has absmax exactly 127 * 2^k, k in {-1, 0}.
+
+    Then d = amax / 127 = 2^k exactly, fp16(d) = 2^k and 1/d is exact, so the
+    quantizer's only free decisions are the roundings of x / d (ties at .5
+    included).  With unit weight scales every block term 0.5 * 2^k * S_b is a
+    multiple of 2^-2 and every partial sum stays below 2^21, so the result is
+    exact in fp32 in any summation order: outputs of two calls agree bit for
+    bit exactly when their int8 blocks do, whatever launch shapes they take."""
+    rng = np.random.default_rng(seed)
+    nb = K // 32
+    k = rng.integers(-1, 1, (V, nb, 1)).astype(np.float32)
+    step = np.float32(2.0) ** k
+    blk = np.clip(rng.standard_normal((V, nb, 32)).astype(np.float32) * 40, -126, 126)
+    ties = rng.random((V, nb, 32)) < 0.25
+    blk = np.where(ties, np.round(blk) + 0.5, blk) * step
+    pos = rng.integers(0, 32, (V, nb))
+    sign = np.where(rng.random((V, nb)) < 0.5, -1.0, 1.0).astype(np.float32)
+    np.put_along_axis(blk, pos[..., None], (sign[..., None] * 127.0 * step), axis=2)
+    return synth.bf16_bits(blk.reshape(V, K))
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["C3", "C4"])
 def test_full_size_bf16_activations(name):
     """The DeepSeek-shaped 2-bit and 3-bit workloads at full size fed bf16
-    activations, every output checked."""
+    activations, every output checked.
+
+    Random x: against the oracle within the float tolerance (the bf16-input
+    and int8-input calls may take different launch shapes at this size, so
+    their float results may differ in rounding).  Exact-sum x with unit weight
+    scales: bit for bit against the same call on the oracle's int8 blocks and
+    against the oracle rounded to fp32, which pins every integer decision of
+    the in-kernel quantizer at the tuned full-size launch."""
+    from gpu_util import assert_exact
     inp = synth.make(name)
     wl = inp.wl
-    xb = _bf16_x(70, inp.x.shape[0], wl.K)
-    y_b, y_q, qx, d = _gather_pair(inp, xb)
-    _same_bits(y_b, y_q, name)
+    V = inp.x.shape[0]
+    xb = _bf16_x(70, V, wl.K)
+    y_b, _, qx, d = _gather_pair(inp, xb)
     inp.x, inp.xs = qx, d
     yr, A = oracle_call(inp)
     assert_parity(y_b, yr, A, name)
+
+    unit = np.full(inp.scales.shape[:-1] + (inp.scales.shape[-1] // 2,), 0x3C00, np.uint16)
+    inp.scales = unit.view(np.uint8)
+    xb = _exact_sum_bf16_x(71, V, wl.K)
+    y_b, y_q, qx, d = _gather_pair(inp, xb)
+    assert np.all(d.view(np.uint16) & 0x03FF == 0), "exact-sum x: scales must be powers of two"
+    _same_bits(y_b, y_q, name + " exact-sum")
+    inp.x, inp.xs = qx, d
+    yr, _ = oracle_call(inp)
+    assert_exact(y_b, yr, name + " exact-sum")
 
 
 @pytest.mark.parametrize("name", ["C3q", "C4q"])
