@@ -34,6 +34,12 @@ extern const void *const kTableQCB_cb2s[4][3];
 extern const void *const kTableQCB_cb3[4][3];
 }  // namespace qmv_w8
 
+// Dense MXFP4 x bf16 with 2 to 4 vectors on the matrix cores (qmv_k_mxfp4m.hip):
+// [waves 4, 8][K split 1, 2][unit steps in flight 4, 7].
+namespace qmv {
+extern const void *const kTableDense4[2][2][2];
+}
+
 namespace {
 
 using namespace qmv;
@@ -332,6 +338,58 @@ int kind_of(int wfmt, int K)
     return wfmt == QMV_W_MXFP4 ? kMXFP4 : wfmt == QMV_W_CB3 ? kCB3 : (K % 64 == 0 ? kCB2 : kCB2S);
 }
 
+// Dense MXFP4 x bf16, 2 <= M <= 4: one wave per quad of rows, 16 units of a
+// row per load instruction, the 4x4x4 bf16 MFMA for the multiplies.  Shape:
+// 8 waves and K split in two (two waves per quad) keep 16 waves on each CU
+// once a call has 2 workgroups per CU; small calls use 4-wave workgroups
+// without the split so that more CUs get work.
+struct Dense4Shape { int wi, ki, ci; };     // waves 4/8, K split 1/2, steps in flight 4/7
+
+Dense4Shape dense4_shape(int N, int K)
+{
+    const long long quads = (N + 3) / 4;
+    const int steps = (K / 32 + 15) / 16;
+    if (quads >= 4 * 256 && steps >= 8)        // >= one 4-quad workgroup per CU
+        return {1, 1, 1};
+    return {0, 0, steps >= 7 ? 1 : 0};
+}
+
+// LDS of one workgroup: activations (K/32 + 1 units of 256 B), the scale
+// rows of its row quads (+ up to 15 bytes of alignment, in 16-byte chunks),
+// the K-part combine area.
+size_t dense4_lds(int K, int qpw, int ksplit)
+{
+    const size_t rsb = (size_t)K / 32;
+    return 256 * (rsb + 1) + 16 * ((qpw * 4 * rsb + 30) / 16) + (ksplit == 2 ? 64 * (size_t)qpw : 0);
+}
+
+std::once_flag g_d4_once[2][2][2];
+hipError_t g_d4_err[2][2][2];
+
+qmv_status_t launch_dense4(const void *codes, const void *scales, const void *x, float *y, int M,
+                           int N, int K, hipStream_t stream)
+{
+    Args a = base_args(QMV_W_MXFP4, QMV_A_BF16, kMXFP4, codes, scales, 1, nullptr, M, 1, x, nullptr,
+                       0, y, N, K);
+    const Dense4Shape sh = dense4_shape(N, K);
+    const int waves = sh.wi ? 8 : 4, ksplit = sh.ki ? 2 : 1;
+    const int qpw = waves / ksplit;
+    const void *fn = kTableDense4[sh.wi][sh.ki][sh.ci];
+    std::call_once(g_d4_once[sh.wi][sh.ki][sh.ci], [&] {
+        g_d4_err[sh.wi][sh.ki][sh.ci] = hipFuncSetAttribute(
+            fn, hipFuncAttributeMaxDynamicSharedMemorySize, dense4_lds(kMaxK, 8, 2));
+    });
+    if (g_d4_err[sh.wi][sh.ki][sh.ci] != hipSuccess)
+        return QMV_EHIP;
+    const size_t lds = dense4_lds(K, qpw, ksplit);
+    const unsigned quads = (unsigned)((N + 3) / 4);
+    const dim3 grid((quads + qpw - 1) / qpw);
+    void *kargs[] = {&a};
+    if (hipLaunchKernel(fn, grid, dim3(64 * waves), kargs, lds, stream) != hipSuccess)
+        return QMV_EHIP;
+    return QMV_OK;
+}
+
 // codes2/scales2 non-null selects the gate/up mode: codes/scales are the gate
 // projection, codes2/scales2 the up projection, y = swiglu(gate x, up x).
 qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, const void *codes2,
@@ -342,6 +400,8 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
     const bool gather = ids != nullptr;
     const bool gate_up = codes2 != nullptr;
     const int kind = kind_of(wfmt, K);
+    if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M >= 2)
+        return launch_dense4(codes, scales, x, y, M, N, K, stream);
     const int units = K / kUnitWeights[kind];
     const int nv_needed = !gather ? M : (x_per_slot ? (M * top_k < 4 ? M * top_k : 4) : M);
     int variant, rt;

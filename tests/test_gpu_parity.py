@@ -185,13 +185,23 @@ def test_writes_nothing_past_y(name):
 
 
 @pytest.mark.parametrize("wfmt", FMTS)
-def test_dense_equals_single_expert_gather(wfmt):
-    g = _custom(wfmt, "gather", M=2, N=50, K=448, E=4, top_k=1, seed=8, ids=[[2], [2]])
-    d = _custom(wfmt, "dense", M=2, N=50, K=448, seed=8)
+@pytest.mark.parametrize("M", [1, 2])
+def test_dense_equals_single_expert_gather(wfmt, M):
+    """A gather whose every token picks expert e is the dense call on W[e]:
+    bit for bit where both run the same kernel family; MXFP4 x bf16 with
+    M >= 2 runs the dense call on the matrix cores (another summation order),
+    so there both are held to the oracle's tolerance on the same inputs."""
+    g = _custom(wfmt, "gather", M=M, N=50, K=448, E=4, top_k=1, seed=8, ids=[[2]] * M)
+    d = _custom(wfmt, "dense", M=M, N=50, K=448, seed=8)
     d.codes, d.scales, d.x, d.xs = g.codes[2], g.scales[2], g.x, g.xs
     yg = gpu_call(g).cpu().numpy()[:, 0, :]
     yd = gpu_call(d).cpu().numpy()
-    assert np.array_equal(yg.view(np.uint32), yd.view(np.uint32))
+    if wfmt == "mxfp4" and M >= 2:
+        yr, A = oracle_call(d)
+        assert_parity(yd, yr, A, "dense")
+        assert_parity(yg, yr, A, "gather")
+    else:
+        assert np.array_equal(yg.view(np.uint32), yd.view(np.uint32))
 
 
 def test_runs_on_callers_stream():
