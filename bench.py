@@ -27,8 +27,9 @@ oracle on a bounded sample of the same workload on all host cores, and
 other shapes measured the same way (not the headline), among them the fused
 gate/up + SwiGLU calls (qmv_gather_moe_swiglu) C2gu and C3gu and the down
 projections with the router-weighted combine (qmv_gather_moe_combine) C4c and
-C2c, and the 2-bit and 3-bit gathers fed bf16 activations that the kernel
-quantizes while staging them, C3q and C4q.
+C2c, the 2-bit and 3-bit gathers fed bf16 activations that the kernel
+quantizes while staging them, C3q and C4q, and the gpt-oss gather with MXFP4
+weights and int8 activations (fp16 scale per 32), C2i.
 """
 from __future__ import annotations
 
@@ -106,7 +107,7 @@ def other_bytes(wl):
 # Rotation plan: layer copies so that between two reads of the same weights
 # more than the 256 MB Infinity Cache of other weights is read.
 ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40, "C2gu": 4, "C3gu": 1,
-            "C4c": 2, "C2c": 32, "C3q": 2, "C4q": 2}
+            "C4c": 2, "C2c": 32, "C3q": 2, "C4q": 2, "C2i": 32}
 
 
 class Prepared:
@@ -386,7 +387,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c,C3q,C4q",
+    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c,C3q,C4q,C2i",
                     help="other shapes to measure besides the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")

@@ -17,7 +17,8 @@ Layouts (C-contiguous device tensors, see include/qmv.h):
     x       bfloat16 [M][K] / int8 [M][K]; per-slot: [M][top_k][K]
     x_scales float16 [...][K/32] for int8 activations
 bf16 activations with 2-bit or 3-bit weights (x_scales None) are quantized
-to int8 per 32 inside the kernel (QMV_A_BF16_Q8).
+to int8 per 32 inside the kernel (QMV_A_BF16_Q8); MXFP4 weights take bf16
+activations or int8 activations with their scales (QMV_A_Q8B32).
 """
 from __future__ import annotations
 
@@ -113,10 +114,12 @@ _SCALE_DT = (torch.uint8, torch.float16)
 
 def _afmt(w, x):
     """Activation format from the weight format and x's dtype: MXFP4 takes
-    bf16; 2-/3-bit weights take int8 (+ scales) or bf16 (quantized in-kernel)."""
+    bf16 or int8 (+ scales); 2-/3-bit weights take int8 (+ scales) or bf16
+    (quantized in-kernel)."""
+    is_bf16 = isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16
     if w == W_MXFP4:
-        return A_BF16, (torch.bfloat16,)
-    if isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16:
+        return (A_BF16, (torch.bfloat16,)) if is_bf16 else (A_Q8B32, (torch.int8,))
+    if is_bf16:
         return A_BF16_Q8, (torch.bfloat16,)
     return A_Q8B32, (torch.int8,)
 

@@ -18,7 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-KERNEL_SOURCES = ["qmv_k_mxfp4.hip", "qmv_k_cb2.hip", "qmv_k_cb2s.hip", "qmv_k_cb3.hip",
+KERNEL_SOURCES = ["qmv_k_mxfp4.hip", "qmv_k_mxfp4i.hip", "qmv_k_cb2.hip", "qmv_k_cb2s.hip", "qmv_k_cb3.hip",
                   "qmv_k_cb2q.hip", "qmv_k_cb2sq.hip", "qmv_k_cb3q.hip"]
 # (source, extra flags, object): the launcher, the probe, the dense multi-vector
 # MXFP4 matrix-core kernels (their workgroup size is a template argument), and

@@ -32,6 +32,9 @@ extern const void *const kTableQGU_cb3[2][4][5];
 extern const void *const kTableQCB_cb2[4][3];
 extern const void *const kTableQCB_cb2s[4][3];
 extern const void *const kTableQCB_cb3[4][3];
+extern const void *const kTable_mxfp4i[3][4][5];
+extern const void *const kTableGU_mxfp4i[2][4][5];
+extern const void *const kTableCB_mxfp4i[4][3];
 }  // namespace qmv_w8
 
 // Dense MXFP4 x bf16 with 2 to 4 vectors on the matrix cores (qmv_k_mxfp4m.hip):
@@ -89,6 +92,7 @@ const void *kernel_for(int wi, int kind, int variant, int li, int ci, bool gate_
         if (gate_up) {
             switch (kind) {
             case kMXFP4: return qmv_w8::kTableGU_mxfp4[variant][li][ci];
+            case kMXFP4I: return qmv_w8::kTableGU_mxfp4i[variant][li][ci];
             case kCB2: return qmv_w8::kTableGU_cb2[variant][li][ci];
             case kCB2S: return qmv_w8::kTableGU_cb2s[variant][li][ci];
             default: return qmv_w8::kTableGU_cb3[variant][li][ci];
@@ -96,6 +100,7 @@ const void *kernel_for(int wi, int kind, int variant, int li, int ci, bool gate_
         }
         switch (kind) {
         case kMXFP4: return qmv_w8::kTable_mxfp4[variant][li][ci];
+        case kMXFP4I: return qmv_w8::kTable_mxfp4i[variant][li][ci];
         case kCB2: return qmv_w8::kTable_cb2[variant][li][ci];
         case kCB2S: return qmv_w8::kTable_cb2s[variant][li][ci];
         default: return qmv_w8::kTable_cb3[variant][li][ci];
@@ -104,6 +109,7 @@ const void *kernel_for(int wi, int kind, int variant, int li, int ci, bool gate_
     if (gate_up) {
         switch (kind) {
         case kMXFP4: return kTableGU_mxfp4[variant][li][ci];
+        case kMXFP4I: return kTableGU_mxfp4i[variant][li][ci];
         case kCB2: return kTableGU_cb2[variant][li][ci];
         case kCB2S: return kTableGU_cb2s[variant][li][ci];
         default: return kTableGU_cb3[variant][li][ci];
@@ -111,6 +117,7 @@ const void *kernel_for(int wi, int kind, int variant, int li, int ci, bool gate_
     }
     switch (kind) {
     case kMXFP4: return kTable_mxfp4[variant][li][ci];
+    case kMXFP4I: return kTable_mxfp4i[variant][li][ci];
     case kCB2: return kTable_cb2[variant][li][ci];
     case kCB2S: return kTable_cb2s[variant][li][ci];
     default: return kTable_cb3[variant][li][ci];
@@ -136,6 +143,7 @@ const void *combine_kernel_for(int wi, int kind, int li, int ci, bool q8)
     if (wi == 1) {
         switch (kind) {
         case kMXFP4: return qmv_w8::kTableCB_mxfp4[li][ci];
+        case kMXFP4I: return qmv_w8::kTableCB_mxfp4i[li][ci];
         case kCB2: return qmv_w8::kTableCB_cb2[li][ci];
         case kCB2S: return qmv_w8::kTableCB_cb2s[li][ci];
         default: return qmv_w8::kTableCB_cb3[li][ci];
@@ -143,15 +151,16 @@ const void *combine_kernel_for(int wi, int kind, int li, int ci, bool q8)
     }
     switch (kind) {
     case kMXFP4: return kTableCB_mxfp4[li][ci];
+    case kMXFP4I: return kTableCB_mxfp4i[li][ci];
     case kCB2: return kTableCB_cb2[li][ci];
     case kCB2S: return kTableCB_cb2s[li][ci];
     default: return kTableCB_cb3[li][ci];
     }
 }
 
-constexpr int kUnitWeights[4] = {Fmt<kMXFP4>::W, Fmt<kCB2>::W, Fmt<kCB2S>::W, Fmt<kCB3>::W};
-constexpr int kUnitXB[4] = {Fmt<kMXFP4>::XB, Fmt<kCB2>::XB, Fmt<kCB2S>::XB, Fmt<kCB3>::XB};
-constexpr int kUnitAB[4] = {Fmt<kMXFP4>::AB, Fmt<kCB2>::AB, Fmt<kCB2S>::AB, Fmt<kCB3>::AB};
+constexpr int kUnitWeights[5] = {Fmt<kMXFP4>::W, Fmt<kCB2>::W, Fmt<kCB2S>::W, Fmt<kCB3>::W, Fmt<kMXFP4I>::W};
+constexpr int kUnitXB[5] = {Fmt<kMXFP4>::XB, Fmt<kCB2>::XB, Fmt<kCB2S>::XB, Fmt<kCB3>::XB, Fmt<kMXFP4I>::XB};
+constexpr int kUnitAB[5] = {Fmt<kMXFP4>::AB, Fmt<kCB2>::AB, Fmt<kCB2S>::AB, Fmt<kCB3>::AB, Fmt<kMXFP4I>::AB};
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -177,8 +186,8 @@ qmv_status_t validate(int wfmt, const void *codes, const void *scales, long long
         return QMV_EINVAL;
     if (wfmt < QMV_W_MXFP4 || wfmt > QMV_W_CB3 || afmt < QMV_A_BF16 || afmt > QMV_A_BF16_Q8)
         return QMV_EUNSUPPORTED;
-    // pairs: (MXFP4, BF16), (CB2 or CB3, Q8B32), (CB2 or CB3, BF16_Q8)
-    if ((wfmt == QMV_W_MXFP4) != (afmt == QMV_A_BF16))
+    // pairs: (MXFP4, BF16), (MXFP4, Q8B32), (CB2 or CB3, Q8B32), (CB2 or CB3, BF16_Q8)
+    if ((wfmt == QMV_W_MXFP4) ? afmt == QMV_A_BF16_Q8 : afmt == QMV_A_BF16)
         return QMV_EUNSUPPORTED;
     if (M > kMaxM || top_k > kMaxTopK || K % 32 != 0 || K > kMaxK)
         return QMV_EUNSUPPORTED;
@@ -294,10 +303,10 @@ bool tuned_shape(int kind, int variant, bool gate_up, bool q8, int K, int N, int
     return false;
 }
 
-std::once_flag g_attr_once[2][2][2][4][3][4][5];        // [q8][waves][gate_up][kind][variant][lpr][cpl]
-hipError_t g_attr_err[2][2][2][4][3][4][5];
-std::once_flag g_cattr_once[2][2][4][4][3];             // [q8][waves][kind][lpr][cpl]
-hipError_t g_cattr_err[2][2][4][4][3];
+std::once_flag g_attr_once[2][2][2][5][3][4][5];        // [q8][waves][gate_up][kind][variant][lpr][cpl]
+hipError_t g_attr_err[2][2][2][5][3][4][5];
+std::once_flag g_cattr_once[2][2][5][4][3];             // [q8][waves][kind][lpr][cpl]
+hipError_t g_cattr_err[2][2][5][4][3];
 
 // Arguments common to every kernel of a call (Args in qmv_device.hpp).
 Args base_args(int wfmt, int afmt, int kind, const void *codes, const void *scales, int E,
@@ -333,9 +342,11 @@ Args base_args(int wfmt, int afmt, int kind, const void *codes, const void *scal
     return a;
 }
 
-int kind_of(int wfmt, int K)
+int kind_of(int wfmt, int afmt, int K)
 {
-    return wfmt == QMV_W_MXFP4 ? kMXFP4 : wfmt == QMV_W_CB3 ? kCB3 : (K % 64 == 0 ? kCB2 : kCB2S);
+    if (wfmt == QMV_W_MXFP4)
+        return afmt == QMV_A_Q8B32 ? kMXFP4I : kMXFP4;
+    return wfmt == QMV_W_CB3 ? kCB3 : (K % 64 == 0 ? kCB2 : kCB2S);
 }
 
 // Dense MXFP4 x bf16, 2 <= M <= 4: one wave per quad of rows, 16 units of a
@@ -399,7 +410,7 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
 {
     const bool gather = ids != nullptr;
     const bool gate_up = codes2 != nullptr;
-    const int kind = kind_of(wfmt, K);
+    const int kind = kind_of(wfmt, afmt, K);
     if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M >= 2)
         return launch_dense4(codes, scales, x, y, M, N, K, stream);
     const int units = K / kUnitWeights[kind];
@@ -450,7 +461,7 @@ qmv_status_t launch_combine(int wfmt, int afmt, const void *codes, const void *s
                             const void *x, const void *xs, int x_per_slot, float *y, int N, int K,
                             hipStream_t stream)
 {
-    const int kind = kind_of(wfmt, K);
+    const int kind = kind_of(wfmt, afmt, K);
     Args a = base_args(wfmt, afmt, kind, codes, scales, E, ids, M, top_k, x, xs, x_per_slot, y, N, K);
     a.route_w = route_w;
     a.x_early = 1;

@@ -23,6 +23,7 @@
 //   CB2    64 weights: 16 B of 2-bit codes + 2 fp16 scales (int8 x, 64 B)
 //   CB2S   32 weights:  8 B of 2-bit codes + 1 fp16 scale  (int8 x, 32 B)
 //   CB3    32 weights: 12 B of 3-bit codes + 2 fp16 scales (int8 x, 32 B)
+//   MXFP4I 32 weights: 16 B of nibbles + 1 E8M0 byte      (int8 x as bf16, 64 B)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,7 +44,9 @@ namespace QMV_NS {
 constexpr int kWaves = QMV_WAVES;        // wave64s per workgroup
 constexpr int kThreads = 64 * kWaves;
 
-enum Kind : int { kMXFP4 = 0, kCB2 = 1, kCB2S = 2, kCB3 = 3 };
+// kMXFP4I: MXFP4 codes with int8 activations (fp16 scale per 32), staged as
+// exact bf16 so that the MXFP4 decode and bf16 dot serve both.
+enum Kind : int { kMXFP4 = 0, kCB2 = 1, kCB2S = 2, kCB3 = 3, kMXFP4I = 4 };
 
 // XB: LDS bytes of activations per unit and vector; AB: LDS bytes of
 // per-unit activation side data (scales, sums).
@@ -52,6 +55,7 @@ template <> struct Fmt<kMXFP4> { static constexpr int W = 32, XB = 64, AB = 0; }
 template <> struct Fmt<kCB2>   { static constexpr int W = 64, XB = 64, AB = 16; };
 template <> struct Fmt<kCB2S>  { static constexpr int W = 32, XB = 32, AB = 8; };
 template <> struct Fmt<kCB3>   { static constexpr int W = 32, XB = 32, AB = 4; };
+template <> struct Fmt<kMXFP4I> { static constexpr int W = 32, XB = 64, AB = 4; };
 
 struct Args {
     const uint8_t *codes;
@@ -304,8 +308,8 @@ __device__ __forceinline__ int item_vec(const Item &it, int m)
     return m == 0 ? it.vec[0] : m == 1 ? it.vec[1] : m == 2 ? it.vec[2] : it.vec[3];
 }
 
-// Staging items: MXFP4 -- one 16-byte chunk of bf16; CB2/CB3 -- one 32-byte
-// block of int8 (two chunks).
+// Staging items: MXFP4 -- one 16-byte chunk of bf16; CB2/CB3/MXFP4I -- one
+// 32-byte block of int8 (two chunks).
 template <int F> struct XItem { static constexpr int chunks = (F == kMXFP4) ? 1 : 2; };
 
 template <int F>
@@ -395,6 +399,16 @@ __device__ __forceinline__ int sum_i8x16(uint4 v)
     return __builtin_amdgcn_sdot4((int)v.w, 0x01010101, s, false);
 }
 
+// Bytes 2h and 2h+1 of w (int8) -> two bf16 in one dword, the first in the
+// low half.  |q| <= 128 has at most 8 significant bits, so the f32 value's
+// top 16 bits are the exact bf16.
+__device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w, int h)
+{
+    const float f0 = (float)(int8_t)(w >> (16 * h));
+    const float f1 = (float)(int8_t)(w >> (16 * h + 8));
+    return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+}
+
 // Write staging item i (already in registers) to its LDS place.
 //  MXFP4: chunk c of a vector = bf16 x[8c..8c+7], stored in natural order so
 //         byte b of code dword q pairs with bf16 dword b of chunk q.
@@ -403,6 +417,8 @@ __device__ __forceinline__ int sum_i8x16(uint4 v)
 //         is c - 1.5, so a block's integer sum is 2*dot(c, q) - 3*sum(q)).
 //  CB3:   block b -> its two half-blocks in the cb3_half order; side data
 //         0.5*xs per block.
+//  MXFP4I: block b -> unit b's four chunks of bf16 (int8 values are exact in
+//         bf16), laid out as MXFP4's; side data xs per block.
 template <int F, int NVMAX>
 __device__ __forceinline__ void xput_blk(const Args &a, const Item &it, uint8_t *lds, int i,
                                          uint4 lo, uint4 hi, uint32_t xsb)
@@ -413,6 +429,14 @@ __device__ __forceinline__ void xput_blk(const Args &a, const Item &it, uint8_t 
     uint8_t *dst = lds + __umul24(m, a.lds_vec_bytes);
     if constexpr (F == kMXFP4) {
         *(uint4 *)(dst + 16 * chunk_pos<4>(c >> 2, c & 3)) = lo;
+    } else if constexpr (F == kMXFP4I) {
+        const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *(uint4 *)(dst + 16 * chunk_pos<4>(c, q)) =
+                make_uint4(i8x2_bf16(d[2 * q], 0), i8x2_bf16(d[2 * q], 1),
+                           i8x2_bf16(d[2 * q + 1], 0), i8x2_bf16(d[2 * q + 1], 1));
+        ((float *)(dst + a.units * Fmt<F>::XB))[c] = (float)__builtin_bit_cast(_Float16, (uint16_t)xsb);
     } else {
         constexpr int CH = Fmt<F>::XB / 16;
         const int xbytes = a.units * Fmt<F>::XB;
@@ -566,6 +590,7 @@ template <> struct Unit<kMXFP4> { u32x4 c; uint32_t s; static constexpr int CB =
 template <> struct Unit<kCB2>   { u32x4 c; uint32_t s; static constexpr int CB = 16, SB = 4; };
 template <> struct Unit<kCB2S>  { u32x2 c; uint32_t s; static constexpr int CB = 8, SB = 2; };
 template <> struct Unit<kCB3>   { u32x3 c; uint32_t s; static constexpr int CB = 12, SB = 4; };
+template <> struct Unit<kMXFP4I> { u32x4 c; uint32_t s; static constexpr int CB = 16, SB = 1; };
 
 // ------------------------------------------------------------------ MAC per unit
 // Each mac_* adds the unit's contribution for RT rows and NV vectors.
@@ -640,6 +665,64 @@ __device__ __forceinline__ void mac_mxfp4(const Unit<kMXFP4> (&w)[RT], const uin
                 d1 = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * q + 3], __builtin_bit_cast(bf16x2, xd[3]), d1, false);
             }
             acc[r][v] = __builtin_fmaf(d0 + d1, sc, acc[r][v]);
+        }
+    }
+}
+
+// MXFP4 x int8 (kMXFP4I).  The activations sit in LDS as exact bf16 in the
+// MXFP4 layout, their fp16 block scale as an f32 per unit after them.  Every
+// product e2m1 * 2^(s-127) * q carries the block's factor 2^(s-127) and at
+// most 10 significant bits, and the 32 of a block sum to below 2^16 of its
+// least step, so the block sum the bf16 dot builds is exact in f32 in any
+// order -- the integer dot product of the weights' 2*e2m1 values with q,
+// scaled -- and the activation scale is applied once per block.  The same
+// decode as MXFP4 x bf16 (hardware fp4 conversion, v_dot2c) costs 1 VALU per
+// weight here, where decoding nibbles to signed int8 for v_dot4 would take
+// about 2 (there is no fp4 -> int8 conversion, and the sign needs its own
+// selects).
+template <int LPR, int RT, int NV>
+__device__ __forceinline__ void mac_mxfp4i(const Unit<kMXFP4I> (&w)[RT], const uint8_t *lds,
+                                           int vec_bytes, int xbytes, int u0, int cu, bool fast,
+                                           float (&acc)[RT][NV])
+{
+    uint4 xq[NV][4];
+    float xs[NV];
+    const int u = u0 + cu * LPR;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xq[v][q] = lds_read16(lds + v * vec_bytes + 16 * chunk_at<4, LPR>(u0, cu, q));
+        xs[v] = *(const float *)(lds + v * vec_bytes + xbytes + 4 * u);
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const uint32_t cw[4] = {w[r].c.x, w[r].c.y, w[r].c.z, w[r].c.w};
+        const float sc = fast ? __uint_as_float(w[r].s << 23) : 1.0f;
+        bf16x2 wv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            wv[4 * q + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], sc, 0);
+            wv[4 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], sc, 1);
+            wv[4 * q + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], sc, 2);
+            wv[4 * q + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[q], sc, 3);
+        }
+        const float ws = fast ? 1.0f : e8m0_f32(w[r].s);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t xd[4] = {xq[v][q].x, xq[v][q].y, xq[v][q].z, xq[v][q].w};
+                d0 = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * q + 0], __builtin_bit_cast(bf16x2, xd[0]), d0, false);
+                d1 = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * q + 1], __builtin_bit_cast(bf16x2, xd[1]), d1, false);
+                d0 = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * q + 2], __builtin_bit_cast(bf16x2, xd[2]), d0, false);
+                d1 = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * q + 3], __builtin_bit_cast(bf16x2, xd[3]), d1, false);
+            }
+            // slow path: the activation scale first, the power of two last, so
+            // a tiny weight scale does not underflow a product of two scales
+            acc[r][v] = fast ? __builtin_fmaf(d0 + d1, xs[v], acc[r][v])
+                             : __builtin_fmaf((d0 + d1) * xs[v], ws, acc[r][v]);
         }
     }
 }
@@ -803,7 +886,7 @@ constexpr int kStream = 2;
 template <int F>
 __device__ __forceinline__ uint32_t load_scale(__amdgpu_buffer_rsrc_t rs, uint32_t os)
 {
-    if constexpr (F == kMXFP4) return __builtin_amdgcn_raw_buffer_load_b8(rs, os, 0, 0);
+    if constexpr (F == kMXFP4 || F == kMXFP4I) return __builtin_amdgcn_raw_buffer_load_b8(rs, os, 0, 0);
     else if constexpr (F == kCB2S) return __builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0);
     else return __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
 }
@@ -811,7 +894,7 @@ __device__ __forceinline__ uint32_t load_scale(__amdgpu_buffer_rsrc_t rs, uint32
 template <int F>
 __device__ __forceinline__ void load_codes(Unit<F> &w, __amdgpu_buffer_rsrc_t rc, uint32_t oc)
 {
-    if constexpr (F == kMXFP4 || F == kCB2) w.c = __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, kStream);
+    if constexpr (F == kMXFP4 || F == kCB2 || F == kMXFP4I) w.c = __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, kStream);
     else if constexpr (F == kCB2S) w.c = __builtin_amdgcn_raw_buffer_load_b64(rc, oc, 0, kStream);
     else w.c = __builtin_amdgcn_raw_buffer_load_b96(rc, oc, 0, kStream);
 }
@@ -861,7 +944,7 @@ __device__ __forceinline__ void mac_seg(Unit<F> (&w)[CPL][RT], const Args &a, co
     constexpr int LEAD = Lead<CPL>::v;
     const int xbytes = U * Fmt<F>::XB;
     bool fast = true;              // MXFP4: every scale byte of the segment in [2, 252]
-    if constexpr (F == kMXFP4) {
+    if constexpr (F == kMXFP4 || F == kMXFP4I) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
 #pragma unroll
@@ -873,6 +956,7 @@ __device__ __forceinline__ void mac_seg(Unit<F> (&w)[CPL][RT], const Args &a, co
         if (c + LEAD < CPL) load_step<F, LPR, CPL, RT>(w, rc, oc, seg_unit, u0 - seg_unit, U, c + LEAD);
         if (u0 + c * LPR < U) {
             if constexpr (F == kMXFP4) mac_mxfp4<LPR, RT, NV>(w[c], lds, a.lds_vec_bytes, u0, c, fast, acc);
+            else if constexpr (F == kMXFP4I) mac_mxfp4i<LPR, RT, NV>(w[c], lds, a.lds_vec_bytes, xbytes, u0, c, fast, acc);
             else if constexpr (F == kCB3) mac_cb3<LPR, RT, NV>(w[c], lds, a.lds_vec_bytes, xbytes, u0, c, acc);
             else mac_cb2<F, LPR, RT, NV>(w[c], lds, a.lds_vec_bytes, xbytes, u0, c, acc);
         }
@@ -1049,7 +1133,7 @@ __device__ __forceinline__ void mac_seg_diag(Unit<F> (&w)[CPL][RT], const Args &
     constexpr int LEAD = Lead<CPL>::v;
     const int xbytes = U * Fmt<F>::XB;
     bool fast = true;
-    if constexpr (F == kMXFP4) {
+    if constexpr (F == kMXFP4 || F == kMXFP4I) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
 #pragma unroll
@@ -1067,6 +1151,7 @@ __device__ __forceinline__ void mac_seg_diag(Unit<F> (&w)[CPL][RT], const Args &
                 float(&a1)[1][1] = *reinterpret_cast<float(*)[1][1]>(&acc[r]);
                 const uint8_t *l = lds + vo[r];
                 if constexpr (F == kMXFP4) mac_mxfp4<LPR, 1, 1>(w1, l, 0, u0, c, fast, a1);
+                else if constexpr (F == kMXFP4I) mac_mxfp4i<LPR, 1, 1>(w1, l, 0, xbytes, u0, c, fast, a1);
                 else if constexpr (F == kCB3) mac_cb3<LPR, 1, 1>(w1, l, 0, xbytes, u0, c, a1);
                 else mac_cb2<F, LPR, 1, 1>(w1, l, 0, xbytes, u0, c, a1);
             }
@@ -1177,6 +1262,9 @@ extern const void *const kTableCB_mxfp4[4][3];
 extern const void *const kTableCB_cb2[4][3];
 extern const void *const kTableCB_cb2s[4][3];
 extern const void *const kTableCB_cb3[4][3];
+extern const void *const kTable_mxfp4i[3][4][5];
+extern const void *const kTableGU_mxfp4i[2][4][5];
+extern const void *const kTableCB_mxfp4i[4][3];
 // The same for bf16 activations quantized in staging (2-bit and 3-bit only).
 extern const void *const kTableQ_cb2[3][4][5];
 extern const void *const kTableQ_cb2s[3][4][5];

@@ -1,0 +1,13 @@
+// qmv_k_mxfp4i.hip -- kernel instantiations for MXFP4 weights with int8
+// activations (one translation unit per format so the build runs in
+// parallel; built once per workgroup size, see QMV_NS in qmv_device.hpp).
+#include "qmv_device.hpp"
+
+namespace QMV_NS {
+extern const void *const kTable_mxfp4i[3][4][5];
+const void *const kTable_mxfp4i[3][4][5] = QMV_TABLE(kMXFP4I, false);
+extern const void *const kTableGU_mxfp4i[2][4][5];
+const void *const kTableGU_mxfp4i[2][4][5] = QMV_TABLE_GU(kMXFP4I, false);
+extern const void *const kTableCB_mxfp4i[4][3];
+const void *const kTableCB_mxfp4i[4][3] = QMV_TABLE_CB(kMXFP4I, false);
+}  // namespace QMV_NS

@@ -61,8 +61,12 @@
  *                      q[k] = clamp(rint(x[k] * (1 / d16)), -127, 127),
  *                            ties to even; q = 0 where d16 is 0 or Inf.
  *                    Activations must be finite.
- * Supported pairs: (MXFP4, BF16), (CB2, Q8B32), (CB3, Q8B32), (CB2, BF16_Q8),
- * (CB3, BF16_Q8).
+ * Supported pairs: (MXFP4, BF16), (MXFP4, Q8B32), (CB2, Q8B32), (CB3, Q8B32),
+ * (CB2, BF16_Q8), (CB3, BF16_Q8).  With (MXFP4, Q8B32) every 32-weight block
+ * shares one E8M0 weight scale and one activation scale (both are per 32 of
+ * k), and the block's sum of e2m1 x int8 products is formed exactly (it is
+ * the integer dot product of the 2*e2m1 values with q, times the weight
+ * scale / 2) before the activation scale multiplies it.
  *
  * ------------------------------------------------------------- conventions
  * Ownership: every pointer is a device pointer owned by the caller.  The

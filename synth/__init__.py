@@ -68,11 +68,14 @@ class Workload:
     ids: str = "distinct"     # distinct within a token; overlaps across tokens allowed
     desc: str = ""
     x_bf16: bool = False      # 2-/3-bit weights fed bf16 activations (quantized in the kernel)
+    x_q8: bool = False        # MXFP4 weights fed int8 activations with a scale per 32
 
     @property
     def afmt(self) -> str:
         if self.x_bf16 and self.wfmt != "mxfp4":
             return "bf16q8"
+        if self.x_q8 and self.wfmt == "mxfp4":
+            return "q8"
         return afmt_of(self.wfmt)
 
     def scaled(self, **kw) -> "Workload":
@@ -125,7 +128,8 @@ COMBINE_WORKLOADS = {
 
 
 # The 2-bit and 3-bit gathers fed bf16 activations, which the kernel quantizes
-# to int8 per 32 while staging them (no separate quantize launch).
+# to int8 per 32 while staging them (no separate quantize launch); the MXFP4
+# gather fed int8 activations.
 QUANT_WORKLOADS = {
     "C3q": WORKLOADS["C3"].scaled(name="C3q", x_bf16=True, seed=10,
                                   desc="DeepSeek-shaped 2-bit MoE gate/up gather, 4 of 256, "
@@ -133,6 +137,10 @@ QUANT_WORKLOADS = {
     "C4q": WORKLOADS["C4"].scaled(name="C4q", x_bf16=True, seed=11,
                                   desc="3-bit MoE down-proj gather, 4 of 256, K=2048, N=7168, "
                                        "per-slot bf16 x quantized in the kernel"),
+    # MXFP4 weights with int8 activations (fp16 scale per 32)
+    "C2i": WORKLOADS["C2"].scaled(name="C2i", x_q8=True, seed=12,
+                                  desc="gpt-oss-20b MoE decode gather, 4 of 32, K=N=2880, MXFP4 "
+                                       "weights x int8 activations with an fp16 scale per 32"),
 }
 
 

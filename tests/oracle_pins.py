@@ -141,9 +141,9 @@ def _random_x(rng, fmt, V, K, small_ints=False, unit_xs=False):
     return q, xs.view(np.uint16)
 
 
-def _dense_one_expert(o, fmt, codes, scales, x, xs):
+def _dense_one_expert(o, fmt, codes, scales, x, xs, afmt=None):
     ids = np.zeros((x.shape[0], 1), np.int32)
-    y, A = o.gather(fmt, codes[None], scales[None], ids, _afmt(fmt), x, xs)
+    y, A = o.gather(fmt, codes[None], scales[None], ids, afmt or _afmt(fmt), x, xs)
     return y[:, 0, :], A[:, 0, :]
 
 
@@ -343,6 +343,16 @@ def check_unit_scale_exact(o):
     vals = np.array(ref_code_values("mxfp4"))[ref_codes("mxfp4", codes, K)]
     want = vals @ ref_bf16(x[0])
     assert np.array_equal(y[0], want), "mxfp4 unit scale"
+    # MXFP4 weights with int8 activations at unit scales (E8M0 127, fp16 1.0):
+    # twice the result is the int64 matmul of the doubled e2m1 values (all
+    # integers) with q, int8 -128 included
+    codes, scales = _random_rows(rng, "mxfp4", 32, K, unit_scales=True)
+    q, xs = _random_x(rng, "cb2", 1, K, unit_xs=True)
+    y, A = _dense_one_expert(o, "mxfp4", codes, scales, q, xs, afmt="q8")
+    v2 = (2 * np.array(ref_code_values("mxfp4"))).astype(np.int64)[ref_codes("mxfp4", codes, K)]
+    want = v2 @ q[0].astype(np.int64)
+    assert np.array_equal(y[0] * 2, want.astype(np.float64)), "mxfp4 x int8 unit scale"
+    assert np.array_equal(A[0] * 2, (np.abs(v2) @ np.abs(q[0].astype(np.int64))).astype(np.float64))
 
 
 # ---------------------------------------------------------------- P8 gather semantics

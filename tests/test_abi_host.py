@@ -80,7 +80,8 @@ def gather(L, wfmt=W_MXFP4, codes=FAKE, scales=FAKE, E=32, ids=FAKE, M=1, top_k=
     (dict(codes=None), EINVAL), (dict(scales=None), EINVAL), (dict(x=None), EINVAL),
     (dict(y=None), EINVAL), (dict(M=0), EINVAL), (dict(N=0), EINVAL), (dict(K=0), EINVAL),
     (dict(N=-5), EINVAL), (dict(M=5), EUNSUP), (dict(K=48), EUNSUP), (dict(K=16416), EUNSUP),
-    (dict(afmt=A_Q8, xs=FAKE), EUNSUP), (dict(wfmt=W_CB2), EUNSUP), (dict(wfmt=7), EUNSUP),
+    (dict(afmt=A_Q8, xs=None), EINVAL), (dict(afmt=A_Q8, xs=FAKE + 2), EINVAL),
+    (dict(wfmt=W_CB2), EUNSUP), (dict(wfmt=7), EUNSUP),
     (dict(afmt=3), EUNSUP), (dict(afmt=2), EUNSUP), (dict(codes=FAKE + 8), EINVAL),
     (dict(x=FAKE + 2), EINVAL), (dict(wfmt=W_CB2, afmt=2, x=FAKE + 8), EINVAL),
     (dict(wfmt=W_CB3, afmt=2, x=FAKE, codes=FAKE + 2), EINVAL),
@@ -158,7 +159,7 @@ def combine(L, wfmt=W_CB3, codes=FAKE, scales=FAKE, E=256, ids=FAKE, rw=FAKE, M=
     (dict(codes=None), EINVAL), (dict(y=FAKE + 1), EINVAL), (dict(xs=None), EINVAL),
     (dict(M=5), EUNSUP), (dict(top_k=17), EUNSUP), (dict(top_k=0), EINVAL),
     (dict(K=2048 + 16), EUNSUP), (dict(afmt=A_BF16, xs=None), EUNSUP),
-    (dict(wfmt=W_MXFP4), EUNSUP), (dict(E=0), EINVAL),
+    (dict(wfmt=W_MXFP4, afmt=2, xs=None), EUNSUP), (dict(E=0), EINVAL),
 ])
 def test_combine_validation(L, kw, want):
     assert combine(L, **kw) == want
