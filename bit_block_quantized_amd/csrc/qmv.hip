@@ -19,28 +19,28 @@ extern const void *const kTableGU_mxfp4[2][4][5];
 extern const void *const kTableGU_cb2[2][4][5];
 extern const void *const kTableGU_cb2s[2][4][5];
 extern const void *const kTableGU_cb3[2][4][5];
-extern const void *const kTableCB_mxfp4[4][3];
-extern const void *const kTableCB_cb2[4][3];
-extern const void *const kTableCB_cb2s[4][3];
-extern const void *const kTableCB_cb3[4][3];
+extern const void *const kTableCB_mxfp4[4][4];
+extern const void *const kTableCB_cb2[4][4];
+extern const void *const kTableCB_cb2s[4][4];
+extern const void *const kTableCB_cb3[4][4];
 extern const void *const kTableQ_cb2[3][4][5];
 extern const void *const kTableQ_cb2s[3][4][5];
 extern const void *const kTableQ_cb3[3][4][5];
 extern const void *const kTableQGU_cb2[2][4][5];
 extern const void *const kTableQGU_cb2s[2][4][5];
 extern const void *const kTableQGU_cb3[2][4][5];
-extern const void *const kTableQCB_cb2[4][3];
-extern const void *const kTableQCB_cb2s[4][3];
-extern const void *const kTableQCB_cb3[4][3];
+extern const void *const kTableQCB_cb2[4][4];
+extern const void *const kTableQCB_cb2s[4][4];
+extern const void *const kTableQCB_cb3[4][4];
 extern const void *const kTable_mxfp4i[3][4][5];
 extern const void *const kTableGU_mxfp4i[2][4][5];
-extern const void *const kTableCB_mxfp4i[4][3];
+extern const void *const kTableCB_mxfp4i[4][4];
 }  // namespace qmv_w8
 
 // Dense MXFP4 x bf16 with 2 to 4 vectors on the matrix cores (qmv_k_mxfp4m.hip):
-// [waves 4, 8][K split 1, 2][unit steps in flight 4, 7].
+// [4 waves, 8 waves] per workgroup.
 namespace qmv {
-extern const void *const kTableDense4[2][2][2];
+extern const void *const kTableDense4[2];
 }
 
 namespace {
@@ -214,18 +214,18 @@ qmv_status_t validate(int wfmt, const void *codes, const void *scales, long long
 // in [8, 14] x 256 (else the nearest), then the larger CPL, then more waves.
 struct Shape { int li, ci, lpr, cpl; };
 
-// Variant 3 is the combine kernel: CPL menu {1, 2, 4}, every LPR.
+// Variant 3 is the combine kernel: CPL menu {1, 2, 3, 4}, every LPR.
 Shape pick_shape(int variant, int units, long long rows_total, int rt)
 {
-    const bool small_cpl = variant >= 2;
+    const int *cmenu = variant == 3 ? kMenuCplC : variant == 2 ? kMenuCpl2 : kMenuCpl01;
     const bool no_lpr8 = variant == 2;
-    const int ncpl = small_cpl ? 3 : 5;
+    const int ncpl = variant == 3 ? 4 : variant == 2 ? 3 : 5;
     double best_eff = 0.0;
     for (int li = 0; li < 4; ++li)
         for (int ci = 0; ci < ncpl; ++ci) {
             const int lpr = kMenuLpr[li];
             if (no_lpr8 && lpr == 8) continue;
-            const int cpl = small_cpl ? kMenuCpl2[ci] : kMenuCpl01[ci];
+            const int cpl = cmenu[ci];
             const long long seg = (long long)lpr * cpl;
             const double eff = (double)units / (double)(((units + seg - 1) / seg) * seg);
             if (eff > best_eff) best_eff = eff;
@@ -237,7 +237,7 @@ Shape pick_shape(int variant, int units, long long rows_total, int rt)
         for (int ci = 0; ci < ncpl; ++ci) {
             const int lpr = kMenuLpr[li];
             if (no_lpr8 && lpr == 8) continue;
-            const int cpl = small_cpl ? kMenuCpl2[ci] : kMenuCpl01[ci];
+            const int cpl = cmenu[ci];
             const long long seg = (long long)lpr * cpl;
             const double eff = (double)units / (double)(((units + seg - 1) / seg) * seg);
             if (eff < 0.85 * best_eff) continue;
@@ -276,7 +276,8 @@ constexpr Tuned kTuned[] = {
     {kMXFP4, 1, 0, 7168, 2048, 16, 4, 8, 7},     // 4 tokens x top-4 of 256
     {kMXFP4, 2, 0, 7168, 7168, 1, 8, 64, 4},     // dense, 4 tokens
     {kCB3,   3, 0, 2048, 7168, 4, 8, 32, 1},     // 3-bit down + router-weighted combine
-    {kMXFP4, 3, 0, 2880, 2880, 4, 8, 32, 2},     // gpt-oss down + router-weighted combine
+    {kMXFP4, 3, 0, 2880, 2880, 4, 8, 32, 3},     // gpt-oss down + router-weighted combine
+    {kMXFP4I, 0, 0, 2880, 2880, 4, 4, 32, 3},    // gpt-oss expert projection, int8 x
     // bf16 activations quantized in staging: larger workgroups quantize the
     // activation vector fewer times over (C3 7.10 -> 6.48 us, C4 10.04 -> 9.17 us)
     {kCB2,   0, 0, 7168, 2048, 4, 8, 32, 4, 1},  // 2-bit gate/up, bf16 x
@@ -291,11 +292,12 @@ bool tuned_shape(int kind, int variant, bool gate_up, bool q8, int K, int N, int
             t.N != N || t.pairs != pairs || t.q8 != (q8 ? 1 : 0))
             continue;
         wi = t.waves == 8 ? 1 : 0;
-        const int ncpl = variant >= 2 ? 3 : 5;
+        const int *cmenu = variant == 3 ? kMenuCplC : variant == 2 ? kMenuCpl2 : kMenuCpl01;
+        const int ncpl = variant == 3 ? 4 : variant == 2 ? 3 : 5;
         for (int li = 0; li < 4; ++li)
             for (int ci = 0; ci < ncpl; ++ci)
                 if (kMenuLpr[li] == t.lpr &&
-                    (variant >= 2 ? kMenuCpl2[ci] : kMenuCpl01[ci]) == t.cpl) {
+                    cmenu[ci] == t.cpl) {
                     sh = {li, ci, t.lpr, t.cpl};
                     return true;
                 }
@@ -305,8 +307,8 @@ bool tuned_shape(int kind, int variant, bool gate_up, bool q8, int K, int N, int
 
 std::once_flag g_attr_once[2][2][2][5][3][4][5];        // [q8][waves][gate_up][kind][variant][lpr][cpl]
 hipError_t g_attr_err[2][2][2][5][3][4][5];
-std::once_flag g_cattr_once[2][2][5][4][3];             // [q8][waves][kind][lpr][cpl]
-hipError_t g_cattr_err[2][2][5][4][3];
+std::once_flag g_cattr_once[2][2][5][4][4];             // [q8][waves][kind][lpr][cpl]
+hipError_t g_cattr_err[2][2][5][4][4];
 
 // Arguments common to every kernel of a call (Args in qmv_device.hpp).
 Args base_args(int wfmt, int afmt, int kind, const void *codes, const void *scales, int E,
@@ -350,53 +352,48 @@ int kind_of(int wfmt, int afmt, int K)
 }
 
 // Dense MXFP4 x bf16, 2 <= M <= 4: one wave per quad of rows, 16 units of a
-// row per load instruction, the 4x4x4 bf16 MFMA for the multiplies.  Shape:
-// 8 waves and K split in two (two waves per quad) keep 16 waves on each CU
-// once a call has 2 workgroups per CU; small calls use 4-wave workgroups
-// without the split so that more CUs get work.
-struct Dense4Shape { int wi, ki, ci; };     // waves 4/8, K split 1/2, steps in flight 4/7
-
-Dense4Shape dense4_shape(int N, int K)
+// row per load instruction, the 4x4x4 bf16 MFMA for the multiplies, 4 unit
+// steps in flight.  Measured on the 4-vector 7168 x 7168 call (MI355X,
+// weights rotated past the Infinity Cache): 8-wave workgroups 8.6 us, 4-wave
+// 10.7 us -- every workgroup stages all of x, so fewer, larger workgroups
+// stage it fewer times -- and 7 steps in flight or K split over two waves
+// per quad were slower still.  Calls with fewer than 1024 row quads (128
+// 8-wave workgroups) use 4-wave workgroups so that more CUs get work.
+int dense4_waves(int N)
 {
-    const long long quads = (N + 3) / 4;
-    const int steps = (K / 32 + 15) / 16;
-    if (quads >= 4 * 256 && steps >= 8)        // >= one 4-quad workgroup per CU
-        return {1, 1, 1};
-    return {0, 0, steps >= 7 ? 1 : 0};
+    return (N + 3) / 4 >= 1024 ? 8 : 4;
 }
 
-// LDS of one workgroup: activations (K/32 + 1 units of 256 B), the scale
-// rows of its row quads (+ up to 15 bytes of alignment, in 16-byte chunks),
-// the K-part combine area.
-size_t dense4_lds(int K, int qpw, int ksplit)
+// LDS of one workgroup: activations (K/32 + 1 units of 256 B), then the
+// scale rows of its row quads (+ up to 15 bytes of alignment, in 16-byte
+// chunks).
+size_t dense4_lds(int K, int waves)
 {
     const size_t rsb = (size_t)K / 32;
-    return 256 * (rsb + 1) + 16 * ((qpw * 4 * rsb + 30) / 16) + (ksplit == 2 ? 64 * (size_t)qpw : 0);
+    return 256 * (rsb + 1) + 16 * ((waves * 4 * rsb + 30) / 16);
 }
 
-std::once_flag g_d4_once[2][2][2];
-hipError_t g_d4_err[2][2][2];
+std::once_flag g_d4_once[2];
+hipError_t g_d4_err[2];
 
 qmv_status_t launch_dense4(const void *codes, const void *scales, const void *x, float *y, int M,
                            int N, int K, hipStream_t stream)
 {
     Args a = base_args(QMV_W_MXFP4, QMV_A_BF16, kMXFP4, codes, scales, 1, nullptr, M, 1, x, nullptr,
                        0, y, N, K);
-    const Dense4Shape sh = dense4_shape(N, K);
-    const int waves = sh.wi ? 8 : 4, ksplit = sh.ki ? 2 : 1;
-    const int qpw = waves / ksplit;
-    const void *fn = kTableDense4[sh.wi][sh.ki][sh.ci];
-    std::call_once(g_d4_once[sh.wi][sh.ki][sh.ci], [&] {
-        g_d4_err[sh.wi][sh.ki][sh.ci] = hipFuncSetAttribute(
-            fn, hipFuncAttributeMaxDynamicSharedMemorySize, dense4_lds(kMaxK, 8, 2));
+    const int waves = dense4_waves(N);
+    const int wi = waves == 8 ? 1 : 0;
+    const void *fn = kTableDense4[wi];
+    std::call_once(g_d4_once[wi], [&] {
+        g_d4_err[wi] = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           dense4_lds(kMaxK, waves));
     });
-    if (g_d4_err[sh.wi][sh.ki][sh.ci] != hipSuccess)
+    if (g_d4_err[wi] != hipSuccess)
         return QMV_EHIP;
-    const size_t lds = dense4_lds(K, qpw, ksplit);
     const unsigned quads = (unsigned)((N + 3) / 4);
-    const dim3 grid((quads + qpw - 1) / qpw);
+    const dim3 grid((quads + waves - 1) / waves);
     void *kargs[] = {&a};
-    if (hipLaunchKernel(fn, grid, dim3(64 * waves), kargs, lds, stream) != hipSuccess)
+    if (hipLaunchKernel(fn, grid, dim3(64 * waves), kargs, dense4_lds(K, waves), stream) != hipSuccess)
         return QMV_EHIP;
     return QMV_OK;
 }

@@ -1246,6 +1246,7 @@ __global__ __launch_bounds__(kThreads) void qmv_combine_kernel(const Args a)
 constexpr int kMenuLpr[4] = {8, 16, 32, 64};
 constexpr int kMenuCpl01[5] = {1, 2, 3, 4, 7};
 constexpr int kMenuCpl2[3] = {1, 2, 4};
+constexpr int kMenuCplC[4] = {1, 2, 3, 4};     // combine kernel
 
 // Kernel tables, one per format kind (qmv_k_*.hip): [variant][lpr][cpl].
 extern const void *const kTable_mxfp4[3][4][5];
@@ -1257,14 +1258,14 @@ extern const void *const kTableGU_mxfp4[2][4][5];
 extern const void *const kTableGU_cb2[2][4][5];
 extern const void *const kTableGU_cb2s[2][4][5];
 extern const void *const kTableGU_cb3[2][4][5];
-// Combine kernels: [lpr][cpl in {1, 2, 4}].
-extern const void *const kTableCB_mxfp4[4][3];
-extern const void *const kTableCB_cb2[4][3];
-extern const void *const kTableCB_cb2s[4][3];
-extern const void *const kTableCB_cb3[4][3];
+// Combine kernels: [lpr][cpl in {1, 2, 3, 4}].
+extern const void *const kTableCB_mxfp4[4][4];
+extern const void *const kTableCB_cb2[4][4];
+extern const void *const kTableCB_cb2s[4][4];
+extern const void *const kTableCB_cb3[4][4];
 extern const void *const kTable_mxfp4i[3][4][5];
 extern const void *const kTableGU_mxfp4i[2][4][5];
-extern const void *const kTableCB_mxfp4i[4][3];
+extern const void *const kTableCB_mxfp4i[4][4];
 // The same for bf16 activations quantized in staging (2-bit and 3-bit only).
 extern const void *const kTableQ_cb2[3][4][5];
 extern const void *const kTableQ_cb2s[3][4][5];
@@ -1272,9 +1273,9 @@ extern const void *const kTableQ_cb3[3][4][5];
 extern const void *const kTableQGU_cb2[2][4][5];
 extern const void *const kTableQGU_cb2s[2][4][5];
 extern const void *const kTableQGU_cb3[2][4][5];
-extern const void *const kTableQCB_cb2[4][3];
-extern const void *const kTableQCB_cb2s[4][3];
-extern const void *const kTableQCB_cb3[4][3];
+extern const void *const kTableQCB_cb2[4][4];
+extern const void *const kTableQCB_cb2s[4][4];
+extern const void *const kTableQCB_cb3[4][4];
 
 }  // namespace QMV_NS
 
@@ -1293,7 +1294,7 @@ extern const void *const kTableQCB_cb3[4][3];
       { QMV_ROW01(F, 1, 8, 0, Q), QMV_ROW01(F, 1, 16, 0, Q), QMV_ROW01(F, 1, 32, 0, Q), QMV_ROW01(F, 1, 64, 0, Q) }, \
       { QMV_NOROW, QMV_ROW2(F, 2, 16, Q), QMV_ROW2(F, 2, 32, Q), QMV_ROW2(F, 2, 64, Q) } }
 #define QMV_KC(F, L, C, Q) (const void *)&::QMV_NS::qmv_combine_kernel<F, L, C, Q>
-#define QMV_ROWC(F, L, Q) { QMV_KC(F, L, 1, Q), QMV_KC(F, L, 2, Q), QMV_KC(F, L, 4, Q) }
+#define QMV_ROWC(F, L, Q) { QMV_KC(F, L, 1, Q), QMV_KC(F, L, 2, Q), QMV_KC(F, L, 3, Q), QMV_KC(F, L, 4, Q) }
 #define QMV_TABLE_CB(F, Q) { QMV_ROWC(F, 8, Q), QMV_ROWC(F, 16, Q), QMV_ROWC(F, 32, Q), QMV_ROWC(F, 64, Q) }
 #define QMV_TABLE_GU(F, Q) \
     { { QMV_ROW01(F, 0, 8, 1, Q), QMV_ROW01(F, 0, 16, 1, Q), QMV_ROW01(F, 0, 32, 1, Q), QMV_ROW01(F, 0, 64, 1, Q) }, \

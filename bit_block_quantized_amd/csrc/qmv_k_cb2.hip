@@ -8,6 +8,6 @@ extern const void *const kTable_cb2[3][4][5];
 const void *const kTable_cb2[3][4][5] = QMV_TABLE(kCB2, false);
 extern const void *const kTableGU_cb2[2][4][5];
 const void *const kTableGU_cb2[2][4][5] = QMV_TABLE_GU(kCB2, false);
-extern const void *const kTableCB_cb2[4][3];
-const void *const kTableCB_cb2[4][3] = QMV_TABLE_CB(kCB2, false);
+extern const void *const kTableCB_cb2[4][4];
+const void *const kTableCB_cb2[4][4] = QMV_TABLE_CB(kCB2, false);
 }  // namespace QMV_NS

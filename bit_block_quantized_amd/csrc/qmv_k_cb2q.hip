@@ -9,6 +9,6 @@ extern const void *const kTableQ_cb2[3][4][5];
 const void *const kTableQ_cb2[3][4][5] = QMV_TABLE(kCB2, true);
 extern const void *const kTableQGU_cb2[2][4][5];
 const void *const kTableQGU_cb2[2][4][5] = QMV_TABLE_GU(kCB2, true);
-extern const void *const kTableQCB_cb2[4][3];
-const void *const kTableQCB_cb2[4][3] = QMV_TABLE_CB(kCB2, true);
+extern const void *const kTableQCB_cb2[4][4];
+const void *const kTableQCB_cb2[4][4] = QMV_TABLE_CB(kCB2, true);
 }  // namespace QMV_NS

@@ -8,6 +8,6 @@ extern const void *const kTable_cb2s[3][4][5];
 const void *const kTable_cb2s[3][4][5] = QMV_TABLE(kCB2S, false);
 extern const void *const kTableGU_cb2s[2][4][5];
 const void *const kTableGU_cb2s[2][4][5] = QMV_TABLE_GU(kCB2S, false);
-extern const void *const kTableCB_cb2s[4][3];
-const void *const kTableCB_cb2s[4][3] = QMV_TABLE_CB(kCB2S, false);
+extern const void *const kTableCB_cb2s[4][4];
+const void *const kTableCB_cb2s[4][4] = QMV_TABLE_CB(kCB2S, false);
 }  // namespace QMV_NS

@@ -9,6 +9,6 @@ extern const void *const kTableQ_cb2s[3][4][5];
 const void *const kTableQ_cb2s[3][4][5] = QMV_TABLE(kCB2S, true);
 extern const void *const kTableQGU_cb2s[2][4][5];
 const void *const kTableQGU_cb2s[2][4][5] = QMV_TABLE_GU(kCB2S, true);
-extern const void *const kTableQCB_cb2s[4][3];
-const void *const kTableQCB_cb2s[4][3] = QMV_TABLE_CB(kCB2S, true);
+extern const void *const kTableQCB_cb2s[4][4];
+const void *const kTableQCB_cb2s[4][4] = QMV_TABLE_CB(kCB2S, true);
 }  // namespace QMV_NS

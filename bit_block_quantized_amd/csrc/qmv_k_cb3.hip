@@ -8,6 +8,6 @@ extern const void *const kTable_cb3[3][4][5];
 const void *const kTable_cb3[3][4][5] = QMV_TABLE(kCB3, false);
 extern const void *const kTableGU_cb3[2][4][5];
 const void *const kTableGU_cb3[2][4][5] = QMV_TABLE_GU(kCB3, false);
-extern const void *const kTableCB_cb3[4][3];
-const void *const kTableCB_cb3[4][3] = QMV_TABLE_CB(kCB3, false);
+extern const void *const kTableCB_cb3[4][4];
+const void *const kTableCB_cb3[4][4] = QMV_TABLE_CB(kCB3, false);
 }  // namespace QMV_NS

@@ -9,6 +9,6 @@ extern const void *const kTableQ_cb3[3][4][5];
 const void *const kTableQ_cb3[3][4][5] = QMV_TABLE(kCB3, true);
 extern const void *const kTableQGU_cb3[2][4][5];
 const void *const kTableQGU_cb3[2][4][5] = QMV_TABLE_GU(kCB3, true);
-extern const void *const kTableQCB_cb3[4][3];
-const void *const kTableQCB_cb3[4][3] = QMV_TABLE_CB(kCB3, true);
+extern const void *const kTableQCB_cb3[4][4];
+const void *const kTableQCB_cb3[4][4] = QMV_TABLE_CB(kCB3, true);
 }  // namespace QMV_NS

@@ -8,6 +8,6 @@ extern const void *const kTable_mxfp4i[3][4][5];
 const void *const kTable_mxfp4i[3][4][5] = QMV_TABLE(kMXFP4I, false);
 extern const void *const kTableGU_mxfp4i[2][4][5];
 const void *const kTableGU_mxfp4i[2][4][5] = QMV_TABLE_GU(kMXFP4I, false);
-extern const void *const kTableCB_mxfp4i[4][3];
-const void *const kTableCB_mxfp4i[4][3] = QMV_TABLE_CB(kMXFP4I, false);
+extern const void *const kTableCB_mxfp4i[4][4];
+const void *const kTableCB_mxfp4i[4][4] = QMV_TABLE_CB(kMXFP4I, false);
 }  // namespace QMV_NS

@@ -40,9 +40,9 @@
 // then an exact bf16 normal); otherwise the step is decoded unscaled, its
 // tile multiplied by the exactly built 2^(s-127) per row and added.
 //
-// K may be split over KSPLIT waves per quad (more waves per CU to cover
-// memory latency); the parts are added in a fixed order through LDS, so
-// results are bitwise reproducible.
+// Every wave covers the whole of K for its quad, so results are bitwise
+// reproducible (splitting K over two waves per quad, for more waves per CU,
+// measured slower: every workgroup then stages all of x for half the rows).
 #include "qmv_device.hpp"
 
 namespace qmv {
@@ -99,27 +99,23 @@ __device__ __forceinline__ u32x4 load_scale_chunk(__amdgpu_buffer_rsrc_t rs, uin
     return load16_edge(rs, off, lo);
 }
 
-template <int WAVES, int KSPLIT, int CPL>
+template <int WAVES, int CPL>
 __global__ __launch_bounds__(64 * WAVES) void qmv_dense4_kernel(const Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int T = 64 * WAVES;
-    constexpr int QPW = WAVES / KSPLIT;            // row quads per workgroup
+    constexpr int QPW = WAVES;                     // row quads per workgroup
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int qw = wave % QPW;
-    const int part = wave / QPW;
+    const int qw = threadIdx.x >> 6;
     const int blk = lane >> 2;
     const int r = lane & 3;                        // row of the quad (A) and vector (B)
     const int quad = blockIdx.x * QPW + qw;
     const int U = a.units;
-    const int S = (U + 15) >> 4;                   // unit steps over K
-    const int per = (S + KSPLIT - 1) / KSPLIT;
-    const int s0 = min(S, part * per);
-    const int s1 = min(S, s0 + per);
+    const int s0 = 0;
+    const int s1 = (U + 15) >> 4;                  // unit steps over K
 
     // LDS: activations (U + 1 units of 256 B), then this workgroup's rows of
-    // E8M0 scales, then the K-part combine area.
+    // E8M0 scales.
     uint8_t *const lds_sc = lds + 256 * (U + 1);
 
     // 1. activation and scale chunks into registers, before the weight loads
@@ -252,7 +248,7 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_dense4_kernel(const Args a)
     }
 
     // 5. sum the 16 blocks' tiles (butterfly over lane bits 2..5: every lane
-    //    of a column ends with the same bits), then the K parts in order
+    //    of a column ends with the same bits)
     f32x4 acc = acc0 + acc1;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -260,25 +256,14 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_dense4_kernel(const Args a)
         for (int m = 4; m < 64; m <<= 1) acc[v] += __shfl_xor(acc[v], m);
     }
     // lane 4 * v + j (blk = v < 4) owns row 4 * quad + v of vector j
-    float val = blk == 0 ? acc[0] : blk == 1 ? acc[1] : blk == 2 ? acc[2] : acc[3];
-    if constexpr (KSPLIT == 2) {
-        float *comb = (float *)(lds_sc + 16 * ((QPW * 4 * a.rsb + 15 + 15) >> 4));
-        if (part == 1 && blk < 4) comb[qw * 16 + lane] = val;
-        __syncthreads();
-        if (part == 1) return;
-        if (blk < 4) val += comb[qw * 16 + lane];
-    }
+    const float val = blk == 0 ? acc[0] : blk == 1 ? acc[1] : blk == 2 ? acc[2] : acc[3];
     const int row = quad * 4 + blk;
     if (blk < 4 && r < a.M && row < a.N) a.y[r * a.N + row] = val;
 }
 
-// [waves 4, 8][ksplit 1, 2][cpl 4, 7]
-extern const void *const kTableDense4[2][2][2];
-const void *const kTableDense4[2][2][2] = {
-    {{(const void *)&qmv_dense4_kernel<4, 1, 4>, (const void *)&qmv_dense4_kernel<4, 1, 7>},
-     {(const void *)&qmv_dense4_kernel<4, 2, 4>, (const void *)&qmv_dense4_kernel<4, 2, 7>}},
-    {{(const void *)&qmv_dense4_kernel<8, 1, 4>, (const void *)&qmv_dense4_kernel<8, 1, 7>},
-     {(const void *)&qmv_dense4_kernel<8, 2, 4>, (const void *)&qmv_dense4_kernel<8, 2, 7>}},
-};
+// [4 waves, 8 waves], 4 unit steps in flight
+extern const void *const kTableDense4[2];
+const void *const kTableDense4[2] = {(const void *)&qmv_dense4_kernel<4, 4>,
+                                     (const void *)&qmv_dense4_kernel<8, 4>};
 
 }  // namespace qmv

@@ -5,10 +5,10 @@ load).  Needs an MI355X.
 Against the oracle on the same seeded inputs: every output within
 1e-3 * sum |w x|; bit-exact at unit scales with small-integer activations
 (every partial sum is then an exact fp32 integer, so the MFMA's summation
-order cannot show); NaN exactly where the oracle has NaN.  Shapes cover every
-launch shape the launcher picks (small calls: 4-wave workgroups, whole K per
-wave; large calls: 8 waves with K split over two waves), partial last unit
-steps (K not a multiple of 512), ragged row quads (N % 4 != 0) and M = 2, 3.
+order cannot show); NaN exactly where the oracle has NaN.  Shapes cover both
+launch shapes the launcher picks (fewer than 1024 row quads: 4-wave
+workgroups; more: 8-wave), partial last unit steps (K not a multiple of
+512), ragged row quads (N % 4 != 0) and M = 2, 3.
 """
 import numpy as np
 import pytest
@@ -41,7 +41,7 @@ def test_k_sweep(M, K):
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 61, 4093, 4100])
 def test_n_ragged(N):
-    """Small N: 4-wave workgroups; N >= 4096: 8 waves with K split in two."""
+    """N < 4096: 4-wave workgroups; N >= 4096: 8-wave workgroups."""
     _check(_dense(4, N, 7168 if N > 4000 else 1056, seed=200 + N), f"N={N}")
 
 
