@@ -235,7 +235,7 @@ def test_rejects_misaligned_and_leaves_y():
 def test_graph_replays_match_eager():
     """Calls captured in a HIP graph give the eager results on every replay,
     with eager work and synchronizations between the replays."""
-    cases = [synth.make(synth.WORKLOADS[n].scaled(**SMALL[n])) for n in ("C2", "C3", "C4", "C5a")]
+    cases = [synth.make(synth.WORKLOADS[n].scaled(**SMALL[n])) for n in ("C2", "C3", "C4", "C5a", "C5b")]
     devs = [to_dev(inp) for inp in cases]
     eager = [gpu_call(inp, dev).clone() for inp, dev in zip(cases, devs)]
     outs = [torch.empty_like(e) for e in eager]
