@@ -928,20 +928,29 @@ __device__ __forceinline__ void load_step(Unit<F> (&w)[CPL][RT], const __amdgpu_
 }
 
 // Unit steps whose code loads are in flight ahead of the step being computed.
-// Vector-memory loads of a wave complete in issue order, so issuing a whole
-// row segment at once would make every step wait for the slowest request;
-// a short lead lets decode follow the data as it streams in.
-#ifndef QMV_LEAD
-#define QMV_LEAD 1
-#endif
-template <int CPL> struct Lead { static constexpr int v = (QMV_LEAD > 0 && QMV_LEAD < CPL) ? QMV_LEAD : CPL; };
+// Vector-memory loads of a wave complete in issue order, so a long lead makes
+// early steps wait behind later requests, and a short one exposes more of
+// each request's latency.  Measured on MI355X (weights rotated past the
+// Infinity Cache), A/B in one process: the MXFP4 x bf16 gather/dense kernel
+// is fastest with 3 steps of lead (the gpt-oss gather, 3 units per lane:
+// 5.94 -> 5.78 us; the 4-token gather, 7 units per lane: 23.9 -> 23.4 us;
+// the fused gate/up and the tiny dense call unchanged); every other kernel
+// with 1: 2-bit and 3-bit weights +2-3% at lead 2 or 3, MXFP4 x int8 +4.6%,
+// and the combine kernel, whose lanes carry 4 slots' rows, +14% at lead 3.
+template <int F, int CPL> struct Lead {
+    static constexpr int want = F == kMXFP4 ? 3 : 1;
+    static constexpr int v = want < CPL ? want : CPL;
+};
+template <int CPL> struct Lead1 {                  // the combine kernel
+    static constexpr int v = 1 < CPL ? 1 : CPL;
+};
 
 template <int F, int LPR, int CPL, int RT, int NV>
 __device__ __forceinline__ void mac_seg(Unit<F> (&w)[CPL][RT], const Args &a, const uint8_t *lds,
                                         const __amdgpu_buffer_rsrc_t (&rc)[RT], const uint32_t (&oc)[RT],
                                         int seg_unit, int u0, int U, float (&acc)[RT][NV])
 {
-    constexpr int LEAD = Lead<CPL>::v;
+    constexpr int LEAD = Lead<F, CPL>::v;
     const int xbytes = U * Fmt<F>::XB;
     bool fast = true;              // MXFP4: every scale byte of the segment in [2, 252]
     if constexpr (F == kMXFP4 || F == kMXFP4I) {
@@ -1009,7 +1018,7 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
     Unit<F> w[CPL][RT];
     load_scales<F, LPR, CPL, RT>(w, rs, os, 0, li, U);
 #pragma unroll
-    for (int c = 0; c < Lead<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, 0, li, U, c);
+    for (int c = 0; c < Lead<F, CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, 0, li, U, c);
     xstore<F, NVMAX, Q>(a, it, lds, xr);
     __syncthreads();
     if (xrest<F, NVMAX, Q>(a, it, lds)) __syncthreads();
@@ -1026,7 +1035,7 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
         if (++seg >= nseg) break;
         load_scales<F, LPR, CPL, RT>(w, rs, os, seg * SEG, li, U);
 #pragma unroll
-        for (int c = 0; c < Lead<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, seg * SEG, li, U, c);
+        for (int c = 0; c < Lead<F, CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, seg * SEG, li, U, c);
     }
 
 #pragma unroll
@@ -1130,7 +1139,7 @@ __device__ __forceinline__ void mac_seg_diag(Unit<F> (&w)[CPL][RT], const Args &
                                              const int (&vo)[RT], const bool (&valid)[RT],
                                              int seg_unit, int u0, int U, float (&acc)[RT])
 {
-    constexpr int LEAD = Lead<CPL>::v;
+    constexpr int LEAD = Lead1<CPL>::v;
     const int xbytes = U * Fmt<F>::XB;
     bool fast = true;
     if constexpr (F == kMXFP4 || F == kMXFP4I) {
@@ -1210,7 +1219,7 @@ __global__ __launch_bounds__(kThreads) void qmv_combine_kernel(const Args a)
         Unit<F> w[CPL][RT];
         load_scales<F, LPR, CPL, RT>(w, rs, os, 0, li, U);
 #pragma unroll
-        for (int c = 0; c < Lead<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, 0, li, U, c);
+        for (int c = 0; c < Lead1<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, 0, li, U, c);
         if (g == 0 || restage) {
             if (restage) __syncthreads();          // every wave is done with the last group's vectors
             xstore<F, 4, Q>(a, it, lds, xr);
@@ -1227,7 +1236,7 @@ __global__ __launch_bounds__(kThreads) void qmv_combine_kernel(const Args a)
             if (++seg >= nseg) break;
             load_scales<F, LPR, CPL, RT>(w, rs, os, seg * SEG, li, U);
 #pragma unroll
-            for (int c = 0; c < Lead<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, seg * SEG, li, U, c);
+            for (int c = 0; c < Lead1<CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, seg * SEG, li, U, c);
         }
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
