@@ -29,7 +29,9 @@ gate/up + SwiGLU calls (qmv_gather_moe_swiglu) C2gu and C3gu and the down
 projections with the router-weighted combine (qmv_gather_moe_combine) C4c and
 C2c, the 2-bit and 3-bit gathers fed bf16 activations that the kernel
 quantizes while staging them, C3q and C4q, and the gpt-oss gather with MXFP4
-weights and int8 activations (fp16 scale per 32), C2i.
+weights and int8 activations (fp16 scale per 32), C2i, and a gpt-oss prefill
+chunk (512 tokens x top-4 of 32 experts) on the expert-batched matrix-core
+path, C6, whose entry also carries its MFMA rate against the dense bf16 peak.
 """
 from __future__ import annotations
 
@@ -46,6 +48,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
 WFMT = {"mxfp4": 0, "cb2": 1, "cb3": 2}
 HEADLINE = "C2"
 METRIC = "effective weight GB/s and µs/call per expert-gather GEMV; % of HBM peak"
@@ -107,7 +110,7 @@ def other_bytes(wl):
 # Rotation plan: layer copies so that between two reads of the same weights
 # more than the 256 MB Infinity Cache of other weights is read.
 ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40, "C2gu": 4, "C3gu": 1,
-            "C4c": 2, "C2c": 32, "C3q": 2, "C4q": 2, "C2i": 32}
+            "C4c": 2, "C2c": 32, "C3q": 2, "C4q": 2, "C2i": 32, "C6": 8}
 
 
 class Prepared:
@@ -168,6 +171,9 @@ class Prepared:
         self.calls = calls
         n_unique = np.array([len(e) for e in experts])
         self.wbytes = np.array([weight_bytes(wl, u) for u in n_unique], np.float64) * len(self.w)
+        pairs = (np.array([(i >= 0).sum() for i in ids], np.float64) if routed
+                 else np.full(calls, float(wl.M)))
+        self.flops = 2.0 * pairs * wl.N * wl.K
         self.abytes = self.wbytes + other_bytes(wl)
         self.lib = q.lib()
         self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -298,6 +304,13 @@ def measure(name, steps, warmup, hot=True):
         "pct_hbm_peak": 100.0 * (ab / t / 1e9) / HBM_PEAK_GBS,
         "layers_rotated": p.L,
     }
+    if p.wl.M > 4:
+        # many vectors per expert: also a matrix-core product (2 flops per
+        # weight per routed vector)
+        fl = float(p.flops[sel].mean())
+        res["flops_per_call"] = fl
+        res["mfma_TFLOPs"] = fl / t / 1e12
+        res["pct_mfma_bf16_peak"] = 100.0 * fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS
     ts, v = stream_ceiling(p, warmup, min(steps, 500))
     wcode = float(p.wbytes[warmup:warmup + min(steps, 500)].mean())
     res["stream_ceiling_us_per_call"] = ts * 1e6
@@ -387,7 +400,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c,C3q,C4q,C2i",
+    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c,C3q,C4q,C2i,C6",
                     help="other shapes to measure besides the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")

@@ -43,6 +43,13 @@ namespace qmv {
 extern const void *const kTableDense4[2];
 }
 
+// MXFP4 x bf16 with more than 4 vectors: expert-batched gather and dense
+// calls on the 16x16x32 bf16 matrix cores (qmv_k_mxfp4b.hip): [128, 256]
+// rows per tile.
+namespace qmv {
+extern const void *const kTableBatched[2];
+}
+
 namespace {
 
 using namespace qmv;
@@ -52,6 +59,11 @@ constexpr int kWaveMenu[2] = {4, 8};     // wave64s per workgroup: qmv, qmv_w8
 constexpr int kMaxK = 16384;
 constexpr int kMaxM = 4;
 constexpr int kMaxTopK = 16;
+// The batched MXFP4 x bf16 path (M > 4): (token, slot) pairs and experts are
+// sorted in LDS, 16-bit indices, one bucket per expert plus one for ids
+// outside [0, E).
+constexpr int kMaxPairsBatched = 8192;
+constexpr int kMaxEBatched = 1023;
 
 // Kernels for bf16 activations quantized in staging (2-bit and 3-bit weights).
 const void *kernel_for_q8(int wi, int kind, int variant, int li, int ci, bool gate_up)
@@ -176,7 +188,8 @@ long long row_scale_bytes(int wfmt, long long K)
 // Host-only argument checks (no HIP call, no pointer dereference).
 qmv_status_t validate(int wfmt, const void *codes, const void *scales, long long E,
                       const int32_t *ids, bool gather, int M, int top_k, int afmt,
-                      const void *x, const void *xs, const float *y, int N, int K)
+                      const void *x, const void *xs, const float *y, int N, int K,
+                      bool batched_ok = false)
 {
     if (!codes || !scales || !x || !y || (gather && !ids))
         return QMV_EINVAL;
@@ -189,8 +202,14 @@ qmv_status_t validate(int wfmt, const void *codes, const void *scales, long long
     // pairs: (MXFP4, BF16), (MXFP4, Q8B32), (CB2 or CB3, Q8B32), (CB2 or CB3, BF16_Q8)
     if ((wfmt == QMV_W_MXFP4) ? afmt == QMV_A_BF16_Q8 : afmt == QMV_A_BF16)
         return QMV_EUNSUPPORTED;
-    if (M > kMaxM || top_k > kMaxTopK || K % 32 != 0 || K > kMaxK)
+    if (top_k > kMaxTopK || K % 32 != 0 || K > kMaxK)
         return QMV_EUNSUPPORTED;
+    if (M > kMaxM) {
+        // more than 4 vectors: MXFP4 x bf16 dense and plain gather calls only
+        if (!batched_ok || wfmt != QMV_W_MXFP4 || afmt != QMV_A_BF16 ||
+            (long long)M * (gather ? top_k : 1) > kMaxPairsBatched || (gather && E > kMaxEBatched))
+            return QMV_EUNSUPPORTED;
+    }
     const uintptr_t calign = (wfmt == QMV_W_CB2 && K % 64 != 0) ? 8 : (wfmt == QMV_W_CB3 ? 4 : 16);
     if (!aligned(codes, calign) || !aligned(x, 16) || !aligned(y, 4) ||
         (wfmt != QMV_W_MXFP4 && !aligned(scales, 4)) || (xs && !aligned(xs, 4)) ||
@@ -373,6 +392,60 @@ size_t dense4_lds(int K, int waves)
     return 256 * (rsb + 1) + 16 * ((waves * 4 * rsb + 30) / 16);
 }
 
+// Batched MXFP4 x bf16 (M > 4): LDS of one workgroup = one 128-weight
+// slice of 128 vectors (32 KB), then the routing tables (count, vector
+// offset and tile offset per bucket, wave totals) and the sorted pair list.
+size_t batched_lds(int buckets, int pairs)
+{
+    return (size_t)128 * 256 + 12 * (size_t)(buckets + 1) + 32 + (((size_t)2 * pairs + 15) & ~(size_t)15);
+}
+
+int g_cu_count[64];
+std::once_flag g_cu_once[64];
+
+int cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    std::call_once(g_cu_once[dev], [&] {
+        int n = 0;
+        const bool ok = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+        g_cu_count[dev] = ok && n > 0 ? n : 256;
+    });
+    return g_cu_count[dev];
+}
+
+// Grid: a tile is (expert, row tile) for a gather and (chunk of <= 128
+// vectors, row tile) for a dense call; the ids are read on the device, so
+// the host bounds the tile count by row tiles x min(pairs, buckets) and
+// launches at most two workgroups per CU, each looping over tiles.  256-row
+// tiles read the activations half as often as 128-row tiles; they are taken
+// when they still give every CU two tiles.
+qmv_status_t launch_batched(const void *codes, const void *scales, int E, const int32_t *ids, int M,
+                            int top_k, const void *x, int x_per_slot, float *y, int N, int K,
+                            hipStream_t stream)
+{
+    const bool gather = ids != nullptr;
+    Args a = base_args(QMV_W_MXFP4, QMV_A_BF16, kMXFP4, codes, scales, gather ? E : 1, ids, M,
+                       gather ? top_k : 1, x, nullptr, gather ? x_per_slot : 0, y, N, K);
+    const int pairs = gather ? M * top_k : M;
+    const int buckets = gather ? E + 1 : 1;
+    const long long groups = gather ? (pairs < buckets ? pairs : buckets) : (pairs + 127) / 128;
+    const int cus = cu_count();
+    const long long nt4 = (N + 255) / 256;
+    const int rfi = nt4 * groups >= 2LL * cus ? 1 : 0;
+    const long long nt = rfi ? nt4 : (N + 127) / 128;
+    long long upper = nt * groups;
+    if (upper > 2LL * cus) upper = 2LL * cus;
+    const void *fn = kTableBatched[rfi];
+    void *kargs[] = {&a};
+    if (hipLaunchKernel(fn, dim3((unsigned)upper), dim3(256), kargs, batched_lds(buckets, pairs), stream) !=
+        hipSuccess)
+        return QMV_EHIP;
+    return QMV_OK;
+}
+
 std::once_flag g_d4_once[2];
 hipError_t g_d4_err[2];
 
@@ -408,6 +481,8 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
     const bool gather = ids != nullptr;
     const bool gate_up = codes2 != nullptr;
     const int kind = kind_of(wfmt, afmt, K);
+    if (!gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM)
+        return launch_batched(codes, scales, E, ids, M, top_k, x, x_per_slot, y, N, K, stream);
     if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M >= 2)
         return launch_dense4(codes, scales, x, y, M, N, K, stream);
     const int units = K / kUnitWeights[kind];
@@ -500,7 +575,7 @@ QMV_API qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void 
                        float *y, int M, int N, int K, hipStream_t stream)
 {
     const qmv_status_t s = validate(wfmt, w_codes, w_scales, 1, nullptr, false, M, 1, afmt,
-                                    x, afmt == QMV_A_Q8B32 ? x_scales : nullptr, y, N, K);
+                                    x, afmt == QMV_A_Q8B32 ? x_scales : nullptr, y, N, K, true);
     if (s != QMV_OK)
         return s;
     return launch(wfmt, afmt, w_codes, w_scales, nullptr, nullptr, 1, nullptr, M, 1, x,
@@ -513,7 +588,7 @@ QMV_API qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const 
                             int x_per_slot, float *y, int N, int K, hipStream_t stream)
 {
     const qmv_status_t s = validate(wfmt, w_codes, w_scales, E, expert_ids, true, M, top_k, afmt,
-                                    x, afmt == QMV_A_Q8B32 ? x_scales : nullptr, y, N, K);
+                                    x, afmt == QMV_A_Q8B32 ? x_scales : nullptr, y, N, K, true);
     if (s != QMV_OK)
         return s;
     return launch(wfmt, afmt, w_codes, w_scales, nullptr, nullptr, E, expert_ids, M, top_k, x,
@@ -560,9 +635,10 @@ QMV_API const char *qmv_strerror(qmv_status_t status)
     switch (status) {
     case QMV_OK: return "success";
     case QMV_EINVAL: return "invalid argument (null or misaligned pointer, or a size <= 0)";
-    case QMV_EUNSUPPORTED: return "unsupported shape or format (M in [1,4], top_k in [1,16], "
-                                  "K % 32 == 0 and K <= 16384; pairs MXFP4+BF16, CB2/CB3+Q8B32, "
-                                  "CB2/CB3+BF16_Q8)";
+    case QMV_EUNSUPPORTED: return "unsupported shape or format (M in [1,4], or up to 8192 "
+                                  "(token, slot) pairs with E <= 1023 for MXFP4+BF16 dense and "
+                                  "gather calls; top_k in [1,16], K % 32 == 0 and K <= 16384; "
+                                  "pairs MXFP4+BF16, MXFP4+Q8B32, CB2/CB3+Q8B32, CB2/CB3+BF16_Q8)";
     case QMV_EHIP: return "the HIP runtime rejected the kernel launch";
     }
     return "unknown status";

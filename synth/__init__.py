@@ -24,6 +24,8 @@ Workload shapes (the expert-projection GEMVs the pages measure):
 * ``C5a`` verify width 4: 4 tokens x top-4 of 256 (distinct within a token,
   overlaps across tokens allowed), MXFP4, K=7168, N=2048.
 * ``C5b`` dense MXFP4, M=4, K=N=7168.
+* ``C6``  prefill chunk: 512 tokens x top-4 of 32 (gpt-oss-20b), MXFP4 x bf16,
+  K=N=2880 -- the expert-batched path for more than 4 vectors.
 
 Activation recipe: bf16 activations are N(0,1) samples rounded to bf16 by
 torch's float32 -> bfloat16 cast (round to nearest even).  int8 activations
@@ -144,8 +146,19 @@ QUANT_WORKLOADS = {
 }
 
 
+# More than 4 vectors per call (MXFP4 x bf16, the expert-batched matrix-core
+# path): a gpt-oss-20b prefill chunk, every token routed to 4 of the 32
+# experts, so each expert meets about 64 of the 2048 (token, slot) pairs.
+BATCHED_WORKLOADS = {
+    "C6": Workload("C6", "gather", "mxfp4", M=512, N=2880, K=2880, seed=13, E=32, top_k=4,
+                   desc="gpt-oss-20b MoE prefill chunk: 512 tokens x top-4 of 32 experts, "
+                        "K=N=2880, MXFP4 x bf16, expert-batched"),
+}
+
+
 def workload(name: str) -> Workload:
-    for table in (WORKLOADS, GATE_UP_WORKLOADS, COMBINE_WORKLOADS, QUANT_WORKLOADS):
+    for table in (WORKLOADS, GATE_UP_WORKLOADS, COMBINE_WORKLOADS, QUANT_WORKLOADS,
+                  BATCHED_WORKLOADS):
         if name in table:
             return table[name]
     raise KeyError(name)

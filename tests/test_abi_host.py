@@ -79,7 +79,10 @@ def gather(L, wfmt=W_MXFP4, codes=FAKE, scales=FAKE, E=32, ids=FAKE, M=1, top_k=
 @pytest.mark.parametrize("kw,want", [
     (dict(codes=None), EINVAL), (dict(scales=None), EINVAL), (dict(x=None), EINVAL),
     (dict(y=None), EINVAL), (dict(M=0), EINVAL), (dict(N=0), EINVAL), (dict(K=0), EINVAL),
-    (dict(N=-5), EINVAL), (dict(M=5), EUNSUP), (dict(K=48), EUNSUP), (dict(K=16416), EUNSUP),
+    (dict(N=-5), EINVAL), (dict(K=48), EUNSUP), (dict(K=16416), EUNSUP),
+    # more than 4 vectors: MXFP4 x bf16 only, at most 8192 of them
+    (dict(M=8193), EUNSUP), (dict(M=5, afmt=A_Q8, xs=FAKE), EUNSUP),
+    (dict(M=5, wfmt=W_CB2, afmt=A_Q8, xs=FAKE), EUNSUP),
     (dict(afmt=A_Q8, xs=None), EINVAL), (dict(afmt=A_Q8, xs=FAKE + 2), EINVAL),
     (dict(wfmt=W_CB2), EUNSUP), (dict(wfmt=7), EUNSUP),
     (dict(afmt=3), EUNSUP), (dict(afmt=2), EUNSUP), (dict(codes=FAKE + 8), EINVAL),
@@ -93,7 +96,10 @@ def test_dense_validation(L, kw, want):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(ids=None), EINVAL), (dict(E=0), EINVAL), (dict(top_k=0), EINVAL),
-    (dict(top_k=17), EUNSUP), (dict(M=5), EUNSUP), (dict(K=2880 + 16), EUNSUP),
+    (dict(top_k=17), EUNSUP), (dict(K=2880 + 16), EUNSUP),
+    # more than 4 vectors: MXFP4 x bf16, at most 8192 (token, slot) pairs and 1023 experts
+    (dict(M=2049), EUNSUP), (dict(M=5, E=1024), EUNSUP), (dict(M=5, afmt=A_Q8, xs=FAKE), EUNSUP),
+    (dict(M=5, wfmt=W_CB3, afmt=A_Q8, xs=FAKE), EUNSUP),
     (dict(wfmt=W_CB2, afmt=A_Q8, xs=None), EINVAL),
     (dict(wfmt=W_CB3, afmt=A_BF16), EUNSUP),
     (dict(wfmt=W_CB2, afmt=A_Q8, xs=FAKE, scales=FAKE + 2), EINVAL),
