@@ -44,8 +44,8 @@ extern const void *const kTableDense4[2];
 }
 
 // MXFP4 x bf16 with more than 4 vectors: expert-batched gather and dense
-// calls on the 16x16x32 bf16 matrix cores (qmv_k_mxfp4b.hip): [128, 256]
-// rows per tile.
+// calls on the 16x16x32 bf16 matrix cores (qmv_k_mxfp4b.hip): [4 waves and
+// 128 rows per tile, 8 waves and 256 rows per tile].
 namespace qmv {
 extern const void *const kTableBatched[2];
 }
@@ -397,7 +397,7 @@ size_t dense4_lds(int K, int waves)
 // offset and tile offset per bucket, wave totals) and the sorted pair list.
 size_t batched_lds(int buckets, int pairs)
 {
-    return (size_t)128 * 256 + 12 * (size_t)(buckets + 1) + 32 + (((size_t)2 * pairs + 15) & ~(size_t)15);
+    return (size_t)128 * 256 + 12 * (size_t)(buckets + 1) + 64 + (((size_t)2 * pairs + 15) & ~(size_t)15);
 }
 
 int g_cu_count[64];
@@ -419,9 +419,10 @@ int cu_count()
 // Grid: a tile is (expert, row tile) for a gather and (chunk of <= 128
 // vectors, row tile) for a dense call; the ids are read on the device, so
 // the host bounds the tile count by row tiles x min(pairs, buckets) and
-// launches at most two workgroups per CU, each looping over tiles.  256-row
-// tiles read the activations half as often as 128-row tiles; they are taken
-// when they still give every CU two tiles.
+// launches at most one 8-wave or two 4-wave workgroups per CU, each looping
+// over tiles.  8-wave workgroups (256-row tiles, two waves per SIMD) read
+// the activations half as often per weight byte; they are taken when they
+// still give every CU a tile.
 qmv_status_t launch_batched(const void *codes, const void *scales, int E, const int32_t *ids, int M,
                             int top_k, const void *x, int x_per_slot, float *y, int N, int K,
                             hipStream_t stream)
@@ -434,13 +435,14 @@ qmv_status_t launch_batched(const void *codes, const void *scales, int E, const 
     const long long groups = gather ? (pairs < buckets ? pairs : buckets) : (pairs + 127) / 128;
     const int cus = cu_count();
     const long long nt4 = (N + 255) / 256;
-    const int rfi = nt4 * groups >= 2LL * cus ? 1 : 0;
+    const int rfi = nt4 * groups >= cus ? 1 : 0;
     const long long nt = rfi ? nt4 : (N + 127) / 128;
     long long upper = nt * groups;
-    if (upper > 2LL * cus) upper = 2LL * cus;
+    if (upper > (rfi ? 1LL : 2LL) * cus) upper = (rfi ? 1LL : 2LL) * cus;
+    upper = (upper + 7) & ~7LL;                    // the kernel deals tiles to 8 XCDs
     const void *fn = kTableBatched[rfi];
     void *kargs[] = {&a};
-    if (hipLaunchKernel(fn, dim3((unsigned)upper), dim3(256), kargs, batched_lds(buckets, pairs), stream) !=
+    if (hipLaunchKernel(fn, dim3((unsigned)upper), dim3(rfi ? 512 : 256), kargs, batched_lds(buckets, pairs), stream) !=
         hipSuccess)
         return QMV_EHIP;
     return QMV_OK;

@@ -17,8 +17,8 @@
 // atomics order an expert's pairs differently in each workgroup, so a chunk
 // must never be a tile of its own: two workgroups would cut different sets.
 // A dense call has one bucket in index order, and there each chunk is a tile
-// (more tiles for the same rows).  Workgroups take tiles blockIdx.x,
-// blockIdx.x + gridDim.x, ... until the list ends.
+// (more tiles for the same rows).  Workgroups take the list's tiles in an
+// XCD-aware order until it ends.
 //
 // Inside a tile, wave w owns 16*RF rows as RF fragments of 16.  The K axis is
 // walked in 128-weight slices.  Lane 16q + r loads row r's 32-weight block
@@ -31,19 +31,19 @@
 //
 // Decode: v_cvt_scalef32_pk_bf16_fp4 turns 8 nibbles into the A operand with
 // the E8M0 scale folded in; e2m1 * 2^(s-127) is an exact bf16 normal for
-// s in [2, 252].  A slice with any other scale byte (rare) is decoded
-// unscaled and multiplied one lane group at a time (the other groups' A set
-// to zero), each group's partial tile then scaled by its exactly built
-// 2^(s-127) per row.
+// s in [2, 252].  A chunk whose weights hold any other scale byte (never in
+// real weights: they are 2^-127, 2^-126, 2^126, 2^127 and NaN) is recomputed
+// by a plain exact path after the loop, which keeps the loop itself to one
+// path.
 //
 // Activations: per slice, every workgroup stages the tile's vectors' 128
 // bf16 values into LDS (256 bytes per vector; chunk index xor-ed with the
 // vector's low 4 bits so that the 16 lanes of one ds_read_b128 quarter hit
 // 16 distinct bank groups).  Weight loads run two slices ahead; the next
 // slice's activations are loaded into registers while the current slice
-// multiplies.  Loads complete in issue order, so each slice issues its
-// activation loads before the weight loads of two slices later: waiting for
-// the activations never waits for weights not yet needed.
+// multiplies.  Loads complete in issue order, so the activations are loaded
+// two slices ahead into two register sets, before the weight loads of the
+// next slice: waiting for them never waits for weights not yet needed.
 //
 // Every output element is one MFMA column's dot product over the whole of K
 // in a fixed order, so results do not depend on where a vector lands in the
@@ -56,7 +56,6 @@ namespace qmv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBThreads = 256;          // 4 wave64s
 constexpr int kBVecMax = 128;           // vectors per tile: 8 column fragments of 16
 constexpr int kBXBytes = kBVecMax * 256;
 constexpr uint32_t kBPast = 0x80000000u;   // >= every buffer size: reads zeros
@@ -83,11 +82,45 @@ __device__ __forceinline__ int tiles_of(int c, int nt, bool chunk_tiles)
     return c == 0 ? 0 : (chunk_tiles ? (c + kBVecMax - 1) / kBVecMax : 1) * nt;
 }
 
-template <int RF>
-__global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
+// The outputs of one chunk of vectors over rows [row_lo, row_lo + rows),
+// computed exactly as the per-block definition reads: each 32-weight block's
+// sum of e2m1 * x in fp32, times 2^(s-127) built exactly (so scale bytes 0,
+// 1, 253, 254 and 255 come out as they should).  One output per thread at a
+// time, plain loads: slow, and only run for chunks whose weights hold a scale
+// byte outside [2, 252].
+__device__ __noinline__ void batched_chunk_exact(const Args &a, const uint8_t *codes, const uint8_t *scales,
+                                                 const uint16_t *vecs, int nv, int row_lo, int rows)
+{
+    const bool gather = a.ids != nullptr;
+    for (int o = threadIdx.x; o < rows * nv; o += blockDim.x) {
+        const int n = row_lo + o % rows;
+        const int i = vecs[o / rows];
+        const int xrow = gather && a.x_per_slot ? i : (gather ? i / a.top_k : i);
+        const uint16_t *xv = (const uint16_t *)(a.x + (size_t)xrow * a.x_vec_bytes);
+        const uint8_t *cw = codes + (size_t)n * a.rcb;
+        float acc = 0.0f;
+        for (int blk = 0; blk < a.units; ++blk) {
+            float part = 0.0f;
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t byte = cw[16 * blk + j];
+                const bf16x2 w = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(byte, 1.0f, 0);
+                part = __builtin_fmaf((float)w[0], __uint_as_float((uint32_t)xv[32 * blk + 2 * j] << 16), part);
+                part = __builtin_fmaf((float)w[1], __uint_as_float((uint32_t)xv[32 * blk + 2 * j + 1] << 16), part);
+            }
+            acc = __builtin_fmaf(part, e8m0_f32(scales[(size_t)n * a.rsb + blk]), acc);
+        }
+        a.y[(size_t)i * a.N + n] = acc;
+    }
+}
+
+template <int RF, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void qmv_batched_kernel(const Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    constexpr int TR = 64 * RF;                    // rows per tile
+    constexpr int kBThreads = 64 * WAVES;
+    constexpr int TR = 16 * RF * WAVES;            // rows per tile
+    constexpr int BPT = 1024 / kBThreads;          // scan buckets per thread
+    constexpr int XJ = 2048 / kBThreads;           // 16-byte staging chunks per thread and slice
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -103,8 +136,8 @@ __global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
     int *const cnt = (int *)(lds + kBXBytes);
     int *const voff = cnt + (nb + 1);
     int *const toff = voff + (nb + 1);
-    int *const wsum = toff + (nb + 1);             // 2 x 4 wave totals
-    uint16_t *const perm = (uint16_t *)(wsum + 8);
+    int *const wsum = toff + (nb + 1);             // 2 x 8 wave totals
+    uint16_t *const perm = (uint16_t *)(wsum + 16);
     uint32_t *const tmp = (uint32_t *)lds;         // (bucket << 16 | rank) per pair, in the x area
 
     // 1. counting sort of the pairs by expert (a dense call: one bucket, index order)
@@ -121,10 +154,10 @@ __global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
     }
     __syncthreads();
     {
-        int c[4], sv = 0, st = 0;
+        int c[BPT], sv = 0, st = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int b = 4 * tid + j;
+        for (int j = 0; j < BPT; ++j) {
+            const int b = BPT * tid + j;
             c[j] = b < nb ? cnt[b] : 0;
             sv += c[j];
             st += tiles_of(c[j], NT, !gather);
@@ -135,13 +168,13 @@ __global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
             const int tv = __shfl_up(sv, d), tt = __shfl_up(st, d);
             if (lane >= d) { sv += tv; st += tt; }
         }
-        if (lane == 63) { wsum[w] = sv; wsum[4 + w] = st; }
+        if (lane == 63) { wsum[w] = sv; wsum[8 + w] = st; }
         __syncthreads();
         int ev = sv - ov, et = st - ot;
-        for (int k = 0; k < w; ++k) { ev += wsum[k]; et += wsum[4 + k]; }
+        for (int k = 0; k < w; ++k) { ev += wsum[k]; et += wsum[8 + k]; }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int b = 4 * tid + j;
+        for (int j = 0; j < BPT; ++j) {
+            const int b = BPT * tid + j;
             if (b < nb) { voff[b] = ev; toff[b] = et; }
             ev += c[j];
             et += tiles_of(c[j], NT, !gather);
@@ -160,7 +193,16 @@ __global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, x_bytes);
     const bool vec4 = (a.N & 3) == 0 && ((uintptr_t)a.y & 15) == 0;
 
-    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    // Workgroups are dealt to the 8 XCDs in turn (workgroup b to XCD b % 8;
+    // the grid is a multiple of 8).  Each XCD takes one contiguous eighth of
+    // the expert-major tile list, so its L2 holds the activation rows of a
+    // few experts only, shared by the row tiles of one expert that its CUs
+    // stream at the same time.
+    const int per = (total + 7) >> 3;
+    const int xcd = blockIdx.x & 7;
+    for (int xl = blockIdx.x >> 3; xl < per; xl += gridDim.x >> 3) {
+        const int t = xcd * per + xl;
+        if (t >= total) break;
         // 2. the tile: bucket, row tile (and chunk, for a dense call)
         int lo = 0, hi = nb;
         while (hi - lo > 1) {
@@ -178,7 +220,7 @@ __global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
         for (int chunk = ct; chunk < (gather ? nch : ct + 1); ++chunk) {
             const int vstart = voff[b] + chunk * cs;
             const int nv = min(cs, c - chunk * cs);
-            const int nf = (nv + 15) >> 4;
+            int nf = (nv + 15) >> 4;
 
             f32x4 acc[RF][8];
 #pragma unroll
@@ -197,12 +239,13 @@ __global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
                     oc[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rcb + 16u * q : kBPast;
                     os[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rsb + q : kBPast;
                 }
-                // activation rows of this thread's staging chunks: vectors tid/16 + 16j, k-chunk tid%16
+                // activation rows of this thread's staging chunks: vectors tid/16 + (threads/16) j,
+                // k-chunk tid%16
                 const int pos = tid & 15;
-                uint32_t xo[8];
+                uint32_t xo[XJ];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int v = (tid >> 4) + 16 * j;
+                for (int j = 0; j < XJ; ++j) {
+                    const int v = (tid >> 4) + (kBThreads / 16) * j;
                     uint32_t o = kBPast;
                     if (v < nv) {
                         const int i = perm[vstart + v];
@@ -212,24 +255,23 @@ __global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
                     xo[j] = o;
                 }
 
-                uint4 xr[8];
-                auto load_x = [&](int s) {
+                auto load_x = [&](int s, uint4 (&xr)[XJ]) {
                     const int k = 128 * s + 8 * pos;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
+                    for (int j = 0; j < XJ; ++j) {
                         const uint32_t o = (k < a.K && xo[j] != kBPast) ? xo[j] + 2u * k : kBPast;
                         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
                         xr[j] = make_uint4(v[0], v[1], v[2], v[3]);
                     }
                 };
-                auto put_x = [&]() {
+                // every row of the buffer, used or not (unconditional stores keep
+                // the loads ahead of them; unused rows hold zeros)
+                auto put_x = [&](const uint4 (&xr)[XJ]) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int v = (tid >> 4) + 16 * j;
-                        if (v < nf * 16) *(uint4 *)(lds + bx_off(v, pos)) = xr[j];
-                    }
+                    for (int j = 0; j < XJ; ++j)
+                        *(uint4 *)(lds + bx_off((tid >> 4) + (kBThreads / 16) * j, pos)) = xr[j];
                 };
-                auto load_w = [&](int s, u32x4 (&wc)[RF], uint32_t (&sb)[RF]) {
+                auto load_w = [&](int s, u32x4 (&wc)[RF], uint8_t (&sb)[RF]) {
                     const bool ok = s < S && 4 * s + q < U;
 #pragma unroll
                     for (int f = 0; f < RF; ++f) {
@@ -238,16 +280,20 @@ __global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
                         sb[f] = __builtin_amdgcn_raw_buffer_load_b8(rs, okf ? os[f] + 4u * s : kBPast, 0, 0);
                     }
                 };
-                auto compute = [&](int s, const u32x4 (&wc)[RF], const uint32_t (&sbr)[RF]) {
+                // A slice whose scale bytes are all in [2, 252] (every real
+                // weight) is exact with the scale folded into the convert; any
+                // other byte only marks the chunk for the exact recomputation
+                // below, which keeps this loop free of a second path (and the
+                // accumulators out of the VALU).
+                int slow = 0;
+                auto compute = [&](int s, const u32x4 (&wc)[RF], const uint8_t (&sbr)[RF]) {
                     const bool ok = 4 * s + q < U;
                     bf16x8 A[RF][4];
-                    uint32_t sb[RF];
-                    bool fast[RF];
 #pragma unroll
                     for (int f = 0; f < RF; ++f) {
-                        sb[f] = (ok && oc[f] != kBPast) ? sbr[f] : 127u;
-                        fast[f] = __all((sb[f] - 2u) <= 250u);
-                        const float sc = fast[f] ? __uint_as_float(sb[f] << 23) : 1.0f;
+                        const uint32_t sb = (ok && oc[f] != kBPast) ? (uint32_t)sbr[f] : 127u;
+                        slow |= (sb - 2u) > 250u;
+                        const float sc = __uint_as_float(sb << 23);
 #pragma unroll
                         for (int k = 0; k < 4; ++k) A[f][k] = dec8(wc[f][k], sc);
                     }
@@ -259,57 +305,49 @@ __global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
                             for (int k = 0; k < 4; ++k)
                                 Bv[k] = __builtin_bit_cast(bf16x8, lds_read16(lds + bx_off(16 * g + r, 4 * q + k)));
 #pragma unroll
-                            for (int f = 0; f < RF; ++f) {
-                                if (fast[f]) {
+                            for (int f = 0; f < RF; ++f)
 #pragma unroll
-                                    for (int k = 0; k < 4; ++k)
-                                        acc[f][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[f][k], Bv[k], acc[f][g], 0, 0, 0);
-                                } else {
-                                    // one lane group (one 32-weight block per row) at a time
-                                    const bf16x8 z = {};
-#pragma unroll
-                                    for (int qq = 0; qq < 4; ++qq) {
-                                        f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                                        for (int k = 0; k < 4; ++k)
-                                            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q == qq ? A[f][k] : z, Bv[k], p, 0, 0, 0);
-                                        // p[v] is row 4 (lane / 16) + v of the fragment; its block's
-                                        // scale byte sits in lane 16 qq + 4 (lane / 16) + v
-#pragma unroll
-                                        for (int v = 0; v < 4; ++v) {
-                                            const uint32_t sv = (uint32_t)__shfl((int)sb[f], 16 * qq + 4 * q + v);
-                                            acc[f][g][v] = __builtin_fmaf(p[v], e8m0_f32(sv), acc[f][g][v]);
-                                        }
-                                    }
-                                }
-                            }
+                                for (int k = 0; k < 4; ++k)
+                                    acc[f][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[f][k], Bv[k], acc[f][g], 0, 0, 0);
                         }
                     }
                 };
 
-                // 3. slices: weights two ahead, activations one ahead (one LDS buffer)
+                // 3. slices.  Loads complete in issue order, so waiting for the
+                //    activations of slice s + 1 also waits for everything issued
+                //    before them: they are issued two slices ahead (two register
+                //    sets), ahead of the weights of slice s + 1, which then have
+                //    two slices of time as well.
                 u32x4 wc0[RF], wc1[RF];
-                uint32_t sb0[RF], sb1[RF];
-                load_x(0);
+                uint8_t sb0[RF], sb1[RF];          // widened only where used
+                uint4 xr0[XJ], xr1[XJ];
+                load_x(0, xr0);
                 load_w(0, wc0, sb0);
+                load_x(1, xr1);
                 load_w(1, wc1, sb1);
-                put_x();
+                put_x(xr0);
                 __syncthreads();
+                // (an odd slice count gets one more slice of zeros: no branch
+                // inside the loop, so no join the compiler must wait at)
                 for (int s = 0; s < S; s += 2) {
-                    load_x(s + 1);
+                    load_x(s + 2, xr0);
                     compute(s, wc0, sb0);
                     load_w(s + 2, wc0, sb0);
                     __syncthreads();
-                    put_x();
+                    put_x(xr1);
                     __syncthreads();
-                    if (s + 1 < S) {
-                        load_x(s + 2);
-                        compute(s + 1, wc1, sb1);
-                        load_w(s + 3, wc1, sb1);
-                        __syncthreads();
-                        put_x();
-                        __syncthreads();
-                    }
+                    load_x(s + 3, xr1);
+                    compute(s + 1, wc1, sb1);
+                    load_w(s + 3, wc1, sb1);
+                    __syncthreads();
+                    put_x(xr0);
+                    __syncthreads();
+                }
+                if (__syncthreads_or(slow)) {
+                    const int e = gather ? b : 0;
+                    batched_chunk_exact(a, a.codes + (long long)e * a.expert_cb, a.scales + (long long)e * a.expert_sb,
+                                        perm + vstart, nv, rt * TR, min(TR, a.N - rt * TR));
+                    nf = 0;                        // stored: nothing left for step 4
                 }
             }
 
@@ -338,9 +376,9 @@ __global__ __launch_bounds__(kBThreads) void qmv_batched_kernel(const Args a)
     }
 }
 
-// Rows per tile: 128 (RF 2), 256 (RF 4).
+// [128 rows per tile (2 fragments x 4 waves), 256 rows per tile (2 fragments x 8 waves)]
 extern const void *const kTableBatched[2];
-const void *const kTableBatched[2] = {(const void *)&qmv_batched_kernel<2>,
-                                      (const void *)&qmv_batched_kernel<4>};
+const void *const kTableBatched[2] = {(const void *)&qmv_batched_kernel<2, 4>,
+                                      (const void *)&qmv_batched_kernel<2, 8>};
 
 }  // namespace qmv
