@@ -44,8 +44,8 @@ extern const void *const kTableDense4[2];
 }
 
 // MXFP4 x bf16 with more than 4 vectors: expert-batched gather and dense
-// calls on the 16x16x32 bf16 matrix cores (qmv_k_mxfp4b.hip): [4 waves and
-// 128 rows per tile, 8 waves and 256 rows per tile].
+// calls on the 16x16x32 bf16 matrix cores (qmv_k_mxfp4b.hip): 4-wave
+// workgroups, [128, 256] rows per tile.
 namespace qmv {
 extern const void *const kTableBatched[2];
 }
@@ -392,13 +392,17 @@ size_t dense4_lds(int K, int waves)
     return 256 * (rsb + 1) + 16 * ((waves * 4 * rsb + 30) / 16);
 }
 
-// Batched MXFP4 x bf16 (M > 4): LDS of one workgroup = one 128-weight
-// slice of 128 vectors (32 KB), then the routing tables (count, vector
-// offset and tile offset per bucket, wave totals) and the sorted pair list.
+// Batched MXFP4 x bf16 (M > 4): LDS of one workgroup = a ring of 4
+// activation slice buffers (128 weights of 128 vectors, 32 KB each), then
+// the routing tables (count, vector offset and tile offset per bucket, wave
+// totals) and the sorted pair list: at most 128 + 12 + 16 KB.
 size_t batched_lds(int buckets, int pairs)
 {
-    return (size_t)128 * 256 + 12 * (size_t)(buckets + 1) + 64 + (((size_t)2 * pairs + 15) & ~(size_t)15);
+    return (size_t)4 * 128 * 256 + 12 * (size_t)(buckets + 1) + 64 + (((size_t)2 * pairs + 15) & ~(size_t)15);
 }
+
+std::once_flag g_b_once[2];
+hipError_t g_b_err[2];
 
 int g_cu_count[64];
 std::once_flag g_cu_once[64];
@@ -419,10 +423,9 @@ int cu_count()
 // Grid: a tile is (expert, row tile) for a gather and (chunk of <= 128
 // vectors, row tile) for a dense call; the ids are read on the device, so
 // the host bounds the tile count by row tiles x min(pairs, buckets) and
-// launches at most one 8-wave or two 4-wave workgroups per CU, each looping
-// over tiles.  8-wave workgroups (256-row tiles, two waves per SIMD) read
-// the activations half as often per weight byte; they are taken when they
-// still give every CU a tile.
+// launches one workgroup per CU (its LDS ring takes 128 KB), each looping
+// over tiles.  256-row tiles stage the activations half as often per weight
+// byte; they are taken when they still give every CU a tile.
 qmv_status_t launch_batched(const void *codes, const void *scales, int E, const int32_t *ids, int M,
                             int top_k, const void *x, int x_per_slot, float *y, int N, int K,
                             hipStream_t stream)
@@ -438,11 +441,17 @@ qmv_status_t launch_batched(const void *codes, const void *scales, int E, const 
     const int rfi = nt4 * groups >= cus ? 1 : 0;
     const long long nt = rfi ? nt4 : (N + 127) / 128;
     long long upper = nt * groups;
-    if (upper > (rfi ? 1LL : 2LL) * cus) upper = (rfi ? 1LL : 2LL) * cus;
+    if (upper > cus) upper = cus;
     upper = (upper + 7) & ~7LL;                    // the kernel deals tiles to 8 XCDs
     const void *fn = kTableBatched[rfi];
+    std::call_once(g_b_once[rfi], [&] {
+        g_b_err[rfi] = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           batched_lds(kMaxEBatched + 1, kMaxPairsBatched));
+    });
+    if (g_b_err[rfi] != hipSuccess)
+        return QMV_EHIP;
     void *kargs[] = {&a};
-    if (hipLaunchKernel(fn, dim3((unsigned)upper), dim3(rfi ? 512 : 256), kargs, batched_lds(buckets, pairs), stream) !=
+    if (hipLaunchKernel(fn, dim3((unsigned)upper), dim3(256), kargs, batched_lds(buckets, pairs), stream) !=
         hipSuccess)
         return QMV_EHIP;
     return QMV_OK;

@@ -57,7 +57,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBVecMax = 128;           // vectors per tile: 8 column fragments of 16
-constexpr int kBXBytes = kBVecMax * 256;
+constexpr int kBXBytes = kBVecMax * 256;     // one activation slice buffer
+constexpr int kBAhead = 3;                     // slices loaded ahead of the one multiplied
+constexpr int kBRing = kBAhead + 1;            // activation slice buffers in LDS
+
+// s_waitcnt immediate (gfx9 layout) that waits for vmcnt <= N only.
+template <int N> struct kVmcnt {
+    static constexpr int enc = (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
+};
 constexpr uint32_t kBPast = 0x80000000u;   // >= every buffer size: reads zeros
 
 // LDS offset of 16-byte chunk pos (k = 8 pos .. 8 pos + 7 of the slice) of tile vector v.
@@ -88,7 +95,7 @@ __device__ __forceinline__ int tiles_of(int c, int nt, bool chunk_tiles)
 // 1, 253, 254 and 255 come out as they should).  One output per thread at a
 // time, plain loads: slow, and only run for chunks whose weights hold a scale
 // byte outside [2, 252].
-__device__ __noinline__ void batched_chunk_exact(const Args &a, const uint8_t *codes, const uint8_t *scales,
+__device__ __forceinline__ void batched_chunk_exact(const Args &a, const uint8_t *codes, const uint8_t *scales,
                                                  const uint16_t *vecs, int nv, int row_lo, int rows)
 {
     const bool gather = a.ids != nullptr;
@@ -114,13 +121,13 @@ __device__ __noinline__ void batched_chunk_exact(const Args &a, const uint8_t *c
 }
 
 template <int RF, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void qmv_batched_kernel(const Args a)
+__global__ __launch_bounds__(64 * WAVES, 1) void qmv_batched_kernel(const Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int kBThreads = 64 * WAVES;
     constexpr int TR = 16 * RF * WAVES;            // rows per tile
     constexpr int BPT = 1024 / kBThreads;          // scan buckets per thread
-    constexpr int XJ = 2048 / kBThreads;           // 16-byte staging chunks per thread and slice
+    constexpr int XJ = 32 / WAVES;                 // staging instructions (4 vectors each) per wave and slice
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -133,7 +140,7 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_kernel(const Args a)
     const int U = a.units;                         // 32-weight blocks per row
     const int S = (U + 3) >> 2;                    // 128-weight slices
 
-    int *const cnt = (int *)(lds + kBXBytes);
+    int *const cnt = (int *)(lds + kBRing * kBXBytes);
     int *const voff = cnt + (nb + 1);
     int *const toff = voff + (nb + 1);
     int *const wsum = toff + (nb + 1);             // 2 x 8 wave totals
@@ -189,8 +196,7 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_kernel(const Args a)
     __syncthreads();
     const int total = toff[nb];
 
-    const long long x_bytes = (long long)(gather && a.x_per_slot ? B : a.M) * a.x_vec_bytes;
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, x_bytes);
+    const int x_bytes = (gather && a.x_per_slot ? B : a.M) * a.x_vec_bytes;   // < 2^31
     const bool vec4 = (a.N & 3) == 0 && ((uintptr_t)a.y & 15) == 0;
 
     // Workgroups are dealt to the 8 XCDs in turn (workgroup b to XCD b % 8;
@@ -239,13 +245,19 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_kernel(const Args a)
                     oc[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rcb + 16u * q : kBPast;
                     os[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rsb + q : kBPast;
                 }
-                // activation rows of this thread's staging chunks: vectors tid/16 + (threads/16) j,
-                // k-chunk tid%16
-                const int pos = tid & 15;
+                // Activation staging: direct loads from global memory into a ring
+                // of kBRing LDS slice buffers (each lane's 16 bytes land at the
+                // instruction's LDS base + 16 * lane).  One instruction fills 4
+                // vectors x 256 bytes; wave w issues the vector quads w + WAVES j.
+                // Lane 16 h + p of quad d fills slot p of vector 4 d + h with the
+                // chunk the swizzle puts there, k-chunk p ^ (vector & 15).
+                const int wv = __builtin_amdgcn_readfirstlane(w);
                 uint32_t xo[XJ];
+                int xpos[XJ];
 #pragma unroll
                 for (int j = 0; j < XJ; ++j) {
-                    const int v = (tid >> 4) + (kBThreads / 16) * j;
+                    const int v = 4 * (wv + WAVES * j) + (lane >> 4);
+                    xpos[j] = (lane & 15) ^ (v & 15);
                     uint32_t o = kBPast;
                     if (v < nv) {
                         const int i = perm[vstart + v];
@@ -254,22 +266,17 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_kernel(const Args a)
                     }
                     xo[j] = o;
                 }
-
-                auto load_x = [&](int s, uint4 (&xr)[XJ]) {
-                    const int k = 128 * s + 8 * pos;
+                auto issue_x = [&](int s) {
+                    // (built here from kernel arguments, so it stays in scalar registers)
+                    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, x_bytes);
+                    uint8_t *const buf = lds + (s % kBRing) * kBXBytes;
 #pragma unroll
                     for (int j = 0; j < XJ; ++j) {
+                        const int k = 128 * s + 8 * xpos[j];
                         const uint32_t o = (k < a.K && xo[j] != kBPast) ? xo[j] + 2u * k : kBPast;
-                        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
-                        xr[j] = make_uint4(v[0], v[1], v[2], v[3]);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rx, (__attribute__((address_space(3))) void *)(buf + 1024 * (wv + WAVES * j)), 16, o, 0, 0, 0);
                     }
-                };
-                // every row of the buffer, used or not (unconditional stores keep
-                // the loads ahead of them; unused rows hold zeros)
-                auto put_x = [&](const uint4 (&xr)[XJ]) {
-#pragma unroll
-                    for (int j = 0; j < XJ; ++j)
-                        *(uint4 *)(lds + bx_off((tid >> 4) + (kBThreads / 16) * j, pos)) = xr[j];
                 };
                 auto load_w = [&](int s, u32x4 (&wc)[RF], uint8_t (&sb)[RF]) {
                     const bool ok = s < S && 4 * s + q < U;
@@ -288,6 +295,7 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_kernel(const Args a)
                 int slow = 0;
                 auto compute = [&](int s, const u32x4 (&wc)[RF], const uint8_t (&sbr)[RF]) {
                     const bool ok = 4 * s + q < U;
+                    const uint8_t *const buf = lds + (s % kBRing) * kBXBytes;
                     bf16x8 A[RF][4];
 #pragma unroll
                     for (int f = 0; f < RF; ++f) {
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_kernel(const Args a)
                             bf16x8 Bv[4];
 #pragma unroll
                             for (int k = 0; k < 4; ++k)
-                                Bv[k] = __builtin_bit_cast(bf16x8, lds_read16(lds + bx_off(16 * g + r, 4 * q + k)));
+                                Bv[k] = __builtin_bit_cast(bf16x8, lds_read16(buf + bx_off(16 * g + r, 4 * q + k)));
 #pragma unroll
                             for (int f = 0; f < RF; ++f)
 #pragma unroll
@@ -312,37 +320,45 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_kernel(const Args a)
                         }
                     }
                 };
+                // Top of slice s: this wave's loads of slice s are done once at
+                // most kAfter of its later loads are outstanding (loads complete
+                // in issue order, and every slice issues the same number); the
+                // barrier then covers the other waves' parts of the buffer.
+                constexpr int kAfter = 2 * RF + (kBAhead - 1) * (XJ + 2 * RF);
+                static_assert(kAfter < 64, "vmcnt holds at most 63");
+                auto slice_ready = [&]() {
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_waitcnt(kVmcnt<kAfter>::enc);
+                    __syncthreads();
+                };
 
-                // 3. slices.  Loads complete in issue order, so waiting for the
-                //    activations of slice s + 1 also waits for everything issued
-                //    before them: they are issued two slices ahead (two register
-                //    sets), ahead of the weights of slice s + 1, which then have
-                //    two slices of time as well.
-                u32x4 wc0[RF], wc1[RF];
-                uint8_t sb0[RF], sb1[RF];          // widened only where used
-                uint4 xr0[XJ], xr1[XJ];
-                load_x(0, xr0);
+                // 3. slices, kBAhead (3) ahead for activations and weights alike;
+                //    the slice count is padded to a multiple of 3 (the padding
+                //    reads past the buffers: zeros).
+                u32x4 wc0[RF], wc1[RF], wc2[RF];
+                uint8_t sb0[RF], sb1[RF], sb2[RF];   // widened only where used
+                issue_x(0);
                 load_w(0, wc0, sb0);
-                load_x(1, xr1);
+                issue_x(1);
                 load_w(1, wc1, sb1);
-                put_x(xr0);
-                __syncthreads();
-                // (an odd slice count gets one more slice of zeros: no branch
-                // inside the loop, so no join the compiler must wait at)
-                for (int s = 0; s < S; s += 2) {
-                    load_x(s + 2, xr0);
+                issue_x(2);
+                load_w(2, wc2, sb2);
+                for (int s = 0; s < S; s += 3) {
+                    slice_ready();
+                    issue_x(s + 3);
                     compute(s, wc0, sb0);
-                    load_w(s + 2, wc0, sb0);
-                    __syncthreads();
-                    put_x(xr1);
-                    __syncthreads();
-                    load_x(s + 3, xr1);
+                    load_w(s + 3, wc0, sb0);
+                    slice_ready();
+                    issue_x(s + 4);
                     compute(s + 1, wc1, sb1);
-                    load_w(s + 3, wc1, sb1);
-                    __syncthreads();
-                    put_x(xr0);
-                    __syncthreads();
+                    load_w(s + 4, wc1, sb1);
+                    slice_ready();
+                    issue_x(s + 5);
+                    compute(s + 2, wc2, sb2);
+                    load_w(s + 5, wc2, sb2);
                 }
+                // the ring's last loads land before the next chunk reuses it
+                __builtin_amdgcn_s_waitcnt(kVmcnt<0>::enc);
                 if (__syncthreads_or(slow)) {
                     const int e = gather ? b : 0;
                     batched_chunk_exact(a, a.codes + (long long)e * a.expert_cb, a.scales + (long long)e * a.expert_sb,
@@ -376,9 +392,10 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_kernel(const Args a)
     }
 }
 
-// [128 rows per tile (2 fragments x 4 waves), 256 rows per tile (2 fragments x 8 waves)]
+// 4 waves (one per SIMD: all 512 registers of a lane), [128 rows per tile
+// (2 fragments per wave), 256 rows per tile (4 fragments per wave)]
 extern const void *const kTableBatched[2];
 const void *const kTableBatched[2] = {(const void *)&qmv_batched_kernel<2, 4>,
-                                      (const void *)&qmv_batched_kernel<2, 8>};
+                                      (const void *)&qmv_batched_kernel<4, 4>};
 
 }  // namespace qmv
