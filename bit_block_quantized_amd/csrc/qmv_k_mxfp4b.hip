@@ -4,8 +4,8 @@
 //
 // With many vectors per expert the work is a grouped matrix product: each
 // expert's weight rows meet every vector routed to it (mlxcel issue,
-// "Background": the expert-batched gather_qmm path that prefill takes once
-// enough tokens share each expert).  Every workgroup first sorts the call's
+// "Problem / Background": the expert-batched gather_qmm path that prefill
+// takes once enough tokens share each expert).  Every workgroup first sorts the call's
 // (token, slot) pairs by expert in LDS (a counting sort over the ids: count,
 // prefix-sum, place), so nothing is allocated and no second launch is needed.
 // The sorted list defines the tiles:
@@ -39,11 +39,12 @@
 // Activations: per slice, every workgroup stages the tile's vectors' 128
 // bf16 values into LDS (256 bytes per vector; chunk index xor-ed with the
 // vector's low 4 bits so that the 16 lanes of one ds_read_b128 quarter hit
-// 16 distinct bank groups).  Weight loads run two slices ahead; the next
-// slice's activations are loaded into registers while the current slice
-// multiplies.  Loads complete in issue order, so the activations are loaded
-// two slices ahead into two register sets, before the weight loads of the
-// next slice: waiting for them never waits for weights not yet needed.
+// 16 distinct bank groups), with direct global-to-LDS loads into a ring of
+// four slice buffers.  Loads complete in issue order per wave, so a load's
+// lead can be no longer than that of the loads waited on after it: the
+// activations and the weights of a slice are issued together, three slices
+// ahead, each slice starts with one wait on the wave's own loads and a
+// barrier, and no register holds staged activations.
 //
 // Every output element is one MFMA column's dot product over the whole of K
 // in a fixed order, so results do not depend on where a vector lands in the

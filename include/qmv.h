@@ -79,7 +79,9 @@
  * scales, x_scales, expert ids and y 4 bytes.
  *
  * Limits: 1 <= M <= 4, 1 <= top_k <= 16, K % 32 == 0, 32 <= K <= 16384,
- * N >= 1, E >= 1.
+ * N >= 1, E >= 1.  qmv_dense and qmv_gather_moe with (MXFP4, BF16) also take
+ * M > 4 (a prefill chunk or a wide verify batch), up to 8192 (token, slot)
+ * pairs (M for a dense call, M * top_k for a gather) and E <= 1023.
  *
  * Errors: arguments are checked on the host before anything is launched; on
  * a failed check the call returns the status, launches nothing and leaves y
@@ -116,6 +118,8 @@ typedef enum {
  *   x, x_scales        M activation vectors ([M][K], [M][K/32])
  *   y                  fp32 [M][N]
  * This is the gather below with one expert, top_k = 1 and ids all 0.
+ * With (MXFP4, BF16) and M > 4 it runs on the batched matrix-core kernel
+ * described under qmv_gather_moe.
  */
 qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
                        qmv_afmt_t afmt, const void *x, const void *x_scales,
@@ -133,6 +137,12 @@ qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scale
  *   y           fp32 [M][top_k][N]
  * Each distinct expert's weights are streamed from memory once per call and
  * applied to every activation vector routed to it (up to four per pass).
+ * With (MXFP4, BF16) and M > 4 (the expert-batched product that prefill
+ * takes once many tokens share each expert: mlxcel issue, "Problem / Background"),
+ * every workgroup sorts the (token, slot) pairs by expert in LDS and
+ * multiplies each expert's rows with all of its vectors, up to 128 at a
+ * time, on the 16x16x32 bf16 matrix cores; the result is the same
+ * definition, within the same tolerance, and bitwise repeatable.
  */
 qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales, int E,
                             const int32_t *expert_ids, int M, int top_k,
