@@ -161,3 +161,9 @@ def test_prefill_chunk_full_size_sampled():
                           [r * wl.N + np.arange(wl.N) for r in rows])
     yr, A = oracle_call(inp, outs=outs)
     assert_parity(y[outs], yr, A, "C6 sampled")
+
+
+def test_gather_tall_tiles():
+    """Enough (expert, row tile) tiles for the 192-row kernel (one per CU and
+    more), with a ragged last tile and N % 4 != 0 (element-wise stores)."""
+    _check(synth.make(_wl("gather", 96, 1001, 256, E=48, top_k=4, seed=101)), "192-row tiles")
