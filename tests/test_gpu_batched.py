@@ -167,3 +167,17 @@ def test_gather_tall_tiles():
     """Enough (expert, row tile) tiles for the 192-row kernel (one per CU and
     more), with a ragged last tile and N % 4 != 0 (element-wise stores)."""
     _check(synth.make(_wl("gather", 96, 1001, 256, E=48, top_k=4, seed=101)), "192-row tiles")
+
+
+def test_every_id_invalid_gives_zeros():
+    inp = synth.make(_wl("gather", 40, 77, 128, E=5, top_k=3, seed=111))
+    inp.ids[...] = -7
+    out = torch.full((40, 3, 77), float("nan"), device="cuda")
+    y = gpu_call(inp, y=out).cpu().numpy()
+    assert (y == 0).all()
+
+
+def test_pair_limit_per_slot():
+    """8192 (token, slot) pairs, one activation vector each."""
+    _check(synth.make(_wl("gather", 1024, 12, 64, E=24, top_k=8, x_per_slot=True, seed=121)),
+           "8192 per-slot pairs")
