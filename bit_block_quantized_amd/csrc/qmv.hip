@@ -44,8 +44,8 @@ extern const void *const kTableDense4[2];
 }
 
 // MXFP4 x bf16 with more than 4 vectors: expert-batched gather and dense
-// calls on the 16x16x32 bf16 matrix cores (qmv_k_mxfp4b.hip): 4-wave
-// workgroups, [128, 192] rows per tile.
+// calls on the 16x16x32 bf16 matrix cores (qmv_k_mxfp4b.hip): [4 waves and
+// 128 rows, 8 waves and 256 rows] per tile.
 namespace qmv {
 extern const void *const kTableBatched[2];
 }
@@ -424,11 +424,11 @@ int cu_count()
 // vectors, row tile) for a dense call; the ids are read on the device, so
 // the host bounds the tile count by row tiles x min(pairs, buckets) and
 // launches one workgroup per CU (its LDS ring takes 128 KB), each looping
-// over tiles.  Taller tiles restage the activations less often per weight
-// byte, shorter ones balance the CUs better; measured on the 512-token
-// gpt-oss prefill chunk (32 experts, K = N = 2880): 256-row tiles (384)
-// 119 us, 128-row tiles (736) 103 us, 192-row tiles (480) 97 us.  192-row
-// tiles are taken when they give every CU at least one.
+// over tiles.  Measured on the 512-token gpt-oss prefill chunk (32 experts,
+// K = N = 2880), 4-wave workgroups: 256-row tiles (384) 119 us, 128-row
+// (736) 103 us, 192-row (480) 97 us; 8-wave workgroups with 256-row tiles
+// (two waves per SIMD hide each other's LDS and matrix-core latencies)
+// 91 us.  The 8-wave shape is taken when it gives every CU a tile.
 qmv_status_t launch_batched(const void *codes, const void *scales, int E, const int32_t *ids, int M,
                             int top_k, const void *x, int x_per_slot, float *y, int N, int K,
                             hipStream_t stream)
@@ -440,9 +440,9 @@ qmv_status_t launch_batched(const void *codes, const void *scales, int E, const 
     const int buckets = gather ? E + 1 : 1;
     const long long groups = gather ? (pairs < buckets ? pairs : buckets) : (pairs + 127) / 128;
     const int cus = cu_count();
-    const long long nt3 = (N + 191) / 192;
-    const int rfi = nt3 * groups >= cus ? 1 : 0;
-    const long long nt = rfi ? nt3 : (N + 127) / 128;
+    const long long nt8 = (N + 255) / 256;
+    const int rfi = nt8 * groups >= cus ? 1 : 0;
+    const long long nt = rfi ? nt8 : (N + 127) / 128;
     long long upper = nt * groups;
     if (upper > cus) upper = cus;
     upper = (upper + 7) & ~7LL;                    // the kernel deals tiles to 8 XCDs
@@ -454,7 +454,7 @@ qmv_status_t launch_batched(const void *codes, const void *scales, int E, const 
     if (g_b_err[rfi] != hipSuccess)
         return QMV_EHIP;
     void *kargs[] = {&a};
-    if (hipLaunchKernel(fn, dim3((unsigned)upper), dim3(256), kargs, batched_lds(buckets, pairs), stream) !=
+    if (hipLaunchKernel(fn, dim3((unsigned)upper), dim3(rfi ? 512 : 256), kargs, batched_lds(buckets, pairs), stream) !=
         hipSuccess)
         return QMV_EHIP;
     return QMV_OK;

@@ -393,10 +393,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void qmv_batched_kernel(const Args a
     }
 }
 
-// 4 waves (one per SIMD: all 512 registers of a lane), [128 rows per tile
-// (2 fragments per wave), 192 rows per tile (3 fragments per wave)]
+// [4 waves x 2 fragments: 128 rows per tile, 8 waves x 2 fragments: 256 rows
+// per tile (two waves per SIMD)]
 extern const void *const kTableBatched[2];
 const void *const kTableBatched[2] = {(const void *)&qmv_batched_kernel<2, 4>,
-                                      (const void *)&qmv_batched_kernel<3, 4>};
+                                      (const void *)&qmv_batched_kernel<2, 8>};
 
 }  // namespace qmv

@@ -164,9 +164,10 @@ def test_prefill_chunk_full_size_sampled():
 
 
 def test_gather_tall_tiles():
-    """Enough (expert, row tile) tiles for the 192-row kernel (one per CU and
-    more), with a ragged last tile and N % 4 != 0 (element-wise stores)."""
-    _check(synth.make(_wl("gather", 96, 1001, 256, E=48, top_k=4, seed=101)), "192-row tiles")
+    """Enough (expert, row tile) tiles for the 8-wave 256-row kernel (one per
+    CU and more), with a ragged last tile and N % 4 != 0 (element-wise
+    stores)."""
+    _check(synth.make(_wl("gather", 96, 1281, 256, E=48, top_k=4, seed=101)), "256-row tiles")
 
 
 def test_every_id_invalid_gives_zeros():
