@@ -5,12 +5,12 @@
 // With many vectors per expert the work is a grouped matrix product: each
 // expert's weight rows meet every vector routed to it (mlxcel issue,
 // "Problem / Background": the expert-batched gather_qmm path that prefill
-// takes once enough tokens share each expert).  Every workgroup first sorts the call's
-// (token, slot) pairs by expert in LDS (a counting sort over the ids: count,
-// prefix-sum, place), so nothing is allocated and no second launch is needed.
-// The sorted list defines the tiles:
+// takes once enough tokens share each expert).  Every workgroup first sorts
+// the call's (token, slot) pairs by expert in LDS (a counting sort over the
+// ids: count, prefix-sum, place), so nothing is allocated and no second
+// launch is needed.  The sorted list defines the tiles:
 //
-//   tile = (expert, 64*RF weight rows);
+//   tile = (expert, 16 * RF * WAVES weight rows);
 //
 // the workgroup multiplies the tile's rows with all of the expert's vectors,
 // in chunks of at most 128 (equal chunks when an expert has more).  The LDS
