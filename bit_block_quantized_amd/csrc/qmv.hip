@@ -63,6 +63,9 @@ constexpr int kMaxTopK = 16;
 // sorted in LDS, 16-bit indices, one bucket per expert plus one for ids
 // outside [0, E).
 constexpr int kMaxPairsBatched = 8192;
+// Dense MXFP4 x bf16 calls with 5..20 vectors run as groups of 4 on the
+// decode kernels (one expert gives the batched kernel too few tiles).
+constexpr int kDenseGroupsMaxM = 20;
 constexpr int kMaxEBatched = 1023;
 
 // Kernels for bf16 activations quantized in staging (2-bit and 3-bit weights).
@@ -495,6 +498,23 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
     const bool gather = ids != nullptr;
     const bool gate_up = codes2 != nullptr;
     const int kind = kind_of(wfmt, afmt, K);
+    if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM && M <= kDenseGroupsMaxM) {
+        // A dense call with a few more than 4 vectors: groups of up to 4 on
+        // the decode kernels, each a launch over its own rows of x and y.
+        // A dense call is one expert, so the batched kernel has only N / 128
+        // tiles for it (56 workgroups for N = 7168): measured on 7168 x 7168,
+        // 4 vectors 8.75 us, 5 to 16 vectors 52-53 us batched, against
+        // 8.75 us per group of 4 here.
+        for (int m0 = 0; m0 < M; m0 += kMaxM) {
+            const int mg = M - m0 < kMaxM ? M - m0 : kMaxM;
+            const qmv_status_t st = launch(wfmt, afmt, codes, scales, nullptr, nullptr, 1, nullptr, mg, 1,
+                                           (const uint8_t *)x + (size_t)m0 * K * 2, nullptr, 0,
+                                           y + (size_t)m0 * N, N, K, stream);
+            if (st != QMV_OK)
+                return st;
+        }
+        return QMV_OK;
+    }
     if (!gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM)
         return launch_batched(codes, scales, E, ids, M, top_k, x, x_per_slot, y, N, K, stream);
     if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M >= 2)

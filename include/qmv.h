@@ -118,8 +118,9 @@ typedef enum {
  *   x, x_scales        M activation vectors ([M][K], [M][K/32])
  *   y                  fp32 [M][N]
  * This is the gather below with one expert, top_k = 1 and ids all 0.
- * With (MXFP4, BF16) and M > 4 it runs on the batched matrix-core kernel
- * described under qmv_gather_moe.
+ * With (MXFP4, BF16), 5 <= M <= 20 runs as groups of up to 4 vectors on the
+ * 4-vector kernels (one launch per group), and M > 20 on the batched
+ * matrix-core kernel described under qmv_gather_moe.
  */
 qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
                        qmv_afmt_t afmt, const void *x, const void *x_scales,
