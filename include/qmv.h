@@ -143,7 +143,10 @@ qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scale
  * every workgroup sorts the (token, slot) pairs by expert in LDS and
  * multiplies each expert's rows with all of its vectors, up to 128 at a
  * time, on the 16x16x32 bf16 matrix cores; the result is the same
- * definition, within the same tolerance, and bitwise repeatable.
+ * definition, within the same tolerance, and bitwise repeatable.  A call
+ * with at most 64 tokens and fewer than two (token, slot) pairs per expert
+ * (M * top_k < 2 E) reuses too few weights for that: it runs as groups of
+ * up to 4 tokens on the decode kernels, one launch per group.
  */
 qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales, int E,
                             const int32_t *expert_ids, int M, int top_k,

@@ -182,3 +182,21 @@ def test_pair_limit_per_slot():
     """8192 (token, slot) pairs, one activation vector each."""
     _check(synth.make(_wl("gather", 1024, 12, 64, E=24, top_k=8, x_per_slot=True, seed=121)),
            "8192 per-slot pairs")
+
+
+@pytest.mark.parametrize("M,top_k,E,per_slot", [(5, 4, 256, False), (8, 4, 256, False),
+                                                (6, 2, 64, True), (64, 4, 256, False)])
+def test_gather_few_pairs_per_expert(M, top_k, E, per_slot):
+    """Fewer than two pairs per expert: groups of up to 4 tokens on the decode
+    kernels (a ragged last group included), broadcast and per-slot x."""
+    _check(synth.make(_wl("gather", M, 40, 256, E=E, top_k=top_k, x_per_slot=per_slot, seed=131 + M)),
+           f"few pairs M={M} top_k={top_k} E={E}")
+
+
+def test_gather_few_pairs_invalid_ids():
+    inp = synth.make(_wl("gather", 7, 33, 160, E=100, top_k=3, seed=141))
+    inp.ids[5, 1] = -1
+    inp.ids[6, :] = 100
+    y = gpu_call(inp).cpu().numpy()
+    assert (y[5, 1] == 0).all() and (y[6] == 0).all()
+    _check(inp, "few pairs, invalid ids")
