@@ -230,9 +230,76 @@ class Prepared:
             raise RuntimeError(f"{self.name}: probe status {s}")
 
 
-def time_graph(fn, first, count):
+_FLUSH = {}
+
+
+def flush_caches(stream):
+    """Read 512 MiB of memory that no workload touches (the stream probe over
+    a buffer of its own), so that neither L2 nor the 256 MB Infinity Cache
+    holds any weights when a timed replay starts."""
+    import torch
+
+    import bit_block_quantized_amd as q
+    if "buf" not in _FLUSH:
+        _FLUSH["buf"] = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+        _FLUSH["sink"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+        base, n = _FLUSH["buf"].data_ptr(), 4
+        _FLUSH["regions"] = [(base + r * (128 << 20), 128 << 20) for r in range(n)]
+    q.qmv_probe_stream_read(_FLUSH["regions"], 3, _FLUSH["sink"], stream=stream)
+
+
+class ClockSampler:
+    """Polls the shader and memory clock levels (sysfs pp_dpm_sclk and
+    pp_dpm_mclk, the level in use marked '*') from a host thread while the
+    timed work runs; reports each level seen with its sample count."""
+
+    def __init__(self):
+        import glob
+        import threading
+        self.files = [f for d in sorted(glob.glob("/sys/class/drm/card*/device"))
+                      for f in (os.path.join(d, "pp_dpm_sclk"), os.path.join(d, "pp_dpm_mclk"))
+                      if os.path.exists(f)]
+        self.seen = {}
+        self.n = 0
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set() and self.files:
+            for f in self.files:
+                try:
+                    with open(f) as fh:
+                        cur = [ln.strip() for ln in fh if ln.strip().endswith("*")]
+                except OSError:
+                    continue
+                key = (os.path.basename(os.path.dirname(os.path.dirname(f))) + ":" +
+                       os.path.basename(f), cur[0] if cur else None)
+                self.seen[key] = self.seen.get(key, 0) + 1
+            self.n += 1
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+
+    def report(self):
+        if not self.files:
+            return None
+        out = {}
+        for (f, lvl), c in sorted(self.seen.items(), key=lambda kv: str(kv[0])):
+            out.setdefault(f, {})[str(lvl)] = c
+        return {"sampled_during_timed_replay": out, "polls": self.n}
+
+
+def time_graph(fn, first, count, clocks=None):
     """Capture fn(i, stream) for i in [first, first+count) into one graph,
-    replay it once (untimed), then replay it timed.  Returns seconds per call."""
+    replay it once (untimed: graph upload, clocks up), read 512 MiB of
+    unrelated memory so no cache holds the weights, then replay it timed.
+    Returns seconds per call.  ``clocks`` (a ClockSampler) polls the clock
+    levels during the timed replay."""
     import torch
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
@@ -250,11 +317,16 @@ def time_graph(fn, first, count):
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(s):
+        flush_caches(s)
         torch.cuda.synchronize()
+        if clocks is not None:
+            clocks.__enter__()
         e0.record(s)
         g.replay()
         e1.record(s)
     torch.cuda.synchronize()
+    if clocks is not None:
+        clocks.__exit__(None, None, None)
     return e0.elapsed_time(e1) * 1e-3 / count
 
 
@@ -285,14 +357,59 @@ def stream_ceiling(p, first, count):
     return best
 
 
-def measure(name, steps, warmup, hot=True):
+def stream_sweep(sizes_mib=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024)):
+    """Time the read-only stream probe over one region of S bytes for a range
+    of S (best of its launch shapes, each call on a fresh part of a 2 GiB
+    buffer so no cache holds it), and fit t = t0 + S / BW by least squares
+    over S >= 4 MiB: t0 is the fixed cost of one launch (dispatch, first
+    request's latency, drain) and BW the streaming bandwidth."""
+    import torch
+
+    import bit_block_quantized_amd as q
+    total = 2 << 30
+    buf = torch.zeros(total, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    base = buf.data_ptr()
+    rows = []
+    for mib in sizes_mib:
+        size = mib << 20
+        slots = total // size
+        calls = max(20, min(400, (8 << 30) // size))
+
+        def probe(i, h, v, size=size, slots=slots):
+            ptrs = (ctypes.c_void_p * 1)(base + (i % slots) * size)
+            sizes = (ctypes.c_longlong * 1)(size)
+            s = q.lib().qmv_probe_stream_read(1, ptrs, sizes, v, sink.data_ptr(), ctypes.c_void_p(h))
+            if s != 0:
+                raise RuntimeError(f"probe status {s}")
+        best = None
+        for v in range(q.PROBE_VARIANTS):
+            t = time_graph(lambda i, h: probe(i, h, v), 0, calls)
+            if best is None or t < best[0]:
+                best = (t, v)
+        rows.append({"MiB": mib, "us": round(best[0] * 1e6, 3),
+                     "GBps": round(size / best[0] / 1e9, 1), "variant": best[1]})
+        print(f"stream sweep {mib} MiB: {best[0] * 1e6:.3f} us, {size / best[0] / 1e9:.1f} GB/s",
+              file=sys.stderr, flush=True)
+    fit = [r for r in rows if r["MiB"] >= 4]
+    S = np.array([r["MiB"] * 1048576.0 for r in fit])
+    T = np.array([r["us"] * 1e-6 for r in fit])
+    A = np.stack([np.ones_like(S), S], axis=1)
+    (t0, inv_bw), *_ = np.linalg.lstsq(A, T, rcond=None)
+    return {"sweep": rows, "fit": {"t0_us": round(t0 * 1e6, 3), "BW_GBps": round(1.0 / inv_bw / 1e9, 1),
+                                   "over": "S >= 4 MiB"}}
+
+
+def measure(name, steps, warmup, hot=True, clocks=None):
     """Cold (rotated) timing of the workload, then the stream ceiling for the
     same calls, the hot-cache timing and the eager-launch timing."""
     import torch
+    print(f"bench: {name}: preparing inputs", file=sys.stderr, flush=True)
     p = Prepared(name, warmup + steps)
+    print(f"bench: {name}: timing {steps} calls", file=sys.stderr, flush=True)
     if warmup:
         time_graph(p.call, 0, warmup)
-    t = time_graph(p.call, warmup, steps)
+    t = time_graph(p.call, warmup, steps, clocks=clocks)
     sel = slice(warmup, warmup + steps)
     wb = float(p.wbytes[sel].mean())
     ab = float(p.abytes[sel].mean())
@@ -378,8 +495,8 @@ def cpu_baseline(p, target_s=10.0, threads=None):
 
 
 def gpu_clocks():
-    """Shader and memory clock levels from sysfs (plain file reads; the level
-    in use is marked '*'), or None where the driver does not expose them."""
+    """Shader and memory clock levels from sysfs after the run: (level marked
+    in use, highest level), or None where the driver does not expose them."""
     import glob
     out = {}
     for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
@@ -406,6 +523,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-hot", action="store_true")
+    ap.add_argument("--stream-sweep", action="store_true",
+                    help="only time the read-only stream probe over sizes 1 MiB..1 GiB and fit "
+                         "t = t0 + bytes/BW (prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library is a single-GPU operator "
@@ -414,8 +534,12 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if args.stream_sweep:
+        print(json.dumps({"stream_sweep": stream_sweep()}), flush=True)
+        return
 
-    p, head = measure(HEADLINE, args.steps, args.warmup, hot=not args.no_hot)
+    clocks = ClockSampler()
+    p, head = measure(HEADLINE, args.steps, args.warmup, hot=not args.no_hot, clocks=clocks)
     extra = {}
     if not args.no_extra:
         for name in [w for w in args.workloads.split(",") if w and w != HEADLINE]:
@@ -444,7 +568,8 @@ def main():
                         "x bf16 -> f32, 4 of 32 experts, 1 token, K=N=2880",
             "E": 32, "top_k": 4, "M": 1, "N": 2880, "K": 2880,
             "layers_rotated": head["layers_rotated"],
-            "timing": "HIP graph of the K calls, HIP events on the replay stream",
+            "timing": "HIP graph of the K calls, HIP events on the replay stream; 512 MiB of "
+                      "unrelated memory read just before the timed replay",
         },
         "us_per_call": round(head["us_per_call"], 3),
         "pct_hbm_peak": round(head["pct_hbm_peak"], 2),
@@ -474,7 +599,8 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
         out["cpu_baseline_1thread"] = cpu_baseline(p, args.cpu_seconds / 2, threads=1)
-    out["gpu_clocks"] = gpu_clocks()
+    out["gpu_clocks"] = clocks.report()
+    out["gpu_clock_levels"] = gpu_clocks()
     print(json.dumps(out), flush=True)
 
 

@@ -124,17 +124,102 @@ def _afmt(w, x):
     return A_Q8B32, (torch.int8,)
 
 
-def qmv_dense(wfmt, w_codes, w_scales, x, x_scales=None, y=None, stream=None):
-    """Dense GEMV: y[m][n] = sum_k w(n,k) x(m,k); returns y (float32 [M][N])."""
-    w = _wfmt(wfmt)
-    dev = w_codes.device
+def _row_bytes(w, K):
+    """(code bytes, scale bytes) of one weight row of K weights."""
+    if w == W_MXFP4:
+        return K // 2, K // 32
+    if w == W_CB2:
+        return K // 4, 2 * (K // 32)
+    return 3 * K // 8, 2 * (K // 16)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_weights(w, codes, scales, lead, K, what=("w_codes", "w_scales")):
+    """codes/scales hold exactly the rows the kernel will address: leading
+    dimensions ``lead`` ((E, N) or (N,)) and the row bytes of K weights."""
+    rcb, rsb = _row_bytes(w, K)
+    rows = 1
+    for d in lead:
+        rows *= d
+    for t, name, per_row in ((codes, what[0], rcb), (scales, what[1], rsb)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        _need(tuple(t.shape[:len(lead)]) == tuple(lead) and _nbytes(t) == rows * per_row,
+              f"{name} has shape {tuple(t.shape)} ({_nbytes(t)} bytes), expected leading "
+              f"dimensions {tuple(lead)} and {per_row} bytes per row for K={K} "
+              f"({rows * per_row} bytes)")
+
+
+def _check_x(x, x_scales, vectors, K, a):
+    """x holds ``vectors`` activation vectors of K values, and x_scales (int8
+    activations) one fp16 scale per 32 of them."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
+    _need(x.dim() >= 1 and x.shape[-1] == K and x.numel() == vectors * K,
+          f"x has shape {tuple(x.shape)}, expected {vectors} vectors of K={K}")
+    if a == A_Q8B32:
+        _need(isinstance(x_scales, torch.Tensor), "int8 activations need x_scales (float16, one per 32)")
+        _need(x_scales.numel() == vectors * (K // 32),
+              f"x_scales has shape {tuple(x_scales.shape)}, expected {vectors} x {K // 32} fp16 scales")
+    else:
+        _need(x_scales is None, "x_scales is only used with int8 activations")
+
+
+def _check_y(y, shape):
+    n = 1
+    for d in shape:
+        n *= d
+    _need(isinstance(y, torch.Tensor) and y.numel() == n and y.dtype == torch.float32,
+          f"y has shape {tuple(y.shape)} and dtype {y.dtype}, expected float32 {tuple(shape)}")
+
+
+def _check_ids(expert_ids):
+    if not isinstance(expert_ids, torch.Tensor):
+        raise TypeError("expert_ids must be a torch.Tensor")
+    _need(expert_ids.dim() == 2, f"expert_ids has shape {tuple(expert_ids.shape)}, expected [M][top_k]")
+    return expert_ids.shape[0], expert_ids.shape[1]
+
+
+def _per_slot(x, x_per_slot, M, top_k):
+    """Per-slot activations: explicit, or [M][top_k][K] when x is 3-D."""
+    if x_per_slot is None:
+        return isinstance(x, torch.Tensor) and x.dim() == 3
+    x_per_slot = bool(x_per_slot)
+    if isinstance(x, torch.Tensor) and x.dim() == 3:
+        _need(x_per_slot and tuple(x.shape[:2]) == (M, top_k),
+              f"x has shape {tuple(x.shape)}: a 3-D x is [M][top_k][K] per-slot activations")
+    return x_per_slot
+
+
+def _gpu(dev, fn):
     if dev.type != "cuda":
-        raise ValueError("qmv_dense runs on the GPU only; pass device tensors")
+        raise ValueError(f"{fn} runs on the GPU only; pass device tensors")
+
+
+def qmv_dense(wfmt, w_codes, w_scales, x, x_scales=None, y=None, stream=None):
+    """Dense GEMV: y[m][n] = sum_k w(n,k) x(m,k); returns y (float32 [M][N]).
+    ``x`` is [M][K]."""
+    w = _wfmt(wfmt)
+    _need(isinstance(x, torch.Tensor) and x.dim() == 2, "x must be a 2-D tensor [M][K]")
     M, K = x.shape
     N = w_codes.shape[0]
+    a, xd = _afmt(w, x)
+    _check_weights(w, w_codes, w_scales, (N,), K)
+    _check_x(x, x_scales, M, K, a)
+    if y is not None:
+        _check_y(y, (M, N))
+    dev = w_codes.device
+    _gpu(dev, "qmv_dense")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    a, xd = _afmt(w, x)
     s = lib().qmv_dense(w, _dev_ptr(w_codes, "w_codes", (torch.uint8,), dev),
                         _dev_ptr(w_scales, "w_scales", _SCALE_DT, dev), a,
                         _dev_ptr(x, "x", xd, dev),
@@ -144,28 +229,33 @@ def qmv_dense(wfmt, w_codes, w_scales, x, x_scales=None, y=None, stream=None):
     return y
 
 
-def qmv_gather_moe(wfmt, w_codes, w_scales, expert_ids, x, x_scales=None, x_per_slot=False,
+def qmv_gather_moe(wfmt, w_codes, w_scales, expert_ids, x, x_scales=None, x_per_slot=None,
                    y=None, stream=None):
     """Expert-gathered GEMV; returns y (float32 [M][top_k][N]).
 
-    ``x`` is [M][K], or [M][top_k][K] with ``x_per_slot=True``.
+    ``x`` is [M][K] (one vector per token), or [M][top_k][K] per (token,
+    slot); ``x_per_slot`` defaults to ``x.dim() == 3``.
     """
     w = _wfmt(wfmt)
-    dev = w_codes.device
-    if dev.type != "cuda":
-        raise ValueError("qmv_gather_moe runs on the GPU only; pass device tensors")
+    M, top_k = _check_ids(expert_ids)
     E, N = w_codes.shape[0], w_codes.shape[1]
-    M, top_k = expert_ids.shape
     K = x.shape[-1]
+    per_slot = _per_slot(x, x_per_slot, M, top_k)
+    a, xd = _afmt(w, x)
+    _check_weights(w, w_codes, w_scales, (E, N), K)
+    _check_x(x, x_scales, M * top_k if per_slot else M, K, a)
+    if y is not None:
+        _check_y(y, (M, top_k, N))
+    dev = w_codes.device
+    _gpu(dev, "qmv_gather_moe")
     if y is None:
         y = torch.empty((M, top_k, N), dtype=torch.float32, device=dev)
-    a, xd = _afmt(w, x)
     s = lib().qmv_gather_moe(w, _dev_ptr(w_codes, "w_codes", (torch.uint8,), dev),
                              _dev_ptr(w_scales, "w_scales", _SCALE_DT, dev), E,
                              _dev_ptr(expert_ids, "expert_ids", (torch.int32,), dev), M, top_k, a,
                              _dev_ptr(x, "x", xd, dev),
                              _dev_ptr(x_scales, "x_scales", (torch.float16,), dev),
-                             int(bool(x_per_slot)),
+                             int(per_slot),
                              _dev_ptr(y, "y", (torch.float32,), dev), N, K, _stream(dev, stream))
     _check(s)
     return y
@@ -176,15 +266,19 @@ def qmv_gather_moe_swiglu(wfmt, gate_codes, gate_scales, up_codes, up_scales, ex
     """Fused gate/up projection with SwiGLU: y = silu(gate x) * (up x);
     returns y (float32 [M][top_k][N]).  ``x`` is the tokens' [M][K]."""
     w = _wfmt(wfmt)
-    dev = gate_codes.device
-    if dev.type != "cuda":
-        raise ValueError("qmv_gather_moe_swiglu runs on the GPU only; pass device tensors")
+    M, top_k = _check_ids(expert_ids)
     E, N = gate_codes.shape[0], gate_codes.shape[1]
-    M, top_k = expert_ids.shape
     K = x.shape[-1]
+    a, xd = _afmt(w, x)
+    _check_weights(w, gate_codes, gate_scales, (E, N), K, ("gate_codes", "gate_scales"))
+    _check_weights(w, up_codes, up_scales, (E, N), K, ("up_codes", "up_scales"))
+    _check_x(x, x_scales, M, K, a)
+    if y is not None:
+        _check_y(y, (M, top_k, N))
+    dev = gate_codes.device
+    _gpu(dev, "qmv_gather_moe_swiglu")
     if y is None:
         y = torch.empty((M, top_k, N), dtype=torch.float32, device=dev)
-    a, xd = _afmt(w, x)
     s = lib().qmv_gather_moe_swiglu(
         w, _dev_ptr(gate_codes, "gate_codes", (torch.uint8,), dev),
         _dev_ptr(gate_scales, "gate_scales", _SCALE_DT, dev),
@@ -198,29 +292,37 @@ def qmv_gather_moe_swiglu(wfmt, gate_codes, gate_scales, up_codes, up_scales, ex
 
 
 def qmv_gather_moe_combine(wfmt, w_codes, w_scales, expert_ids, route_weights, x, x_scales=None,
-                           x_per_slot=True, y=None, stream=None):
+                           x_per_slot=None, y=None, stream=None):
     """Down projection with the router-weighted top-k combine:
     y[t][n] = sum_j route_weights[t][j] * (w(ids[t][j]) . x(t, j)); returns y
-    (float32 [M][N]).  ``x`` is [M][top_k][K] (``x_per_slot=True``) or [M][K]."""
+    (float32 [M][N]).  ``x`` is [M][top_k][K] per (token, slot) -- the usual
+    down-projection input -- or [M][K]; ``x_per_slot`` defaults to
+    ``x.dim() == 3``."""
     w = _wfmt(wfmt)
-    dev = w_codes.device
-    if dev.type != "cuda":
-        raise ValueError("qmv_gather_moe_combine runs on the GPU only; pass device tensors")
+    M, top_k = _check_ids(expert_ids)
     E, N = w_codes.shape[0], w_codes.shape[1]
-    M, top_k = expert_ids.shape
-    if tuple(route_weights.shape) != (M, top_k):
-        raise ValueError(f"route_weights has shape {tuple(route_weights.shape)}, expected {(M, top_k)}")
+    if not isinstance(route_weights, torch.Tensor):
+        raise TypeError("route_weights must be a torch.Tensor")
+    _need(tuple(route_weights.shape) == (M, top_k),
+          f"route_weights has shape {tuple(route_weights.shape)}, expected {(M, top_k)}")
     K = x.shape[-1]
+    per_slot = _per_slot(x, x_per_slot, M, top_k)
+    a, xd = _afmt(w, x)
+    _check_weights(w, w_codes, w_scales, (E, N), K)
+    _check_x(x, x_scales, M * top_k if per_slot else M, K, a)
+    if y is not None:
+        _check_y(y, (M, N))
+    dev = w_codes.device
+    _gpu(dev, "qmv_gather_moe_combine")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    a, xd = _afmt(w, x)
     s = lib().qmv_gather_moe_combine(
         w, _dev_ptr(w_codes, "w_codes", (torch.uint8,), dev),
         _dev_ptr(w_scales, "w_scales", _SCALE_DT, dev), E,
         _dev_ptr(expert_ids, "expert_ids", (torch.int32,), dev),
         _dev_ptr(route_weights, "route_weights", (torch.float32,), dev), M, top_k, a,
         _dev_ptr(x, "x", xd, dev), _dev_ptr(x_scales, "x_scales", (torch.float16,), dev),
-        int(bool(x_per_slot)), _dev_ptr(y, "y", (torch.float32,), dev), N, K,
+        int(per_slot), _dev_ptr(y, "y", (torch.float32,), dev), N, K,
         _stream(dev, stream))
     _check(s)
     return y

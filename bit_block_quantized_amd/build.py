@@ -10,6 +10,7 @@ library is compiled for gfx950 only.  Packed-FP32 VALU forms are switched off
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 import tempfile
@@ -41,21 +42,73 @@ FLAGS = [
 ]
 
 
+# Every kernel's register and memory budget comes out of the compiler as
+# remarks (one block per kernel); the build refuses any kernel that uses
+# per-lane scratch memory.  Some kernels count their outstanding vector-memory
+# loads by hand (an s_waitcnt vmcnt(N) that assumes a fixed number of loads
+# per step); a register spill would add scratch loads and stores to that count
+# and turn the wait into a silent race, and in the others it would be a
+# performance bug.
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+_REMARK = re.compile(r"remark:\s+(Function Name|ScratchSize \[bytes/lane\]|VGPRs Spill|Dynamic Stack|"
+                     r"VGPRs|AGPRs|Occupancy \[waves/SIMD\]):\s*(\S+)")
+
+
+def parse_resource_usage(text: str) -> dict:
+    """Per-kernel resource remarks from the compiler's output:
+    {kernel symbol: {field: value}}."""
+    kernels, cur = {}, None
+    for field, value in _REMARK.findall(text):
+        if field == "Function Name":
+            cur = kernels.setdefault(value, {})
+        elif cur is not None:
+            cur[field] = value
+    return kernels
+
+
+def scratch_violations(kernels: dict) -> list:
+    """Kernels that use scratch memory: scratch bytes, spilled VGPRs or a
+    dynamic stack."""
+    bad = []
+    for name, r in sorted(kernels.items()):
+        if (int(r.get("ScratchSize [bytes/lane]", "0")) != 0 or int(r.get("VGPRs Spill", "0")) != 0 or
+                r.get("Dynamic Stack", "False") != "False"):
+            bad.append((name, r))
+    return bad
+
+
+class ScratchError(RuntimeError):
+    pass
+
+
 def build(out: str = LIB, extra: list | None = None, verbose: bool = False) -> str:
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     with tempfile.TemporaryDirectory(prefix="qmv_build_") as tmp:
         def compile_one(unit):
             src, defs, objname = unit
             obj = os.path.join(tmp, objname)
-            cmd = [HIPCC, *FLAGS, *inc, *defs, *(extra or []), "-c", os.path.join(CSRC, src),
-                   "-o", obj]
+            cmd = [HIPCC, *FLAGS, RESOURCE_REMARKS, *inc, *defs, *(extra or []), "-c",
+                   os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
-            subprocess.run(cmd, check=True)
-            return obj
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                sys.stderr.write(r.stderr)
+                raise subprocess.CalledProcessError(r.returncode, cmd)
+            return obj, parse_resource_usage(r.stderr)
         jobs = min(len(UNITS), max(1, os.cpu_count() or 1))
         with ThreadPoolExecutor(jobs) as ex:
-            objs = list(ex.map(compile_one, UNITS))
+            res = list(ex.map(compile_one, UNITS))
+        objs = [o for o, _ in res]
+        kernels = {}
+        for _, k in res:
+            kernels.update(k)
+        bad = scratch_violations(kernels)
+        if bad:
+            raise ScratchError("kernels using scratch memory: " +
+                               "; ".join(f"{n} {r}" for n, r in bad))
+        if verbose:
+            print(f"{len(kernels)} kernels, none uses scratch memory", flush=True)
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qmv_host.hpp"
+
 // The kernels are instantiated twice, with 4 and with 8 wave64s per
 // workgroup (a larger workgroup stages the activations once for twice the
 // rows); QMV_NS keeps the two sets of names apart.
@@ -44,18 +46,7 @@ namespace QMV_NS {
 constexpr int kWaves = QMV_WAVES;        // wave64s per workgroup
 constexpr int kThreads = 64 * kWaves;
 
-// kMXFP4I: MXFP4 codes with int8 activations (fp16 scale per 32), staged as
-// exact bf16 so that the MXFP4 decode and bf16 dot serve both.
-enum Kind : int { kMXFP4 = 0, kCB2 = 1, kCB2S = 2, kCB3 = 3, kMXFP4I = 4 };
-
-// XB: LDS bytes of activations per unit and vector; AB: LDS bytes of
-// per-unit activation side data (scales, sums).
-template <int F> struct Fmt;
-template <> struct Fmt<kMXFP4> { static constexpr int W = 32, XB = 64, AB = 0; };
-template <> struct Fmt<kCB2>   { static constexpr int W = 64, XB = 64, AB = 16; };
-template <> struct Fmt<kCB2S>  { static constexpr int W = 32, XB = 32, AB = 8; };
-template <> struct Fmt<kCB3>   { static constexpr int W = 32, XB = 32, AB = 4; };
-template <> struct Fmt<kMXFP4I> { static constexpr int W = 32, XB = 64, AB = 4; };
+using namespace qmv_cfg;      // format kinds, unit sizes, launch menus (qmv_host.hpp)
 
 struct Args {
     const uint8_t *codes;
@@ -1248,14 +1239,6 @@ __global__ __launch_bounds__(kThreads) void qmv_combine_kernel(const Args a)
     }
     if (li == 0 && n < a.N) a.y[t * a.N + n] = y;      // M * N < 2^31
 }
-
-// Kernel menus.  Variant 0: one vector per item, 2 rows per lane.  Variant 1:
-// up to four vectors per item (gather with M > 1 or per-slot activations),
-// 2 rows per lane.  Variant 2: dense with M > 1, 4 rows per lane.
-constexpr int kMenuLpr[4] = {8, 16, 32, 64};
-constexpr int kMenuCpl01[5] = {1, 2, 3, 4, 7};
-constexpr int kMenuCpl2[3] = {1, 2, 4};
-constexpr int kMenuCplC[4] = {1, 2, 3, 4};     // combine kernel
 
 // Kernel tables, one per format kind (qmv_k_*.hip): [variant][lpr][cpl].
 extern const void *const kTable_mxfp4[3][4][5];

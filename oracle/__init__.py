@@ -31,10 +31,11 @@ AFMT = {"bf16": A_BF16, "q8": A_Q8}
 
 def build(out: str = _LIB, mutant: int = 0) -> str:
     """Compile the oracle with gcc -O2 (no SIMD intrinsics) into ``out``."""
+    tmp = f"{out}.tmp{os.getpid()}"
     cmd = ["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-fno-fast-math",
-           f"-DORACLE_MUTANT={int(mutant)}", _SRC, "-o", out + ".tmp", "-lm"]
+           f"-DORACLE_MUTANT={int(mutant)}", _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(out + ".tmp", out)
+    os.replace(tmp, out)
     return out
 
 

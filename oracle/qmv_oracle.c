@@ -468,6 +468,8 @@ int oracle_qmv_combine_sel(int wfmt, const uint8_t *codes, const uint8_t *scales
                 return -1;
 #if ORACLE_MUTANT == 11
             double wj = (double)w[t * top_k + (j + 1) % top_k];   /* mutant: weights shifted */
+#elif ORACLE_MUTANT == 15
+            double wj = fabs((double)w[t * top_k + j]);           /* mutant: weight signs dropped */
 #else
             double wj = (double)w[t * top_k + j];
 #endif

@@ -496,6 +496,45 @@ def check_combine(o):
         assert np.allclose(yd[1], want, rtol=1e-12, atol=1e-12 * np.abs(gb).max()), fmt
 
 
+def check_combine_signed(o):
+    """Router weights of either sign, and weights that sum to zero: a negative
+    one-hot weight gives exactly the negated gather row; negating every weight
+    negates y exactly and leaves A (which sums |w| |w x|) unchanged; two slots
+    of one expert fed the same vector with weights a and -a cancel, leaving
+    the other slots' sum."""
+    rng = _rng(19)
+    K, N, E, M, top_k = 96, 10, 4, 2, 4
+    for fmt in ("mxfp4", "cb2", "cb3"):
+        afmt = _afmt(fmt)
+        codes = np.stack([_random_rows(rng, fmt, N, K)[0] for _ in range(E)])
+        scales = np.stack([_random_rows(rng, fmt, N, K)[1] for _ in range(E)])
+        x, xs = _random_x(rng, fmt, M * top_k, K)
+        ids = np.array([[1, 1, 3, 0], [2, 0, 3, 1]], np.int32)
+        w = rng.uniform(-1.0, 1.0, size=(M, top_k)).astype(np.float32)
+        w[0, 2] = -abs(w[0, 2])
+        y, A = o.combine(fmt, codes, scales, ids, w, afmt, x, xs)
+        g, _ = o.gather(fmt, codes, scales, ids, afmt, x, xs, x_per_slot=True)
+        oh = np.zeros_like(w)
+        oh[1, 2] = -1.0
+        y1, _ = o.combine(fmt, codes, scales, ids, oh, afmt, x, xs)
+        assert np.array_equal(y1[1], -g[1, 2]) and not y1[0].any(), fmt
+        yn, An = o.combine(fmt, codes, scales, ids, -w, afmt, x, xs)
+        assert np.array_equal(yn, -y) and np.array_equal(An, A), fmt
+        ya, Aa = o.combine(fmt, codes, scales, ids, np.abs(w), afmt, x, xs)
+        assert np.array_equal(Aa, A), fmt
+        # token 0: expert 1 in slots 0 and 1; with broadcast activations and
+        # weights +a / -a the two slots cancel
+        xb, xsb = _random_x(rng, fmt, M, K)
+        wz = w.copy()
+        wz[0, 0], wz[0, 1] = 0.375, -0.375
+        yz, _ = o.combine(fmt, codes, scales, ids, wz, afmt, xb, xsb, x_per_slot=False)
+        gb, _ = o.gather(fmt, codes, scales, ids, afmt, xb, xsb)
+        want = wz[0, 2] * gb[0, 2] + wz[0, 3] * gb[0, 3]
+        assert np.allclose(yz[0], want, rtol=1e-12, atol=1e-12 * np.abs(gb).max()), fmt
+        if np.abs(gb[0, 0]).max() > 0:
+            assert not np.allclose(yz[0], want + 0.75 * gb[0, 0], rtol=1e-9, atol=0), fmt
+
+
 # ---------------------------------------------------------------- P11 activation quantizer
 def check_f2h_library(o):
     """The oracle's binary16 encoder against numpy's float32 -> float16 cast
@@ -582,6 +621,7 @@ ALL_CHECKS = [
     check_gather_semantics,
     check_swiglu,
     check_combine,
+    check_combine_signed,
     check_f2h_library,
     check_q8_hand_worked,
     check_q8_invariants,

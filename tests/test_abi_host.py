@@ -76,7 +76,7 @@ def gather(L, wfmt=W_MXFP4, codes=FAKE, scales=FAKE, E=32, ids=FAKE, M=1, top_k=
                             None)
 
 
-@pytest.mark.parametrize("kw,want", [
+DENSE_CASES = [
     (dict(codes=None), EINVAL), (dict(scales=None), EINVAL), (dict(x=None), EINVAL),
     (dict(y=None), EINVAL), (dict(M=0), EINVAL), (dict(N=0), EINVAL), (dict(K=0), EINVAL),
     (dict(N=-5), EINVAL), (dict(K=48), EUNSUP), (dict(K=16416), EUNSUP),
@@ -89,12 +89,15 @@ def gather(L, wfmt=W_MXFP4, codes=FAKE, scales=FAKE, E=32, ids=FAKE, M=1, top_k=
     (dict(x=FAKE + 2), EINVAL), (dict(wfmt=W_CB2, afmt=2, x=FAKE + 8), EINVAL),
     (dict(wfmt=W_CB3, afmt=2, x=FAKE, codes=FAKE + 2), EINVAL),
     (dict(y=FAKE + 2), EINVAL),
-])
+]
+
+
+@pytest.mark.parametrize("kw,want", DENSE_CASES)
 def test_dense_validation(L, kw, want):
     assert dense(L, **kw) == want
 
 
-@pytest.mark.parametrize("kw,want", [
+GATHER_CASES = [
     (dict(ids=None), EINVAL), (dict(E=0), EINVAL), (dict(top_k=0), EINVAL),
     (dict(top_k=17), EUNSUP), (dict(K=2880 + 16), EUNSUP),
     # more than 4 vectors: MXFP4 x bf16, at most 8192 (token, slot) pairs and 1023 experts
@@ -107,7 +110,11 @@ def test_dense_validation(L, kw, want):
     (dict(wfmt=W_CB3, afmt=A_Q8, xs=FAKE, codes=FAKE + 2), EINVAL),
     (dict(ids=FAKE + 1), EINVAL),
     (dict(E=2 ** 31 - 1, N=2 ** 31 - 1, K=16384), EUNSUP),
-])
+    (dict(wfmt=W_CB2, afmt=A_Q8, xs=FAKE, codes=FAKE + 4, K=96), EINVAL),
+]
+
+
+@pytest.mark.parametrize("kw,want", GATHER_CASES)
 def test_gather_validation(L, kw, want):
     assert gather(L, **kw) == want
 
@@ -144,12 +151,15 @@ def swiglu(L, wfmt=W_MXFP4, gc=FAKE, gs=FAKE, uc=FAKE, us=FAKE, E=32, ids=FAKE, 
                                    None)
 
 
-@pytest.mark.parametrize("kw,want", [
+SWIGLU_CASES = [
     (dict(uc=None), EINVAL), (dict(us=None), EINVAL), (dict(gc=None), EINVAL),
     (dict(uc=FAKE + 8), EINVAL), (dict(ids=None), EINVAL), (dict(M=5), EUNSUP),
     (dict(K=100), EUNSUP), (dict(wfmt=W_CB2), EUNSUP),
     (dict(wfmt=W_CB3, afmt=A_Q8, xs=FAKE, us=FAKE + 2), EINVAL),
-])
+]
+
+
+@pytest.mark.parametrize("kw,want", SWIGLU_CASES)
 def test_swiglu_validation(L, kw, want):
     assert swiglu(L, **kw) == want
 
@@ -160,13 +170,16 @@ def combine(L, wfmt=W_CB3, codes=FAKE, scales=FAKE, E=256, ids=FAKE, rw=FAKE, M=
                                     per_slot, y, N, K, None)
 
 
-@pytest.mark.parametrize("kw,want", [
+COMBINE_CASES = [
     (dict(rw=None), EINVAL), (dict(rw=FAKE + 2), EINVAL), (dict(ids=None), EINVAL),
     (dict(codes=None), EINVAL), (dict(y=FAKE + 1), EINVAL), (dict(xs=None), EINVAL),
     (dict(M=5), EUNSUP), (dict(top_k=17), EUNSUP), (dict(top_k=0), EINVAL),
     (dict(K=2048 + 16), EUNSUP), (dict(afmt=A_BF16, xs=None), EUNSUP),
     (dict(wfmt=W_MXFP4, afmt=2, xs=None), EUNSUP), (dict(E=0), EINVAL),
-])
+]
+
+
+@pytest.mark.parametrize("kw,want", COMBINE_CASES)
 def test_combine_validation(L, kw, want):
     assert combine(L, **kw) == want
 

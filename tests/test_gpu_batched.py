@@ -9,8 +9,16 @@ Against the oracle on the same seeded inputs: every output within
 show); NaN exactly where the oracle has NaN; zero rows for ids outside
 [0, E).  Cases: dense and gather, broadcast and per-slot activations,
 experts with more than 128 vectors (chunked), all pairs on one expert,
-ragged N and K (partial 128-weight slices), the pair and expert limits, and
-the full-size prefill chunk on sampled outputs.
+ragged N and K (partial 128-weight slices), E8M0 bytes outside [2, 252] and
+Inf activations, the pair and expert limits, and the full-size prefill chunk
+on sampled outputs.
+
+Which kernel a call reaches: dense calls with 5 to 20 vectors and gathers
+with at most 64 tokens and fewer than two (token, slot) pairs per expert run
+as groups of up to 4 vectors on the decode kernels (test_dense with M <= 20
+and test_gather_few_pairs_* cover that route); every other call with more
+than 4 vectors runs on the batched kernel, so the special-value cases below
+use dense calls with M >= 21 or gathers with M * top_k >= 2 E.
 """
 import numpy as np
 import pytest
@@ -87,10 +95,22 @@ def test_exact_at_unit_scales(case):
     _check(inp, f"unit {case}", exact=True)
 
 
+def _assert_special(inp, what):
+    y = gpu_call(inp).cpu().numpy()
+    yr, A = oracle_call(inp)
+    # outputs whose |w x| sum passes fp32's range may overflow either way
+    m = (A < 3.0e38) | np.isnan(yr)
+    assert np.array_equal(np.isnan(y[m]), np.isnan(yr[m])), what
+    fin = (A < 3.0e38) & ~np.isnan(yr)
+    assert_parity(y[fin], yr[fin], A[fin], what)
+    return yr
+
+
 def test_e8m0_special_scales():
-    """Slices holding scale bytes outside [2, 252] take the unscaled path:
-    0 (2^-127, an fp32 subnormal), 1, 253, 254 and 255 (NaN)."""
-    inp = synth.make(_wl("dense", 8, 40, 320, seed=61))
+    """Slices holding scale bytes outside [2, 252] take the exact path:
+    0 (2^-127, an fp32 subnormal), 1, 253, 254 and 255 (NaN).  A dense call
+    with 24 vectors (the batched kernel)."""
+    inp = synth.make(_wl("dense", 24, 40, 320, seed=61))
     inp.scales[0, :] = 0
     inp.scales[1, :] = 1
     inp.scales[2, :] = 254
@@ -98,25 +118,35 @@ def test_e8m0_special_scales():
     inp.scales[4, :] = [0, 127, 254, 127, 1, 253, 2, 252, 127, 127]
     inp.scales[17, 9] = 0                    # one byte in the last (partial) slice
     inp.scales[39, 0] = 255
-    y = gpu_call(inp).cpu().numpy()
-    yr, A = oracle_call(inp)
+    yr = _assert_special(inp, "e8m0 specials, dense")
     assert np.isnan(yr[:, 3]).all() and np.isnan(yr[:, 39]).all()
-    # outputs whose |w x| sum passes fp32's range may overflow either way
-    m = (A < 3.0e38) | np.isnan(yr)
-    assert np.array_equal(np.isnan(y[m]), np.isnan(yr[m]))
-    fin = (A < 3.0e38) & ~np.isnan(yr)
-    assert_parity(y[fin], yr[fin], A[fin], "e8m0 specials")
+
+
+def test_e8m0_special_scales_gather_chunked():
+    """A special scale byte in an expert that holds more than 128 vectors
+    (two chunks), and in another expert's last rows, on a gather."""
+    inp = synth.make(_wl("gather", 300, 70, 416, E=3, top_k=1, seed=62))
+    inp.ids[:200, 0] = 1                      # expert 1: 200 vectors
+    inp.ids[200:, 0] = np.where(np.arange(100) % 2 == 0, 0, 2)
+    inp.scales[1, 5, 3] = 0
+    inp.scales[1, 6, :] = 254
+    inp.scales[1, 69, 12] = 255
+    inp.scales[2, 68, 0] = 1
+    inp.scales[2, 0, 12] = 253
+    yr = _assert_special(inp, "e8m0 specials, gather")
+    assert np.isnan(yr[:200, 0, 69]).all()
 
 
 def test_inf_activation_stays_in_its_column():
-    """An Inf activation reaches only the outputs of its own vector."""
-    inp = synth.make(_wl("dense", 20, 36, 480, seed=71))
+    """An Inf activation reaches only the outputs of its own vector (dense,
+    24 vectors: the batched kernel)."""
+    inp = synth.make(_wl("dense", 24, 36, 480, seed=71))
     inp.x[7, 100] = 0x7F80                   # +Inf
     y = gpu_call(inp).cpu().numpy()
     yr, A = oracle_call(inp)
     assert np.array_equal(np.isnan(y), np.isnan(yr)) and np.array_equal(np.isinf(y), np.isinf(yr))
     ok = np.isfinite(yr)
-    assert ok[np.arange(20) != 7].all()
+    assert ok[np.arange(24) != 7].all()
     assert_parity(y[ok], yr[ok], A[ok], "inf column")
 
 

@@ -3,13 +3,20 @@
 
 The oracle gives g, u (fp64) and their sum |w x| scales Ag, Au.  The GPU's g
 and u each carry the gather's error bound, at most 1e-3 * A; silu has slope
-at most 1.1 in magnitude, so the fused output obeys
+at most 1.1 in magnitude, so propagating those errors gives
 
-    |y - y_ref| <= 1e-3 * (1.1 |u| Ag + |silu(g)| Au + 1.1e-3 Ag Au)
-                   + 1e-5 (1 + |g|) |y_ref|
+    E1 = 1e-3 * (1.1 |u| Ag + |silu(g)| Au + 1.1e-3 Ag Au).
 
-where the last term covers fp32 evaluation of silu (the exponential's
-relative error grows with |g|) and the final product.
+On top of that the kernel evaluates silu(g) * u = g / (1 + e^-g) * u in
+fp32.  Its exponential is the hardware base-2 exponential of g * log2(e):
+rounding that product to fp32 moves the exponent by at most |g| log2(e)
+2^-24, a relative error of at most |g| 2^-24 in e^-g, and the instruction
+itself is within 1 ulp (2^-23); the add, the IEEE division and the final
+product add 2^-24 each.  An error in e^-g reaches 1 + e^-g at most in full,
+so the fp32 evaluation is within (|g| + 5) 2^-24 of silu(g') u' in relative
+terms.  With a factor 4 of margin the bar is
+
+    |y - y_ref| <= E1 + 2^-22 (|g| + 8) (|y_ref| + E1).
 """
 from concurrent.futures import ThreadPoolExecutor
 
@@ -71,8 +78,8 @@ def assert_swiglu_parity(y_gpu, ref, what=""):
     yg = np.asarray(y_gpu, np.float64).reshape(-1)
     assert np.isfinite(yg).all(), f"{what}: non-finite output"
     silu = g / (1.0 + np.exp(-np.clip(g, -700, 700)))
-    bound = (TOL * (SILU_SLOPE * np.abs(u) * Ag + np.abs(silu) * Au + SILU_SLOPE * TOL * Ag * Au)
-             + 1e-5 * (1 + np.abs(g)) * np.abs(y))
+    e1 = TOL * (SILU_SLOPE * np.abs(u) * Ag + np.abs(silu) * Au + SILU_SLOPE * TOL * Ag * Au)
+    bound = e1 + 2.0 ** -22 * (np.abs(g) + 8.0) * (np.abs(y) + e1)
     err = np.abs(yg - y)
     bad = np.nonzero(err > bound)[0]
     assert bad.size == 0, (f"{what}: {bad.size} of {y.size} outputs out of tolerance; first at "

@@ -9,7 +9,7 @@ qmv_oracle.c), on the CPU only:
   swapped in SwiGLU            10 sigmoid(g) * u in place of silu(g) * u
   11 combine weights shifted by one slot   12 combine drops the last slot
   13 q8 quantizer rounds ties away from zero   14 q8 quantizer uses the
-  unrounded scale.
+  unrounded scale   15 combine drops the router weights' signs.
 The idea of requiring a sign-dropped decode to fail comes from mlxcel issue
 #2178, Acceptance Criteria.
 """
@@ -22,10 +22,10 @@ import oracle_pins as pins
 ORDER = [pins.check_hand_worked, pins.check_codebooks_match_pages, pins.check_e2m1_table,
          pins.check_e8m0_library, pins.check_unpackers_agree, pins.check_gather_semantics,
          pins.check_unit_scale_exact, pins.check_block_factored, pins.check_fp16_exhaustive,
-         pins.check_bf16_exhaustive, pins.check_random_blocks_exact, pins.check_mxfp4_one_hot, pins.check_swiglu, pins.check_combine, pins.check_q8_hand_worked, pins.check_f2h_library, pins.check_q8_invariants]
+         pins.check_bf16_exhaustive, pins.check_random_blocks_exact, pins.check_mxfp4_one_hot, pins.check_swiglu, pins.check_combine, pins.check_combine_signed, pins.check_q8_hand_worked, pins.check_f2h_library, pins.check_q8_invariants]
 
 
-@pytest.mark.parametrize("mutant", range(1, 15))
+@pytest.mark.parametrize("mutant", range(1, 16))
 def test_mutant_is_caught(mutant):
     o = oracle.load(mutant)
     caught = []
