@@ -110,7 +110,19 @@ def other_bytes(wl):
 # Rotation plan: layer copies so that between two reads of the same weights
 # more than the 256 MB Infinity Cache of other weights is read.
 ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40, "C2gu": 4, "C3gu": 1,
-            "C4c": 2, "C2c": 32, "C3q": 2, "C4q": 2, "C2i": 32, "C6": 8}
+            "C4c": 2, "C2c": 32, "C3q": 2, "C4q": 2, "C2i": 32, "C6": 8, "C6gu": 4, "C6d": 40}
+
+
+def merge_regions(regions):
+    """(address, bytes) ranges sorted, with touching ranges joined (adjacent
+    experts of one tensor are one range), each under 2 GiB."""
+    out = []
+    for a, n in sorted(regions):
+        if out and out[-1][0] + out[-1][1] == a and out[-1][1] + n < (1 << 31):
+            out[-1] = (out[-1][0], out[-1][1] + n)
+        else:
+            out.append((a, n))
+    return out
 
 
 class Prepared:
@@ -173,7 +185,7 @@ class Prepared:
         self.wbytes = np.array([weight_bytes(wl, u) for u in n_unique], np.float64) * len(self.w)
         pairs = (np.array([(i >= 0).sum() for i in ids], np.float64) if routed
                  else np.full(calls, float(wl.M)))
-        self.flops = 2.0 * pairs * wl.N * wl.K
+        self.flops = 2.0 * pairs * wl.N * wl.K * len(self.w)
         self.abytes = self.wbytes + other_bytes(wl)
         self.lib = q.lib()
         self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -203,8 +215,8 @@ class Prepared:
                          self.y.data_ptr(), wl.M, wl.N, wl.K)
                 (self.args_hot if hot else self.args).append(a)
                 if not hot:
-                    reg = [(cp + int(e) * rcb, rcb) for cp, _ in wp for e in experts[i]] + \
-                          [(sp + int(e) * rsb, rsb) for _, sp in wp for e in experts[i]]
+                    reg = merge_regions([(cp + int(e) * rcb, rcb) for cp, _ in wp for e in experts[i]] +
+                                        [(sp + int(e) * rsb, rsb) for _, sp in wp for e in experts[i]])
                     n = len(reg)
                     self.regions.append((n, (ctypes.c_void_p * n)(*[r[0] for r in reg]),
                                          (ctypes.c_longlong * n)(*[r[1] for r in reg])))
@@ -544,6 +556,8 @@ def main():
     if not args.no_extra:
         for name in [w for w in args.workloads.split(",") if w and w != HEADLINE]:
             pe, r = measure(name, max(50, args.steps // 5), 10, hot=not args.no_hot)
+            print(f"bench: {name}: {r['us_per_call']:.3f} us/call, {r['pct_hbm_peak']:.1f}% of HBM peak, "
+                  f"stream ceiling {r['stream_ceiling_us_per_call']:.3f} us", file=sys.stderr, flush=True)
             r["desc"] = pe.wl.desc
             extra[name] = r
             del pe

@@ -43,11 +43,17 @@ namespace qmv {
 extern const void *const kTableDense4[2];
 }
 
-// MXFP4 x bf16 with more than 4 vectors: expert-batched gather and dense
-// calls on the 16x16x32 bf16 matrix cores (qmv_k_mxfp4b.hip): [4 waves and
-// 128 rows, 8 waves and 256 rows] per tile.
+// MXFP4 x bf16 with more than 4 vectors: expert-batched gather, fused
+// gate/up gather and dense calls on the 32x32x16 bf16 matrix cores
+// (qmv_k_mxfp4b.hip): a menu of kernel shapes, each (waves per workgroup,
+// 32-row fragments per wave, most vectors per chunk); gate/up kernels hold a
+// gate and an up fragment per output fragment.
 namespace qmv {
-extern const void *const kTableBatched[2];
+constexpr int kBatchedMenu = 4;
+extern const int kBatchedShapes[kBatchedMenu][3];
+extern const void *const kTableBatched[kBatchedMenu];
+extern const int kBatchedShapesGU[kBatchedMenu][3];
+extern const void *const kTableBatchedGU[kBatchedMenu];
 }
 
 namespace {
@@ -199,17 +205,16 @@ Args base_args(int wfmt, int afmt, int kind, const void *codes, const void *scal
     return a;
 }
 
-// Batched MXFP4 x bf16 (M > 4): LDS of one workgroup = a ring of 4
-// activation slice buffers (128 weights of 128 vectors, 32 KB each), then
-// the routing tables (count, vector offset and tile offset per bucket, wave
-// totals) and the sorted pair list: at most 128 + 12 + 16 KB.
-size_t batched_lds(int buckets, int pairs)
+// Batched MXFP4 x bf16 (M > 4): LDS of one workgroup = a ring of 2
+// activation slice buffers (128 weights of vmax vectors, 256 B each), the
+// pair scan's counts and the tile's pair list: at most 64 + 1 + 16 KB.
+size_t batched_lds(int vmax, int pairs)
 {
-    return (size_t)4 * 128 * 256 + 12 * (size_t)(buckets + 1) + 64 + (((size_t)2 * pairs + 15) & ~(size_t)15);
+    return (size_t)2 * vmax * 256 + 4 * (32 * 8 + 4) + (((size_t)2 * pairs + 15) & ~(size_t)15);
 }
 
-std::once_flag g_b_once[2];
-hipError_t g_b_err[2];
+std::once_flag g_b_once[2][kBatchedMenu];
+hipError_t g_b_err[2][kBatchedMenu];
 
 int g_cu_count[64];
 std::once_flag g_cu_once[64];
@@ -227,41 +232,89 @@ int cu_count()
     return g_cu_count[dev];
 }
 
-// Grid: a tile is (expert, row tile) for a gather and (chunk of <= 128
-// vectors, row tile) for a dense call; the ids are read on the device, so
-// the host bounds the tile count by row tiles x min(pairs, buckets) and
-// launches one workgroup per CU (its LDS ring takes 128 KB), each looping
-// over tiles.  Measured on the 512-token gpt-oss prefill chunk (32 experts,
-// K = N = 2880), 4-wave workgroups: 256-row tiles (384) 119 us, 128-row
-// (736) 103 us, 192-row (480) 97 us; 8-wave workgroups with 256-row tiles
-// (two waves per SIMD hide each other's LDS and matrix-core latencies)
-// 91 us.  The 8-wave shape is taken when it gives every CU a tile.
-qmv_status_t launch_batched(const void *codes, const void *scales, int E, const int32_t *ids, int M,
-                            int top_k, const void *x, int x_per_slot, float *y, int N, int K,
-                            hipStream_t stream)
+// Tiles: (expert, R rows) for a gather, (chunk of vectors, R rows) for a
+// dense call, one workgroup each; R = 32 x fragments x waves.  The choice
+// minimizes the estimated time of the call: every CU streams, per weight,
+// R * 0.53 bytes of its tile's codes and scales (twice for gate/up) and
+// 2 bytes per vector of activations, one tile after another, so the time is
+// the number of rounds of tiles over the CUs times that per-tile stream; ties
+// go to taller tiles (fewer re-reads of the activations).  A gather's busy
+// tiles are its experts that some pair selects, estimated as min(E, pairs).
+// Dense calls also choose the vector chunk: a single weight matrix of a few
+// thousand rows gives too few row tiles to fill the GPU, and two chunks of
+// 32 vectors give twice the tiles for twice the weight reads (L2 serves the
+// second).
+struct BatchedPlan { int shape, waves, rows, chunk, row_tiles, tiles, cap; };
+
+BatchedPlan plan_batched(bool gather, bool gate_up, int E, int pairs, int N)
+{
+    const int cus = cu_count();
+    BatchedPlan best = {0, 0, 0, 0, 0, 0, 0};
+    double best_cost = 0.0;
+    const int busy = gather ? (pairs < E ? pairs : E) : 1;
+    const double vbar = gather ? (double)pairs / busy : 0.0;
+    for (int sh = 0; sh < kBatchedMenu; ++sh)
+        for (int ci = 0; ci < (gather ? 1 : 3); ++ci) {
+            const int *const m = gate_up ? kBatchedShapesGU[sh] : kBatchedShapes[sh];
+            const int waves = m[0], cap = m[2];
+            const int rows = 32 * m[1] * waves / (gate_up ? 2 : 1);
+            int chunk = 0;
+            if (!gather) {
+                chunk = ci == 0 ? (pairs < cap ? pairs : cap) : ci == 1 ? 64 : 32;
+                if (chunk > cap || (ci > 0 && chunk >= pairs)) continue;
+            }
+            const int rt = (N + rows - 1) / rows;
+            const long long tiles = (long long)rt * (gather ? busy : (pairs + chunk - 1) / chunk);
+            const long long rounds = (tiles + cus - 1) / cus;
+            // a gather tile takes its expert's vectors in passes of at most cap
+            const double passes = gather ? (vbar > cap ? vbar / cap + 1.0 : 1.0) : 1.0;
+            const double v = gather ? vbar : (double)chunk;
+            const double cost = (double)rounds * (passes * rows * 0.53125 * (gate_up ? 2 : 1) + 2.0 * v);
+            if (best.rows == 0 || cost < best_cost * 0.999) {
+                best = {sh, waves, rows, chunk, rt, 0, cap};
+                best_cost = cost;
+            }
+        }
+    best.tiles = best.row_tiles * (gather ? E : (pairs + best.chunk - 1) / best.chunk);
+    return best;
+}
+
+// Grid: one workgroup per tile, dealt to the XCDs in contiguous runs (the
+// kernel maps workgroup b to tile (b % 8) * per_xcd + b / 8).  Measured on
+// the 512-token gpt-oss prefill chunk (32 experts, K = N = 2880): see the
+// kernel's header for the tile shapes.
+qmv_status_t launch_batched(const void *codes, const void *scales, const void *codes2, const void *scales2,
+                            int E, const int32_t *ids, int M, int top_k, const void *x, int x_per_slot,
+                            float *y, int N, int K, hipStream_t stream)
 {
     const bool gather = ids != nullptr;
+    const bool gate_up = codes2 != nullptr;
     Args a = base_args(QMV_W_MXFP4, QMV_A_BF16, kMXFP4, codes, scales, gather ? E : 1, ids, M,
                        gather ? top_k : 1, x, nullptr, gather ? x_per_slot : 0, y, N, K);
+    a.codes2 = (const uint8_t *)codes2;
+    a.scales2 = (const uint8_t *)scales2;
     const int pairs = gather ? M * top_k : M;
-    const int buckets = gather ? E + 1 : 1;
-    const long long groups = gather ? (pairs < buckets ? pairs : buckets) : (pairs + 127) / 128;
-    const int cus = cu_count();
-    const long long nt8 = (N + 255) / 256;
-    const int rfi = nt8 * groups >= cus ? 1 : 0;
-    const long long nt = rfi ? nt8 : (N + 127) / 128;
-    long long upper = nt * groups;
-    if (upper > cus) upper = cus;
-    upper = (upper + 7) & ~7LL;                    // the kernel deals tiles to 8 XCDs
-    const void *fn = kTableBatched[rfi];
-    std::call_once(g_b_once[rfi], [&] {
-        g_b_err[rfi] = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           batched_lds(kMaxEBatched + 1, kMaxPairsBatched));
+    const BatchedPlan pl = plan_batched(gather, gate_up, gather ? E : 1, pairs, N);
+    a.rows_per_tile = pl.rows;
+    a.bt_row_tiles = pl.row_tiles;
+    a.bt_tiles = pl.tiles;
+    a.bt_per_xcd = (pl.tiles + 7) / 8;
+    a.bt_chunk = pl.chunk;
+    // the activation ring holds the most vectors one chunk can have
+    int vmost = gather ? pairs : pl.chunk;
+    vmost = vmost < pl.cap ? vmost : pl.cap;
+    a.bt_vmax = vmost <= 32 ? 32 : vmost <= 64 ? 64 : vmost <= 96 ? 96 : 128;
+    const int gu = gate_up ? 1 : 0;
+    const void *fn = gate_up ? kTableBatchedGU[pl.shape] : kTableBatched[pl.shape];
+    std::call_once(g_b_once[gu][pl.shape], [&] {
+        g_b_err[gu][pl.shape] = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                    batched_lds(128, kMaxPairsBatched));
     });
-    if (g_b_err[rfi] != hipSuccess)
+    if (g_b_err[gu][pl.shape] != hipSuccess)
         return QMV_EHIP;
     void *kargs[] = {&a};
-    if (hipLaunchKernel(fn, dim3((unsigned)upper), dim3(rfi ? 512 : 256), kargs, batched_lds(buckets, pairs), stream) !=
+    const size_t lds = batched_lds(a.bt_vmax, gather ? pairs : 0);
+    if (hipLaunchKernel(fn, dim3((unsigned)(8 * a.bt_per_xcd)), dim3(64 * pl.waves), kargs, lds, stream) !=
         hipSuccess)
         return QMV_EHIP;
     return QMV_OK;
@@ -319,7 +372,7 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
         }
         return QMV_OK;
     }
-    if (gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM && M <= kGatherGroupsMaxM &&
+    if (gather && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM && M <= kGatherGroupsMaxM &&
         (long long)M * top_k < 2LL * E) {
         // A gather with fewer than two (token, slot) pairs per expert reuses
         // almost no weights, and the decode kernels stream them faster: groups
@@ -329,7 +382,7 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
         const size_t xrow = (size_t)K * 2 * (x_per_slot ? top_k : 1);
         for (int m0 = 0; m0 < M; m0 += kMaxM) {
             const int mg = M - m0 < kMaxM ? M - m0 : kMaxM;
-            const qmv_status_t st = launch(wfmt, afmt, codes, scales, nullptr, nullptr, E, ids + (size_t)m0 * top_k,
+            const qmv_status_t st = launch(wfmt, afmt, codes, scales, codes2, scales2, E, ids + (size_t)m0 * top_k,
                                            mg, top_k, (const uint8_t *)x + (size_t)m0 * xrow, nullptr, x_per_slot,
                                            y + (size_t)m0 * top_k * N, N, K, stream);
             if (st != QMV_OK)
@@ -337,8 +390,8 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
         }
         return QMV_OK;
     }
-    if (!gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM)
-        return launch_batched(codes, scales, E, ids, M, top_k, x, x_per_slot, y, N, K, stream);
+    if (kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM)
+        return launch_batched(codes, scales, codes2, scales2, E, ids, M, top_k, x, x_per_slot, y, N, K, stream);
     if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M >= 2)
         return launch_dense4(codes, scales, x, y, M, N, K, stream);
     const int units = K / kUnitWeights[kind];

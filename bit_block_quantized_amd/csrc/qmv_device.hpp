@@ -68,6 +68,13 @@ struct Args {
     int x_early;             // activation vectors known before routing
     int rows_per_tile;
     int lds_vec_bytes;       // LDS bytes per staged activation vector
+    // batched kernels (more than 4 vectors): tiles of (expert or vector
+    // chunk, row tile), dealt to the 8 XCDs in contiguous runs
+    int bt_row_tiles;        // row tiles per expert
+    int bt_tiles;            // tiles in the call
+    int bt_per_xcd;          // tiles per XCD (ceil(bt_tiles / 8))
+    int bt_chunk;            // dense: vectors per tile
+    int bt_vmax;             // vectors the activation ring holds (32, 64 or 128)
 };
 
 // ------------------------------------------------------------------ helpers

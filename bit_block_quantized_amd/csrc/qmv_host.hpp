@@ -48,9 +48,8 @@ constexpr int kWaveMenu[2] = {4, 8};     // wave64s per workgroup: qmv, qmv_w8
 constexpr int kMaxK = 16384;
 constexpr int kMaxM = 4;
 constexpr int kMaxTopK = 16;
-// The batched MXFP4 x bf16 path (M > 4): (token, slot) pairs and experts are
-// sorted in LDS, 16-bit indices, one bucket per expert plus one for ids
-// outside [0, E).
+// The batched MXFP4 x bf16 path (M > 4): every workgroup lists its expert's
+// (token, slot) pairs in LDS as 16-bit indices; the tiles cover every expert.
 constexpr int kMaxPairsBatched = 8192;
 // Dense MXFP4 x bf16 calls with 5..20 vectors run as groups of 4 on the
 // decode kernels (one expert gives the batched kernel too few tiles).
@@ -103,7 +102,7 @@ inline qmv_status_t validate(int wfmt, const void *codes, const void *scales, lo
     if (top_k > kMaxTopK || K % 32 != 0 || K > kMaxK)
         return QMV_EUNSUPPORTED;
     if (M > kMaxM) {
-        // more than 4 vectors: MXFP4 x bf16 dense and plain gather calls only
+        // more than 4 vectors: MXFP4 x bf16 dense, gather and gate/up calls
         if (!batched_ok || wfmt != QMV_W_MXFP4 || afmt != QMV_A_BF16 ||
             (long long)M * (gather ? top_k : 1) > kMaxPairsBatched || (gather && E > kMaxEBatched))
             return QMV_EUNSUPPORTED;
@@ -150,10 +149,11 @@ inline qmv_status_t check_swiglu(int wfmt, const void *gate_codes, const void *g
                                  const float *y, int N, int K)
 {
     const void *xs = used_xs(afmt, x_scales);
-    const qmv_status_t s = validate(wfmt, gate_codes, gate_scales, E, ids, true, M, top_k, afmt, x, xs, y, N, K);
+    const qmv_status_t s = validate(wfmt, gate_codes, gate_scales, E, ids, true, M, top_k, afmt, x, xs, y, N, K,
+                                    true);
     if (s != QMV_OK)
         return s;
-    return validate(wfmt, up_codes, up_scales, E, ids, true, M, top_k, afmt, x, xs, y, N, K);
+    return validate(wfmt, up_codes, up_scales, E, ids, true, M, top_k, afmt, x, xs, y, N, K, true);
 }
 
 inline qmv_status_t check_combine(int wfmt, const void *codes, const void *scales, int E, const int32_t *ids,
@@ -301,8 +301,9 @@ inline const char *status_text(int status)
     case QMV_OK: return "success";
     case QMV_EINVAL: return "invalid argument (null or misaligned pointer, or a size <= 0)";
     case QMV_EUNSUPPORTED: return "unsupported shape or format (M in [1,4], or up to 8192 "
-                                  "(token, slot) pairs with E <= 1023 for MXFP4+BF16 dense and "
-                                  "gather calls; top_k in [1,16], K % 32 == 0 and K <= 16384; "
+                                  "(token, slot) pairs with E <= 1023 for MXFP4+BF16 dense, "
+                                  "gather and gate/up calls; top_k in [1,16], K % 32 == 0 and "
+                                  "K <= 16384; "
                                   "pairs MXFP4+BF16, MXFP4+Q8B32, CB2/CB3+Q8B32, CB2/CB3+BF16_Q8)";
     case QMV_EHIP: return "the HIP runtime rejected the kernel launch";
     }

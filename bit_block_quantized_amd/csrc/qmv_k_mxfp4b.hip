@@ -1,33 +1,40 @@
 // qmv_k_mxfp4b.hip -- MXFP4 x bf16 products with more than 4 activation
-// vectors: the expert-batched gather (a prefill chunk, a wide verify batch)
-// and the dense call, on the 16x16x32 bf16 matrix cores.
+// vectors: the expert-batched gather (a prefill chunk, a wide verify batch),
+// the fused gate/up gather with SwiGLU, and the dense call, on the 16x16x32
+// bf16 matrix cores.
 //
 // With many vectors per expert the work is a grouped matrix product: each
 // expert's weight rows meet every vector routed to it (mlxcel issue,
 // "Problem / Background": the expert-batched gather_qmm path that prefill
-// takes once enough tokens share each expert).  Every workgroup first sorts
-// the call's (token, slot) pairs by expert in LDS (a counting sort over the
-// ids: count, prefix-sum, place), so nothing is allocated and no second
-// launch is needed.  The sorted list defines the tiles:
+// takes once enough tokens share each expert).
 //
-//   tile = (expert, 16 * RF * WAVES weight rows);
+// Tiles.  A tile is (expert, R consecutive weight rows), R = 16 * RF * WAVES
+// (for the gate/up kernel R counts output rows: each holds a gate and an up
+// row).  The grid has one workgroup per tile of every expert, whether or not
+// any pair selects it, so the tiling needs no device-wide knowledge of the
+// ids and no sort: a workgroup lists its own expert's (token, slot) pairs in
+// index order by scanning the ids with ballots (deterministic, no atomics),
+// and leaves at once when there are none.  The tiles of expert 0 also write
+// the zero rows of pairs whose id is outside [0, E).  Workgroup b runs on XCD
+// b % 8 (the dispatcher deals workgroups round robin); the tiles are dealt to
+// XCDs in contiguous, expert-major runs, so each XCD's L2 holds the
+// activation rows of a few experts, shared by the row tiles that stream them
+// side by side.  A dense call is one expert whose vectors come in index
+// order; there the vectors are split into chunks and each (chunk, row tile)
+// is a tile, so even a single weight matrix gives enough tiles.
 //
-// the workgroup multiplies the tile's rows with all of the expert's vectors,
-// in chunks of at most 128 (equal chunks when an expert has more).  The LDS
-// atomics order an expert's pairs differently in each workgroup, so a chunk
-// must never be a tile of its own: two workgroups would cut different sets.
-// A dense call has one bucket in index order, and there each chunk is a tile
-// (more tiles for the same rows).  Workgroups take the list's tiles in an
-// XCD-aware order until it ends.
-//
-// Inside a tile, wave w owns 16*RF rows as RF fragments of 16.  The K axis is
-// walked in 128-weight slices.  Lane 16q + r loads row r's 32-weight block
-// 4s + q of slice s (16 contiguous bytes), so one load instruction reads 16
-// rows x 64 bytes.  The MFMA's 32-long k axis is then the lane's own block in
-// four 8-weight steps t: in step t, lane group q supplies k = 32(4s + q) + 8t
-// .. + 7 of its row (A) and the matching 8 activations of column r (B).  The
-// dot product does not care which physical k sits in which MFMA slot as long
-// as A and B agree, so this layout costs nothing.
+// Inside a tile, wave w owns RF fragments of 32 rows, multiplied on the
+// 32x32x16 bf16 MFMA (measured on MI355X: about twice the rate per flop of
+// the 16x16x32 form).  K is walked in 128-weight slices.  Lane (r, h) =
+// lane 32 h + r loads row r's 32-weight blocks h and 2 + h of slice s (16
+// contiguous bytes each).  The MFMA's 16-long k axis is split between the
+// lane halves h: in step (jb, t), half h supplies weights 8t .. 8t + 7 of
+// block 2 jb + h of its row (A) and the same 8 activations of vector r (B).
+// The dot product does not care which physical k sits in which MFMA slot as
+// long as A and B agree, so this layout costs nothing.  An expert's vectors
+// are taken up to VCAP at a time (equal chunks when it has more), and the
+// kernel body is compiled for 32, 64, 96 and 128 vectors so that a tile with
+// few vectors loads and multiplies no empty fragments.
 //
 // Decode: v_cvt_scalef32_pk_bf16_fp4 turns 8 nibbles into the A operand with
 // the E8M0 scale folded in; e2m1 * 2^(s-127) is an exact bf16 normal for
@@ -36,39 +43,33 @@
 // by a plain exact path after the loop, which keeps the loop itself to one
 // path.
 //
-// Activations: per slice, every workgroup stages the tile's vectors' 128
-// bf16 values into LDS (256 bytes per vector; chunk index xor-ed with the
-// vector's low 4 bits so that the 16 lanes of one ds_read_b128 quarter hit
-// 16 distinct bank groups), with direct global-to-LDS loads into a ring of
-// four slice buffers.  Loads complete in issue order per wave, so a load's
-// lead can be no longer than that of the loads waited on after it: the
-// activations and the weights of a slice are issued together, three slices
-// ahead, each slice starts with one wait on the wave's own loads and a
-// barrier, and no register holds staged activations.
+// Activations: per slice, the tile's vectors' 128 bf16 values are loaded
+// into registers three slices ahead and written into one of two LDS slice
+// buffers one slice ahead (256 bytes per vector; the 16-byte chunk index
+// xor-ed with the vector's low 4 bits, so the 16 lanes of one ds_read_b128
+// quarter hit 16 distinct bank groups); one barrier per slice.  Weights go
+// straight to registers, three slices ahead.  Every load is an ordinary
+// register load, so the compiler's waits cover exactly what each step uses
+// (direct global-to-LDS loads were measured slower here: the compiler's wait
+// counts do not account for them, which cut the prefetch depth).
 //
 // Every output element is one MFMA column's dot product over the whole of K
-// in a fixed order, so results do not depend on where a vector lands in the
-// sorted list (the LDS counting sort's order within an expert may vary) and
-// are bitwise reproducible.
+// in a fixed order, so results are bitwise reproducible.
 #include "qmv_device.hpp"
 
 namespace qmv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBVecMax = 128;           // vectors per tile: 8 column fragments of 16
-constexpr int kBXBytes = kBVecMax * 256;     // one activation slice buffer
-constexpr int kBAhead = 3;                     // slices loaded ahead of the one multiplied
-constexpr int kBRing = kBAhead + 1;            // activation slice buffers in LDS
+constexpr int kBVecMax = 128;                  // vectors per chunk
+constexpr int kBRing = 2;                      // activation slice buffers in LDS
+constexpr int kBMaxRounds = 32;                // id scan rounds: 8192 pairs / 256 threads
+constexpr int kBatchedMenu = 4;                // kernel shapes (kBatchedShapes)
+constexpr uint32_t kBPast = 0x80000000u;       // >= every buffer size: reads zeros
 
-// s_waitcnt immediate (gfx9 layout) that waits for vmcnt <= N only.
-template <int N> struct kVmcnt {
-    static constexpr int enc = (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
-};
-constexpr uint32_t kBPast = 0x80000000u;   // >= every buffer size: reads zeros
-
-// LDS offset of 16-byte chunk pos (k = 8 pos .. 8 pos + 7 of the slice) of tile vector v.
+// LDS offset of 16-byte chunk pos (k = 8 pos .. 8 pos + 7 of the slice) of ring vector v.
 __device__ __forceinline__ int bx_off(int v, int pos)
 {
     return v * 256 + 16 * (pos ^ (v & 15));
@@ -84,10 +85,67 @@ __device__ __forceinline__ bf16x8 dec8(uint32_t w, float sc)
                                    __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Tiles of a bucket with c pairs: row tiles, times chunks when chunks are tiles.
-__device__ __forceinline__ int tiles_of(int c, int nt, bool chunk_tiles)
+// LDS of a batched workgroup past the activation ring: scan counts
+// (kBMaxRounds * 8 + 1 ints) and the tile's pair list (16-bit pair indices).
+struct BLds {
+    int *cnt;
+    uint16_t *perm;
+};
+
+// The pairs of bucket `bucket` (an expert, or -1 for ids outside [0, E)) in
+// index order, written to L.perm; returns their number.  Every thread loads
+// the ids i = tid + j * THREADS, a ballot per round j gives each wave's
+// matches, one wave turns the (round, wave) counts into offsets, and each
+// thread writes its matches at their rank: the list is the same in every
+// workgroup and needs no atomics.
+// (The ids, pair count and expert count come by value: a reference to the
+// kernel's argument block would make the compiler copy it to scratch.)
+template <int THREADS>
+__device__ int list_pairs(const int32_t *ids, int B, int E, int bucket, const BLds &L)
 {
-    return c == 0 ? 0 : (chunk_tiles ? (c + kBVecMax - 1) / kBVecMax : 1) * nt;
+    constexpr int W = THREADS / 64;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int rounds = (B + THREADS - 1) / THREADS;        // <= kBMaxRounds
+    uint32_t mask = 0;
+#pragma unroll
+    for (int j = 0; j < kBMaxRounds; ++j) {
+        const int i = tid + j * THREADS;
+        if (j < rounds && i < B) {
+            const int e = ids[i];
+            const bool m = bucket >= 0 ? e == bucket : (unsigned)e >= (unsigned)E;
+            mask |= (uint32_t)m << j;
+        }
+    }
+    for (int j = 0; j < rounds; ++j) {
+        const unsigned long long bal = __ballot((mask >> j) & 1u);
+        if (lane == 0) L.cnt[j * W + w] = __popcll(bal);
+    }
+    __syncthreads();
+    if (w == 0) {                                   // exclusive scan of <= 128 counts, 2 per lane
+        const int n = rounds * W;
+        const int v0 = 2 * lane < n ? L.cnt[2 * lane] : 0;
+        const int v1 = 2 * lane + 1 < n ? L.cnt[2 * lane + 1] : 0;
+        int s = v0 + v1;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(s, d);
+            if (lane >= d) s += t;
+        }
+        const int ex = s - v0 - v1;
+        if (2 * lane < n) L.cnt[2 * lane] = ex;
+        if (2 * lane + 1 < n) L.cnt[2 * lane + 1] = ex + v0;
+        if (lane == 63) L.cnt[kBMaxRounds * 8] = s;
+    }
+    __syncthreads();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int j = 0; j < rounds; ++j) {
+        const bool m = (mask >> j) & 1u;
+        const unsigned long long bal = __ballot(m);
+        if (m) L.perm[L.cnt[j * W + w] + __popcll(bal & below)] = (uint16_t)(tid + j * THREADS);
+    }
+    const int total = L.cnt[kBMaxRounds * 8];
+    __syncthreads();
+    return total;
 }
 
 // The outputs of one chunk of vectors over rows [row_lo, row_lo + rows),
@@ -95,308 +153,320 @@ __device__ __forceinline__ int tiles_of(int c, int nt, bool chunk_tiles)
 // sum of e2m1 * x in fp32, times 2^(s-127) built exactly (so scale bytes 0,
 // 1, 253, 254 and 255 come out as they should).  One output per thread at a
 // time, plain loads: slow, and only run for chunks whose weights hold a scale
-// byte outside [2, 252].
-__device__ __forceinline__ void batched_chunk_exact(const Args &a, const uint8_t *codes, const uint8_t *scales,
-                                                 const uint16_t *vecs, int nv, int row_lo, int rows)
+// byte outside [2, 252].  MODE 1 forms the gate and up sums and stores
+// silu(gate) * up.
+template <int MODE>
+__device__ __forceinline__ void batched_chunk_exact(const Args &a, int e, const uint16_t *vecs, int vstart,
+                                                    int nv, int row_lo, int rows)
 {
     const bool gather = a.ids != nullptr;
     for (int o = threadIdx.x; o < rows * nv; o += blockDim.x) {
         const int n = row_lo + o % rows;
-        const int i = vecs[o / rows];
+        const int i = gather ? (int)vecs[o / rows] : vstart + o / rows;
         const int xrow = gather && a.x_per_slot ? i : (gather ? i / a.top_k : i);
         const uint16_t *xv = (const uint16_t *)(a.x + (size_t)xrow * a.x_vec_bytes);
-        const uint8_t *cw = codes + (size_t)n * a.rcb;
-        float acc = 0.0f;
-        for (int blk = 0; blk < a.units; ++blk) {
-            float part = 0.0f;
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t byte = cw[16 * blk + j];
-                const bf16x2 w = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(byte, 1.0f, 0);
-                part = __builtin_fmaf((float)w[0], __uint_as_float((uint32_t)xv[32 * blk + 2 * j] << 16), part);
-                part = __builtin_fmaf((float)w[1], __uint_as_float((uint32_t)xv[32 * blk + 2 * j + 1] << 16), part);
+        float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int h = 0; h < (MODE == 1 ? 2 : 1); ++h) {
+            const uint8_t *codes = (h ? a.codes2 : a.codes) + (long long)e * a.expert_cb;
+            const uint8_t *scales = (h ? a.scales2 : a.scales) + (long long)e * a.expert_sb;
+            const uint8_t *cw = codes + (size_t)n * a.rcb;
+            for (int blk = 0; blk < a.units; ++blk) {
+                float part = 0.0f;
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t byte = cw[16 * blk + j];
+                    const bf16x2 wv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(byte, 1.0f, 0);
+                    part = __builtin_fmaf((float)wv[0], __uint_as_float((uint32_t)xv[32 * blk + 2 * j] << 16), part);
+                    part = __builtin_fmaf((float)wv[1], __uint_as_float((uint32_t)xv[32 * blk + 2 * j + 1] << 16), part);
+                }
+                acc[h] = __builtin_fmaf(part, e8m0_f32(scales[(size_t)n * a.rsb + blk]), acc[h]);
             }
-            acc = __builtin_fmaf(part, e8m0_f32(scales[(size_t)n * a.rsb + blk]), acc);
         }
-        a.y[(size_t)i * a.N + n] = acc;
+        a.y[(size_t)i * a.N + n] = MODE == 1 ? swiglu(acc[0], acc[1]) : acc[0];
     }
 }
 
-template <int RF, int WAVES>
+// One chunk of nv <= VMAX vectors (ring slots 0..nv-1) against this tile's
+// rows.  vecs: the chunk's pair indices (gather), or nullptr with the
+// vectors vstart .. vstart + nv - 1 (dense).
+template <int RF, int WAVES, int MODE, int VMAX>
+__device__ __forceinline__ void batched_chunk(const Args &a, uint8_t *lds, int e, int row_base,
+                                              const uint16_t *vecs, int vstart, int nv)
+{
+    constexpr int TR = 32 * RF * WAVES / (MODE == 1 ? 2 : 1);   // output rows per tile
+    constexpr int XJ = VMAX / (4 * WAVES);          // staging loads (4 vectors each) per wave and slice
+    constexpr int CF = VMAX / 32;                   // column fragments of 32 vectors
+    constexpr int RH = MODE == 1 ? RF / 2 : RF;      // output row fragments per wave
+    static_assert(XJ >= 1 && (MODE == 0 || RF % 2 == 0), "batched kernel shape");
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int r = lane & 31;                        // row (A) / vector (B) within a fragment
+    const int h = lane >> 5;                        // k half of an MFMA step
+    const bool gather = a.ids != nullptr;
+    const int U = a.units;                          // 32-weight blocks per row
+    const int S = (U + 3) >> 2;                     // 128-weight slices
+    const int row0 = row_base + 32 * RH * w;        // this wave's first output row
+    const int nf = (nv + 31) >> 5;                  // column fragments in use
+
+    f32x16 acc[RF][CF];
+#pragma unroll
+    for (int f = 0; f < RF; ++f)
+#pragma unroll
+        for (int g = 0; g < CF; ++g)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) acc[f][g][k] = 0.0f;
+
+    // lane (r, h) streams blocks h and 2 + h of each 128-weight slice of its
+    // fragments' row r
+    __amdgpu_buffer_rsrc_t rc[RF], rs[RF];
+    uint32_t oc[RF], os[RF];
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+        const bool up = MODE == 1 && f >= RH;
+        rc[f] = buffer_rsrc((up ? a.codes2 : a.codes) + (long long)e * a.expert_cb, a.expert_cb);
+        rs[f] = buffer_rsrc((up ? a.scales2 : a.scales) + (long long)e * a.expert_sb, a.expert_sb);
+        const int n = row0 + 32 * (MODE == 1 ? f % RH : f) + r;
+        oc[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rcb + 16u * h : kBPast;
+        os[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rsb + h : kBPast;
+    }
+    // Activation staging: lane 16 c + p of load j holds chunk p (k = 8 p ..
+    // 8 p + 7 of the slice) of ring vector 4 (w + WAVES j) + c, and writes it
+    // where the swizzle puts it.  The loads go through registers (not direct
+    // to LDS), so the compiler's own waits track every load in flight.
+    const int x_bytes = (gather && a.x_per_slot ? a.M * a.top_k : a.M) * a.x_vec_bytes;   // < 2^31
+    uint32_t xo[XJ];
+    int xdst[XJ];
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+        const int v = 4 * (w + WAVES * j) + (lane >> 4);
+        xdst[j] = bx_off(v, lane & 15);
+        uint32_t o = kBPast;
+        if (v < nv) {
+            const int i = gather ? (int)vecs[v] : vstart + v;
+            const int row = gather && a.x_per_slot ? i : (gather ? i / a.top_k : i);
+            o = (uint32_t)row * (uint32_t)a.x_vec_bytes + 16u * (lane & 15);
+        }
+        xo[j] = o;
+    }
+    // (the lambdas below capture no kernel argument: taking the argument
+    // block's address would make the compiler copy it to scratch memory)
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, x_bytes);
+    const int K = a.K;
+    auto load_x = [&](int s, u32x4 (&xr)[XJ]) {
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) {
+            const bool ok = s < S && 128 * s + 8 * (lane & 15) < K && xo[j] != kBPast;
+            xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? xo[j] + 256u * s : kBPast, 0, 0);
+        }
+    };
+    auto store_x = [&](int s, const u32x4 (&xr)[XJ]) {
+        uint8_t *const buf = lds + (s % kBRing) * (VMAX * 256);
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) *(u32x4 *)(buf + xdst[j]) = xr[j];
+    };
+    // (scale bytes one at a time: a row's scales start at any byte, and an
+    // unaligned dword load is far slower than two byte loads)
+    auto load_w = [&](int s, u32x4 (&wc)[RF][2], uint8_t (&sb)[RF][2]) {
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const bool okf = s < S && 4 * s + 2 * jb + h < U && oc[f] != kBPast;
+                wc[f][jb] = __builtin_amdgcn_raw_buffer_load_b128(rc[f], okf ? oc[f] + 64u * s + 32u * jb : kBPast, 0, 0);
+                sb[f][jb] = __builtin_amdgcn_raw_buffer_load_b8(rs[f], okf ? os[f] + 4u * s + 2u * jb : kBPast, 0, 0);
+            }
+        }
+    };
+    // A slice whose scale bytes are all in [2, 252] (every real weight) is
+    // exact with the scale folded into the convert; any other byte only marks
+    // the chunk for the exact recomputation below, which keeps this loop free
+    // of a second path (and the accumulators out of the VALU).
+    int slow = 0;
+    auto compute = [&](int s, const u32x4 (&wc)[RF][2], const uint8_t (&sbr)[RF][2]) {
+        const uint8_t *const buf = lds + (s % kBRing) * (VMAX * 256);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const bool ok = 4 * s + 2 * jb + h < U;
+            float sc[RF];
+#pragma unroll
+            for (int f = 0; f < RF; ++f) {
+                const uint32_t sb = (ok && oc[f] != kBPast) ? (uint32_t)sbr[f][jb] : 127u;
+                slow |= (sb - 2u) > 250u;
+                sc[f] = __uint_as_float(sb << 23);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                // step (jb, t): lane half h supplies weights 8t .. 8t + 7 of
+                // block 2 jb + h of the slice, and the same 8 activations;
+                // every fragment's activations are read before the MFMAs
+                bf16x8 Bv[CF];
+#pragma unroll
+                for (int g = 0; g < CF; ++g)
+                    if (g < nf) Bv[g] = __builtin_bit_cast(bf16x8, lds_read16(buf + bx_off(32 * g + r, 4 * (2 * jb + h) + t)));
+                bf16x8 A[RF];
+#pragma unroll
+                for (int f = 0; f < RF; ++f) A[f] = dec8(wc[f][jb][t], sc[f]);
+#pragma unroll
+                for (int g = 0; g < CF; ++g) {
+                    if (g < nf) {
+#pragma unroll
+                        for (int f = 0; f < RF; ++f)
+                            acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[f], Bv[g], acc[f][g], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    };
+
+    // Slices: weights are loaded 3 slices ahead and activations 2 (register
+    // sets rotating over 3 and 2 slices; the loop is unrolled 6 times), the
+    // activations of slice s + 1 are written to the LDS ring (2 slice
+    // buffers) while slice s is multiplied; one barrier per slice publishes
+    // the buffer just written and frees the one the next write reuses.  The
+    // slice count is padded to a multiple of 6 (the padding reads past the
+    // buffers: zeros).
+    u32x4 wc0[RF][2], wc1[RF][2], wc2[RF][2];
+    uint8_t sb0[RF][2], sb1[RF][2], sb2[RF][2];          // widened only where used
+    u32x4 xr0[XJ], xr1[XJ];
+    load_w(0, wc0, sb0);
+    load_x(0, xr0);
+    load_w(1, wc1, sb1);
+    load_x(1, xr1);
+    load_w(2, wc2, sb2);
+    store_x(0, xr0);
+    load_x(2, xr0);
+    // step s: x(s + 1) sits in register set (s + 1) % 2 (loaded two slices
+    // ago); it is written to LDS and the set refilled with x(s + 3)
+    auto step = [&](int s, u32x4 (&wc)[RF][2], uint8_t (&sb)[RF][2], u32x4 (&xn)[XJ]) {
+        __syncthreads();
+        store_x(s + 1, xn);
+        load_x(s + 3, xn);
+        compute(s, wc, sb);
+        load_w(s + 3, wc, sb);
+    };
+    for (int s = 0; s < S; s += 6) {
+        step(s, wc0, sb0, xr1);
+        step(s + 1, wc1, sb1, xr0);
+        step(s + 2, wc2, sb2, xr1);
+        step(s + 3, wc0, sb0, xr0);
+        step(s + 4, wc1, sb1, xr1);
+        step(s + 5, wc2, sb2, xr0);
+    }
+    if (__syncthreads_or(slow)) {
+        batched_chunk_exact<MODE>(a, e, vecs, vstart, nv, row_base, min(TR, a.N - row_base));
+        __syncthreads();
+        return;
+    }
+
+    // store: lane (vector r, half h) holds rows 8 i + 4 h .. + 3 of each
+    // fragment, four consecutive rows of one vector per i
+    const bool vec4 = (a.N & 3) == 0 && ((uintptr_t)a.y & 15) == 0;
+#pragma unroll
+    for (int g = 0; g < CF; ++g) {
+        const int col = 32 * g + r;
+        if (g < nf && col < nv) {
+            const int i = gather ? (int)vecs[col] : vstart + col;
+            float *const yrow = a.y + (size_t)i * a.N;
+#pragma unroll
+            for (int f = 0; f < RH; ++f) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int n0 = row0 + 32 * f + 8 * ii + 4 * h;
+                    if (n0 < a.N) {
+                        float v[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            v[k] = MODE == 1 ? swiglu(acc[f][g][4 * ii + k], acc[f + RH][g][4 * ii + k])
+                                             : acc[f][g][4 * ii + k];
+                        if (vec4) {
+                            *(float4 *)(yrow + n0) = make_float4(v[0], v[1], v[2], v[3]);
+                        } else {
+#pragma unroll
+                            for (int k = 0; k < 4; ++k)
+                                if (n0 + k < a.N) yrow[n0 + k] = v[k];
+                        }
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();                                // the next chunk refills the ring
+}
+
+// VCAP: the most vectors one chunk holds (register budget: RF * VCAP / 4
+// accumulators per lane).
+template <int RF, int WAVES, int MODE, int VCAP>
 __global__ __launch_bounds__(64 * WAVES, 1) void qmv_batched_kernel(const Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    constexpr int kBThreads = 64 * WAVES;
-    constexpr int TR = 16 * RF * WAVES;            // rows per tile
-    constexpr int BPT = 1024 / kBThreads;          // scan buckets per thread
-    constexpr int XJ = 32 / WAVES;                 // staging instructions (4 vectors each) per wave and slice
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
-    const int r = lane & 15;
-    const int q = lane >> 4;
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int TR = 32 * RF * WAVES / (MODE == 1 ? 2 : 1);
+    // the tile: XCD b % 8 takes the contiguous run of tiles
+    // [xcd * per_xcd, (xcd + 1) * per_xcd)
+    const int b = blockIdx.x;
+    const int t = (b & 7) * a.bt_per_xcd + (b >> 3);
+    if (t >= a.bt_tiles) return;
+    const int bucket = t / a.bt_row_tiles;            // expert (gather) or vector chunk (dense)
+    const int rt = t - bucket * a.bt_row_tiles;
+    const int row_base = rt * TR;
     const bool gather = a.ids != nullptr;
-    const int B = gather ? a.M * a.top_k : a.M;    // (token, slot) pairs
-    const int nb = gather ? a.E + 1 : 1;           // buckets: experts, then invalid ids
-    const int NT = (a.N + TR - 1) / TR;
-    const int U = a.units;                         // 32-weight blocks per row
-    const int S = (U + 3) >> 2;                    // 128-weight slices
+    BLds L;
+    L.cnt = (int *)(lds + kBRing * a.bt_vmax * 256);
+    L.perm = (uint16_t *)(L.cnt + kBMaxRounds * 8 + 4);
 
-    int *const cnt = (int *)(lds + kBRing * kBXBytes);
-    int *const voff = cnt + (nb + 1);
-    int *const toff = voff + (nb + 1);
-    int *const wsum = toff + (nb + 1);             // 2 x 8 wave totals
-    uint16_t *const perm = (uint16_t *)(wsum + 16);
-    uint32_t *const tmp = (uint32_t *)lds;         // (bucket << 16 | rank) per pair, in the x area
-
-    // 1. counting sort of the pairs by expert (a dense call: one bucket, index order)
-    for (int b = tid; b < nb; b += kBThreads) cnt[b] = gather ? 0 : B;
-    __syncthreads();
-    for (int i = tid; i < B; i += kBThreads) {
-        int b = 0, rank = i;
-        if (gather) {
-            const int e = a.ids[i];
-            b = (unsigned)e < (unsigned)a.E ? e : a.E;
-            rank = atomicAdd(&cnt[b], 1);
+    int e = 0, c = 0, vstart = 0;
+    const uint16_t *vecs = nullptr;
+    if (gather) {
+        if (bucket == 0) {
+            // the tiles of expert 0 also write the zero rows of invalid ids
+            const int ci = list_pairs<THREADS>(a.ids, a.M * a.top_k, a.E, -1, L);
+            const int rows = min(TR, a.N - row_base);
+            for (int o = threadIdx.x; o < ci * rows; o += THREADS)
+                a.y[(size_t)L.perm[o / rows] * a.N + row_base + o % rows] = 0.0f;
+            __syncthreads();
         }
-        tmp[i] = ((uint32_t)b << 16) | (uint32_t)rank;
+        e = bucket;
+        c = list_pairs<THREADS>(a.ids, a.M * a.top_k, a.E, bucket, L);
+        if (c == 0) return;
+        vecs = L.perm;
+    } else {
+        vstart = bucket * a.bt_chunk;
+        c = min(a.bt_chunk, a.M - vstart);
     }
-    __syncthreads();
-    {
-        int c[BPT], sv = 0, st = 0;
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-            const int b = BPT * tid + j;
-            c[j] = b < nb ? cnt[b] : 0;
-            sv += c[j];
-            st += tiles_of(c[j], NT, !gather);
-        }
-        const int ov = sv, ot = st;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int tv = __shfl_up(sv, d), tt = __shfl_up(st, d);
-            if (lane >= d) { sv += tv; st += tt; }
-        }
-        if (lane == 63) { wsum[w] = sv; wsum[8 + w] = st; }
-        __syncthreads();
-        int ev = sv - ov, et = st - ot;
-        for (int k = 0; k < w; ++k) { ev += wsum[k]; et += wsum[8 + k]; }
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-            const int b = BPT * tid + j;
-            if (b < nb) { voff[b] = ev; toff[b] = et; }
-            ev += c[j];
-            et += tiles_of(c[j], NT, !gather);
-        }
-        if (tid == kBThreads - 1) { voff[nb] = ev; toff[nb] = et; }
-    }
-    __syncthreads();
-    for (int i = tid; i < B; i += kBThreads) {
-        const uint32_t v = tmp[i];
-        perm[voff[v >> 16] + (v & 0xFFFFu)] = (uint16_t)i;
-    }
-    __syncthreads();
-    const int total = toff[nb];
-
-    const int x_bytes = (gather && a.x_per_slot ? B : a.M) * a.x_vec_bytes;   // < 2^31
-    const bool vec4 = (a.N & 3) == 0 && ((uintptr_t)a.y & 15) == 0;
-
-    // Workgroups are dealt to the 8 XCDs in turn (workgroup b to XCD b % 8;
-    // the grid is a multiple of 8).  Each XCD takes one contiguous eighth of
-    // the expert-major tile list, so its L2 holds the activation rows of a
-    // few experts only, shared by the row tiles of one expert that its CUs
-    // stream at the same time.
-    const int per = (total + 7) >> 3;
-    const int xcd = blockIdx.x & 7;
-    for (int xl = blockIdx.x >> 3; xl < per; xl += gridDim.x >> 3) {
-        const int t = xcd * per + xl;
-        if (t >= total) break;
-        // 2. the tile: bucket, row tile (and chunk, for a dense call)
-        int lo = 0, hi = nb;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (toff[mid] <= t) lo = mid; else hi = mid;
-        }
-        const int b = lo;
-        const int local = t - toff[b];
-        const int c = voff[b + 1] - voff[b];
-        const int nch = (c + kBVecMax - 1) / kBVecMax;
-        const int cs = (c + nch - 1) / nch;
-        const int ct = gather ? 0 : local / NT;    // the tile's chunk, if chunks are tiles
-        const int rt = local - ct * NT;
-        const int row0 = rt * TR + 16 * RF * w;    // this wave's first row
-        for (int chunk = ct; chunk < (gather ? nch : ct + 1); ++chunk) {
-            const int vstart = voff[b] + chunk * cs;
-            const int nv = min(cs, c - chunk * cs);
-            int nf = (nv + 15) >> 4;
-
-            f32x4 acc[RF][8];
-#pragma unroll
-            for (int f = 0; f < RF; ++f)
-#pragma unroll
-                for (int g = 0; g < 8; ++g) acc[f][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-            if (b < a.E || !gather) {
-                const int e = gather ? b : 0;
-                const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (long long)e * a.expert_cb, a.expert_cb);
-                const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.scales + (long long)e * a.expert_sb, a.expert_sb);
-                uint32_t oc[RF], os[RF];
-#pragma unroll
-                for (int f = 0; f < RF; ++f) {
-                    const int n = row0 + 16 * f + r;
-                    oc[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rcb + 16u * q : kBPast;
-                    os[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rsb + q : kBPast;
-                }
-                // Activation staging: direct loads from global memory into a ring
-                // of kBRing LDS slice buffers (each lane's 16 bytes land at the
-                // instruction's LDS base + 16 * lane).  One instruction fills 4
-                // vectors x 256 bytes; wave w issues the vector quads w + WAVES j.
-                // Lane 16 h + p of quad d fills slot p of vector 4 d + h with the
-                // chunk the swizzle puts there, k-chunk p ^ (vector & 15).
-                const int wv = __builtin_amdgcn_readfirstlane(w);
-                uint32_t xo[XJ];
-                int xpos[XJ];
-#pragma unroll
-                for (int j = 0; j < XJ; ++j) {
-                    const int v = 4 * (wv + WAVES * j) + (lane >> 4);
-                    xpos[j] = (lane & 15) ^ (v & 15);
-                    uint32_t o = kBPast;
-                    if (v < nv) {
-                        const int i = perm[vstart + v];
-                        const int row = gather && a.x_per_slot ? i : (gather ? i / a.top_k : i);
-                        o = (uint32_t)row * (uint32_t)a.x_vec_bytes;
-                    }
-                    xo[j] = o;
-                }
-                auto issue_x = [&](int s) {
-                    // (built here from kernel arguments, so it stays in scalar registers)
-                    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, x_bytes);
-                    uint8_t *const buf = lds + (s % kBRing) * kBXBytes;
-#pragma unroll
-                    for (int j = 0; j < XJ; ++j) {
-                        const int k = 128 * s + 8 * xpos[j];
-                        const uint32_t o = (k < a.K && xo[j] != kBPast) ? xo[j] + 2u * k : kBPast;
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                            rx, (__attribute__((address_space(3))) void *)(buf + 1024 * (wv + WAVES * j)), 16, o, 0, 0, 0);
-                    }
-                };
-                auto load_w = [&](int s, u32x4 (&wc)[RF], uint8_t (&sb)[RF]) {
-                    const bool ok = s < S && 4 * s + q < U;
-#pragma unroll
-                    for (int f = 0; f < RF; ++f) {
-                        const bool okf = ok && oc[f] != kBPast;
-                        wc[f] = __builtin_amdgcn_raw_buffer_load_b128(rc, okf ? oc[f] + 64u * s : kBPast, 0, kStream);
-                        sb[f] = __builtin_amdgcn_raw_buffer_load_b8(rs, okf ? os[f] + 4u * s : kBPast, 0, 0);
-                    }
-                };
-                // A slice whose scale bytes are all in [2, 252] (every real
-                // weight) is exact with the scale folded into the convert; any
-                // other byte only marks the chunk for the exact recomputation
-                // below, which keeps this loop free of a second path (and the
-                // accumulators out of the VALU).
-                int slow = 0;
-                auto compute = [&](int s, const u32x4 (&wc)[RF], const uint8_t (&sbr)[RF]) {
-                    const bool ok = 4 * s + q < U;
-                    const uint8_t *const buf = lds + (s % kBRing) * kBXBytes;
-                    bf16x8 A[RF][4];
-#pragma unroll
-                    for (int f = 0; f < RF; ++f) {
-                        const uint32_t sb = (ok && oc[f] != kBPast) ? (uint32_t)sbr[f] : 127u;
-                        slow |= (sb - 2u) > 250u;
-                        const float sc = __uint_as_float(sb << 23);
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) A[f][k] = dec8(wc[f][k], sc);
-                    }
-#pragma unroll
-                    for (int g = 0; g < 8; ++g) {
-                        if (g < nf) {
-                            bf16x8 Bv[4];
-#pragma unroll
-                            for (int k = 0; k < 4; ++k)
-                                Bv[k] = __builtin_bit_cast(bf16x8, lds_read16(buf + bx_off(16 * g + r, 4 * q + k)));
-#pragma unroll
-                            for (int f = 0; f < RF; ++f)
-#pragma unroll
-                                for (int k = 0; k < 4; ++k)
-                                    acc[f][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[f][k], Bv[k], acc[f][g], 0, 0, 0);
-                        }
-                    }
-                };
-                // Top of slice s: this wave's loads of slice s are done once at
-                // most kAfter of its later loads are outstanding (loads complete
-                // in issue order, and every slice issues the same number); the
-                // barrier then covers the other waves' parts of the buffer.
-                constexpr int kAfter = 2 * RF + (kBAhead - 1) * (XJ + 2 * RF);
-                static_assert(kAfter < 64, "vmcnt holds at most 63");
-                auto slice_ready = [&]() {
-                    __builtin_amdgcn_sched_barrier(0);
-                    __builtin_amdgcn_s_waitcnt(kVmcnt<kAfter>::enc);
-                    __syncthreads();
-                };
-
-                // 3. slices, kBAhead (3) ahead for activations and weights alike;
-                //    the slice count is padded to a multiple of 3 (the padding
-                //    reads past the buffers: zeros).
-                u32x4 wc0[RF], wc1[RF], wc2[RF];
-                uint8_t sb0[RF], sb1[RF], sb2[RF];   // widened only where used
-                issue_x(0);
-                load_w(0, wc0, sb0);
-                issue_x(1);
-                load_w(1, wc1, sb1);
-                issue_x(2);
-                load_w(2, wc2, sb2);
-                for (int s = 0; s < S; s += 3) {
-                    slice_ready();
-                    issue_x(s + 3);
-                    compute(s, wc0, sb0);
-                    load_w(s + 3, wc0, sb0);
-                    slice_ready();
-                    issue_x(s + 4);
-                    compute(s + 1, wc1, sb1);
-                    load_w(s + 4, wc1, sb1);
-                    slice_ready();
-                    issue_x(s + 5);
-                    compute(s + 2, wc2, sb2);
-                    load_w(s + 5, wc2, sb2);
-                }
-                // the ring's last loads land before the next chunk reuses it
-                __builtin_amdgcn_s_waitcnt(kVmcnt<0>::enc);
-                if (__syncthreads_or(slow)) {
-                    const int e = gather ? b : 0;
-                    batched_chunk_exact(a, a.codes + (long long)e * a.expert_cb, a.scales + (long long)e * a.expert_sb,
-                                        perm + vstart, nv, rt * TR, min(TR, a.N - rt * TR));
-                    nf = 0;                        // stored: nothing left for step 4
-                }
-            }
-
-            // 4. store: lane 16 (row quad) + column; invalid ids give zero rows
-#pragma unroll
-            for (int f = 0; f < RF; ++f) {
-                const int n0 = row0 + 16 * f + 4 * q;
-#pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    const int col = 16 * g + r;
-                    if (g < nf && col < nv && n0 < a.N) {
-                        const int i = perm[vstart + col];
-                        float *yp = a.y + (size_t)i * a.N + n0;
-                        if (vec4) {
-                            *(float4 *)yp = make_float4(acc[f][g][0], acc[f][g][1], acc[f][g][2], acc[f][g][3]);
-                        } else {
-#pragma unroll
-                            for (int v = 0; v < 4; ++v)
-                                if (n0 + v < a.N) yp[v] = acc[f][g][v];
-                        }
-                    }
-                }
-            }
-            __syncthreads();                           // the next chunk restages x
-        }
+    // an expert's vectors in equal chunks of at most VCAP (dense: one chunk);
+    // the ring holds bt_vmax >= every chunk's vectors
+    const int nch = (c + VCAP - 1) / VCAP;
+    const int cs = (c + nch - 1) / nch;
+    for (int ch = 0; ch < nch; ++ch) {
+        const int nv = min(cs, c - ch * cs);
+        const uint16_t *cv = vecs ? vecs + ch * cs : nullptr;
+        const int vs = vstart + ch * cs;
+        if (nv <= 32)
+            batched_chunk<RF, WAVES, MODE, 32>(a, lds, e, row_base, cv, vs, nv);
+        else if (nv <= 64 || VCAP == 64)
+            batched_chunk<RF, WAVES, MODE, (VCAP < 64 ? 32 : 64)>(a, lds, e, row_base, cv, vs, nv);
+        else if (nv <= 96 || VCAP == 96)
+            batched_chunk<RF, WAVES, MODE, (VCAP < 96 ? 32 : 96)>(a, lds, e, row_base, cv, vs, nv);
+        else
+            batched_chunk<RF, WAVES, MODE, (VCAP < 128 ? 32 : 128)>(a, lds, e, row_base, cv, vs, nv);
     }
 }
 
-// [4 waves x 2 fragments: 128 rows per tile, 8 waves x 2 fragments: 256 rows
-// per tile (two waves per SIMD)]
-extern const void *const kTableBatched[2];
-const void *const kTableBatched[2] = {(const void *)&qmv_batched_kernel<2, 4>,
-                                      (const void *)&qmv_batched_kernel<2, 8>};
+// Instantiations: (waves per workgroup, 32-row fragments per wave, most
+// vectors per chunk), the chunk capacity as large as the register budget
+// allows without scratch memory.  Gate/up kernels hold a gate and an up
+// fragment per output fragment.
+#define QMV_BK(RF, W, MODE, VCAP) (const void *)&qmv_batched_kernel<RF, W, MODE, VCAP>
+extern const int kBatchedShapes[kBatchedMenu][3];
+const int kBatchedShapes[kBatchedMenu][3] = {{4, 1, 128}, {4, 2, 96}, {4, 3, 96}, {8, 1, 128}};
+extern const void *const kTableBatched[kBatchedMenu];
+const void *const kTableBatched[kBatchedMenu] = {QMV_BK(1, 4, 0, 128), QMV_BK(2, 4, 0, 96), QMV_BK(3, 4, 0, 96),
+                                                 QMV_BK(1, 8, 0, 128)};
+extern const int kBatchedShapesGU[kBatchedMenu][3];
+const int kBatchedShapesGU[kBatchedMenu][3] = {{4, 2, 128}, {4, 4, 64}, {4, 6, 32}, {8, 2, 64}};
+extern const void *const kTableBatchedGU[kBatchedMenu];
+const void *const kTableBatchedGU[kBatchedMenu] = {QMV_BK(2, 4, 1, 128), QMV_BK(4, 4, 1, 64), QMV_BK(6, 4, 1, 32),
+                                                   QMV_BK(2, 8, 1, 64)};
+#undef QMV_BK
 
 }  // namespace qmv

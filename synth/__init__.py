@@ -25,7 +25,9 @@ Workload shapes (the expert-projection GEMVs the pages measure):
   overlaps across tokens allowed), MXFP4, K=7168, N=2048.
 * ``C5b`` dense MXFP4, M=4, K=N=7168.
 * ``C6``  prefill chunk: 512 tokens x top-4 of 32 (gpt-oss-20b), MXFP4 x bf16,
-  K=N=2880 -- the expert-batched path for more than 4 vectors.
+  K=N=2880 -- the expert-batched path for more than 4 vectors; ``C6gu`` the
+  same chunk through the fused gate/up projection with SwiGLU; ``C6d`` a
+  dense 7168 x 7168 MXFP4 matrix against 64 vectors.
 
 Activation recipe: bf16 activations are N(0,1) samples rounded to bf16 by
 torch's float32 -> bfloat16 cast (round to nearest even).  int8 activations
@@ -153,6 +155,12 @@ BATCHED_WORKLOADS = {
     "C6": Workload("C6", "gather", "mxfp4", M=512, N=2880, K=2880, seed=13, E=32, top_k=4,
                    desc="gpt-oss-20b MoE prefill chunk: 512 tokens x top-4 of 32 experts, "
                         "K=N=2880, MXFP4 x bf16, expert-batched"),
+    "C6gu": Workload("C6gu", "gate_up", "mxfp4", M=512, N=2880, K=2880, seed=14, E=32, top_k=4,
+                     e8m0=(115, 120),
+                     desc="gpt-oss-20b MoE prefill chunk, fused gate+up with SwiGLU: 512 tokens "
+                          "x top-4 of 32 experts, K=N=2880, MXFP4 x bf16, expert-batched"),
+    "C6d": Workload("C6d", "dense", "mxfp4", M=64, N=7168, K=7168, seed=15,
+                    desc="dense MXFP4 x bf16, 64 vectors, K=N=7168 (batched matrix-core path)"),
 }
 
 

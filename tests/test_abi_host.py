@@ -153,7 +153,10 @@ def swiglu(L, wfmt=W_MXFP4, gc=FAKE, gs=FAKE, uc=FAKE, us=FAKE, E=32, ids=FAKE, 
 
 SWIGLU_CASES = [
     (dict(uc=None), EINVAL), (dict(us=None), EINVAL), (dict(gc=None), EINVAL),
-    (dict(uc=FAKE + 8), EINVAL), (dict(ids=None), EINVAL), (dict(M=5), EUNSUP),
+    (dict(uc=FAKE + 8), EINVAL), (dict(ids=None), EINVAL),
+    # more than 4 tokens: MXFP4 x bf16 only, at most 8192 pairs and 1023 experts
+    (dict(M=5, wfmt=W_CB2, afmt=A_Q8, xs=FAKE), EUNSUP), (dict(M=5, E=1024), EUNSUP),
+    (dict(M=2049), EUNSUP), (dict(M=5, afmt=A_Q8, xs=FAKE), EUNSUP),
     (dict(K=100), EUNSUP), (dict(wfmt=W_CB2), EUNSUP),
     (dict(wfmt=W_CB3, afmt=A_Q8, xs=FAKE, us=FAKE + 2), EINVAL),
 ]

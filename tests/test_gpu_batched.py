@@ -193,6 +193,20 @@ def test_prefill_chunk_full_size_sampled():
     assert_parity(y[outs], yr, A, "C6 sampled")
 
 
+def test_dense_wide_full_size_sampled():
+    """Dense 7168 x 7168 MXFP4 against 64 vectors (the batched kernel, vector
+    chunks as tiles) as bench.py launches it: sampled outputs and 2 whole
+    rows of y."""
+    inp = synth.make(synth.workload("C6d"))
+    y = gpu_call(inp).cpu().numpy().reshape(-1)
+    wl = inp.wl
+    rng = np.random.default_rng(7)
+    outs = np.concatenate([rng.choice(y.size, size=4000, replace=False),
+                           np.arange(wl.N), 37 * wl.N + np.arange(wl.N)])
+    yr, A = oracle_call(inp, outs=outs)
+    assert_parity(y[outs], yr, A, "C6d sampled")
+
+
 def test_gather_tall_tiles():
     """Enough (expert, row tile) tiles for the 8-wave 256-row kernel (one per
     CU and more), with a ragged last tile and N % 4 != 0 (element-wise

@@ -161,6 +161,34 @@ def test_one_hot_weights_equal_gather_rows(wfmt):
         assert np.array_equal(y[0].view(np.uint32), g[0, j].view(np.uint32)), j
 
 
+@pytest.mark.parametrize("wfmt", FMTS)
+def test_signed_and_zero_sum_weights(wfmt):
+    """Router weights of either sign (uniform in [-1, 1]) against the oracle;
+    at unit scales, a token whose weights are +a and -a on two slots of one
+    expert fed the same vector gets exactly the other slots' sum, and negated
+    weights give exactly the negated result."""
+    wl = _combine_wl(wfmt, M=3, N=66, K=320, E=5, top_k=4, seed=17)
+    inp = synth.make(wl)
+    w = np.random.default_rng(171).uniform(-1.0, 1.0, size=(3, 4)).astype(np.float32)
+    y = gpu_combine(inp, weights=w).cpu().numpy()
+    yr, A = oracle_combine(inp, weights=w)
+    assert_parity(y, yr, A, f"{wfmt} signed weights")
+    # zero-sum: broadcast activations, slots 0 and 1 of token 0 on one expert
+    wlb = _combine_wl(wfmt, M=2, N=66, K=320, E=5, top_k=4, x_per_slot=False, seed=18)
+    inp = _unit_scale(synth.make(wlb))
+    inp.ids[0, :] = [3, 3, 1, 4]
+    wz = np.array([[0.75, -0.75, 0.5, -2.0], [-0.25, 1.0, -0.5, 0.125]], np.float32)
+    y = gpu_combine(inp, weights=wz).cpu().numpy()
+    yr, _ = oracle_combine(inp, weights=wz)
+    assert_exact(y, yr, f"{wfmt} zero-sum weights")
+    yn = gpu_combine(inp, weights=-wz).cpu().numpy()
+    assert np.array_equal(yn, -y)
+    only = wz.copy()
+    only[0, :2] = 0.0
+    y2 = gpu_combine(inp, weights=only).cpu().numpy()
+    assert np.array_equal(y[0], y2[0])
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_bitwise_deterministic(name):
     inp = synth.make(synth.COMBINE_WORKLOADS[name].scaled(**SMALL[name]))

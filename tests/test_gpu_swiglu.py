@@ -103,6 +103,12 @@ CASES = {
     "cb2 ragged": ("C3", dict(E=16, N=105)),
     "cb3 K=2048": ("C4", dict(E=16, N=1024, x_per_slot=False)),
     "mxfp4 M=4": ("C5a", dict(E=12, N=59)),
+    # more than 4 tokens: the batched matrix-core kernel (many pairs per
+    # expert), and groups of 4 tokens on the decode kernels (few)
+    "mxfp4 batched M=64": ("C2", dict(E=8, N=300, M=64)),
+    "mxfp4 batched ragged": ("C2", dict(E=3, N=77, K=416, M=200, top_k=2)),
+    "mxfp4 batched one expert": ("C2", dict(E=1, N=130, K=96, M=150, top_k=1)),
+    "mxfp4 few pairs M=6": ("C5a", dict(E=64, N=59, M=6)),
 }
 
 
@@ -163,3 +169,18 @@ def test_swiglu_full_size(base):
     y = gpu_swiglu(inp).cpu().numpy()
     worst = assert_swiglu_parity(y, oracle_swiglu(inp), base)
     print(f"{base} gate/up: worst |err| / bound = {worst:.3e}")
+
+
+def test_prefill_gate_up_full_size_sampled():
+    """The gpt-oss-20b prefill chunk through the fused gate/up projection
+    (512 tokens x top-4 of 32, K=N=2880; the batched kernel) as bench.py
+    launches it: 4000 sampled outputs and 4 whole (token, slot) rows."""
+    inp = synth.make_gate_up(synth.workload("C6gu"))
+    y = gpu_swiglu(inp).cpu().numpy().reshape(-1)
+    wl = inp.wl
+    rng = np.random.default_rng(6)
+    rows = rng.choice(wl.M * wl.top_k, size=4, replace=False)
+    outs = np.concatenate([rng.choice(y.size, size=4000, replace=False)] +
+                          [r * wl.N + np.arange(wl.N) for r in rows])
+    worst = assert_swiglu_parity(y[outs], oracle_swiglu(inp, outs=outs), "C6gu sampled")
+    print(f"C6gu: worst |err| / bound = {worst:.3e}")
