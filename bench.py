@@ -49,6 +49,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+# int8 dot products on the vector ALU (v_dot4_i32_i8: 4 multiply-adds per lane,
+# 16 lanes per SIMD per clock): 256 CUs x 4 SIMDs x 16 x 8 ops x 2.4 GHz
+DOT4_I8_PEAK_TOPS = 256 * 4 * 16 * 8 * 2.4e9 / 1e12
 WFMT = {"mxfp4": 0, "cb2": 1, "cb3": 2}
 HEADLINE = "C2"
 METRIC = "effective weight GB/s and µs/call per expert-gather GEMV; % of HBM peak"
@@ -110,7 +113,8 @@ def other_bytes(wl):
 # Rotation plan: layer copies so that between two reads of the same weights
 # more than the 256 MB Infinity Cache of other weights is read.
 ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40, "C2gu": 4, "C3gu": 1,
-            "C4c": 2, "C2c": 32, "C3q": 2, "C4q": 2, "C2i": 32, "C6": 8, "C6gu": 4, "C6d": 40}
+            "C4c": 2, "C2c": 32, "C3q": 2, "C4q": 2, "C2i": 32, "C6": 8, "C6gu": 4, "C6d": 40,
+            "C7": 1, "C8": 1}
 
 
 def merge_regions(regions):
@@ -434,12 +438,17 @@ def measure(name, steps, warmup, hot=True, clocks=None):
         "layers_rotated": p.L,
     }
     if p.wl.M > 4:
-        # many vectors per expert: also a matrix-core product (2 flops per
-        # weight per routed vector)
+        # many vectors per expert: also a product (2 ops per weight per routed
+        # vector), on the matrix cores (MXFP4 x bf16) or as int8 dot products
+        # on the vector ALU (int8 activations)
         fl = float(p.flops[sel].mean())
         res["flops_per_call"] = fl
-        res["mfma_TFLOPs"] = fl / t / 1e12
-        res["pct_mfma_bf16_peak"] = 100.0 * fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS
+        if p.wl.afmt == "bf16":
+            res["mfma_TFLOPs"] = fl / t / 1e12
+            res["pct_mfma_bf16_peak"] = 100.0 * fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS
+        else:
+            res["int8_TOPs"] = fl / t / 1e12
+            res["pct_dot4_i8_alu_peak"] = 100.0 * fl / t / 1e12 / DOT4_I8_PEAK_TOPS
     ts, v = stream_ceiling(p, warmup, min(steps, 500))
     wcode = float(p.wbytes[warmup:warmup + min(steps, 500)].mean())
     res["stream_ceiling_us_per_call"] = ts * 1e6
@@ -529,7 +538,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c,C3q,C4q,C2i,C6",
+    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c,C3q,C4q,C2i,C6,C7,C8",
                     help="other shapes to measure besides the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")

@@ -132,6 +132,26 @@ const void *kernel_for(int wi, int kind, int variant, int li, int ci, bool gate_
     }
 }
 
+// Grouped kernels (more than 4 tokens through the decode kernels' MACs), all
+// with 4-wave workgroups.
+const void *grouped_kernel_for(int kind, int mode, int li, int ci, bool q8)
+{
+    if (q8) {
+        switch (kind) {
+        case kCB2: return kTableQGR_cb2[mode][li][ci];
+        case kCB2S: return kTableQGR_cb2s[mode][li][ci];
+        default: return kTableQGR_cb3[mode][li][ci];
+        }
+    }
+    switch (kind) {
+    case kMXFP4: return kTableGR_mxfp4[mode][li][ci];
+    case kMXFP4I: return kTableGR_mxfp4i[mode][li][ci];
+    case kCB2: return kTableGR_cb2[mode][li][ci];
+    case kCB2S: return kTableGR_cb2s[mode][li][ci];
+    default: return kTableGR_cb3[mode][li][ci];
+    }
+}
+
 const void *combine_kernel_for(int wi, int kind, int li, int ci, bool q8)
 {
     if (q8) {
@@ -210,7 +230,7 @@ Args base_args(int wfmt, int afmt, int kind, const void *codes, const void *scal
 // pair scan's counts and the tile's pair list: at most 64 + 1 + 16 KB.
 size_t batched_lds(int vmax, int pairs)
 {
-    return (size_t)2 * vmax * 256 + 4 * (32 * 8 + 4) + (((size_t)2 * pairs + 15) & ~(size_t)15);
+    return (size_t)2 * vmax * 256 + kPairCountBytes + (((size_t)2 * pairs + 15) & ~(size_t)15);
 }
 
 std::once_flag g_b_once[2][kBatchedMenu];
@@ -320,6 +340,55 @@ qmv_status_t launch_batched(const void *codes, const void *scales, const void *c
     return QMV_OK;
 }
 
+std::once_flag g_gr_once[2][2][2][5][4][5];             // [q8][waves][mode][kind][lpr][cpl]
+hipError_t g_gr_err[2][2][2][5][4][5];
+
+// More than 4 tokens on the decode kernels' MACs (every format pair; MXFP4 x
+// bf16 when few pairs share an expert): grid (row tiles, experts), each
+// workgroup taking its expert's vectors four at a time.  The launch shape is
+// the decode kernels' choice for the rows the call streams at least once
+// (min(E, pairs) experts' rows); bf16 activations quantized in staging use
+// 8-wave workgroups, as their tuned decode shapes do.
+qmv_status_t launch_grouped(int wfmt, int afmt, const void *codes, const void *scales, const void *codes2,
+                            const void *scales2, int E, const int32_t *ids, int M, int top_k, const void *x,
+                            const void *xs, int x_per_slot, float *y, int N, int K, hipStream_t stream)
+{
+    const bool gather = ids != nullptr;
+    const bool gate_up = codes2 != nullptr;
+    const int kind = kind_of(wfmt, afmt, K);
+    const bool q8 = afmt == QMV_A_BF16_Q8;
+    const int wi = 0;
+    const int pairs = gather ? M * top_k : M;
+    const int busy = gather ? (pairs < E ? pairs : E) : 1;
+    const int units = K / kUnitWeights[kind];
+    const Shape sh = pick_shape(1, units, (long long)N * busy * (gate_up ? 2 : 1), 2);
+    Args a = base_args(wfmt, afmt, kind, codes, scales, gather ? E : 1, ids, M, gather ? top_k : 1, x, xs,
+                       gather ? x_per_slot : 0, y, N, K);
+    a.codes2 = (const uint8_t *)codes2;
+    a.scales2 = (const uint8_t *)scales2;
+    const int waves = kWaveMenu[wi];
+    a.rows_per_tile = waves * (64 / sh.lpr) * (gate_up ? 1 : 2);
+    const int mode = gate_up ? 1 : 0;
+    const void *fn = grouped_kernel_for(kind, mode, sh.li, sh.ci, q8);
+    auto lds_of = [&](int vec_bytes, int np) {
+        return (size_t)4 * vec_bytes + kPairCountBytes + (((size_t)2 * np + 15) & ~(size_t)15);
+    };
+    std::call_once(g_gr_once[q8][wi][mode][kind][sh.li][sh.ci], [&] {
+        const int umax = kMaxK / kUnitWeights[kind];
+        const int vmax = (umax * (kUnitXB[kind] + kUnitAB[kind]) + 15) & ~15;
+        g_gr_err[q8][wi][mode][kind][sh.li][sh.ci] = hipFuncSetAttribute(
+            fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_of(vmax, kMaxPairsBatched));
+    });
+    if (g_gr_err[q8][wi][mode][kind][sh.li][sh.ci] != hipSuccess)
+        return QMV_EHIP;
+    const dim3 grid((unsigned)((N + a.rows_per_tile - 1) / a.rows_per_tile), (unsigned)(gather ? E : 1));
+    void *kargs[] = {&a};
+    if (hipLaunchKernel(fn, grid, dim3(64 * waves), kargs, lds_of(a.lds_vec_bytes, gather ? pairs : 0), stream) !=
+        hipSuccess)
+        return QMV_EHIP;
+    return QMV_OK;
+}
+
 std::once_flag g_d4_once[2];
 hipError_t g_d4_err[2];
 
@@ -372,26 +441,19 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
         }
         return QMV_OK;
     }
-    if (gather && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM && M <= kGatherGroupsMaxM &&
-        (long long)M * top_k < 2LL * E) {
-        // A gather with fewer than two (token, slot) pairs per expert reuses
-        // almost no weights, and the decode kernels stream them faster: groups
-        // of up to 4 tokens, one launch each over their ids, x and y rows.
-        // Measured (4 of 256 experts, K = 7168, N = 2048): 4 tokens 25 us;
-        // batched, 5 tokens 105 us, 8 tokens 90 us, 16 tokens 175 us.
-        const size_t xrow = (size_t)K * 2 * (x_per_slot ? top_k : 1);
-        for (int m0 = 0; m0 < M; m0 += kMaxM) {
-            const int mg = M - m0 < kMaxM ? M - m0 : kMaxM;
-            const qmv_status_t st = launch(wfmt, afmt, codes, scales, codes2, scales2, E, ids + (size_t)m0 * top_k,
-                                           mg, top_k, (const uint8_t *)x + (size_t)m0 * xrow, nullptr, x_per_slot,
-                                           y + (size_t)m0 * top_k * N, N, K, stream);
-            if (st != QMV_OK)
-                return st;
-        }
-        return QMV_OK;
+    if (M > kMaxM) {
+        // More than 4 tokens: MXFP4 x bf16 on the batched matrix-core kernel
+        // when experts are shared (at least two pairs per expert), every
+        // other case on the grouped kernel.  A gather with fewer than two
+        // (token, slot) pairs per expert reuses almost no weights, and the
+        // decode kernels' MACs stream them faster than the matrix-core tiles
+        // (4 of 256 experts, K = 7168, N = 2048: 5 tokens 105 us and 16
+        // tokens 175 us batched, 32 and 94 us as groups of 4 tokens).
+        if (kind == kMXFP4 && afmt == QMV_A_BF16 && (!gather || (long long)M * top_k >= 2LL * E))
+            return launch_batched(codes, scales, codes2, scales2, E, ids, M, top_k, x, x_per_slot, y, N, K, stream);
+        return launch_grouped(wfmt, afmt, codes, scales, codes2, scales2, E, ids, M, top_k, x, xs, x_per_slot, y,
+                              N, K, stream);
     }
-    if (kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM)
-        return launch_batched(codes, scales, codes2, scales2, E, ids, M, top_k, x, x_per_slot, y, N, K, stream);
     if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M >= 2)
         return launch_dense4(codes, scales, x, y, M, N, K, stream);
     const int units = K / kUnitWeights[kind];

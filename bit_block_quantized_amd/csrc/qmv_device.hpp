@@ -153,6 +153,7 @@ struct Item {
     int nv;
     int vec[4];                   // activation vector index (token, or pair)
     unsigned long long dest[4];   // output rows (pair index bits) of each vector
+    int pair[4];                  // grouped kernel: the one output row of each vector
 };
 
 // Token of pair p (M <= 4 tokens of k slots each), without a division.
@@ -175,7 +176,7 @@ __device__ __forceinline__ Item early_item(const Args &a)
     it.expert = 0;
     it.nv = a.ids == nullptr ? a.M : 1;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) { it.vec[m] = m; it.dest[m] = 0ull; }
+    for (int m = 0; m < 4; ++m) { it.vec[m] = m; it.dest[m] = 0ull; it.pair[m] = 0; }
     return it;
 }
 
@@ -189,7 +190,7 @@ __device__ Item route_one(const Args &a, int item_idx)
     it.expert = 0;
     it.nv = 1;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) { it.vec[m] = 0; it.dest[m] = 0ull; }
+    for (int m = 0; m < 4; ++m) { it.vec[m] = 0; it.dest[m] = 0ull; it.pair[m] = 0; }
     if (a.ids == nullptr) {
         if (item_idx == 0) { it.kind = 0; it.dest[0] = 1ull; }
         return it;
@@ -230,7 +231,7 @@ __device__ Item route(const Args &a, int item_idx)
     it.expert = 0;
     it.nv = 0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) { it.vec[m] = 0; it.dest[m] = 0ull; }
+    for (int m = 0; m < 4; ++m) { it.vec[m] = 0; it.dest[m] = 0ull; it.pair[m] = 0; }
 
     if (a.ids == nullptr) {                       // dense: one item, M vectors
         if (item_idx == 0) {
@@ -986,7 +987,7 @@ __device__ __forceinline__ float swiglu(float g, float u)
 // MODE 0: the lane's RT rows are RT consecutive output rows.  MODE 1 (gate/up,
 // RT == 2): the lane's two rows are row n of the gate and row n of the up
 // projection, and the store writes swiglu(gate, up).
-template <int F, int LPR, int CPL, int RT, int NV, int NVMAX, int MODE, bool Q>
+template <int F, int LPR, int CPL, int RT, int NV, int NVMAX, int MODE, bool Q, bool GR = false>
 __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t *lds, int row_base,
                                           uint4 (&xr)[kXReg])
 {
@@ -1055,11 +1056,15 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
 #pragma unroll
                     for (int r = 1; r < RT; ++r) val = (li == r) ? acc[r][v] : val;
                 }
-                unsigned long long d = it.dest[v];
-                while (d) {
-                    const int p = __ffsll((long long)d) - 1;
-                    d &= d - 1ull;
-                    a.y[p * a.N + n] = val;                     // M * top_k * N < 2^31
+                if constexpr (GR) {
+                    a.y[it.pair[v] * a.N + n] = val;            // M * top_k * N < 2^31
+                } else {
+                    unsigned long long d = it.dest[v];
+                    while (d) {
+                        const int p = __ffsll((long long)d) - 1;
+                        d &= d - 1ull;
+                        a.y[p * a.N + n] = val;                 // M * top_k * N < 2^31
+                    }
                 }
             }
         }
@@ -1100,6 +1105,169 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const Args a)
     }
 }
 
+// ------------------------------------------------------------------ grouped
+// More than 4 tokens (a prefill chunk, a wide verify batch) for every format
+// pair: the expert-batched gather of the pages (mlxcel issue #2178, "Problem /
+// Background"; lucebox-hub PR #19, "Depends on": the verify-batch matmul),
+// taken as groups of up to four of an expert's vectors through the decode
+// kernel's own staging, decode, integer block dots and scale epilogue.
+//
+// The grid is (row tile, expert): every expert gets its row tiles whether or
+// not any pair selects it, so no device-wide sort is needed.  A workgroup
+// lists its expert's (token, slot) pairs in index order with ballots (the
+// same list in every workgroup, no atomics) and leaves at once when there
+// are none; then it streams its rows once per group of four vectors (the
+// first pass from memory, the later ones mostly from L2).  The tiles of
+// expert 0 also write the zero rows of pairs whose id is outside [0, E).  A
+// dense call is expert 0 with the vectors in index order.
+
+// Pair listing: with B <= 8192 pairs and workgroups of 64 to 512 threads
+// there are at most 8192 / 64 + 7 = 135 (round, wave) counts; the scan takes
+// up to 4 per lane.
+constexpr int kMaxCounts = kPairCounts;
+
+// LDS past a workgroup's activation area: the (round, wave) counts and their
+// total (kPairCountBytes) and the expert's pair list (16-bit pair indices).
+struct PairList {
+    int *cnt;
+    uint16_t *perm;
+};
+
+// Bits j of the result: pair tid + (j0 + j) * THREADS is in bucket `bucket`
+// (an expert, or -1 for ids outside [0, E)), for the 8 rounds from j0 (eight
+// loads in flight; the index is clamped so every lane loads).
+template <int THREADS>
+__device__ __forceinline__ uint32_t match8(const int32_t *ids, int B, int E, int bucket, int rounds,
+                                           int j0)
+{
+    const int tid = threadIdx.x;
+    int idv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        idv[j] = E;
+        if (j0 + j < rounds) idv[j] = ids[min(tid + (j0 + j) * THREADS, B - 1)];
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const bool inb = j0 + j < rounds && tid + (j0 + j) * THREADS < B;
+        const bool hit = inb && (bucket >= 0 ? idv[j] == bucket : (unsigned)idv[j] >= (unsigned)E);
+        m |= (uint32_t)hit << j;
+    }
+    return m;
+}
+
+// The pairs of bucket `bucket` in index order, written to L.perm; returns
+// their number.  Thread tid looks at the ids i = tid + j * THREADS: a ballot
+// per round j gives each wave's matches, one wave turns the (round, wave)
+// counts into offsets, and a second pass over the ids (from L2) writes each
+// match at its rank.  The list is the same in every workgroup and needs no
+// atomics.  Needs B <= 8192.
+// (The ids, pair count and expert count come by value: a reference to the
+// kernel's argument block would make the compiler copy it to scratch.)
+template <int THREADS>
+__device__ __forceinline__ int list_pairs(const int32_t *ids, int B, int E, int bucket, PairList L)
+{
+    constexpr int W = THREADS / 64;
+    static_assert((8192 + THREADS - 1) / THREADS * W <= kMaxCounts, "pair-list counts");
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int rounds = (B + THREADS - 1) / THREADS;
+    for (int j0 = 0; j0 < rounds; j0 += 8) {
+        const uint32_t m8 = match8<THREADS>(ids, B, E, bucket, rounds, j0);
+        for (int j = 0; j < 8 && j0 + j < rounds; ++j) {
+            const unsigned long long bal = __ballot((m8 >> j) & 1u);
+            if (lane == 0) L.cnt[(j0 + j) * W + w] = __popcll(bal);
+        }
+    }
+    __syncthreads();
+    if (w == 0) {                                   // exclusive scan of the counts, 4 per lane
+        const int n = rounds * W;
+        int v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = 4 * lane + q < n ? L.cnt[4 * lane + q] : 0;
+        const int mine = v[0] + v[1] + v[2] + v[3];
+        int s = mine;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(s, d);
+            if (lane >= d) s += t;
+        }
+        int ex = s - mine;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (4 * lane + q < n) L.cnt[4 * lane + q] = ex;
+            ex += v[q];
+        }
+        if (lane == 63) L.cnt[kMaxCounts] = s;
+    }
+    __syncthreads();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int j0 = 0; j0 < rounds; j0 += 8) {
+        const uint32_t m8 = match8<THREADS>(ids, B, E, bucket, rounds, j0);
+        for (int j = 0; j < 8 && j0 + j < rounds; ++j) {
+            const bool m = (m8 >> j) & 1u;
+            const unsigned long long bal = __ballot(m);
+            if (m)
+                L.perm[L.cnt[(j0 + j) * W + w] + __popcll(bal & below)] =
+                    (uint16_t)(threadIdx.x + (j0 + j) * THREADS);
+        }
+    }
+    const int total = L.cnt[kMaxCounts];
+    __syncthreads();
+    return total;
+}
+
+template <int F, int LPR, int CPL, int MODE, bool Q>
+__global__ __launch_bounds__(kThreads) void qmv_grouped_kernel(const Args a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int RT = 2;
+    const bool gather = a.ids != nullptr;
+    const int e = blockIdx.y;
+    const int row_base = blockIdx.x * a.rows_per_tile;
+    PairList L;
+    L.cnt = (int *)(lds + 4 * a.lds_vec_bytes);
+    L.perm = (uint16_t *)(L.cnt + kMaxCounts + 4);
+    int c;
+    if (gather) {
+        const int B = a.M * a.top_k;
+        if (e == 0) {
+            const int ci = list_pairs<kThreads>(a.ids, B, a.E, -1, L);
+            const int end = min(a.N, row_base + a.rows_per_tile);
+            const int rows = end - row_base;
+            for (int o = threadIdx.x; o < ci * rows; o += kThreads)
+                a.y[(int)L.perm[o / rows] * a.N + row_base + o % rows] = 0.0f;
+            __syncthreads();
+        }
+        c = list_pairs<kThreads>(a.ids, B, a.E, e, L);
+    } else {
+        c = a.M;
+    }
+    for (int g = 0; g < c; g += 4) {
+        Item it;
+        it.kind = 0;
+        it.expert = e;
+        it.nv = min(4, c - g);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            // the pair list is the same in every lane: keep it in scalar registers
+            const int p = __builtin_amdgcn_readfirstlane(
+                gather ? (int)L.perm[g + (m < it.nv ? m : 0)] : g + (m < it.nv ? m : 0));
+            it.pair[m] = p;
+            it.vec[m] = gather && !a.x_per_slot ? p / a.top_k : p;
+            it.dest[m] = 0ull;
+        }
+        uint4 xr[kXReg];
+        switch (it.nv) {
+        case 1: rows_body<F, LPR, CPL, RT, 1, 4, MODE, Q, true>(a, it, lds, row_base, xr); break;
+        case 2: rows_body<F, LPR, CPL, RT, 2, 4, MODE, Q, true>(a, it, lds, row_base, xr); break;
+        case 3: rows_body<F, LPR, CPL, RT, 3, 4, MODE, Q, true>(a, it, lds, row_base, xr); break;
+        default: rows_body<F, LPR, CPL, RT, 4, 4, MODE, Q, true>(a, it, lds, row_base, xr); break;
+        }
+        __syncthreads();                            // the next group restages the activations
+    }
+}
+
 // ------------------------------------------------------------------ combine
 // Down projection with the router-weighted top-k combine:
 //     y[t][n] = sum_j  w[t][j] * g(t, j, n),   g = the gather output of slot j
@@ -1124,6 +1292,7 @@ __device__ __forceinline__ Item combine_item(const Args &a, int t, int g)
     for (int m = 0; m < 4; ++m) {
         it.vec[m] = a.x_per_slot ? t * a.top_k + 4 * g + m : t;
         it.dest[m] = 0ull;
+        it.pair[m] = 0;
     }
     return it;
 }
@@ -1265,6 +1434,16 @@ extern const void *const kTableCB_cb3[4][4];
 extern const void *const kTable_mxfp4i[3][4][5];
 extern const void *const kTableGU_mxfp4i[2][4][5];
 extern const void *const kTableCB_mxfp4i[4][4];
+// Grouped kernels (more than 4 tokens): [mode 0 or 1][lpr][cpl]; built with
+// 4-wave workgroups only.
+extern const void *const kTableGR_mxfp4[2][4][5];
+extern const void *const kTableGR_mxfp4i[2][4][5];
+extern const void *const kTableGR_cb2[2][4][5];
+extern const void *const kTableGR_cb2s[2][4][5];
+extern const void *const kTableGR_cb3[2][4][5];
+extern const void *const kTableQGR_cb2[2][4][5];
+extern const void *const kTableQGR_cb2s[2][4][5];
+extern const void *const kTableQGR_cb3[2][4][5];
 // The same for bf16 activations quantized in staging (2-bit and 3-bit only).
 extern const void *const kTableQ_cb2[3][4][5];
 extern const void *const kTableQ_cb2s[3][4][5];
@@ -1298,3 +1477,10 @@ extern const void *const kTableQCB_cb3[4][4];
 #define QMV_TABLE_GU(F, Q) \
     { { QMV_ROW01(F, 0, 8, 1, Q), QMV_ROW01(F, 0, 16, 1, Q), QMV_ROW01(F, 0, 32, 1, Q), QMV_ROW01(F, 0, 64, 1, Q) }, \
       { QMV_ROW01(F, 1, 8, 1, Q), QMV_ROW01(F, 1, 16, 1, Q), QMV_ROW01(F, 1, 32, 1, Q), QMV_ROW01(F, 1, 64, 1, Q) } }
+#define QMV_KG(F, L, C, MODE, Q) (const void *)&::QMV_NS::qmv_grouped_kernel<F, L, C, MODE, Q>
+#define QMV_ROWG(F, L, MODE, Q) \
+    { QMV_KG(F, L, 1, MODE, Q), QMV_KG(F, L, 2, MODE, Q), QMV_KG(F, L, 3, MODE, Q), \
+      QMV_KG(F, L, 4, MODE, Q), QMV_KG(F, L, 7, MODE, Q) }
+#define QMV_TABLE_GR(F, Q) \
+    { { QMV_ROWG(F, 8, 0, Q), QMV_ROWG(F, 16, 0, Q), QMV_ROWG(F, 32, 0, Q), QMV_ROWG(F, 64, 0, Q) }, \
+      { QMV_ROWG(F, 8, 1, Q), QMV_ROWG(F, 16, 1, Q), QMV_ROWG(F, 32, 1, Q), QMV_ROWG(F, 64, 1, Q) } }

@@ -37,6 +37,11 @@ constexpr int kMenuCpl01[5] = {1, 2, 3, 4, 7};
 constexpr int kMenuCpl2[3] = {1, 2, 4};
 constexpr int kMenuCplC[4] = {1, 2, 3, 4};
 
+// Pair lists of the grouped and batched kernels (more than 4 tokens): room
+// for this many (round, wave) counts plus a total in LDS, ahead of the list.
+constexpr int kPairCounts = 256;
+constexpr int kPairCountBytes = 4 * (kPairCounts + 4);
+
 }  // namespace qmv_cfg
 
 namespace qmv_host {
@@ -48,15 +53,13 @@ constexpr int kWaveMenu[2] = {4, 8};     // wave64s per workgroup: qmv, qmv_w8
 constexpr int kMaxK = 16384;
 constexpr int kMaxM = 4;
 constexpr int kMaxTopK = 16;
-// The batched MXFP4 x bf16 path (M > 4): every workgroup lists its expert's
-// (token, slot) pairs in LDS as 16-bit indices; the tiles cover every expert.
+// More than 4 tokens (the batched and grouped kernels): every workgroup lists
+// its expert's (token, slot) pairs in LDS as 16-bit indices, scanning the ids
+// in at most 32 rounds of 256 threads; the grid covers every expert.
 constexpr int kMaxPairsBatched = 8192;
 // Dense MXFP4 x bf16 calls with 5..20 vectors run as groups of 4 on the
 // decode kernels (one expert gives the batched kernel too few tiles).
 constexpr int kDenseGroupsMaxM = 20;
-// Gathers with fewer than two pairs per expert and at most 64 tokens run as
-// groups of 4 tokens on the decode kernels.
-constexpr int kGatherGroupsMaxM = 64;
 constexpr int kMaxEBatched = 1023;
 
 constexpr int kUnitWeights[5] = {Fmt<kMXFP4>::W, Fmt<kCB2>::W, Fmt<kCB2S>::W, Fmt<kCB3>::W, Fmt<kMXFP4I>::W};
@@ -102,9 +105,9 @@ inline qmv_status_t validate(int wfmt, const void *codes, const void *scales, lo
     if (top_k > kMaxTopK || K % 32 != 0 || K > kMaxK)
         return QMV_EUNSUPPORTED;
     if (M > kMaxM) {
-        // more than 4 vectors: MXFP4 x bf16 dense, gather and gate/up calls
-        if (!batched_ok || wfmt != QMV_W_MXFP4 || afmt != QMV_A_BF16 ||
-            (long long)M * (gather ? top_k : 1) > kMaxPairsBatched || (gather && E > kMaxEBatched))
+        // more than 4 vectors: at most 8192 (token, slot) pairs and 1023 experts
+        if (!batched_ok || (long long)M * (gather ? top_k : 1) > kMaxPairsBatched ||
+            (gather && E > kMaxEBatched))
             return QMV_EUNSUPPORTED;
     }
     const uintptr_t calign = (wfmt == QMV_W_CB2 && K % 64 != 0) ? 8 : (wfmt == QMV_W_CB3 ? 4 : 16);
@@ -161,7 +164,7 @@ inline qmv_status_t check_combine(int wfmt, const void *codes, const void *scale
                                   const void *x_scales, const float *y, int N, int K)
 {
     const qmv_status_t s = validate(wfmt, codes, scales, E, ids, true, M, top_k, afmt, x,
-                                    used_xs(afmt, x_scales), y, N, K);
+                                    used_xs(afmt, x_scales), y, N, K, true);
     if (s != QMV_OK)
         return s;
     if (!route_weights || !aligned(route_weights, 4))
@@ -300,10 +303,9 @@ inline const char *status_text(int status)
     switch (status) {
     case QMV_OK: return "success";
     case QMV_EINVAL: return "invalid argument (null or misaligned pointer, or a size <= 0)";
-    case QMV_EUNSUPPORTED: return "unsupported shape or format (M in [1,4], or up to 8192 "
-                                  "(token, slot) pairs with E <= 1023 for MXFP4+BF16 dense, "
-                                  "gather and gate/up calls; top_k in [1,16], K % 32 == 0 and "
-                                  "K <= 16384; "
+    case QMV_EUNSUPPORTED: return "unsupported shape or format (more than 4 tokens: at most 8192 "
+                                  "(token, slot) pairs and E <= 1023; top_k in [1,16], "
+                                  "K % 32 == 0 and K <= 16384; "
                                   "pairs MXFP4+BF16, MXFP4+Q8B32, CB2/CB3+Q8B32, CB2/CB3+BF16_Q8)";
     case QMV_EHIP: return "the HIP runtime rejected the kernel launch";
     }

@@ -10,4 +10,8 @@ extern const void *const kTableGU_cb2[2][4][5];
 const void *const kTableGU_cb2[2][4][5] = QMV_TABLE_GU(kCB2, false);
 extern const void *const kTableCB_cb2[4][4];
 const void *const kTableCB_cb2[4][4] = QMV_TABLE_CB(kCB2, false);
+#if QMV_WAVES == 4     // grouped kernels: 4-wave workgroups
+extern const void *const kTableGR_cb2[2][4][5];
+const void *const kTableGR_cb2[2][4][5] = QMV_TABLE_GR(kCB2, false);
+#endif
 }  // namespace QMV_NS

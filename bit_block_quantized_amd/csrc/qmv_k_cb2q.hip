@@ -11,4 +11,8 @@ extern const void *const kTableQGU_cb2[2][4][5];
 const void *const kTableQGU_cb2[2][4][5] = QMV_TABLE_GU(kCB2, true);
 extern const void *const kTableQCB_cb2[4][4];
 const void *const kTableQCB_cb2[4][4] = QMV_TABLE_CB(kCB2, true);
+#if QMV_WAVES == 4     // grouped kernels: 4-wave workgroups
+extern const void *const kTableQGR_cb2[2][4][5];
+const void *const kTableQGR_cb2[2][4][5] = QMV_TABLE_GR(kCB2, true);
+#endif
 }  // namespace QMV_NS

@@ -10,4 +10,8 @@ extern const void *const kTableGU_cb2s[2][4][5];
 const void *const kTableGU_cb2s[2][4][5] = QMV_TABLE_GU(kCB2S, false);
 extern const void *const kTableCB_cb2s[4][4];
 const void *const kTableCB_cb2s[4][4] = QMV_TABLE_CB(kCB2S, false);
+#if QMV_WAVES == 4     // grouped kernels: 4-wave workgroups
+extern const void *const kTableGR_cb2s[2][4][5];
+const void *const kTableGR_cb2s[2][4][5] = QMV_TABLE_GR(kCB2S, false);
+#endif
 }  // namespace QMV_NS

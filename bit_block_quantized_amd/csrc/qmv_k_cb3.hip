@@ -10,4 +10,8 @@ extern const void *const kTableGU_cb3[2][4][5];
 const void *const kTableGU_cb3[2][4][5] = QMV_TABLE_GU(kCB3, false);
 extern const void *const kTableCB_cb3[4][4];
 const void *const kTableCB_cb3[4][4] = QMV_TABLE_CB(kCB3, false);
+#if QMV_WAVES == 4     // grouped kernels: 4-wave workgroups
+extern const void *const kTableGR_cb3[2][4][5];
+const void *const kTableGR_cb3[2][4][5] = QMV_TABLE_GR(kCB3, false);
+#endif
 }  // namespace QMV_NS

@@ -10,4 +10,8 @@ extern const void *const kTableGU_mxfp4[2][4][5];
 const void *const kTableGU_mxfp4[2][4][5] = QMV_TABLE_GU(kMXFP4, false);
 extern const void *const kTableCB_mxfp4[4][4];
 const void *const kTableCB_mxfp4[4][4] = QMV_TABLE_CB(kMXFP4, false);
+#if QMV_WAVES == 4     // grouped kernels: 4-wave workgroups
+extern const void *const kTableGR_mxfp4[2][4][5];
+const void *const kTableGR_mxfp4[2][4][5] = QMV_TABLE_GR(kMXFP4, false);
+#endif
 }  // namespace QMV_NS

@@ -65,7 +65,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBVecMax = 128;                  // vectors per chunk
 constexpr int kBRing = 2;                      // activation slice buffers in LDS
-constexpr int kBMaxRounds = 32;                // id scan rounds: 8192 pairs / 256 threads
 constexpr int kBatchedMenu = 4;                // kernel shapes (kBatchedShapes)
 constexpr uint32_t kBPast = 0x80000000u;       // >= every buffer size: reads zeros
 
@@ -83,69 +82,6 @@ __device__ __forceinline__ bf16x8 dec8(uint32_t w, float sc)
     const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
     return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
                                    __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// LDS of a batched workgroup past the activation ring: scan counts
-// (kBMaxRounds * 8 + 1 ints) and the tile's pair list (16-bit pair indices).
-struct BLds {
-    int *cnt;
-    uint16_t *perm;
-};
-
-// The pairs of bucket `bucket` (an expert, or -1 for ids outside [0, E)) in
-// index order, written to L.perm; returns their number.  Every thread loads
-// the ids i = tid + j * THREADS, a ballot per round j gives each wave's
-// matches, one wave turns the (round, wave) counts into offsets, and each
-// thread writes its matches at their rank: the list is the same in every
-// workgroup and needs no atomics.
-// (The ids, pair count and expert count come by value: a reference to the
-// kernel's argument block would make the compiler copy it to scratch.)
-template <int THREADS>
-__device__ int list_pairs(const int32_t *ids, int B, int E, int bucket, const BLds &L)
-{
-    constexpr int W = THREADS / 64;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int rounds = (B + THREADS - 1) / THREADS;        // <= kBMaxRounds
-    uint32_t mask = 0;
-#pragma unroll
-    for (int j = 0; j < kBMaxRounds; ++j) {
-        const int i = tid + j * THREADS;
-        if (j < rounds && i < B) {
-            const int e = ids[i];
-            const bool m = bucket >= 0 ? e == bucket : (unsigned)e >= (unsigned)E;
-            mask |= (uint32_t)m << j;
-        }
-    }
-    for (int j = 0; j < rounds; ++j) {
-        const unsigned long long bal = __ballot((mask >> j) & 1u);
-        if (lane == 0) L.cnt[j * W + w] = __popcll(bal);
-    }
-    __syncthreads();
-    if (w == 0) {                                   // exclusive scan of <= 128 counts, 2 per lane
-        const int n = rounds * W;
-        const int v0 = 2 * lane < n ? L.cnt[2 * lane] : 0;
-        const int v1 = 2 * lane + 1 < n ? L.cnt[2 * lane + 1] : 0;
-        int s = v0 + v1;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int t = __shfl_up(s, d);
-            if (lane >= d) s += t;
-        }
-        const int ex = s - v0 - v1;
-        if (2 * lane < n) L.cnt[2 * lane] = ex;
-        if (2 * lane + 1 < n) L.cnt[2 * lane + 1] = ex + v0;
-        if (lane == 63) L.cnt[kBMaxRounds * 8] = s;
-    }
-    __syncthreads();
-    const unsigned long long below = (1ull << lane) - 1ull;
-    for (int j = 0; j < rounds; ++j) {
-        const bool m = (mask >> j) & 1u;
-        const unsigned long long bal = __ballot(m);
-        if (m) L.perm[L.cnt[j * W + w] + __popcll(bal & below)] = (uint16_t)(tid + j * THREADS);
-    }
-    const int total = L.cnt[kBMaxRounds * 8];
-    __syncthreads();
-    return total;
 }
 
 // The outputs of one chunk of vectors over rows [row_lo, row_lo + rows),
@@ -410,9 +346,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void qmv_batched_kernel(const Args a
     const int rt = t - bucket * a.bt_row_tiles;
     const int row_base = rt * TR;
     const bool gather = a.ids != nullptr;
-    BLds L;
+    PairList L;
     L.cnt = (int *)(lds + kBRing * a.bt_vmax * 256);
-    L.perm = (uint16_t *)(L.cnt + kBMaxRounds * 8 + 4);
+    L.perm = (uint16_t *)(L.cnt + kMaxCounts + 4);
 
     int e = 0, c = 0, vstart = 0;
     const uint16_t *vecs = nullptr;

@@ -10,4 +10,8 @@ extern const void *const kTableGU_mxfp4i[2][4][5];
 const void *const kTableGU_mxfp4i[2][4][5] = QMV_TABLE_GU(kMXFP4I, false);
 extern const void *const kTableCB_mxfp4i[4][4];
 const void *const kTableCB_mxfp4i[4][4] = QMV_TABLE_CB(kMXFP4I, false);
+#if QMV_WAVES == 4     // grouped kernels: 4-wave workgroups
+extern const void *const kTableGR_mxfp4i[2][4][5];
+const void *const kTableGR_mxfp4i[2][4][5] = QMV_TABLE_GR(kMXFP4I, false);
+#endif
 }  // namespace QMV_NS

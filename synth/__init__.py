@@ -161,6 +161,16 @@ BATCHED_WORKLOADS = {
                           "x top-4 of 32 experts, K=N=2880, MXFP4 x bf16, expert-batched"),
     "C6d": Workload("C6d", "dense", "mxfp4", M=64, N=7168, K=7168, seed=15,
                     desc="dense MXFP4 x bf16, 64 vectors, K=N=7168 (batched matrix-core path)"),
+    # A DeepSeek-shaped prefill chunk on the codebook formats: 512 tokens, each
+    # routed to 4 of 256 experts (about 8 (token, slot) pairs per expert),
+    # int8 activations with a scale per 32.
+    "C7": Workload("C7", "gather", "cb2", M=512, N=2048, K=7168, seed=16, E=256, top_k=4,
+                   desc="DeepSeek-shaped MoE prefill chunk, 2-bit gate/up gather: 512 tokens x "
+                        "top-4 of 256, K=7168, N=2048, int8 x"),
+    "C8": Workload("C8", "gather", "cb3", M=512, N=7168, K=2048, seed=17, E=256, top_k=4,
+                   x_per_slot=True,
+                   desc="DeepSeek-shaped MoE prefill chunk, 3-bit down-proj gather: 512 tokens x "
+                        "top-4 of 256, K=2048, N=7168, per-slot int8 x"),
 }
 
 

@@ -80,9 +80,10 @@ DENSE_CASES = [
     (dict(codes=None), EINVAL), (dict(scales=None), EINVAL), (dict(x=None), EINVAL),
     (dict(y=None), EINVAL), (dict(M=0), EINVAL), (dict(N=0), EINVAL), (dict(K=0), EINVAL),
     (dict(N=-5), EINVAL), (dict(K=48), EUNSUP), (dict(K=16416), EUNSUP),
-    # more than 4 vectors: MXFP4 x bf16 only, at most 8192 of them
-    (dict(M=8193), EUNSUP), (dict(M=5, afmt=A_Q8, xs=FAKE), EUNSUP),
-    (dict(M=5, wfmt=W_CB2, afmt=A_Q8, xs=FAKE), EUNSUP),
+    # more than 4 vectors: every format pair, at most 8192 of them
+    (dict(M=8193), EUNSUP), (dict(M=8193, afmt=A_Q8, xs=FAKE), EUNSUP),
+    (dict(M=9000, wfmt=W_CB2, afmt=A_Q8, xs=FAKE), EUNSUP),
+    (dict(M=5, wfmt=W_CB2, afmt=A_Q8, xs=None), EINVAL),
     (dict(afmt=A_Q8, xs=None), EINVAL), (dict(afmt=A_Q8, xs=FAKE + 2), EINVAL),
     (dict(wfmt=W_CB2), EUNSUP), (dict(wfmt=7), EUNSUP),
     (dict(afmt=3), EUNSUP), (dict(afmt=2), EUNSUP), (dict(codes=FAKE + 8), EINVAL),
@@ -100,9 +101,10 @@ def test_dense_validation(L, kw, want):
 GATHER_CASES = [
     (dict(ids=None), EINVAL), (dict(E=0), EINVAL), (dict(top_k=0), EINVAL),
     (dict(top_k=17), EUNSUP), (dict(K=2880 + 16), EUNSUP),
-    # more than 4 vectors: MXFP4 x bf16, at most 8192 (token, slot) pairs and 1023 experts
-    (dict(M=2049), EUNSUP), (dict(M=5, E=1024), EUNSUP), (dict(M=5, afmt=A_Q8, xs=FAKE), EUNSUP),
-    (dict(M=5, wfmt=W_CB3, afmt=A_Q8, xs=FAKE), EUNSUP),
+    # more than 4 vectors: every format pair, at most 8192 (token, slot) pairs and 1023 experts
+    (dict(M=2049), EUNSUP), (dict(M=5, E=1024), EUNSUP), (dict(M=2049, afmt=A_Q8, xs=FAKE), EUNSUP),
+    (dict(M=5, wfmt=W_CB3, afmt=A_Q8, xs=FAKE, E=1024), EUNSUP),
+    (dict(M=5, wfmt=W_CB3, afmt=A_Q8, xs=FAKE, codes=FAKE + 2), EINVAL),
     (dict(wfmt=W_CB2, afmt=A_Q8, xs=None), EINVAL),
     (dict(wfmt=W_CB3, afmt=A_BF16), EUNSUP),
     (dict(wfmt=W_CB2, afmt=A_Q8, xs=FAKE, scales=FAKE + 2), EINVAL),
@@ -154,9 +156,9 @@ def swiglu(L, wfmt=W_MXFP4, gc=FAKE, gs=FAKE, uc=FAKE, us=FAKE, E=32, ids=FAKE, 
 SWIGLU_CASES = [
     (dict(uc=None), EINVAL), (dict(us=None), EINVAL), (dict(gc=None), EINVAL),
     (dict(uc=FAKE + 8), EINVAL), (dict(ids=None), EINVAL),
-    # more than 4 tokens: MXFP4 x bf16 only, at most 8192 pairs and 1023 experts
-    (dict(M=5, wfmt=W_CB2, afmt=A_Q8, xs=FAKE), EUNSUP), (dict(M=5, E=1024), EUNSUP),
-    (dict(M=2049), EUNSUP), (dict(M=5, afmt=A_Q8, xs=FAKE), EUNSUP),
+    # more than 4 tokens: every format pair, at most 8192 pairs and 1023 experts
+    (dict(M=5, wfmt=W_CB2, afmt=A_Q8, xs=FAKE, E=1024), EUNSUP), (dict(M=5, E=1024), EUNSUP),
+    (dict(M=2049), EUNSUP), (dict(M=2049, afmt=A_Q8, xs=FAKE), EUNSUP),
     (dict(K=100), EUNSUP), (dict(wfmt=W_CB2), EUNSUP),
     (dict(wfmt=W_CB3, afmt=A_Q8, xs=FAKE, us=FAKE + 2), EINVAL),
 ]
@@ -176,7 +178,8 @@ def combine(L, wfmt=W_CB3, codes=FAKE, scales=FAKE, E=256, ids=FAKE, rw=FAKE, M=
 COMBINE_CASES = [
     (dict(rw=None), EINVAL), (dict(rw=FAKE + 2), EINVAL), (dict(ids=None), EINVAL),
     (dict(codes=None), EINVAL), (dict(y=FAKE + 1), EINVAL), (dict(xs=None), EINVAL),
-    (dict(M=5), EUNSUP), (dict(top_k=17), EUNSUP), (dict(top_k=0), EINVAL),
+    (dict(M=2049), EUNSUP), (dict(M=5, E=1024), EUNSUP), (dict(top_k=17), EUNSUP),
+    (dict(top_k=0), EINVAL),
     (dict(K=2048 + 16), EUNSUP), (dict(afmt=A_BF16, xs=None), EUNSUP),
     (dict(wfmt=W_MXFP4, afmt=2, xs=None), EUNSUP), (dict(E=0), EINVAL),
 ]

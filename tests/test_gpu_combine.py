@@ -94,7 +94,7 @@ def test_top_k_groups(wfmt, top_k):
 
 
 @pytest.mark.parametrize("wfmt", FMTS)
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 6, 17])
 @pytest.mark.parametrize("per_slot", [True, False])
 def test_m_sweep(wfmt, M, per_slot):
     wl = _combine_wl(wfmt, M=M, N=70, K=448, E=7, top_k=5, x_per_slot=per_slot, seed=10 + M)

@@ -1,0 +1,183 @@
+"""More than 4 activation vectors on the integer-activation paths: 2-bit and
+3-bit codebook weights against int8 blocks (given, or bf16 quantized while
+staged) and MXFP4 weights against int8 blocks (needs an MI355X).
+
+These calls run on the grouped kernel: one launch, a workgroup per (row tile,
+expert); each workgroup lists the (token, slot) pairs of its expert in LDS
+(the pair order of the call) and takes them four at a time through the decode
+kernels' row loop, so an expert's rows are read once per four of its vectors.
+Dense calls are one expert with every vector.  MXFP4 x bf16 gathers with
+fewer than two pairs per expert take the same route (tests in
+test_gpu_batched.py).
+
+Against the oracle on the same seeded inputs: every output within
+1e-3 * sum |w x|; bit-exact at unit scales with int8 activations (integer
+block sums, exact in fp32 in any order); zero rows for ids outside [0, E);
+experts with far more than 128 vectors; the 8192-pair and 1023-expert
+limits; and the DeepSeek-shaped prefill chunk at full size on sampled
+outputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import assert_exact, assert_parity, gpu_call, oracle_call
+
+pytestmark = pytest.mark.gpu
+
+# (weight format, activation format flag): int8 given, bf16 quantized in the
+# kernel (2-/3-bit), int8 against MXFP4
+PAIRS = [("cb2", ""), ("cb2", "bf16"), ("cb3", ""), ("cb3", "bf16"), ("mxfp4", "q8")]
+
+
+def _wl(wfmt, act, kind, M, N, K, E=1, top_k=1, x_per_slot=False, seed=0):
+    return synth.Workload("grouped", kind, wfmt, M=M, N=N, K=K, seed=seed, E=E, top_k=top_k,
+                          x_per_slot=x_per_slot, x_bf16=act == "bf16", x_q8=act == "q8")
+
+
+def _check(inp, what, exact=False):
+    y = gpu_call(inp).cpu().numpy()
+    yr, A = oracle_call(inp)
+    assert y.shape == yr.shape
+    if exact:
+        assert_exact(y, yr, what)
+    return assert_parity(y, yr, A, what)
+
+
+def _name(p):
+    return f"{p[0]}-{p[1] or 'q8'}"
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=_name)
+@pytest.mark.parametrize("M,N,K", [(5, 37, 64), (9, 130, 544), (24, 301, 2048), (64, 77, 7168)])
+def test_dense(pair, M, N, K):
+    wfmt, act = pair
+    _check(synth.make(_wl(wfmt, act, "dense", M, N, K, seed=M + N)), f"{_name(pair)} dense M={M}")
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=_name)
+@pytest.mark.parametrize("M,top_k,E,N,K,per_slot", [(5, 4, 8, 45, 576, False),
+                                                    (16, 4, 32, 300, 2048, False),
+                                                    (64, 4, 256, 96, 1024, False),
+                                                    (40, 6, 12, 259, 1440, True),
+                                                    (8, 16, 20, 33, 64, True)])
+def test_gather(pair, M, top_k, E, N, K, per_slot):
+    wfmt, act = pair
+    inp = synth.make(_wl(wfmt, act, "gather", M, N, K, E=E, top_k=top_k, x_per_slot=per_slot,
+                         seed=7 * M + E))
+    _check(inp, f"{_name(pair)} gather M={M} top_k={top_k} E={E}")
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=_name)
+def test_one_expert_takes_every_pair(pair):
+    """300 pairs on one expert: 75 groups of four in each of its workgroups."""
+    wfmt, act = pair
+    inp = synth.make(_wl(wfmt, act, "gather", 300, 70, 256, E=4, top_k=1, seed=41))
+    inp.ids[...] = 2
+    _check(inp, f"{_name(pair)} one expert")
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=_name)
+def test_invalid_ids_give_zero_rows(pair):
+    wfmt, act = pair
+    inp = synth.make(_wl(wfmt, act, "gather", 24, 50, 256, E=6, top_k=3, seed=42))
+    inp.ids[0, 1] = -1
+    inp.ids[5, :] = 6
+    inp.ids[9, 2] = 2 ** 31 - 1
+    y = gpu_call(inp).cpu().numpy()
+    assert (y[0, 1] == 0).all() and (y[5] == 0).all() and (y[9, 2] == 0).all()
+    _check(inp, f"{_name(pair)} invalid ids")
+
+
+def _unit(inp, seed=97):
+    """Unit weight and activation scales, int8 activations over the full
+    range: every block sum is an integer and every partial sum is exact."""
+    wl = inp.wl
+    if wl.wfmt == "mxfp4":
+        inp.scales[...] = 127
+    else:
+        inp.scales.view(np.float16)[...] = 1.0
+    rng = np.random.default_rng(seed)
+    inp.x = rng.integers(-128, 128, size=inp.x.shape, dtype=np.int16).astype(np.int8)
+    inp.xs = np.full(inp.x.shape[:-1] + (wl.K // 32,), 1.0, np.float16).view(np.uint16)
+    return inp
+
+
+@pytest.mark.parametrize("wfmt", ["cb2", "cb3", "mxfp4"])
+@pytest.mark.parametrize("case", ["dense", "gather", "per-slot"])
+def test_exact_at_unit_scales(wfmt, case):
+    act = "q8" if wfmt == "mxfp4" else ""
+    wl = {"dense": _wl(wfmt, act, "dense", 24, 77, 2048, seed=51),
+          "gather": _wl(wfmt, act, "gather", 64, 45, 1024, E=32, top_k=4, seed=52),
+          "per-slot": _wl(wfmt, act, "gather", 12, 33, 1056, E=5, top_k=4, x_per_slot=True,
+                          seed=53)}[case]
+    inp = _unit(synth.make(wl))
+    _check(inp, f"unit {wfmt} {case}", exact=True)
+
+
+def test_bf16_quantized_in_kernel_exact_sum():
+    """bf16 activations whose every 32-block has absmax 127 * 2^k quantize to
+    power-of-two scales, so with unit weight scales the call must equal, bit
+    for bit, the same call on the oracle's int8 blocks and the oracle itself
+    rounded to fp32: the in-kernel quantizer's integer decisions are pinned
+    on the grouped kernel."""
+    from test_gpu_quant import _exact_sum_bf16_x
+    for wfmt in ("cb2", "cb3"):
+        inp = synth.make(_wl(wfmt, "bf16", "gather", 20, 64, 1024, E=6, top_k=4, seed=57))
+        inp.scales.view(np.float16)[...] = 1.0
+        xb = _exact_sum_bf16_x(58, inp.x.shape[0], inp.wl.K)
+        inp.x = xb
+        y_b = gpu_call(inp).cpu().numpy()
+        qx, d = oracle.load().quantize_q8(xb)
+        qi = synth.make(_wl(wfmt, "", "gather", 20, 64, 1024, E=6, top_k=4, seed=57))
+        qi.codes, qi.scales, qi.ids = inp.codes, inp.scales, inp.ids
+        qi.x, qi.xs = qx, d
+        y_q = gpu_call(qi).cpu().numpy()
+        assert np.array_equal(y_b.view(np.uint32), y_q.view(np.uint32)), wfmt
+        yr, _ = oracle_call(qi)
+        assert_exact(y_b, yr, f"{wfmt} exact-sum bf16")
+
+
+@pytest.mark.parametrize("pair", [("cb2", ""), ("cb3", "bf16"), ("mxfp4", "q8")], ids=_name)
+def test_pair_and_expert_limits(pair):
+    """8192 (token, slot) pairs (the LDS pair list's limit) and 1023 experts."""
+    wfmt, act = pair
+    _check(synth.make(_wl(wfmt, act, "gather", 2048, 20, 64, E=16, top_k=4, seed=81)),
+           f"{_name(pair)} 8192 pairs")
+    _check(synth.make(_wl(wfmt, act, "gather", 300, 24, 96, E=1023, top_k=4, seed=82)),
+           f"{_name(pair)} 1023 experts")
+
+
+def test_every_id_invalid_gives_zeros():
+    import torch
+    inp = synth.make(_wl("cb3", "", "gather", 40, 77, 128, E=5, top_k=3, seed=111))
+    inp.ids[...] = -7
+    out = torch.full((40, 3, 77), float("nan"), device="cuda")
+    y = gpu_call(inp, y=out).cpu().numpy()
+    assert (y == 0).all()
+
+
+def test_bitwise_deterministic():
+    from gpu_util import to_dev
+    inp = synth.make(_wl("cb2", "bf16", "gather", 96, 200, 1024, E=16, top_k=4, seed=91))
+    dev = to_dev(inp)
+    y1 = gpu_call(inp, dev).cpu().numpy()
+    y2 = gpu_call(inp, dev).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["C7", "C8"])
+def test_prefill_chunk_full_size_sampled(name):
+    """The DeepSeek-shaped prefill chunk (512 tokens x top-4 of 256) as
+    bench.py launches it: 2-bit 7168 -> 2048 and 3-bit 2048 -> 7168 per-slot;
+    sampled outputs and 4 whole (token, slot) rows against the oracle."""
+    inp = synth.make(synth.workload(name))
+    y = gpu_call(inp).cpu().numpy().reshape(-1)
+    wl = inp.wl
+    rng = np.random.default_rng(6)
+    rows = rng.choice(wl.M * wl.top_k, size=4, replace=False)
+    outs = np.concatenate([rng.choice(y.size, size=4000, replace=False)] +
+                          [r * wl.N + np.arange(wl.N) for r in rows])
+    yr, A = oracle_call(inp, outs=outs)
+    assert_parity(y[outs], yr, A, f"{name} sampled")

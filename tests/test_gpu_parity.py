@@ -225,9 +225,15 @@ def test_rejects_misaligned_and_leaves_y():
     with pytest.raises(q.QmvError) as e:
         q.qmv_dense("mxfp4", codes, dev["scales"], dev["x"], y=y)
     assert e.value.status == 1
+    # K = 48 (not a multiple of 32) with buffers sized for it: the binding's
+    # size checks pass and the library refuses the shape
+    codes48 = dev["codes"][:, :24].contiguous()
+    scales48 = dev["scales"][:, :1].contiguous()
     with pytest.raises(q.QmvError) as e:
-        q.qmv_dense("mxfp4", dev["codes"], dev["scales"], dev["x"][:, :48], y=y[:, :256])
+        q.qmv_dense("mxfp4", codes48, scales48, dev["x"][:, :48].contiguous(), y=y)
     assert e.value.status == 2
+    with pytest.raises(ValueError):                    # buffers sized for another K
+        q.qmv_dense("mxfp4", dev["codes"], dev["scales"], dev["x"][:, :48], y=y)
     torch.cuda.synchronize()
     assert (y == 3.0).all()
 

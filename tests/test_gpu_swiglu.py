@@ -42,7 +42,7 @@ def _dev(a, dtype=None):
 def gpu_swiglu(inp, y=None):
     import bit_block_quantized_amd as q
     wl = inp.wl
-    if wl.afmt == "bf16":
+    if wl.afmt in ("bf16", "bf16q8"):
         x = _dev(inp.x.view(np.int16), torch.bfloat16)
         xs = None
     else:
@@ -60,10 +60,14 @@ def oracle_swiglu(inp, outs=None):
     total = int(np.prod(shape))
     sel = np.arange(total, dtype=np.int64) if outs is None else np.asarray(outs, np.int64)
     parts = np.array_split(sel, max(1, min(threads(), len(sel) // 64 + 1)))
+    afmt, x, xs = wl.afmt, inp.x, inp.xs
+    if afmt == "bf16q8":                 # the oracle's quantizer, then the int8 definition
+        x, xs = o.quantize_q8(np.asarray(x).reshape(-1, wl.K))
+        afmt = "q8"
 
     def run(p):
         return o.gather_swiglu(wl.wfmt, inp.gcodes, inp.gscales, inp.ucodes, inp.uscales,
-                               inp.ids, wl.afmt, inp.x, inp.xs, outs=p)
+                               inp.ids, afmt, x, xs, outs=p)
 
     with ThreadPoolExecutor(len(parts)) as ex:
         res = list(ex.map(run, parts))
@@ -109,6 +113,13 @@ CASES = {
     "mxfp4 batched ragged": ("C2", dict(E=3, N=77, K=416, M=200, top_k=2)),
     "mxfp4 batched one expert": ("C2", dict(E=1, N=130, K=96, M=150, top_k=1)),
     "mxfp4 few pairs M=6": ("C5a", dict(E=64, N=59, M=6)),
+    # more than 4 tokens with int8 activations (given, or bf16 quantized in
+    # the kernel): the grouped kernel, 4 pairs at a time per expert
+    "cb2 grouped M=24": ("C3", dict(E=16, N=130, M=24, K=1024)),
+    "cb2 grouped M=40 bf16 x": ("C3", dict(E=6, N=70, M=40, K=2048, x_bf16=True)),
+    "cb3 grouped M=12 bf16 x": ("C4", dict(E=10, N=77, M=12, x_per_slot=False, x_bf16=True)),
+    "cb3 grouped one expert": ("C4", dict(E=1, N=45, K=512, M=150, top_k=1, x_per_slot=False)),
+    "mxfp4 int8 grouped M=20": ("C2", dict(E=8, N=50, M=20, x_q8=True)),
 }
 
 
@@ -123,7 +134,7 @@ def test_swiglu_matches_oracle(case):
 
 
 @pytest.mark.parametrize("wfmt,base", [("mxfp4", "C2"), ("cb2", "C3"), ("cb3", "C4")])
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9])
 def test_swiglu_m_sweep(wfmt, base, M):
     inp = synth.make_gate_up(_wl(base, M=M, E=5, top_k=3, N=45, K=576, x_per_slot=False,
                                  seed=40 + M))
