@@ -340,15 +340,20 @@ qmv_status_t launch_batched(const void *codes, const void *scales, const void *c
     return QMV_OK;
 }
 
-std::once_flag g_gr_once[2][2][2][5][4][5];             // [q8][waves][mode][kind][lpr][cpl]
-hipError_t g_gr_err[2][2][2][5][4][5];
+std::once_flag g_gr_once[2][2][5][4][5];                // [q8][mode][kind][lpr][cpl]
+hipError_t g_gr_err[2][2][5][4][5];
+int g_gr_occ[2][2][5][4][5];                            // workgroups per CU by registers
+
+// LDS of a grouped workgroup: four staged activation vectors, the pair
+// scan's counts, the expert bitmap and the pair list.
+size_t grouped_lds(int vec_bytes, int pairs)
+{
+    return (size_t)4 * vec_bytes + kPairCountBytes + kExpertBitmapBytes + (((size_t)2 * pairs + 15) & ~(size_t)15);
+}
 
 // More than 4 tokens on the decode kernels' MACs (every format pair; MXFP4 x
-// bf16 when few pairs share an expert): grid (row tiles, experts), each
-// workgroup taking its expert's vectors four at a time.  The launch shape is
-// the decode kernels' choice for the rows the call streams at least once
-// (min(E, pairs) experts' rows); bf16 activations quantized in staging use
-// 8-wave workgroups, as their tuned decode shapes do.
+// bf16 when few pairs share an expert): one launch of 4-wave workgroups, each
+// taking a run of (expert slot, row tile) items (plan_grouped).
 qmv_status_t launch_grouped(int wfmt, int afmt, const void *codes, const void *scales, const void *codes2,
                             const void *scales2, int E, const int32_t *ids, int M, int top_k, const void *x,
                             const void *xs, int x_per_slot, float *y, int N, int K, hipStream_t stream)
@@ -357,34 +362,46 @@ qmv_status_t launch_grouped(int wfmt, int afmt, const void *codes, const void *s
     const bool gate_up = codes2 != nullptr;
     const int kind = kind_of(wfmt, afmt, K);
     const bool q8 = afmt == QMV_A_BF16_Q8;
-    const int wi = 0;
+    const int mode = gate_up ? 1 : 0;
     const int pairs = gather ? M * top_k : M;
     const int busy = gather ? (pairs < E ? pairs : E) : 1;
     const int units = K / kUnitWeights[kind];
-    const Shape sh = pick_shape(1, units, (long long)N * busy * (gate_up ? 2 : 1), 2);
     Args a = base_args(wfmt, afmt, kind, codes, scales, gather ? E : 1, ids, M, gather ? top_k : 1, x, xs,
                        gather ? x_per_slot : 0, y, N, K);
     a.codes2 = (const uint8_t *)codes2;
     a.scales2 = (const uint8_t *)scales2;
-    const int waves = kWaveMenu[wi];
-    a.rows_per_tile = waves * (64 / sh.lpr) * (gate_up ? 1 : 2);
-    const int mode = gate_up ? 1 : 0;
-    const void *fn = grouped_kernel_for(kind, mode, sh.li, sh.ci, q8);
-    auto lds_of = [&](int vec_bytes, int np) {
-        return (size_t)4 * vec_bytes + kPairCountBytes + (((size_t)2 * np + 15) & ~(size_t)15);
+    const size_t lds = grouped_lds(a.lds_vec_bytes, gather ? pairs : 0);
+    // per kernel, once: the largest LDS any call may ask for, and how many
+    // workgroups a CU holds by the kernel's registers
+    auto prepare = [&](int li, int ci) -> hipError_t {
+        std::call_once(g_gr_once[q8][mode][kind][li][ci], [&] {
+            const void *f = grouped_kernel_for(kind, mode, li, ci, q8);
+            const int umax = kMaxK / kUnitWeights[kind];
+            const int vmax = (umax * (kUnitXB[kind] + kUnitAB[kind]) + 15) & ~15;
+            hipError_t err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 grouped_lds(vmax, kMaxPairsBatched));
+            int n = 0;
+            if (err == hipSuccess)
+                err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64 * kWaveMenu[0], 0);
+            g_gr_err[q8][mode][kind][li][ci] = err;
+            g_gr_occ[q8][mode][kind][li][ci] = n > 0 ? n : 1;
+        });
+        return g_gr_err[q8][mode][kind][li][ci];
     };
-    std::call_once(g_gr_once[q8][wi][mode][kind][sh.li][sh.ci], [&] {
-        const int umax = kMaxK / kUnitWeights[kind];
-        const int vmax = (umax * (kUnitXB[kind] + kUnitAB[kind]) + 15) & ~15;
-        g_gr_err[q8][wi][mode][kind][sh.li][sh.ci] = hipFuncSetAttribute(
-            fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_of(vmax, kMaxPairsBatched));
-    });
-    if (g_gr_err[q8][wi][mode][kind][sh.li][sh.ci] != hipSuccess)
+    bool failed = false;
+    const long long row_bytes = row_code_bytes(wfmt, K) + row_scale_bytes(wfmt, K);
+    const GroupedPlan p = plan_grouped(units, row_bytes, N, busy, gate_up, cu_count(),
+                                       (long long)lds, [&](int li, int ci) {
+                                           if (prepare(li, ci) != hipSuccess) failed = true;
+                                           return g_gr_occ[q8][mode][kind][li][ci];
+                                       });
+    if (failed)
         return QMV_EHIP;
-    const dim3 grid((unsigned)((N + a.rows_per_tile - 1) / a.rows_per_tile), (unsigned)(gather ? E : 1));
+    a.rows_per_tile = p.rows_per_tile;
+    a.gr_tiles = p.tiles;
+    const void *fn = grouped_kernel_for(kind, mode, p.sh.li, p.sh.ci, q8);
     void *kargs[] = {&a};
-    if (hipLaunchKernel(fn, grid, dim3(64 * waves), kargs, lds_of(a.lds_vec_bytes, gather ? pairs : 0), stream) !=
-        hipSuccess)
+    if (hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(64 * kWaveMenu[0]), kargs, lds, stream) != hipSuccess)
         return QMV_EHIP;
     return QMV_OK;
 }

@@ -75,6 +75,8 @@ struct Args {
     int bt_per_xcd;          // tiles per XCD (ceil(bt_tiles / 8))
     int bt_chunk;            // dense: vectors per tile
     int bt_vmax;             // vectors the activation ring holds (32, 64 or 128)
+    // grouped kernel: work items (expert slot, row tile), slot-major
+    int gr_tiles;            // row tiles per expert
 };
 
 // ------------------------------------------------------------------ helpers
@@ -987,7 +989,10 @@ __device__ __forceinline__ float swiglu(float g, float u)
 // MODE 0: the lane's RT rows are RT consecutive output rows.  MODE 1 (gate/up,
 // RT == 2): the lane's two rows are row n of the gate and row n of the up
 // projection, and the store writes swiglu(gate, up).
-template <int F, int LPR, int CPL, int RT, int NV, int NVMAX, int MODE, bool Q, bool GR = false>
+// STAGE = false: the activations of `it` are already in LDS (the grouped
+// kernel's next row tile of the same vectors): no loads, no barrier.
+template <int F, int LPR, int CPL, int RT, int NV, int NVMAX, int MODE, bool Q, bool GR = false,
+          bool STAGE = true>
 __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t *lds, int row_base,
                                           uint4 (&xr)[kXReg])
 {
@@ -1013,14 +1018,18 @@ __device__ __forceinline__ void rows_body(const Args &a, const Item &it, uint8_t
         os[r] = (uint32_t)__umul24(n, a.rsb) + li * Unit<F>::SB;
     }
 
-    if (!a.x_early) xload<F, NVMAX, Q>(a, it, xr);
+    if constexpr (STAGE) {
+        if (!a.x_early) xload<F, NVMAX, Q>(a, it, xr);
+    }
     Unit<F> w[CPL][RT];
     load_scales<F, LPR, CPL, RT>(w, rs, os, 0, li, U);
 #pragma unroll
     for (int c = 0; c < Lead<F, CPL>::v; ++c) load_step<F, LPR, CPL, RT>(w, rc, oc, 0, li, U, c);
-    xstore<F, NVMAX, Q>(a, it, lds, xr);
-    __syncthreads();
-    if (xrest<F, NVMAX, Q>(a, it, lds)) __syncthreads();
+    if constexpr (STAGE) {
+        xstore<F, NVMAX, Q>(a, it, lds, xr);
+        __syncthreads();
+        if (xrest<F, NVMAX, Q>(a, it, lds)) __syncthreads();
+    }
 
     float acc[RT][NV];
 #pragma unroll
@@ -1112,14 +1121,15 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const Args a)
 // taken as groups of up to four of an expert's vectors through the decode
 // kernel's own staging, decode, integer block dots and scale epilogue.
 //
-// The grid is (row tile, expert): every expert gets its row tiles whether or
-// not any pair selects it, so no device-wide sort is needed.  A workgroup
-// lists its expert's (token, slot) pairs in index order with ballots (the
-// same list in every workgroup, no atomics) and leaves at once when there
-// are none; then it streams its rows once per group of four vectors (the
-// first pass from memory, the later ones mostly from L2).  The tiles of
-// expert 0 also write the zero rows of pairs whose id is outside [0, E).  A
-// dense call is expert 0 with the vectors in index order.
+// The grid is (row tile, expert slot), with min(E, pairs) slots: slot y
+// takes the y-th smallest expert id the call selects (a bitmap of the
+// selected experts in LDS; no device-wide sort) and leaves at once when the
+// call selects fewer.  A workgroup lists its expert's (token, slot) pairs in
+// index order with ballots (the same list in every workgroup, no atomics),
+// then streams its rows once per group of four vectors (the first pass from
+// memory, the later ones mostly from L2).  The tiles of slot 0 also write
+// the zero rows of pairs whose id is outside [0, E).  A dense call is one
+// expert with the vectors in index order.
 
 // Pair listing: with B <= 8192 pairs and workgroups of 64 to 512 threads
 // there are at most 8192 / 64 + 7 = 135 (round, wave) counts; the scan takes
@@ -1133,47 +1143,61 @@ struct PairList {
     uint16_t *perm;
 };
 
-// Bits j of the result: pair tid + (j0 + j) * THREADS is in bucket `bucket`
-// (an expert, or -1 for ids outside [0, E)), for the 8 rounds from j0 (eight
-// loads in flight; the index is clamped so every lane loads).
+// Eight rounds of ids: v[j] = ids[tid + (j0 + j) * THREADS] (index clamped to
+// B - 1 so every lane loads; rounds past the last hold E).  A workgroup loads
+// the first eight rounds once and hands them to every scan below, so calls
+// with up to 8 * THREADS pairs read their ids once per workgroup.
+struct Ids8 {
+    int v[8];
+};
+
 template <int THREADS>
-__device__ __forceinline__ uint32_t match8(const int32_t *ids, int B, int E, int bucket, int rounds,
-                                           int j0)
+__device__ __forceinline__ Ids8 load_ids8(const int32_t *ids, int B, int E, int j0)
 {
-    const int tid = threadIdx.x;
-    int idv[8];
+    const int rounds = (B + THREADS - 1) / THREADS;
+    Ids8 r;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        idv[j] = E;
-        if (j0 + j < rounds) idv[j] = ids[min(tid + (j0 + j) * THREADS, B - 1)];
+        r.v[j] = E;
+        if (j0 + j < rounds) r.v[j] = ids[min((int)threadIdx.x + (j0 + j) * THREADS, B - 1)];
     }
+    return r;
+}
+
+// Bits j of the result: pair tid + (j0 + j) * THREADS (id idv.v[j]) exists
+// and is in bucket `bucket` (an expert, or -1 for ids outside [0, E)).
+template <int THREADS>
+__device__ __forceinline__ uint32_t match8(Ids8 idv, int B, int E, int bucket, int j0)
+{
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const bool inb = j0 + j < rounds && tid + (j0 + j) * THREADS < B;
-        const bool hit = inb && (bucket >= 0 ? idv[j] == bucket : (unsigned)idv[j] >= (unsigned)E);
+        const bool inb = (int)threadIdx.x + (j0 + j) * THREADS < B;
+        const int e = idv.v[j];
+        const bool hit = inb && (bucket >= 0 ? e == bucket : (unsigned)e >= (unsigned)E);
         m |= (uint32_t)hit << j;
     }
     return m;
 }
 
 // The pairs of bucket `bucket` in index order, written to L.perm; returns
-// their number.  Thread tid looks at the ids i = tid + j * THREADS: a ballot
-// per round j gives each wave's matches, one wave turns the (round, wave)
-// counts into offsets, and a second pass over the ids (from L2) writes each
-// match at its rank.  The list is the same in every workgroup and needs no
-// atomics.  Needs B <= 8192.
+// their number.  Thread tid looks at the ids i = tid + j * THREADS (the first
+// eight rounds from `first`, later ones loaded here): a ballot per round j
+// gives each wave's matches, one wave turns the (round, wave) counts into
+// offsets, and a second pass writes each match at its rank.  The list is the
+// same in every workgroup and needs no atomics.  Needs B <= 8192.
 // (The ids, pair count and expert count come by value: a reference to the
 // kernel's argument block would make the compiler copy it to scratch.)
 template <int THREADS>
-__device__ __forceinline__ int list_pairs(const int32_t *ids, int B, int E, int bucket, PairList L)
+__device__ __forceinline__ int list_pairs(const int32_t *ids, int B, int E, int bucket, PairList L, Ids8 first)
 {
     constexpr int W = THREADS / 64;
     static_assert((8192 + THREADS - 1) / THREADS * W <= kMaxCounts, "pair-list counts");
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int rounds = (B + THREADS - 1) / THREADS;
     for (int j0 = 0; j0 < rounds; j0 += 8) {
-        const uint32_t m8 = match8<THREADS>(ids, B, E, bucket, rounds, j0);
+        const Ids8 idv = j0 == 0 ? first : load_ids8<THREADS>(ids, B, E, j0);
+        const uint32_t m8 = match8<THREADS>(idv, B, E, bucket, j0);
         for (int j = 0; j < 8 && j0 + j < rounds; ++j) {
             const unsigned long long bal = __ballot((m8 >> j) & 1u);
             if (lane == 0) L.cnt[(j0 + j) * W + w] = __popcll(bal);
@@ -1203,7 +1227,8 @@ __device__ __forceinline__ int list_pairs(const int32_t *ids, int B, int E, int 
     __syncthreads();
     const unsigned long long below = (1ull << lane) - 1ull;
     for (int j0 = 0; j0 < rounds; j0 += 8) {
-        const uint32_t m8 = match8<THREADS>(ids, B, E, bucket, rounds, j0);
+        const Ids8 idv = j0 == 0 ? first : load_ids8<THREADS>(ids, B, E, j0);
+        const uint32_t m8 = match8<THREADS>(idv, B, E, bucket, j0);
         for (int j = 0; j < 8 && j0 + j < rounds; ++j) {
             const bool m = (m8 >> j) & 1u;
             const unsigned long long bal = __ballot(m);
@@ -1217,54 +1242,155 @@ __device__ __forceinline__ int list_pairs(const int32_t *ids, int B, int E, int 
     return total;
 }
 
+// bm[0..32) = the set of expert ids in [0, E) that occur in ids[0..B)
+// (E <= 1024), in LDS; returns the set's size.
+template <int THREADS>
+__device__ __forceinline__ int expert_bitmap(const int32_t *ids, int B, int E, uint32_t *bm, Ids8 first)
+{
+    const int tid = threadIdx.x;
+    const int rounds = (B + THREADS - 1) / THREADS;
+    if (tid < 32) bm[tid] = 0u;
+    __syncthreads();
+    for (int j0 = 0; j0 < rounds; j0 += 8) {
+        const Ids8 idv = j0 == 0 ? first : load_ids8<THREADS>(ids, B, E, j0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int e = idv.v[j];
+            if (tid + (j0 + j) * THREADS < B && (unsigned)e < (unsigned)E)
+                atomicOr(&bm[e >> 5], 1u << (e & 31));
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        int c = tid < 32 ? __popc(bm[tid]) : 0;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d);
+        if (tid == 0) bm[33] = (uint32_t)c;
+    }
+    __syncthreads();
+    return (int)bm[33];
+}
+
+// The y-th smallest id in the bitmap, or -1 when it holds fewer than y + 1;
+// bm[32] carries the answer to every wave.  Every thread reads it before the
+// next barrier, so the next call cannot overwrite it early.
+__device__ __forceinline__ int kth_expert(uint32_t *bm, int y)
+{
+    const int tid = threadIdx.x;
+    if (tid < 64) {                                 // wave 0: 32 bitmap words
+        const uint32_t word = tid < 32 ? bm[tid] : 0u;
+        const int c = __popc(word);
+        int s = c;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(s, d);
+            if (tid >= d) s += t;
+        }
+        if (y >= s - c && y < s) {                  // the word that holds it
+            uint32_t w = word;
+            for (int k = y - (s - c); k > 0; --k) w &= w - 1u;
+            bm[32] = (uint32_t)(32 * tid + __builtin_ctz(w));
+        } else if (tid == 63 && y >= s) {
+            bm[32] = 0xFFFFFFFFu;
+        }
+    }
+    __syncthreads();
+    return (int)bm[32];
+}
+
+// One group of up to four of an expert's vectors over one row tile.
+template <int F, int LPR, int CPL, int MODE, bool Q, bool STAGE>
+__device__ __forceinline__ void grouped_rows(const Args &a, const Item &it, uint8_t *lds, int row_base)
+{
+    constexpr int RT = 2;
+    uint4 xr[kXReg];
+    switch (it.nv) {
+    case 1: rows_body<F, LPR, CPL, RT, 1, 4, MODE, Q, true, STAGE>(a, it, lds, row_base, xr); break;
+    case 2: rows_body<F, LPR, CPL, RT, 2, 4, MODE, Q, true, STAGE>(a, it, lds, row_base, xr); break;
+    case 3: rows_body<F, LPR, CPL, RT, 3, 4, MODE, Q, true, STAGE>(a, it, lds, row_base, xr); break;
+    default: rows_body<F, LPR, CPL, RT, 4, 4, MODE, Q, true, STAGE>(a, it, lds, row_base, xr); break;
+    }
+}
+
+// Work items are (expert slot, row tile) in slot-major order, over the D
+// distinct experts the call selects (counted in every workgroup from the
+// bitmap); workgroup b takes the contiguous run [b T / G, (b + 1) T / G) of
+// the T = D * tiles items (G workgroups, at most one round of the chip), so
+// every workgroup gets the same number of row tiles within one, and a run
+// changes expert at most a few times.  Per expert the pair list is rebuilt; per row tile the groups
+// of four vectors are streamed, and when the expert has at most four vectors
+// they stay staged in LDS from one row tile to the next.
 template <int F, int LPR, int CPL, int MODE, bool Q>
 __global__ __launch_bounds__(kThreads) void qmv_grouped_kernel(const Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    constexpr int RT = 2;
     const bool gather = a.ids != nullptr;
-    const int e = blockIdx.y;
-    const int row_base = blockIdx.x * a.rows_per_tile;
+    uint8_t *tail = lds + 4 * a.lds_vec_bytes;
     PairList L;
-    L.cnt = (int *)(lds + 4 * a.lds_vec_bytes);
-    L.perm = (uint16_t *)(L.cnt + kMaxCounts + 4);
-    int c;
+    L.cnt = (int *)tail;
+    uint32_t *bm = (uint32_t *)(tail + kPairCountBytes);
+    L.perm = (uint16_t *)(tail + kPairCountBytes + kExpertBitmapBytes);
+    const int tiles = a.gr_tiles, rpt = a.rows_per_tile;
+    const int B = a.M * a.top_k;
+    Ids8 id0;
+    int D = 1;
     if (gather) {
-        const int B = a.M * a.top_k;
-        if (e == 0) {
-            const int ci = list_pairs<kThreads>(a.ids, B, a.E, -1, L);
-            const int end = min(a.N, row_base + a.rows_per_tile);
-            const int rows = end - row_base;
+        id0 = load_ids8<kThreads>(a.ids, B, a.E, 0);
+        D = expert_bitmap<kThreads>(a.ids, B, a.E, bm, id0);
+    }
+    const long long T = (long long)D * tiles;
+    const int i0 = (int)((long long)blockIdx.x * T / gridDim.x);
+    const int i1 = (int)((long long)(blockIdx.x + 1) * T / gridDim.x);
+    if (gather) {
+        // the zero rows of pairs whose id is outside [0, E), row tiles dealt
+        // in runs like the items
+        const int z0 = (int)((long long)blockIdx.x * tiles / gridDim.x);
+        const int z1 = (int)((long long)(blockIdx.x + 1) * tiles / gridDim.x);
+        if (z1 > z0) {
+            const int ci = list_pairs<kThreads>(a.ids, B, a.E, -1, L, id0);
+            const int n0 = z0 * rpt;
+            const int rows = min(a.N, z1 * rpt) - n0;
             for (int o = threadIdx.x; o < ci * rows; o += kThreads)
-                a.y[(int)L.perm[o / rows] * a.N + row_base + o % rows] = 0.0f;
+                a.y[(int)L.perm[o / rows] * a.N + n0 + o % rows] = 0.0f;
             __syncthreads();
         }
-        c = list_pairs<kThreads>(a.ids, B, a.E, e, L);
-    } else {
-        c = a.M;
     }
-    for (int g = 0; g < c; g += 4) {
-        Item it;
-        it.kind = 0;
-        it.expert = e;
-        it.nv = min(4, c - g);
+    int cur = -1, c = 0, e = 0;
+    bool staged = false;
+    for (int i = i0; i < i1; ++i) {
+        const int slot = i / tiles;
+        const int row_base = (i - slot * tiles) * rpt;
+        if (slot != cur) {
+            cur = slot;
+            staged = false;
+            if (gather) {
+                e = kth_expert(bm, slot);           // slot < D: a selected expert
+                c = list_pairs<kThreads>(a.ids, B, a.E, e, L, id0);
+            } else {
+                c = a.M;
+            }
+        }
+        for (int g = 0; g < c; g += 4) {
+            Item it;
+            it.kind = 0;
+            it.expert = e;
+            it.nv = min(4, c - g);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            // the pair list is the same in every lane: keep it in scalar registers
-            const int p = __builtin_amdgcn_readfirstlane(
-                gather ? (int)L.perm[g + (m < it.nv ? m : 0)] : g + (m < it.nv ? m : 0));
-            it.pair[m] = p;
-            it.vec[m] = gather && !a.x_per_slot ? p / a.top_k : p;
-            it.dest[m] = 0ull;
+            for (int m = 0; m < 4; ++m) {
+                // the pair list is the same in every lane: scalar registers
+                const int p = __builtin_amdgcn_readfirstlane(
+                    gather ? (int)L.perm[g + (m < it.nv ? m : 0)] : g + (m < it.nv ? m : 0));
+                it.pair[m] = p;
+                it.vec[m] = gather && !a.x_per_slot ? p / a.top_k : p;
+                it.dest[m] = 0ull;
+            }
+            if (staged && c <= 4)
+                grouped_rows<F, LPR, CPL, MODE, Q, false>(a, it, lds, row_base);
+            else
+                grouped_rows<F, LPR, CPL, MODE, Q, true>(a, it, lds, row_base);
+            if (c > 4) __syncthreads();             // the next group restages the activations
         }
-        uint4 xr[kXReg];
-        switch (it.nv) {
-        case 1: rows_body<F, LPR, CPL, RT, 1, 4, MODE, Q, true>(a, it, lds, row_base, xr); break;
-        case 2: rows_body<F, LPR, CPL, RT, 2, 4, MODE, Q, true>(a, it, lds, row_base, xr); break;
-        case 3: rows_body<F, LPR, CPL, RT, 3, 4, MODE, Q, true>(a, it, lds, row_base, xr); break;
-        default: rows_body<F, LPR, CPL, RT, 4, 4, MODE, Q, true>(a, it, lds, row_base, xr); break;
-        }
-        __syncthreads();                            // the next group restages the activations
+        staged = true;
     }
 }
 

@@ -41,6 +41,9 @@ constexpr int kMenuCplC[4] = {1, 2, 3, 4};
 // for this many (round, wave) counts plus a total in LDS, ahead of the list.
 constexpr int kPairCounts = 256;
 constexpr int kPairCountBytes = 4 * (kPairCounts + 4);
+// The grouped kernel's bitmap of the experts a call selects (E <= 1024) and
+// the word that hands one of them to every wave.
+constexpr int kExpertBitmapBytes = 4 * 36;
 
 }  // namespace qmv_cfg
 
@@ -224,6 +227,76 @@ inline Shape pick_shape(int variant, int units, long long rows_total, int rt)
             if (better) {
                 best = {li, ci, lpr, cpl};
                 for (int k = 0; k < 3; ++k) best_key[k] = key[k];
+            }
+        }
+    return best;
+}
+
+// Grouped kernel (more than 4 tokens on the decode kernels' MACs): the
+// launch shape and the number of workgroups.  Work items are (expert slot,
+// row tile) for `busy` slots; G workgroups take equal contiguous runs of
+// them.  With up to 4 rounds of work G is one round of the chip and the
+// slowest workgroup streams ceil(items / G) row tiles; with more, G = items.  Each row tile costs its
+// weight rows plus a fixed start-up (the first loads' latency, about the
+// time to stream 24 KB at one workgroup's share of the bandwidth).  Among the
+// shapes with little padding of K, take the cheapest slowest workgroup, then
+// the most units in flight.  row_bytes: code and scale bytes of one weight
+// row; occ(li, ci): workgroups per CU the shape's kernel can hold by its
+// registers; lds: bytes of LDS per workgroup.
+struct GroupedPlan {
+    Shape sh;
+    int rows_per_tile;   // output rows per row tile
+    int tiles;           // row tiles per expert
+    int items;           // busy * tiles
+    int grid;            // workgroups
+};
+
+constexpr int kLdsPerCU = 160 * 1024;
+
+template <class Occ>
+inline GroupedPlan plan_grouped(int units, long long row_bytes, int N, int busy, bool gate_up, int cus,
+                                long long lds, Occ occ)
+{
+    const int *cmenu = kMenuCpl01;
+    const int ncpl = 5;
+    double best_eff = 0.0;
+    for (int li = 0; li < 4; ++li)
+        for (int ci = 0; ci < ncpl; ++ci) {
+            const long long seg = (long long)kMenuLpr[li] * cmenu[ci];
+            const double eff = (double)units / (double)(((units + seg - 1) / seg) * seg);
+            if (eff > best_eff) best_eff = eff;
+        }
+    const double startup_rows = 2.0 + 24576.0 / (double)(row_bytes > 0 ? row_bytes : 1);
+    const long long by_lds = lds > 0 ? kLdsPerCU / lds : 1;
+    GroupedPlan best = {{0, 0, kMenuLpr[0], cmenu[0]}, 0, 0, 0, 0};
+    double best_cost = -1.0;
+    for (int li = 0; li < 4; ++li)
+        for (int ci = 0; ci < ncpl; ++ci) {
+            const int lpr = kMenuLpr[li], cpl = cmenu[ci];
+            const long long seg = (long long)lpr * cpl;
+            const double eff = (double)units / (double)(((units + seg - 1) / seg) * seg);
+            if (eff < 0.85 * best_eff) continue;
+            const int rpt = 4 * (64 / lpr) * (gate_up ? 1 : 2);
+            const int wrows = 4 * (64 / lpr) * 2;
+            const int tiles = (N + rpt - 1) / rpt;
+            const long long items = (long long)busy * tiles;
+            long long per_cu = occ(li, ci);
+            if (per_cu > by_lds) per_cu = by_lds;
+            if (per_cu < 1) per_cu = 1;
+            const long long slots = per_cu * cus;
+            // up to 4 rounds of the chip: one round of workgroups, each a run
+            // of row tiles (balanced runs beat a partial last round); more:
+            // one row tile per workgroup (a workgroup that starts as another
+            // retires overlaps its first loads with the other's last ones,
+            // which a run of tiles in one workgroup does not)
+            const long long grid = items > 4 * slots ? items : items < slots ? items : slots;
+            const long long run = (items + grid - 1) / grid;
+            const long long rounds = (grid + slots - 1) / slots;
+            const double cost = (double)(run * rounds) * ((double)wrows / eff + startup_rows);
+            if (best_cost < 0.0 || cost < best_cost * 0.999 ||
+                (cost <= best_cost * 1.001 && cpl > best.sh.cpl)) {
+                best_cost = cost;
+                best = {{li, ci, lpr, cpl}, rpt, tiles, (int)items, (int)grid};
             }
         }
     return best;

@@ -353,16 +353,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void qmv_batched_kernel(const Args a
     int e = 0, c = 0, vstart = 0;
     const uint16_t *vecs = nullptr;
     if (gather) {
+        const Ids8 id0 = load_ids8<THREADS>(a.ids, a.M * a.top_k, a.E, 0);
         if (bucket == 0) {
             // the tiles of expert 0 also write the zero rows of invalid ids
-            const int ci = list_pairs<THREADS>(a.ids, a.M * a.top_k, a.E, -1, L);
+            const int ci = list_pairs<THREADS>(a.ids, a.M * a.top_k, a.E, -1, L, id0);
             const int rows = min(TR, a.N - row_base);
             for (int o = threadIdx.x; o < ci * rows; o += THREADS)
                 a.y[(size_t)L.perm[o / rows] * a.N + row_base + o % rows] = 0.0f;
             __syncthreads();
         }
         e = bucket;
-        c = list_pairs<THREADS>(a.ids, a.M * a.top_k, a.E, bucket, L);
+        c = list_pairs<THREADS>(a.ids, a.M * a.top_k, a.E, bucket, L, id0);
         if (c == 0) return;
         vecs = L.perm;
     } else {
