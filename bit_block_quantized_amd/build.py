@@ -21,13 +21,15 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 KERNEL_SOURCES = ["qmv_k_mxfp4.hip", "qmv_k_mxfp4i.hip", "qmv_k_cb2.hip", "qmv_k_cb2s.hip", "qmv_k_cb3.hip",
                   "qmv_k_cb2q.hip", "qmv_k_cb2sq.hip", "qmv_k_cb3q.hip"]
-# (source, extra flags, object): the launcher, the probe, the MXFP4 x bf16
-# matrix-core kernels for 2-4 vectors and for more (their workgroup size is a
-# template argument or fixed), and every other kernel table twice -- 4 and 8
-# wave64s per workgroup, in namespaces qmv / qmv_w8.
+# (source, extra flags, object): the launcher, the probe, the matrix-core
+# kernels (MXFP4 x bf16 for 2-4 vectors and for more, codebook x int8 for
+# more than 4; their workgroup size is a template argument or fixed), and
+# every other kernel table twice -- 4 and 8 wave64s per workgroup, in
+# namespaces qmv / qmv_w8.
 UNITS = ([("qmv.hip", [], "qmv.o"), ("qmv_probe.hip", [], "qmv_probe.o"),
           ("qmv_k_mxfp4m.hip", [], "qmv_k_mxfp4m.o"),
-          ("qmv_k_mxfp4b.hip", [], "qmv_k_mxfp4b.o")] +
+          ("qmv_k_mxfp4b.hip", [], "qmv_k_mxfp4b.o"),
+          ("qmv_k_cbm.hip", [], "qmv_k_cbm.o")] +
          [(k, [], k.replace(".hip", ".o")) for k in KERNEL_SOURCES] +
          [(k, ["-DQMV_WAVES=8", "-DQMV_NS=qmv_w8"], k.replace(".hip", "_w8.o")) for k in KERNEL_SOURCES])
 SOURCES = [u[0] for u in UNITS]

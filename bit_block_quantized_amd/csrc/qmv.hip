@@ -48,6 +48,13 @@ extern const void *const kTableDense4[2];
 // (qmv_k_mxfp4b.hip): a menu of kernel shapes, each (waves per workgroup,
 // 32-row fragments per wave, most vectors per chunk); gate/up kernels hold a
 // gate and an up fragment per output fragment.
+// 2-bit and 3-bit codebook weights x int8 activations with more than 4
+// vectors per expert on the int8 4x4x4 matrix cores (qmv_k_cbm.hip):
+// [2-bit, 3-bit][vector groups of 4 per staged chunk: 1, 2, 3, 4]; 8 waves.
+namespace qmv {
+extern const void *const kTableGmma[2][4];
+}
+
 namespace qmv {
 constexpr int kBatchedMenu = 4;
 extern const int kBatchedShapes[kBatchedMenu][3];
@@ -406,6 +413,69 @@ qmv_status_t launch_grouped(int wfmt, int afmt, const void *codes, const void *s
     return QMV_OK;
 }
 
+std::once_flag g_gm_once[2][4];
+hipError_t g_gm_err[2][4];
+int g_gm_occ[2][4];                                     // workgroups per CU by registers
+constexpr int kGmWaves = 8;
+constexpr int kGmNvg[4] = {1, 2, 3, 4};
+
+// Codebook weights x int8 activations, more than 4 vectors, several per
+// expert: one launch of the int8 matrix-core kernel.  A workgroup's LDS:
+// the staged vector groups (per group of 4 and unit: the activations in
+// selector order and the per-block side data), the pair scan and bitmap,
+// the pair list.  The groups per chunk cover the average expert's vectors
+// (with room for a few more) as far as the LDS allows; the grid is at most
+// one round of the chip, each workgroup an equal run of (expert, 32-row
+// tile) items, so one staging of a chunk serves many row tiles.
+qmv_status_t launch_gmma(int wfmt, int kind, const void *codes, const void *scales, int E, const int32_t *ids,
+                         int M, int top_k, const void *x, const void *xs, int x_per_slot, float *y, int N, int K,
+                         hipStream_t stream)
+{
+    const bool gather = ids != nullptr;
+    const int fi = kind == kCB2 ? 0 : 1;
+    const int pairs = gather ? M * top_k : M;
+    const int busy = gather ? (pairs < E ? pairs : E) : 1;
+    const int U = K / kUnitWeights[kind];
+    const int Up = (U + 15) & ~15;
+    const size_t group_bytes = (size_t)Up * (fi == 0 ? 256 + 64 : 128 + 16);
+    const size_t tail = kPairCountBytes + kExpertBitmapBytes + (((size_t)2 * (gather ? pairs : 0) + 15) & ~(size_t)15);
+    // groups of 4 for the average expert's vectors and half again (the
+    // counts spread around the average), as far as one workgroup's LDS allows
+    const int avg = (pairs + busy - 1) / busy;
+    const int want = (avg + avg / 2 + 3) / 4;
+    int ni = want < 1 ? 0 : want > 4 ? 3 : want - 1;
+    while (ni > 0 && kGmNvg[ni] * group_bytes + tail > (size_t)kLdsPerCU) --ni;
+    const size_t lds = kGmNvg[ni] * group_bytes + tail;
+    if (lds > (size_t)kLdsPerCU)
+        return QMV_EUNSUPPORTED;
+    const void *fn = kTableGmma[fi][ni];
+    std::call_once(g_gm_once[fi][ni], [&] {
+        hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCU);
+        int n = 0;
+        if (err == hipSuccess)
+            err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * kGmWaves, 0);
+        g_gm_err[fi][ni] = err;
+        g_gm_occ[fi][ni] = n > 0 ? n : 1;
+    });
+    if (g_gm_err[fi][ni] != hipSuccess)
+        return QMV_EHIP;
+    Args a = base_args(wfmt, QMV_A_Q8B32, kind, codes, scales, gather ? E : 1, ids, M, gather ? top_k : 1, x, xs,
+                       gather ? x_per_slot : 0, y, N, K);
+    a.rows_per_tile = 4 * kGmWaves;
+    a.gr_tiles = (N + a.rows_per_tile - 1) / a.rows_per_tile;
+    const long long items = (long long)busy * a.gr_tiles;
+    long long per_cu = g_gm_occ[fi][ni];
+    const long long by_lds = (long long)kLdsPerCU / (long long)lds;
+    if (per_cu > by_lds) per_cu = by_lds;
+    if (per_cu < 1) per_cu = 1;
+    const long long slots = per_cu * cu_count();
+    const unsigned grid = (unsigned)(items < slots ? items : slots);
+    void *kargs[] = {&a};
+    if (hipLaunchKernel(fn, dim3(grid), dim3(64 * kGmWaves), kargs, lds, stream) != hipSuccess)
+        return QMV_EHIP;
+    return QMV_OK;
+}
+
 std::once_flag g_d4_once[2];
 hipError_t g_d4_err[2];
 
@@ -468,6 +538,11 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
         // tokens 175 us batched, 32 and 94 us as groups of 4 tokens).
         if (kind == kMXFP4 && afmt == QMV_A_BF16 && (!gather || (long long)M * top_k >= 2LL * E))
             return launch_batched(codes, scales, codes2, scales2, E, ids, M, top_k, x, x_per_slot, y, N, K, stream);
+        // codebook weights x int8 with at least two vectors per expert on
+        // average: the int8 matrix-core kernel
+        if ((kind == kCB2 || kind == kCB3) && afmt == QMV_A_Q8B32 && !gate_up &&
+            (gather ? (long long)M * top_k >= 2LL * E : M >= 8))
+            return launch_gmma(wfmt, kind, codes, scales, E, ids, M, top_k, x, xs, x_per_slot, y, N, K, stream);
         return launch_grouped(wfmt, afmt, codes, scales, codes2, scales2, E, ids, M, top_k, x, xs, x_per_slot, y,
                               N, K, stream);
     }

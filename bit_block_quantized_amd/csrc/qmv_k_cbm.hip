@@ -1,0 +1,422 @@
+// qmv_k_cbm.hip -- 2-bit and 3-bit codebook weights against int8 activations
+// with more than 4 vectors per expert, on the int8 matrix cores.
+//
+// The pages' verify batch runs the low-bit weights through a batched matmul
+// (lucebox-hub PR #21 "optimize ROCMFPX fp3/fp2 MMVQ on RDNA", Depends on:
+// the batched ROCmFPX MMQ; lucebox-hub PR #19 "speed up fp3 ROCMFPX matvec",
+// Depends on: the fp3 verify-batch matmul).  Its arithmetic is the decode
+// path's: per 32-weight block (16 for 3-bit scales) an exact integer sum of
+// code value x int8 activation, then the block's fp16 weight scale and fp16
+// activation scale.  With several vectors per weight row those integer sums
+// are a small matrix product, and v_mfma_i32_4x4x4_16b_i8 forms them: 16
+// independent 4 x 4 x 4 blocks per wave, block b taking 4 k-values of 4
+// weight rows (lanes 4b..4b+3, A) and the same 4 k-values of 4 vectors (the
+// same lanes, B), accumulating a 4 (row) x 4 (vector) int32 tile, column j
+// in lane 4b + j (layout confirmed on the device).  Each block owns its own
+// stretch of K, as in the dense 4-vector MXFP4 kernel:
+//
+//   wave = one quad of 4 consecutive weight rows;
+//   lane = 4 * blk + r: row r of the quad (A) and vector r of a group (B);
+//   step = 16 units; unit 16 s + blk belongs to block blk.
+//
+// A unit is 64 weights for 2-bit codes (16 bytes, two 32-blocks) and 32 for
+// 3-bit codes (12 bytes, two 16-weight half-blocks); one load instruction
+// reads 4 rows x 256 (192) contiguous bytes.  Each block's int32 tile is
+// read after the k-values of one scale block, scaled and added into fp32:
+//
+//   2-bit: S = 2 * sum(c * q) - 3 * sum(q) (the codebook is c - 1.5, raw
+//          codes c in 0..3 are the A operand), acc += S * (ws * xs / 2);
+//   3-bit: S_h = sum(v * q) per half-block (v = twice the codebook value,
+//          from a v_perm_b32 LUT), acc += (ws_0 S_0 + ws_1 S_1) * xs / 2;
+//
+// the same factors as the decode kernels, so at unit scales every value is
+// an exact integer multiple of 1/2 and the result is bit-exact.  The MFMA
+// replaces 4 v_dot4 per 16 weights and vector; what remains on the VALU is
+// the decode (shared by all vector groups) and 4 multiply-adds per block,
+// row and vector.
+//
+// Vectors: an expert's vectors are taken in chunks of up to 4 * NVG (NVG
+// groups of 4); a chunk is staged into LDS once per workgroup and used for
+// every row tile of the workgroup's run of that expert.  LDS per vector
+// group and unit: the four vectors' activations in the order the selectors
+// need (chunk (q, j) at 16 * (q ^ (u & 3)) * 4 + j within the unit's record,
+// so the 16 lanes of a read quarter hit distinct banks), then the side data
+// {xs/2, -3 sum(q)} per 32-block (2-bit) or xs/2 (3-bit) of each vector.
+// Units past K and vectors past the chunk are staged as zeros.
+//
+// Work: (expert slot, row tile) items as in the grouped decode-MAC kernel
+// (qmv_device.hpp): the y-th selected expert from a bitmap of the ids, the
+// expert's (token, slot) pairs listed in index order, equal contiguous runs
+// of items per workgroup.
+#include "qmv_device.hpp"
+
+namespace qmv {
+
+typedef int i32x4g __attribute__((ext_vector_type(4)));
+
+// lane 4 * (lane / 4) + I of v, for every lane (DPP quad permute)
+template <int I>
+__device__ __forceinline__ uint32_t quad_lane(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, I * 0x55, 0xF, 0xF, false);
+}
+
+template <int F> struct GmFmt;
+// CH: 16-byte activation chunks per unit and vector; SIDE: side bytes per
+// unit and vector; CB: code bytes per unit.
+template <> struct GmFmt<kCB2> { static constexpr int W = 64, CH = 4, SIDE = 16, CB = 16; };
+template <> struct GmFmt<kCB3> { static constexpr int W = 32, CH = 2, SIDE = 4, CB = 12; };
+
+// LDS bytes of one vector group (4 vectors) over Up units.
+template <int F>
+__device__ __forceinline__ int gm_group_bytes(int Up)
+{
+    return Up * (GmFmt<F>::CH * 64 + 4 * GmFmt<F>::SIDE);
+}
+
+template <int F>
+__device__ __forceinline__ int gm_chunk_off(int u, int q, int j)
+{
+    constexpr int CH = GmFmt<F>::CH;
+    return 16 * ((u * CH + (q ^ (u & (CH - 1)))) * 4 + j);
+}
+
+// 3-bit half-block (16 codes: 6 bytes at byte offset OFF of hi:lo) -> four
+// dwords of int8 values, twice the codebook, in the cb3_xorder order.
+template <int OFF>
+__device__ __forceinline__ uint4 cb3_decode_half(uint32_t hi, uint32_t lo)
+{
+    constexpr uint32_t A0 = OFF, A1 = OFF + 1, A2 = OFF + 2, B0 = OFF + 3, B1 = OFF + 4, B2 = OFF + 5;
+    const uint32_t q0 = perm(hi, lo, A0 | (B0 << 8) | (A0 << 16) | (B0 << 24));
+    const uint32_t q1 = perm(hi, lo, A1 | (B1 << 8) | (A1 << 16) | (B1 << 24));
+    const uint32_t q2 = perm(hi, lo, A2 | (B2 << 8) | (A2 << 16) | (B2 << 24));
+    const uint32_t q3 = perm(hi, lo, A0 | (A1 << 8) | (B0 << 16) | (B1 << 24));
+    const uint32_t q4 = perm(hi, lo, A1 | (A2 << 8) | (B1 << 16) | (B2 << 24));
+    const uint32_t s0 = pk_shr<0, 3>(q0) & 0x07070707u;
+    const uint32_t s1 = pk_shr<1, 4>(q1) & 0x07070707u;
+    const uint32_t s2 = pk_shr<2, 5>(q2) & 0x07070707u;
+    const uint32_t s3 = (pk_shr<6, 6>(q3) & 0x00070007u) | ((pk_shr<7, 7>(q4) & 0x00070007u) << 8);
+    uint4 o;
+    o.x = perm(kCb3LutHi, kCb3LutLo, s0);
+    o.y = perm(kCb3LutHi, kCb3LutLo, s1);
+    o.z = perm(kCb3LutHi, kCb3LutLo, s2);
+    o.w = perm(kCb3LutHi, kCb3LutLo, s3);
+    return o;
+}
+
+// Stage vectors [v0, v0 + cc) of the list (pair indices in `pairs`, or the
+// vector indices themselves for a dense call) as ng groups of 4.
+template <int F, int THREADS>
+__device__ __forceinline__ void gm_stage(const Args &a, uint8_t *lds, const uint16_t *pairs, bool gather,
+                                         int v0, int cc, int ng, int Up)
+{
+    constexpr int W = GmFmt<F>::W;
+    const int U = a.units;
+    const int gb = gm_group_bytes<F>(Up);
+    const int xbytes = Up * GmFmt<F>::CH * 64;
+    const int items = ng * 4 * Up;                   // (vector slot, unit)
+    for (int i = threadIdx.x; i < items; i += THREADS) {
+        const int m = i / Up, u = i - m * Up;       // vector slot m of the chunk
+        const int g = m >> 2, j = m & 3;
+        uint8_t *gbase = lds + g * gb;
+        uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0, c2 = c0, c3 = c0;
+        float xs0 = 0.0f, xs1 = 0.0f;
+        if (m < cc && u < U) {
+            const int p = gather ? (int)pairs[v0 + m] : v0 + m;
+            const int vec = gather && !a.x_per_slot ? p / a.top_k : p;
+            const uint8_t *xp = a.x + (size_t)vec * a.K + (size_t)u * W;
+            const uint16_t *sp = a.xs + (size_t)vec * (a.K / 32) + (size_t)u * W / 32;
+            c0 = *(const uint4 *)xp;
+            c1 = *(const uint4 *)(xp + 16);
+            xs0 = 0.5f * (float)__builtin_bit_cast(_Float16, sp[0]);
+            if constexpr (F == kCB2) {
+                c2 = *(const uint4 *)(xp + 32);
+                c3 = *(const uint4 *)(xp + 48);
+                xs1 = 0.5f * (float)__builtin_bit_cast(_Float16, sp[1]);
+            }
+        }
+        if constexpr (F == kCB2) {
+            *(uint4 *)(gbase + gm_chunk_off<F>(u, 0, j)) = cb2_xorder(c0);
+            *(uint4 *)(gbase + gm_chunk_off<F>(u, 1, j)) = cb2_xorder(c1);
+            *(uint4 *)(gbase + gm_chunk_off<F>(u, 2, j)) = cb2_xorder(c2);
+            *(uint4 *)(gbase + gm_chunk_off<F>(u, 3, j)) = cb2_xorder(c3);
+            const int nq0 = -3 * (sum_i8x16(c0) + sum_i8x16(c1));
+            const int nq1 = -3 * (sum_i8x16(c2) + sum_i8x16(c3));
+            *(uint4 *)(gbase + xbytes + 16 * (u * 4 + j)) =
+                make_uint4(__float_as_uint(xs0), __float_as_uint(xs1), (uint32_t)nq0, (uint32_t)nq1);
+        } else {
+            *(uint4 *)(gbase + gm_chunk_off<F>(u, 0, j)) = cb3_xorder(c0);
+            *(uint4 *)(gbase + gm_chunk_off<F>(u, 1, j)) = cb3_xorder(c1);
+            *(float *)(gbase + xbytes + 4 * (u * 4 + j)) = xs0;
+        }
+    }
+}
+
+// One step (16 units, one per block) of NG vector groups: the int32 tiles
+// of each scale block, scaled into acc[g] (rows 0..3 of the quad, vector j
+// of group g).  The groups' MFMA chains are interleaved, so NG independent
+// accumulators are in flight.
+template <int F, int NG>
+__device__ __forceinline__ void gm_step(const uint8_t *lds, int gb, int xbytes, int u, int j,
+                                        const uint32_t (&A)[16], const float (&wlo)[4], const float (&whi)[4],
+                                        float (&acc)[NG][4])
+{
+    if constexpr (F == kCB2) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            uint32_t xv[NG][8];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const uint4 x0 = lds_read16(lds + g * gb + gm_chunk_off<F>(u, 2 * b, j));
+                const uint4 x1 = lds_read16(lds + g * gb + gm_chunk_off<F>(u, 2 * b + 1, j));
+                xv[g][0] = x0.x; xv[g][1] = x0.y; xv[g][2] = x0.z; xv[g][3] = x0.w;
+                xv[g][4] = x1.x; xv[g][5] = x1.y; xv[g][6] = x1.z; xv[g][7] = x1.w;
+            }
+            i32x4g d[NG];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) d[g] = (i32x4g){0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+                    d[g] = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A[8 * b + t], (int)xv[g][t], d[g], 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const uint2 side = *(const uint2 *)(lds + g * gb + xbytes + 16 * (u * 4 + j) + 4 * b);
+                const float xsh = __uint_as_float(side.x);
+                const int nq = (int)((const uint32_t *)(lds + g * gb + xbytes + 16 * (u * 4 + j)))[2 + b];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ws = b == 0 ? wlo[i] : whi[i];
+                    acc[g][i] = __builtin_fmaf((float)(2 * d[g][i] + nq), ws * xsh, acc[g][i]);
+                }
+            }
+        }
+    } else {
+        uint32_t xv[NG][8];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const uint4 x0 = lds_read16(lds + g * gb + gm_chunk_off<F>(u, 0, j));
+            const uint4 x1 = lds_read16(lds + g * gb + gm_chunk_off<F>(u, 1, j));
+            xv[g][0] = x0.x; xv[g][1] = x0.y; xv[g][2] = x0.z; xv[g][3] = x0.w;
+            xv[g][4] = x1.x; xv[g][5] = x1.y; xv[g][6] = x1.z; xv[g][7] = x1.w;
+        }
+        i32x4g d0[NG], d1[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) d0[g] = d1[g] = (i32x4g){0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                d0[g] = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A[t], (int)xv[g][t], d0[g], 0, 0, 0);
+                d1[g] = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A[4 + t], (int)xv[g][4 + t], d1[g], 0, 0, 0);
+            }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float xsh = *(const float *)(lds + g * gb + xbytes + 4 * (u * 4 + j));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float t = __builtin_fmaf(whi[i], (float)d1[g][i], wlo[i] * (float)d0[g][i]);
+                acc[g][i] = __builtin_fmaf(t, xsh, acc[g][i]);
+            }
+        }
+    }
+}
+
+// Codes and scales of flattened step f = (tile ti, step s): this lane's row
+// of the wave's quad in row tile tile0 + ti, unit 16 s + blk.
+template <int F>
+__device__ __forceinline__ void gm_load(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, const Args &a,
+                                        int row0, int ti, int s, int steps, int ntiles, int blk, u32x4 &wc,
+                                        uint32_t &wsd)
+{
+    constexpr int CB = GmFmt<F>::CB;
+    constexpr uint32_t kPast = 0x80000000u;                 // >= every buffer size
+    const bool ok = ti < ntiles && 16 * s + blk < a.units;
+    // rows past N read past the buffer: zeros, no traffic
+    const uint32_t n = (uint32_t)(row0 + ti * a.rows_per_tile);
+    const uint32_t oc = ok ? n * (uint32_t)a.rcb + (uint32_t)((16 * s + blk) * CB) : kPast;
+    const uint32_t os = ok ? n * (uint32_t)a.rsb + (uint32_t)((16 * s + blk) * 4) : kPast;
+    if constexpr (F == kCB2) {
+        wc = __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, kStream);
+    } else {
+        const u32x3 t = __builtin_amdgcn_raw_buffer_load_b96(rc, oc, 0, kStream);
+        wc = (u32x4){t[0], t[1], t[2], 0u};
+    }
+    wsd = __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
+}
+
+// A run of ntiles row tiles (from tile0) of one expert against NG staged
+// vector groups; each wave streams its quad of every tile as one sequence of
+// (tile, step) pairs with CPL steps of loads in flight across tile
+// boundaries, and stores the rows of vectors [v0, v0 + cc) after each tile.
+template <int F, int WAVES, int CPL, int NG>
+__device__ __forceinline__ void gm_run(const Args &a, const uint8_t *lds, const uint16_t *pairs, bool gather,
+                                       int expert, int tile0, int ntiles, int v0, int cc, int Up)
+{
+    const int lane = threadIdx.x & 63;
+    const int blk = lane >> 2, r = lane & 3;
+    const int steps = Up >> 4;
+    const int gb = gm_group_bytes<F>(Up);
+    const int xbytes = Up * GmFmt<F>::CH * 64;
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (long long)expert * a.expert_cb, a.expert_cb);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.scales + (long long)expert * a.expert_sb, a.expert_sb);
+    const int wrow = tile0 * a.rows_per_tile + 4 * (int)(threadIdx.x >> 6);   // the wave's quad, first tile
+    const int row0 = wrow + r;
+    u32x4 wc[CPL];
+    uint32_t wsd[CPL];
+    int lt = 0, ls = 0;                                     // next (tile, step) to load
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        gm_load<F>(rc, rs, a, row0, lt, ls, steps, ntiles, blk, wc[c], wsd[c]);
+        if (++ls == steps) { ls = 0; ++lt; }
+    }
+    float acc[NG][4];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[g][i] = 0.0f;
+
+    int ct = 0, cs = 0;                                     // (tile, step) to compute
+    const int total = ntiles * steps;
+    for (int fb = 0; fb < total; fb += CPL) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            if (fb + c < total) {
+                const int u = 16 * cs + blk;
+                // the quad's four rows' scales for this block's unit
+                const uint32_t sw[4] = {quad_lane<0>(wsd[c]), quad_lane<1>(wsd[c]), quad_lane<2>(wsd[c]),
+                                        quad_lane<3>(wsd[c])};
+                float wlo[4], whi[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    wlo[i] = f16_lo(sw[i]);
+                    whi[i] = f16_hi(sw[i]);
+                }
+                uint32_t A[16];
+                if constexpr (F == kCB2) {
+                    const uint32_t cw[4] = {wc[c][0], wc[c][1], wc[c][2], wc[c][3]};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) A[4 * q + t] = (cw[q] >> (2 * t)) & 0x03030303u;
+                } else {
+                    const uint4 h0 = cb3_decode_half<0>(wc[c][1], wc[c][0]);
+                    const uint4 h1 = cb3_decode_half<2>(wc[c][2], wc[c][1]);
+                    A[0] = h0.x; A[1] = h0.y; A[2] = h0.z; A[3] = h0.w;
+                    A[4] = h1.x; A[5] = h1.y; A[6] = h1.z; A[7] = h1.w;
+#pragma unroll
+                    for (int t = 8; t < 16; ++t) A[t] = 0u;
+                }
+                gm_step<F, NG>(lds, gb, xbytes, u, r, A, wlo, whi, acc);
+                if (cs == steps - 1) {
+                    // tile done: sum the 16 blocks' tiles (butterfly over lane
+                    // bits 2..5), then lane 4 i + j (i < 4) stores row
+                    // 4 quad + i of vector j of each group
+                    const int row = wrow + ct * a.rows_per_tile + blk;
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                            for (int m = 4; m < 64; m <<= 1) acc[g][i] += __shfl_xor(acc[g][i], m);
+                        }
+                        const float val =
+                            blk == 0 ? acc[g][0] : blk == 1 ? acc[g][1] : blk == 2 ? acc[g][2] : acc[g][3];
+                        const int m = 4 * g + r;
+                        if (blk < 4 && m < cc && row < a.N) {
+                            const int p = gather ? (int)pairs[v0 + m] : v0 + m;
+                            a.y[p * a.N + row] = val;       // M * top_k * N < 2^31
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[g][i] = 0.0f;
+                    }
+                }
+                if (++cs == steps) { cs = 0; ++ct; }
+            }
+            gm_load<F>(rc, rs, a, row0, lt, ls, steps, ntiles, blk, wc[c], wsd[c]);
+            if (++ls == steps) { ls = 0; ++lt; }
+        }
+    }
+}
+
+// Work items (expert slot, row tile), slot-major, dealt in equal contiguous
+// runs; per slot the pairs are listed and taken in chunks of up to 4 * NVG
+// vectors, each staged once and streamed against every row tile of the run.
+template <int F, int WAVES, int NVG, int CPL>
+__global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int THREADS = 64 * WAVES;
+    const bool gather = a.ids != nullptr;
+    const int Up = (a.units + 15) & ~15;
+    uint8_t *tail = lds + NVG * gm_group_bytes<F>(Up);
+    PairList L;
+    L.cnt = (int *)tail;
+    uint32_t *bm = (uint32_t *)(tail + kPairCountBytes);
+    L.perm = (uint16_t *)(tail + kPairCountBytes + kExpertBitmapBytes);
+    const int tiles = a.gr_tiles, rpt = a.rows_per_tile;
+    const int B = a.M * a.top_k;
+    Ids8 id0;
+    int D = 1;
+    if (gather) {
+        id0 = load_ids8<THREADS>(a.ids, B, a.E, 0);
+        D = expert_bitmap<THREADS>(a.ids, B, a.E, bm, id0);
+        const int z0 = (int)((long long)blockIdx.x * tiles / gridDim.x);
+        const int z1 = (int)((long long)(blockIdx.x + 1) * tiles / gridDim.x);
+        if (z1 > z0) {                              // zero rows of ids outside [0, E)
+            const int ci = list_pairs<THREADS>(a.ids, B, a.E, -1, L, id0);
+            const int n0 = z0 * rpt;
+            const int rows = min(a.N, z1 * rpt) - n0;
+            for (int o = threadIdx.x; o < ci * rows; o += THREADS)
+                a.y[(int)L.perm[o / rows] * a.N + n0 + o % rows] = 0.0f;
+            __syncthreads();
+        }
+    }
+    const long long T = (long long)D * tiles;
+    int i = (int)((long long)blockIdx.x * T / gridDim.x);
+    const int i1 = (int)((long long)(blockIdx.x + 1) * T / gridDim.x);
+    while (i < i1) {
+        const int slot = i / tiles;
+        const int iend = min(i1, (slot + 1) * tiles);   // this run's items of the slot
+        int e = 0, c = a.M;
+        if (gather) {
+            e = kth_expert(bm, slot);
+            c = list_pairs<THREADS>(a.ids, B, a.E, e, L, id0);
+        }
+        // chunks of equal size (within one vector) when an expert has more
+        // vectors than one chunk holds
+        const int nchunk = (c + 4 * NVG - 1) / (4 * NVG);
+        for (int k = 0, v0 = 0; k < nchunk; ++k) {
+            const int cc = (c - v0) / (nchunk - k) + ((c - v0) % (nchunk - k) != 0);
+            const int ng = (cc + 3) >> 2;
+            gm_stage<F, THREADS>(a, lds, L.perm, gather, v0, cc, ng, Up);
+            __syncthreads();
+            const int tile0 = i - slot * tiles, nt = iend - i;
+            if constexpr (NVG >= 4) {
+                if (ng == 4) gm_run<F, WAVES, CPL, 4>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
+            }
+            if constexpr (NVG >= 3) {
+                if (ng == 3) gm_run<F, WAVES, CPL, 3>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
+            }
+            if constexpr (NVG >= 2) {
+                if (ng == 2) gm_run<F, WAVES, CPL, 2>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
+            }
+            if (ng == 1) gm_run<F, WAVES, CPL, 1>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
+            __syncthreads();                            // the next chunk or expert restages
+            v0 += cc;
+        }
+        i = iend;
+    }
+}
+
+// [format: 2-bit, 3-bit][vector groups per chunk: 1, 2, 3, 4]; 8 waves, 3
+// steps of loads in flight.
+extern const void *const kTableGmma[2][4];
+const void *const kTableGmma[2][4] = {
+    {(const void *)&qmv_gmma_kernel<kCB2, 8, 1, 3>, (const void *)&qmv_gmma_kernel<kCB2, 8, 2, 3>,
+     (const void *)&qmv_gmma_kernel<kCB2, 8, 3, 3>, (const void *)&qmv_gmma_kernel<kCB2, 8, 4, 3>},
+    {(const void *)&qmv_gmma_kernel<kCB3, 8, 1, 3>, (const void *)&qmv_gmma_kernel<kCB3, 8, 2, 3>,
+     (const void *)&qmv_gmma_kernel<kCB3, 8, 3, 3>, (const void *)&qmv_gmma_kernel<kCB3, 8, 4, 3>}};
+
+}  // namespace qmv
