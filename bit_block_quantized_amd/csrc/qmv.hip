@@ -543,6 +543,27 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
         if ((kind == kCB2 || kind == kCB3) && afmt == QMV_A_Q8B32 && !gate_up &&
             (gather ? (long long)M * top_k >= 2LL * E : M >= 8))
             return launch_gmma(wfmt, kind, codes, scales, E, ids, M, top_k, x, xs, x_per_slot, y, N, K, stream);
+        // A gather of at most 64 tokens with fewer than two pairs per expert
+        // (a verify batch over many experts) reuses almost no weights: as
+        // token groups of up to 4 on the decode kernels, one launch per
+        // group, it measured 10-20% faster than one grouped launch (MXFP4,
+        // 4 of 256, 7168 -> 2048: 5 tokens 31.8 against 37.9 us, 16 tokens
+        // 95.5 against 114.6 us; 2-bit, 8 tokens 34.6 against 37.8 us).
+        if (gather && (long long)M * top_k < 2LL * E && M <= kSplitMaxM) {
+            const size_t xe = afmt == QMV_A_Q8B32 ? 1 : 2;                 // bytes per activation
+            const size_t xv = x_per_slot ? (size_t)top_k : 1;             // vectors per token
+            for (int m0 = 0; m0 < M; m0 += kMaxM) {
+                const int mg = M - m0 < kMaxM ? M - m0 : kMaxM;
+                const qmv_status_t st = launch(
+                    wfmt, afmt, codes, scales, codes2, scales2, E, ids + (size_t)m0 * top_k, mg, top_k,
+                    (const uint8_t *)x + (size_t)m0 * xv * K * xe,
+                    xs ? (const void *)((const uint16_t *)xs + (size_t)m0 * xv * (K / 32)) : nullptr, x_per_slot,
+                    y + (size_t)m0 * top_k * N, N, K, stream);
+                if (st != QMV_OK)
+                    return st;
+            }
+            return QMV_OK;
+        }
         return launch_grouped(wfmt, afmt, codes, scales, codes2, scales2, E, ids, M, top_k, x, xs, x_per_slot, y,
                               N, K, stream);
     }

@@ -63,6 +63,7 @@ constexpr int kMaxPairsBatched = 8192;
 // Dense MXFP4 x bf16 calls with 5..20 vectors run as groups of 4 on the
 // decode kernels (one expert gives the batched kernel too few tiles).
 constexpr int kDenseGroupsMaxM = 20;
+constexpr int kSplitMaxM = 64;           // few-pairs gathers split into token groups up to this M
 constexpr int kMaxEBatched = 1023;
 
 constexpr int kUnitWeights[5] = {Fmt<kMXFP4>::W, Fmt<kCB2>::W, Fmt<kCB2S>::W, Fmt<kCB3>::W, Fmt<kMXFP4I>::W};

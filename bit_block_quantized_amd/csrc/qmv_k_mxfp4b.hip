@@ -1,6 +1,6 @@
 // qmv_k_mxfp4b.hip -- MXFP4 x bf16 products with more than 4 activation
 // vectors: the expert-batched gather (a prefill chunk, a wide verify batch),
-// the fused gate/up gather with SwiGLU, and the dense call, on the 16x16x32
+// the fused gate/up gather with SwiGLU, and the dense call, on the 32x32x16
 // bf16 matrix cores.
 //
 // With many vectors per expert the work is a grouped matrix product: each
@@ -8,9 +8,9 @@
 // "Problem / Background": the expert-batched gather_qmm path that prefill
 // takes once enough tokens share each expert).
 //
-// Tiles.  A tile is (expert, R consecutive weight rows), R = 16 * RF * WAVES
-// (for the gate/up kernel R counts output rows: each holds a gate and an up
-// row).  The grid has one workgroup per tile of every expert, whether or not
+// Tiles.  A tile is (expert, R consecutive weight rows), R = 32 * RF * WAVES
+// (for the gate/up kernel R = 16 * RF * WAVES output rows: each holds a gate
+// and an up row).  The grid has one workgroup per tile of every expert, whether or not
 // any pair selects it, so the tiling needs no device-wide knowledge of the
 // ids and no sort: a workgroup lists its own expert's (token, slot) pairs in
 // index order by scanning the ids with ballots (deterministic, no atomics),

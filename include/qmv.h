@@ -1,6 +1,7 @@
 /*
  * qmv.h -- C ABI of libqmv.so: block-quantized GEMV for MoE expert
- * projections on AMD Instinct MI355X (gfx950), batch 1 to 4 tokens.
+ * projections on AMD Instinct MI355X (gfx950): decode (1 to 4 tokens) and
+ * many-token calls (a prefill chunk or a wide verify batch).
  *
  * The library computes, for every output it is asked for,
  *
@@ -60,7 +61,11 @@
  *                      d16 = d rounded to fp16 (nearest even), the scale;
  *                      q[k] = clamp(rint(x[k] * (1 / d16)), -127, 127),
  *                            ties to even; q = 0 where d16 is 0 or Inf.
- *                    Activations must be finite.
+ *                    Activations must be finite.  The pages name the
+ *                    quantizer but print no formula: this is a reading,
+ *                    and no page value pins it (parity unpinned against
+ *                    the pages; the CPU oracle implements the same
+ *                    reading).
  * Supported pairs: (MXFP4, BF16), (MXFP4, Q8B32), (CB2, Q8B32), (CB3, Q8B32),
  * (CB2, BF16_Q8), (CB3, BF16_Q8).  With (MXFP4, Q8B32) every 32-weight block
  * shares one E8M0 weight scale and one activation scale (both are per 32 of
@@ -78,16 +83,23 @@
  * Alignment: codes 16 bytes (8 for CB2 when K % 64 != 0), x 16 bytes,
  * scales, x_scales, expert ids and y 4 bytes.
  *
- * Limits: 1 <= M <= 4, 1 <= top_k <= 16, K % 32 == 0, 32 <= K <= 16384,
- * N >= 1, E >= 1.  qmv_dense and qmv_gather_moe with (MXFP4, BF16) also take
- * M > 4 (a prefill chunk or a wide verify batch), up to 8192 (token, slot)
- * pairs (M for a dense call, M * top_k for a gather) and E <= 1023.
+ * Limits: M >= 1, 1 <= top_k <= 16, K % 32 == 0, 32 <= K <= 16384, N >= 1,
+ * E >= 1, M * top_k * N < 2^31.  With M > 4 (a prefill chunk or a wide
+ * verify batch), on every entry point and format pair: at most 8192
+ * (token, slot) pairs (M for a dense call, M * top_k otherwise) and, for
+ * the routed calls, E <= 1023.
  *
  * Errors: arguments are checked on the host before anything is launched; on
  * a failed check the call returns the status, launches nothing and leaves y
- * untouched.  No check needs a device synchronization.  An expert id outside
- * [0, E) is not an error: that (token, slot) output row is written with
- * zeros (mlxcel issue #2178, Implementation Notes, Edge cases).
+ * untouched.  No check needs a device synchronization.  QMV_EHIP (the
+ * runtime refused a launch) can come after earlier launches of the same
+ * call have run: a dense (MXFP4, BF16) call with 5 to 20 vectors, and a
+ * gather or gate/up call with 5 to 64 tokens and fewer than two (token,
+ * slot) pairs per expert (M * top_k < 2 E), are one launch per group of up
+ * to 4 vectors or tokens, so y may then hold the rows of the groups before
+ * the failing one.  Every other call is one launch.  An expert
+ * id outside [0, E) is not an error: that (token, slot) output row is
+ * written with zeros (mlxcel issue #2178, Implementation Notes, Edge cases).
  *
  * Determinism: results are bitwise identical from run to run (fixed
  * reduction order, no atomics).
@@ -120,7 +132,9 @@ typedef enum {
  * This is the gather below with one expert, top_k = 1 and ids all 0.
  * With (MXFP4, BF16), 5 <= M <= 20 runs as groups of up to 4 vectors on the
  * 4-vector kernels (one launch per group), and M > 20 on the batched
- * matrix-core kernel described under qmv_gather_moe.
+ * matrix-core kernel described under qmv_gather_moe; 2-bit and 3-bit
+ * weights with int8 activations and M >= 8 on the int8 matrix-core kernel;
+ * every other M > 4 call on the grouped kernel.
  */
 qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
                        qmv_afmt_t afmt, const void *x, const void *x_scales,
@@ -138,15 +152,22 @@ qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scale
  *   y           fp32 [M][top_k][N]
  * Each distinct expert's weights are streamed from memory once per call and
  * applied to every activation vector routed to it (up to four per pass).
- * With (MXFP4, BF16) and M > 4 (the expert-batched product that prefill
- * takes once many tokens share each expert: mlxcel issue, "Problem / Background"),
- * every workgroup sorts the (token, slot) pairs by expert in LDS and
- * multiplies each expert's rows with all of its vectors, up to 128 at a
- * time, on the 16x16x32 bf16 matrix cores; the result is the same
- * definition, within the same tolerance, and bitwise repeatable.  A call
- * with at most 64 tokens and fewer than two (token, slot) pairs per expert
- * (M * top_k < 2 E) reuses too few weights for that: it runs as groups of
- * up to 4 tokens on the decode kernels, one launch per group.
+ * With M > 4 (the expert-batched product that prefill takes once many
+ * tokens share each expert: mlxcel issue #2178, "Problem / Background"; the
+ * verify-batch matmul of lucebox-hub PR #19, "Depends on") every workgroup
+ * lists the (token, slot) pairs of its expert in LDS (no host sort, no
+ * workspace) and one launch computes the call:
+ *   (MXFP4, BF16) with M * top_k >= 2 E: each expert's rows against all of
+ *     its vectors, up to 128 at a time, on the 32x32x16 bf16 matrix cores;
+ *   (CB2 with K % 64 == 0 or CB3, Q8B32) with M * top_k >= 2 E: exact int32
+ *     block sums on the int8 4x4x4 matrix cores, up to 16 vectors per
+ *     staged chunk;
+ *   at most 64 tokens with fewer than two pairs per expert: groups of up to
+ *     4 tokens on the decode kernels, one launch per group;
+ *   every other call: the decode kernels' own multiply-adds in one launch,
+ *     four of an expert's vectors at a time.
+ * The result is the same definition within the same tolerance (bit-exact
+ * where the arithmetic is exact) and bitwise repeatable.
  */
 qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales, int E,
                             const int32_t *expert_ids, int M, int top_k,
@@ -163,8 +184,10 @@ qmv_status_t qmv_gather_moe(qmv_wfmt_t wfmt, const void *w_codes, const void *w_
  * weight tensors of the routed experts -- the gate and up expert projections
  * that geo-lucebox PR #31 "DS4 H200: rocmfp2_mix MoE matvec" (Why this kernel)
  * computes in one matvec kernel -- and hands the down projection its input
- * directly.  Arguments, limits and errors as qmv_gather_moe; silu is
- * evaluated in fp32.
+ * directly.  Arguments, limits and errors as qmv_gather_moe (M > 4
+ * included: (MXFP4, BF16) with M * top_k >= 2 E on the batched matrix-core
+ * kernel with a gate and an up fragment per output fragment, every other
+ * call on the grouped kernel); silu is evaluated in fp32.
  */
 qmv_status_t qmv_gather_moe_swiglu(qmv_wfmt_t wfmt, const void *gate_codes, const void *gate_scales,
                                    const void *up_codes, const void *up_scales, int E,
@@ -190,8 +213,9 @@ qmv_status_t qmv_gather_moe_swiglu(qmv_wfmt_t wfmt, const void *gate_codes, cons
  *   y              fp32 [M][N], overwritten (not accumulated into).
  * The slots of a token are summed in slot order; results are bitwise
  * reproducible.  An out-of-range id contributes route_weights[t][j] * 0.
- * Weights, scales and activations, limits and errors as qmv_gather_moe;
- * a null or misaligned route_weights is QMV_EINVAL.
+ * Weights, scales and activations, limits and errors as qmv_gather_moe
+ * (any M: a workgroup per token and row tile); route_weights may be signed
+ * or sum to zero; a null or misaligned route_weights is QMV_EINVAL.
  */
 qmv_status_t qmv_gather_moe_combine(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
                                     int E, const int32_t *expert_ids, const float *route_weights,

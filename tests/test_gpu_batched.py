@@ -1,7 +1,7 @@
 """MXFP4 x bf16 with more than 4 activation vectors: the expert-batched
-matrix-core path (v_mfma_f32_16x16x32_bf16; the call's (token, slot) pairs
-sorted by expert in LDS, tiles of one expert x up to 128 vectors x 128 or
-256 rows).  Needs an MI355X.
+matrix-core path (v_mfma_f32_32x32x16_bf16; every workgroup lists its
+expert's (token, slot) pairs in LDS, tiles of one expert x up to 128 vectors
+x a few 32-row fragments per wave).  Needs an MI355X.
 
 Against the oracle on the same seeded inputs: every output within
 1e-3 * sum |w x|; bit-exact at unit scales with small-integer activations
@@ -13,12 +13,12 @@ ragged N and K (partial 128-weight slices), E8M0 bytes outside [2, 252] and
 Inf activations, the pair and expert limits, and the full-size prefill chunk
 on sampled outputs.
 
-Which kernel a call reaches: dense calls with 5 to 20 vectors and gathers
-with at most 64 tokens and fewer than two (token, slot) pairs per expert run
-as groups of up to 4 vectors on the decode kernels (test_dense with M <= 20
-and test_gather_few_pairs_* cover that route); every other call with more
-than 4 vectors runs on the batched kernel, so the special-value cases below
-use dense calls with M >= 21 or gathers with M * top_k >= 2 E.
+Which kernel a call reaches: dense calls with 5 to 20 vectors run as groups
+of up to 4 vectors on the dense 4-vector kernel (test_dense with M <= 20),
+gathers with fewer than two (token, slot) pairs per expert on the grouped
+decode-MAC kernel (test_gather_few_pairs_*); every other call with more than
+4 vectors runs on the batched kernel, so the special-value cases below use
+dense calls with M >= 21 or gathers with M * top_k >= 2 E.
 """
 import numpy as np
 import pytest

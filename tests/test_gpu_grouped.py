@@ -181,3 +181,29 @@ def test_prefill_chunk_full_size_sampled(name):
                           [r * wl.N + np.arange(wl.N) for r in rows])
     yr, A = oracle_call(inp, outs=outs)
     assert_parity(y[outs], yr, A, f"{name} sampled")
+
+
+@pytest.mark.parametrize("pair", PAIRS + [("mxfp4", "")], ids=lambda p: f"{p[0]}-{p[1] or ('bf16' if p[0] == 'mxfp4' else 'q8')}")
+@pytest.mark.parametrize("M,top_k,E,per_slot", [(80, 2, 200, False), (70, 3, 256, True)])
+def test_few_pairs_many_tokens(pair, M, top_k, E, per_slot):
+    """Fewer than two pairs per expert and more than 64 tokens: one grouped
+    launch (slots over the selected experts, balanced runs of row tiles).
+    With 64 tokens or fewer the same calls run as token groups of 4 on the
+    decode kernels (test_gpu_batched.py, test_gather_few_pairs_per_expert)."""
+    wfmt, act = pair
+    inp = synth.make(_wl(wfmt, act, "gather", M, 96, 512, E=E, top_k=top_k, x_per_slot=per_slot,
+                         seed=3 * M + E))
+    inp.ids[3, 0] = -1
+    _check(inp, f"{wfmt} few pairs M={M}")
+
+
+@pytest.mark.parametrize("pair", [("cb2", ""), ("mxfp4", "q8"), ("cb3", "bf16")], ids=_name)
+def test_few_pairs_split_groups(pair):
+    """At most 64 tokens and fewer than two pairs per expert: token groups of
+    up to 4 (the last one ragged), one decode launch each, per-slot x."""
+    wfmt, act = pair
+    inp = synth.make(_wl(wfmt, act, "gather", 13, 70, 256, E=64, top_k=2, x_per_slot=True, seed=171))
+    inp.ids[12, 1] = 64
+    y = gpu_call(inp).cpu().numpy()
+    assert (y[12, 1] == 0).all()
+    _check(inp, f"{wfmt} split groups")
