@@ -56,7 +56,7 @@ extern const void *const kTableGmma[2][4];
 }
 
 namespace qmv {
-constexpr int kBatchedMenu = 4;
+constexpr int kBatchedMenu = 6;
 extern const int kBatchedShapes[kBatchedMenu][3];
 extern const void *const kTableBatched[kBatchedMenu];
 extern const int kBatchedShapesGU[kBatchedMenu][3];

@@ -65,7 +65,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBVecMax = 128;                  // vectors per chunk
 constexpr int kBRing = 2;                      // activation slice buffers in LDS
-constexpr int kBatchedMenu = 4;                // kernel shapes (kBatchedShapes)
+constexpr int kBatchedMenu = 6;                // kernel shapes (kBatchedShapes)
 constexpr uint32_t kBPast = 0x80000000u;       // >= every buffer size: reads zeros
 
 // LDS offset of 16-byte chunk pos (k = 8 pos .. 8 pos + 7 of the slice) of ring vector v.
@@ -395,15 +395,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void qmv_batched_kernel(const Args a
 // fragment per output fragment.
 #define QMV_BK(RF, W, MODE, VCAP) (const void *)&qmv_batched_kernel<RF, W, MODE, VCAP>
 extern const int kBatchedShapes[kBatchedMenu][3];
-const int kBatchedShapes[kBatchedMenu][3] = {{4, 1, 128}, {4, 2, 96}, {4, 3, 96}, {8, 1, 128}};
+// (waves, 32-row fragments per wave, most vectors per chunk); the 1- and
+// 2-wave shapes give a single weight matrix (a dense call) enough tiles.
+const int kBatchedShapes[kBatchedMenu][3] = {{4, 1, 128}, {4, 2, 96}, {4, 3, 96}, {8, 1, 128}, {1, 1, 32}, {2, 1, 64}};
 extern const void *const kTableBatched[kBatchedMenu];
 const void *const kTableBatched[kBatchedMenu] = {QMV_BK(1, 4, 0, 128), QMV_BK(2, 4, 0, 96), QMV_BK(3, 4, 0, 96),
-                                                 QMV_BK(1, 8, 0, 128)};
+                                                 QMV_BK(1, 8, 0, 128), QMV_BK(1, 1, 0, 32), QMV_BK(1, 2, 0, 64)};
 extern const int kBatchedShapesGU[kBatchedMenu][3];
-const int kBatchedShapesGU[kBatchedMenu][3] = {{4, 2, 128}, {4, 4, 64}, {4, 6, 32}, {8, 2, 64}};
+const int kBatchedShapesGU[kBatchedMenu][3] = {{4, 2, 128}, {4, 4, 64}, {4, 6, 32}, {8, 2, 64}, {1, 2, 32}, {2, 2, 64}};
 extern const void *const kTableBatchedGU[kBatchedMenu];
 const void *const kTableBatchedGU[kBatchedMenu] = {QMV_BK(2, 4, 1, 128), QMV_BK(4, 4, 1, 64), QMV_BK(6, 4, 1, 32),
-                                                   QMV_BK(2, 8, 1, 64)};
+                                                   QMV_BK(2, 8, 1, 64), QMV_BK(2, 1, 1, 32), QMV_BK(2, 2, 1, 64)};
 #undef QMV_BK
 
 }  // namespace qmv
