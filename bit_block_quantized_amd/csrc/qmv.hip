@@ -437,7 +437,7 @@ qmv_status_t launch_gmma(int wfmt, int kind, const void *codes, const void *scal
     const int busy = gather ? (pairs < E ? pairs : E) : 1;
     const int U = K / kUnitWeights[kind];
     const int Up = (U + 15) & ~15;
-    const size_t group_bytes = (size_t)Up * (fi == 0 ? 256 + 64 : 128 + 16);
+    const size_t group_bytes = (size_t)Up * (fi == 0 ? 256 + 32 : 128 + 16);
     const size_t tail = kPairCountBytes + kExpertBitmapBytes + (((size_t)2 * (gather ? pairs : 0) + 15) & ~(size_t)15);
     // groups of 4 for the average expert's vectors and half again (the
     // counts spread around the average), as far as one workgroup's LDS allows

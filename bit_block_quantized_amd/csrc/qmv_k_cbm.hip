@@ -24,8 +24,9 @@
 // reads 4 rows x 256 (192) contiguous bytes.  Each block's int32 tile is
 // read after the k-values of one scale block, scaled and added into fp32:
 //
-//   2-bit: S = 2 * sum(c * q) - 3 * sum(q) (the codebook is c - 1.5, raw
-//          codes c in 0..3 are the A operand), acc += S * (ws * xs / 2);
+//   2-bit: S = sum((2c - 3) q) (the codebook is c - 1.5; a v_perm_b32 LUT
+//          turns the codes into the int8 A operand 2c - 3),
+//          acc += S * (ws * xs / 2);
 //   3-bit: S_h = sum(v * q) per half-block (v = twice the codebook value,
 //          from a v_perm_b32 LUT), acc += (ws_0 S_0 + ws_1 S_1) * xs / 2;
 //
@@ -39,9 +40,9 @@
 // groups of 4); a chunk is staged into LDS once per workgroup and used for
 // every row tile of the workgroup's run of that expert.  LDS per vector
 // group and unit: the four vectors' activations in the order the selectors
-// need (chunk (q, j) at 16 * (q ^ (u & 3)) * 4 + j within the unit's record,
-// so the 16 lanes of a read quarter hit distinct banks), then the side data
-// {xs/2, -3 sum(q)} per 32-block (2-bit) or xs/2 (3-bit) of each vector.
+// need (chunk (q, j) at a swizzled place within the unit's record, so the 16
+// lanes of a read quarter hit distinct banks: gm_chunk_off), then the side data
+// xs/2 per 32-block of each vector.
 // Units past K and vectors past the chunk are staged as zeros.
 //
 // Work: (expert slot, row tile) items as in the grouped decode-MAC kernel
@@ -54,6 +55,9 @@ namespace qmv {
 
 typedef int i32x4g __attribute__((ext_vector_type(4)));
 
+// 2-bit code c (bytes 0..3 of the selector) -> int8 2c - 3: {-3, -1, 1, 3}
+constexpr uint32_t kCb2Lut2 = 0x0301FFFDu;
+
 // lane 4 * (lane / 4) + I of v, for every lane (DPP quad permute)
 template <int I>
 __device__ __forceinline__ uint32_t quad_lane(uint32_t v)
@@ -64,7 +68,7 @@ __device__ __forceinline__ uint32_t quad_lane(uint32_t v)
 template <int F> struct GmFmt;
 // CH: 16-byte activation chunks per unit and vector; SIDE: side bytes per
 // unit and vector; CB: code bytes per unit.
-template <> struct GmFmt<kCB2> { static constexpr int W = 64, CH = 4, SIDE = 16, CB = 16; };
+template <> struct GmFmt<kCB2> { static constexpr int W = 64, CH = 4, SIDE = 8, CB = 16; };
 template <> struct GmFmt<kCB3> { static constexpr int W = 32, CH = 2, SIDE = 4, CB = 12; };
 
 // LDS bytes of one vector group (4 vectors) over Up units.
@@ -74,11 +78,17 @@ __device__ __forceinline__ int gm_group_bytes(int Up)
     return Up * (GmFmt<F>::CH * 64 + 4 * GmFmt<F>::SIDE);
 }
 
+// The 16 lanes of a read quarter take units u .. u + 3 (one chunk q each,
+// four vectors j): the chunk position within a unit's record is xor-ed with
+// the unit's bits above the record's share of a 256-byte bank row, so those
+// 16 chunks fall on 16 distinct 16-byte bank groups (2-bit: 256-byte records,
+// q ^ (u & 3); 3-bit: 128-byte records, q ^ ((u >> 1) & 1)).
 template <int F>
 __device__ __forceinline__ int gm_chunk_off(int u, int q, int j)
 {
     constexpr int CH = GmFmt<F>::CH;
-    return 16 * ((u * CH + (q ^ (u & (CH - 1)))) * 4 + j);
+    const int pos = CH == 4 ? q ^ (u & 3) : q ^ ((u >> 1) & 1);
+    return 16 * ((u * CH + pos) * 4 + j);
 }
 
 // 3-bit half-block (16 codes: 6 bytes at byte offset OFF of hi:lo) -> four
@@ -140,10 +150,7 @@ __device__ __forceinline__ void gm_stage(const Args &a, uint8_t *lds, const uint
             *(uint4 *)(gbase + gm_chunk_off<F>(u, 1, j)) = cb2_xorder(c1);
             *(uint4 *)(gbase + gm_chunk_off<F>(u, 2, j)) = cb2_xorder(c2);
             *(uint4 *)(gbase + gm_chunk_off<F>(u, 3, j)) = cb2_xorder(c3);
-            const int nq0 = -3 * (sum_i8x16(c0) + sum_i8x16(c1));
-            const int nq1 = -3 * (sum_i8x16(c2) + sum_i8x16(c3));
-            *(uint4 *)(gbase + xbytes + 16 * (u * 4 + j)) =
-                make_uint4(__float_as_uint(xs0), __float_as_uint(xs1), (uint32_t)nq0, (uint32_t)nq1);
+            *(uint2 *)(gbase + xbytes + 8 * (u * 4 + j)) = make_uint2(__float_as_uint(xs0), __float_as_uint(xs1));
         } else {
             *(uint4 *)(gbase + gm_chunk_off<F>(u, 0, j)) = cb3_xorder(c0);
             *(uint4 *)(gbase + gm_chunk_off<F>(u, 1, j)) = cb3_xorder(c1);
@@ -182,13 +189,11 @@ __device__ __forceinline__ void gm_step(const uint8_t *lds, int gb, int xbytes, 
                     d[g] = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A[8 * b + t], (int)xv[g][t], d[g], 0, 0, 0);
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                const uint2 side = *(const uint2 *)(lds + g * gb + xbytes + 16 * (u * 4 + j) + 4 * b);
-                const float xsh = __uint_as_float(side.x);
-                const int nq = (int)((const uint32_t *)(lds + g * gb + xbytes + 16 * (u * 4 + j)))[2 + b];
+                const float xsh = *(const float *)(lds + g * gb + xbytes + 8 * (u * 4 + j) + 4 * b);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float ws = b == 0 ? wlo[i] : whi[i];
-                    acc[g][i] = __builtin_fmaf((float)(2 * d[g][i] + nq), ws * xsh, acc[g][i]);
+                    acc[g][i] = __builtin_fmaf((float)d[g][i], ws * xsh, acc[g][i]);
                 }
             }
         }
@@ -295,11 +300,14 @@ __device__ __forceinline__ void gm_run(const Args &a, const uint8_t *lds, const 
                 }
                 uint32_t A[16];
                 if constexpr (F == kCB2) {
+                    // codes c -> int8 2c - 3 (a v_perm_b32 LUT), so the MFMA
+                    // forms the block's integer sum sum((2c - 3) q) itself
                     const uint32_t cw[4] = {wc[c][0], wc[c][1], wc[c][2], wc[c][3]};
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) A[4 * q + t] = (cw[q] >> (2 * t)) & 0x03030303u;
+                        for (int t = 0; t < 4; ++t)
+                            A[4 * q + t] = perm(0u, kCb2Lut2, (cw[q] >> (2 * t)) & 0x03030303u);
                 } else {
                     const uint4 h0 = cb3_decode_half<0>(wc[c][1], wc[c][0]);
                     const uint4 h1 = cb3_decode_half<2>(wc[c][2], wc[c][1]);
