@@ -50,9 +50,10 @@ extern const void *const kTableDense4[2];
 // gate and an up fragment per output fragment.
 // 2-bit and 3-bit codebook weights x int8 activations with more than 4
 // vectors per expert on the int8 4x4x4 matrix cores (qmv_k_cbm.hip):
-// [2-bit, 3-bit][vector groups of 4 per staged chunk: 1, 2, 3, 4]; 8 waves.
+// [int8 x, bf16 x quantized in staging][2-bit, 3-bit][vector groups of 4 per
+// staged chunk: 1, 2, 3, 4]; 8 waves.
 namespace qmv {
-extern const void *const kTableGmma[2][4];
+extern const void *const kTableGmma[2][2][4];
 }
 
 namespace qmv {
@@ -413,9 +414,9 @@ qmv_status_t launch_grouped(int wfmt, int afmt, const void *codes, const void *s
     return QMV_OK;
 }
 
-std::once_flag g_gm_once[2][4];
-hipError_t g_gm_err[2][4];
-int g_gm_occ[2][4];                                     // workgroups per CU by registers
+std::once_flag g_gm_once[2][2][4];
+hipError_t g_gm_err[2][2][4];
+int g_gm_occ[2][2][4];                                  // workgroups per CU by registers
 constexpr int kGmWaves = 8;
 constexpr int kGmNvg[4] = {1, 2, 3, 4};
 
@@ -427,11 +428,12 @@ constexpr int kGmNvg[4] = {1, 2, 3, 4};
 // (with room for a few more) as far as the LDS allows; the grid is at most
 // one round of the chip, each workgroup an equal run of (expert, 32-row
 // tile) items, so one staging of a chunk serves many row tiles.
-qmv_status_t launch_gmma(int wfmt, int kind, const void *codes, const void *scales, int E, const int32_t *ids,
-                         int M, int top_k, const void *x, const void *xs, int x_per_slot, float *y, int N, int K,
-                         hipStream_t stream)
+qmv_status_t launch_gmma(int wfmt, int afmt, int kind, const void *codes, const void *scales, int E,
+                         const int32_t *ids, int M, int top_k, const void *x, const void *xs, int x_per_slot,
+                         float *y, int N, int K, hipStream_t stream)
 {
     const bool gather = ids != nullptr;
+    const int qi = afmt == QMV_A_BF16_Q8 ? 1 : 0;
     const int fi = kind == kCB2 ? 0 : 1;
     const int pairs = gather ? M * top_k : M;
     const int busy = gather ? (pairs < E ? pairs : E) : 1;
@@ -448,23 +450,23 @@ qmv_status_t launch_gmma(int wfmt, int kind, const void *codes, const void *scal
     const size_t lds = kGmNvg[ni] * group_bytes + tail;
     if (lds > (size_t)kLdsPerCU)
         return QMV_EUNSUPPORTED;
-    const void *fn = kTableGmma[fi][ni];
-    std::call_once(g_gm_once[fi][ni], [&] {
+    const void *fn = kTableGmma[qi][fi][ni];
+    std::call_once(g_gm_once[qi][fi][ni], [&] {
         hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCU);
         int n = 0;
         if (err == hipSuccess)
             err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * kGmWaves, 0);
-        g_gm_err[fi][ni] = err;
-        g_gm_occ[fi][ni] = n > 0 ? n : 1;
+        g_gm_err[qi][fi][ni] = err;
+        g_gm_occ[qi][fi][ni] = n > 0 ? n : 1;
     });
-    if (g_gm_err[fi][ni] != hipSuccess)
+    if (g_gm_err[qi][fi][ni] != hipSuccess)
         return QMV_EHIP;
-    Args a = base_args(wfmt, QMV_A_Q8B32, kind, codes, scales, gather ? E : 1, ids, M, gather ? top_k : 1, x, xs,
+    Args a = base_args(wfmt, afmt, kind, codes, scales, gather ? E : 1, ids, M, gather ? top_k : 1, x, xs,
                        gather ? x_per_slot : 0, y, N, K);
     a.rows_per_tile = 4 * kGmWaves;
     a.gr_tiles = (N + a.rows_per_tile - 1) / a.rows_per_tile;
     const long long items = (long long)busy * a.gr_tiles;
-    long long per_cu = g_gm_occ[fi][ni];
+    long long per_cu = g_gm_occ[qi][fi][ni];
     const long long by_lds = (long long)kLdsPerCU / (long long)lds;
     if (per_cu > by_lds) per_cu = by_lds;
     if (per_cu < 1) per_cu = 1;
@@ -540,9 +542,10 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
             return launch_batched(codes, scales, codes2, scales2, E, ids, M, top_k, x, x_per_slot, y, N, K, stream);
         // codebook weights x int8 with at least two vectors per expert on
         // average: the int8 matrix-core kernel
-        if ((kind == kCB2 || kind == kCB3) && afmt == QMV_A_Q8B32 && !gate_up &&
+        if ((kind == kCB2 || kind == kCB3) && (afmt == QMV_A_Q8B32 || afmt == QMV_A_BF16_Q8) && !gate_up &&
             (gather ? (long long)M * top_k >= 2LL * E : M >= 8))
-            return launch_gmma(wfmt, kind, codes, scales, E, ids, M, top_k, x, xs, x_per_slot, y, N, K, stream);
+            return launch_gmma(wfmt, afmt, kind, codes, scales, E, ids, M, top_k, x, xs, x_per_slot, y, N, K,
+                               stream);
         // A gather of at most 64 tokens with fewer than two pairs per expert
         // (a verify batch over many experts) reuses almost no weights: as
         // token groups of up to 4 on the decode kernels, one launch per

@@ -115,8 +115,10 @@ __device__ __forceinline__ uint4 cb3_decode_half(uint32_t hi, uint32_t lo)
 }
 
 // Stage vectors [v0, v0 + cc) of the list (pair indices in `pairs`, or the
-// vector indices themselves for a dense call) as ng groups of 4.
-template <int F, int THREADS>
+// vector indices themselves for a dense call) as ng groups of 4.  Q: the
+// activations are bf16 and each 32-block is quantized here to int8 and an
+// fp16 scale (quant_q8_block, the decode kernels' staging quantizer).
+template <int F, int THREADS, bool Q>
 __device__ __forceinline__ void gm_stage(const Args &a, uint8_t *lds, const uint16_t *pairs, bool gather,
                                          int v0, int cc, int ng, int Up)
 {
@@ -134,15 +136,29 @@ __device__ __forceinline__ void gm_stage(const Args &a, uint8_t *lds, const uint
         if (m < cc && u < U) {
             const int p = gather ? (int)pairs[v0 + m] : v0 + m;
             const int vec = gather && !a.x_per_slot ? p / a.top_k : p;
-            const uint8_t *xp = a.x + (size_t)vec * a.K + (size_t)u * W;
-            const uint16_t *sp = a.xs + (size_t)vec * (a.K / 32) + (size_t)u * W / 32;
-            c0 = *(const uint4 *)xp;
-            c1 = *(const uint4 *)(xp + 16);
-            xs0 = 0.5f * (float)__builtin_bit_cast(_Float16, sp[0]);
-            if constexpr (F == kCB2) {
-                c2 = *(const uint4 *)(xp + 32);
-                c3 = *(const uint4 *)(xp + 48);
-                xs1 = 0.5f * (float)__builtin_bit_cast(_Float16, sp[1]);
+            if constexpr (Q) {
+                // 32 bf16 (64 bytes) per block
+                const uint8_t *xp = a.x + (size_t)vec * a.x_vec_bytes + (size_t)u * W * 2;
+                uint4 r[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) r[k] = *(const uint4 *)(xp + 16 * k);
+                xs0 = 0.5f * (float)__builtin_bit_cast(_Float16, (uint16_t)quant_q8_block(r, c0, c1));
+                if constexpr (F == kCB2) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) r[k] = *(const uint4 *)(xp + 64 + 16 * k);
+                    xs1 = 0.5f * (float)__builtin_bit_cast(_Float16, (uint16_t)quant_q8_block(r, c2, c3));
+                }
+            } else {
+                const uint8_t *xp = a.x + (size_t)vec * a.K + (size_t)u * W;
+                const uint16_t *sp = a.xs + (size_t)vec * (a.K / 32) + (size_t)u * W / 32;
+                c0 = *(const uint4 *)xp;
+                c1 = *(const uint4 *)(xp + 16);
+                xs0 = 0.5f * (float)__builtin_bit_cast(_Float16, sp[0]);
+                if constexpr (F == kCB2) {
+                    c2 = *(const uint4 *)(xp + 32);
+                    c3 = *(const uint4 *)(xp + 48);
+                    xs1 = 0.5f * (float)__builtin_bit_cast(_Float16, sp[1]);
+                }
             }
         }
         if constexpr (F == kCB2) {
@@ -351,7 +367,7 @@ __device__ __forceinline__ void gm_run(const Args &a, const uint8_t *lds, const 
 // Work items (expert slot, row tile), slot-major, dealt in equal contiguous
 // runs; per slot the pairs are listed and taken in chunks of up to 4 * NVG
 // vectors, each staged once and streamed against every row tile of the run.
-template <int F, int WAVES, int NVG, int CPL>
+template <int F, int WAVES, int NVG, int CPL, bool Q>
 __global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -398,7 +414,7 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
         for (int k = 0, v0 = 0; k < nchunk; ++k) {
             const int cc = (c - v0) / (nchunk - k) + ((c - v0) % (nchunk - k) != 0);
             const int ng = (cc + 3) >> 2;
-            gm_stage<F, THREADS>(a, lds, L.perm, gather, v0, cc, ng, Up);
+            gm_stage<F, THREADS, Q>(a, lds, L.perm, gather, v0, cc, ng, Up);
             __syncthreads();
             const int tile0 = i - slot * tiles, nt = iend - i;
             if constexpr (NVG >= 4) {
@@ -418,13 +434,14 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
     }
 }
 
-// [format: 2-bit, 3-bit][vector groups per chunk: 1, 2, 3, 4]; 8 waves, 3
-// steps of loads in flight.
-extern const void *const kTableGmma[2][4];
-const void *const kTableGmma[2][4] = {
-    {(const void *)&qmv_gmma_kernel<kCB2, 8, 1, 3>, (const void *)&qmv_gmma_kernel<kCB2, 8, 2, 3>,
-     (const void *)&qmv_gmma_kernel<kCB2, 8, 3, 3>, (const void *)&qmv_gmma_kernel<kCB2, 8, 4, 3>},
-    {(const void *)&qmv_gmma_kernel<kCB3, 8, 1, 3>, (const void *)&qmv_gmma_kernel<kCB3, 8, 2, 3>,
-     (const void *)&qmv_gmma_kernel<kCB3, 8, 3, 3>, (const void *)&qmv_gmma_kernel<kCB3, 8, 4, 3>}};
+// [int8 activations, bf16 quantized in staging][format: 2-bit, 3-bit]
+// [vector groups per chunk: 1, 2, 3, 4]; 8 waves, 3 steps of loads in flight.
+#define QMV_GM(F, N, Q) (const void *)&qmv_gmma_kernel<F, 8, N, 3, Q>
+#define QMV_GM_ROW(F, Q) {QMV_GM(F, 1, Q), QMV_GM(F, 2, Q), QMV_GM(F, 3, Q), QMV_GM(F, 4, Q)}
+extern const void *const kTableGmma[2][2][4];
+const void *const kTableGmma[2][2][4] = {{QMV_GM_ROW(kCB2, false), QMV_GM_ROW(kCB3, false)},
+                                         {QMV_GM_ROW(kCB2, true), QMV_GM_ROW(kCB3, true)}};
+#undef QMV_GM_ROW
+#undef QMV_GM
 
 }  // namespace qmv

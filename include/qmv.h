@@ -133,7 +133,8 @@ typedef enum {
  * With (MXFP4, BF16), 5 <= M <= 20 runs as groups of up to 4 vectors on the
  * 4-vector kernels (one launch per group), and M > 20 on the batched
  * matrix-core kernel described under qmv_gather_moe; 2-bit and 3-bit
- * weights with int8 activations and M >= 8 on the int8 matrix-core kernel;
+ * weights with int8 (or in-kernel quantized bf16) activations and M >= 8 on
+ * the int8 matrix-core kernel;
  * every other M > 4 call on the grouped kernel.
  */
 qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
@@ -159,9 +160,9 @@ qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scale
  * workspace) and one launch computes the call:
  *   (MXFP4, BF16) with M * top_k >= 2 E: each expert's rows against all of
  *     its vectors, up to 128 at a time, on the 32x32x16 bf16 matrix cores;
- *   (CB2 with K % 64 == 0 or CB3, Q8B32) with M * top_k >= 2 E: exact int32
- *     block sums on the int8 4x4x4 matrix cores, up to 16 vectors per
- *     staged chunk;
+ *   (CB2 with K % 64 == 0 or CB3, Q8B32 or BF16_Q8) with M * top_k >= 2 E:
+ *     exact int32 block sums on the int8 4x4x4 matrix cores, up to 16
+ *     vectors per staged chunk (bf16 x quantized while staged);
  *   at most 64 tokens with fewer than two pairs per expert: groups of up to
  *     4 tokens on the decode kernels, one launch per group;
  *   every other call: the decode kernels' own multiply-adds in one launch,
