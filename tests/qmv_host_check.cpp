@@ -12,7 +12,8 @@
 //   combine wfmt codes scales E ids rw M top_k afmt x xs per_slot y N K -> status
 //   strerror s                                                   -> text
 //   shapes                                                       -> checksum of every pick_shape /
-//                                                                   tuned_shape result over a grid
+//                                                                   tuned_shape / plan_grouped result
+//                                                                   over a grid
 // Pointers are decimal addresses (0 = null).
 #include <stdio.h>
 #include <stdlib.h>
@@ -61,6 +62,26 @@ unsigned long long shapes_checksum()
         printf("untuned shape matched\n");
         exit(3);
     }
+    // grouped-kernel plans: the grid never exceeds the items, the row tiles
+    // cover N, and the tile matches the shape
+    for (int u : {1, 7, 45, 90, 112, 224, 512})
+        for (int N : {1, 33, 2048, 2880, 7168, 100000})
+            for (int busy : {1, 4, 20, 256, 1023})
+                for (bool gu : {false, true})
+                    for (int occ : {1, 3})
+                        for (long long lds : {0LL, 40000LL, 150000LL}) {
+                            const GroupedPlan p = plan_grouped(u, 48LL * u, N, busy, gu, 256, lds,
+                                                               [&](int, int) { return occ; });
+                            const int rpt = 4 * (64 / p.sh.lpr) * (gu ? 1 : 2);
+                            if (p.grid < 1 || p.grid > p.items || p.rows_per_tile != rpt ||
+                                (long long)p.tiles * p.rows_per_tile < N ||
+                                (long long)(p.tiles - 1) * p.rows_per_tile >= N ||
+                                p.items != (long long)busy * p.tiles || p.sh.lpr != kMenuLpr[p.sh.li]) {
+                                printf("bad grouped plan\n");
+                                exit(3);
+                            }
+                            h = h * 1000003 + (unsigned long long)p.grid * 7 + p.sh.li * 5 + p.sh.ci;
+                        }
     for (int N : {1, 4, 1023, 4096, 4097, 1 << 20})
         h = h * 1000003 + dense4_waves(N);
     for (int K : {32, 2880, 7168, kMaxK})
