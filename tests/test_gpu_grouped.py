@@ -207,3 +207,44 @@ def test_few_pairs_split_groups(pair):
     y = gpu_call(inp).cpu().numpy()
     assert (y[12, 1] == 0).all()
     _check(inp, f"{wfmt} split groups")
+
+
+@pytest.mark.parametrize("pair", [("cb2", ""), ("cb2", "bf16"), ("cb3", "")], ids=_name)
+def test_int8_matrix_cores_largest_k(pair):
+    """K = 16384 (the largest K; 256 staged units per vector) on the int8
+    matrix-core kernel: a dense call with 9 vectors and a gather with
+    several vectors per expert."""
+    wfmt, act = pair
+    _check(synth.make(_wl(wfmt, act, "dense", 9, 40, 16384, seed=191)), f"{_name(pair)} K=16384 dense")
+    _check(synth.make(_wl(wfmt, act, "gather", 12, 24, 16384, E=5, top_k=3, seed=192)),
+           f"{_name(pair)} K=16384 gather")
+
+
+def test_int8_matrix_cores_many_experts():
+    """1023 experts with more than two pairs per expert on average (the
+    bitmap's largest expert count) on the int8 matrix-core kernel."""
+    _check(synth.make(_wl("cb3", "", "gather", 600, 40, 128, E=1023, top_k=4, seed=193)), "cb3 1023 experts")
+
+
+def test_int8_matrix_cores_graph_replays():
+    """Calls on the int8 matrix-core kernel captured in a HIP graph give the
+    eager result bit for bit on every replay."""
+    import torch
+    from gpu_util import to_dev
+    inp = synth.make(_wl("cb2", "", "gather", 64, 130, 1024, E=16, top_k=4, seed=194))
+    dev = to_dev(inp)
+    y1 = gpu_call(inp, dev).cpu().numpy()
+    out = torch.empty(y1.shape, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        gpu_call(inp, dev, y=out, stream=s)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        gpu_call(inp, dev, y=out, stream=torch.cuda.current_stream())
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), y1.view(np.uint32))
