@@ -56,6 +56,12 @@ namespace qmv {
 extern const void *const kTableGmma[2][2][4];
 }
 
+// Dense MXFP4 x bf16 with 9 to 32 vectors: 32-row tiles with K split over
+// the waves of a workgroup (qmv_k_mxfp4b.hip): [4 waves, 8 waves].
+namespace qmv {
+extern const void *const kTableBatchedKS[2];
+}
+
 namespace qmv {
 constexpr int kBatchedMenu = 6;
 extern const int kBatchedShapes[kBatchedMenu][3];
@@ -478,6 +484,42 @@ qmv_status_t launch_gmma(int wfmt, int afmt, int kind, const void *codes, const 
     return QMV_OK;
 }
 
+std::once_flag g_ks_once[2];
+hipError_t g_ks_err[2];
+constexpr int kKsVecs = 32;                             // vectors per chunk
+constexpr int kKsMaxM = 32;
+
+// Dense MXFP4 x bf16, 9 to 32 vectors: one launch of K-split tiles (32 rows x
+// a chunk of at most 32 vectors, chunks of equal size); 8 waves per
+// workgroup when K has at least 32 slices of 128 weights, else 4.  LDS: a
+// two-slice activation ring per wave.
+qmv_status_t launch_batched_ks(const void *codes, const void *scales, const void *x, float *y, int M, int N,
+                               int K, hipStream_t stream)
+{
+    Args a = base_args(QMV_W_MXFP4, QMV_A_BF16, kMXFP4, codes, scales, 1, nullptr, M, 1, x, nullptr, 0, y, N,
+                       K);
+    const int slices = (K + 127) / 128;
+    const int wi = slices >= 32 ? 1 : 0;
+    const int waves = wi ? 8 : 4;
+    const int nch = (M + kKsVecs - 1) / kKsVecs;
+    a.bt_chunk = (M + nch - 1) / nch;
+    a.bt_row_tiles = (N + 31) / 32;
+    a.bt_tiles = a.bt_row_tiles * nch;
+    a.bt_per_xcd = (a.bt_tiles + 7) / 8;
+    a.bt_vmax = kKsVecs;
+    const size_t lds = (size_t)waves * 2 * kKsVecs * 256;
+    const void *fn = kTableBatchedKS[wi];
+    std::call_once(g_ks_once[wi], [&] {
+        g_ks_err[wi] = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    });
+    if (g_ks_err[wi] != hipSuccess)
+        return QMV_EHIP;
+    void *kargs[] = {&a};
+    if (hipLaunchKernel(fn, dim3(8 * a.bt_per_xcd), dim3(64 * waves), kargs, lds, stream) != hipSuccess)
+        return QMV_EHIP;
+    return QMV_OK;
+}
+
 std::once_flag g_d4_once[2];
 hipError_t g_d4_err[2];
 
@@ -513,13 +555,19 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
     const bool gather = ids != nullptr;
     const bool gate_up = codes2 != nullptr;
     const int kind = kind_of(wfmt, afmt, K);
+    // Dense MXFP4 x bf16 with 9 to 32 vectors: K-split tiles, one launch.
+    // Measured on 7168 x 7168: 16 vectors 34.3 us as four 4-vector launches,
+    // 20.8 us here; 24 vectors 34.5 (batched) against 21.0; 5 vectors 16.6
+    // as two launches against 20.7 here; 64 vectors 31 (batched) against 40.
+    // Every tile restages all of x through L2 (32 vectors x K bf16 per
+    // 32-row tile: four times the tile's weight bytes at K = 7168), which
+    // bounds this shape.
+    if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kDenseGroupsMaxM && M <= kKsMaxM)
+        return launch_batched_ks(codes, scales, x, y, M, N, K, stream);
     if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM && M <= kDenseGroupsMaxM) {
         // A dense call with a few more than 4 vectors: groups of up to 4 on
-        // the decode kernels, each a launch over its own rows of x and y.
-        // A dense call is one expert, so the batched kernel has only N / 128
-        // tiles for it (56 workgroups for N = 7168): measured on 7168 x 7168,
-        // 4 vectors 8.75 us, 5 to 16 vectors 52-53 us batched, against
-        // 8.75 us per group of 4 here.
+        // the dense 4-vector kernel, each a launch over its own rows of x
+        // and y (7168 x 7168: 4 vectors 8.75 us; 5 vectors 16.6 us).
         for (int m0 = 0; m0 < M; m0 += kMaxM) {
             const int mg = M - m0 < kMaxM ? M - m0 : kMaxM;
             const qmv_status_t st = launch(wfmt, afmt, codes, scales, nullptr, nullptr, 1, nullptr, mg, 1,

@@ -62,7 +62,7 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxPairsBatched = 8192;
 // Dense MXFP4 x bf16 calls with 5..20 vectors run as groups of 4 on the
 // decode kernels (one expert gives the batched kernel too few tiles).
-constexpr int kDenseGroupsMaxM = 20;
+constexpr int kDenseGroupsMaxM = 8;
 constexpr int kSplitMaxM = 64;           // few-pairs gathers split into token groups up to this M
 constexpr int kMaxEBatched = 1023;
 

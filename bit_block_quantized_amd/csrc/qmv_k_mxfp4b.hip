@@ -389,6 +389,167 @@ __global__ __launch_bounds__(64 * WAVES, 1) void qmv_batched_kernel(const Args a
     }
 }
 
+// Dense calls with few vectors per weight matrix (a wide verify batch, a
+// short prompt): one 32-row tile of a single matrix has too little work for
+// a workgroup of waves that each own other rows, and too few tiles fill the
+// GPU.  Here the waves of a workgroup split the tile's K instead: wave w
+// takes the 128-weight slices w, w + WAVES, w + 2 WAVES, ... of the tile
+// (32 rows x a chunk of at most 32 vectors), stages their activations in a
+// two-slice LDS ring of its own (no workgroup barrier in the loop), and the
+// waves' partial tiles are summed in LDS in wave order at the end, so the
+// result is bitwise reproducible.  The loads, decode and MFMA steps are the
+// batched kernel's (lane (r, h): blocks h and 2 + h of row r per slice).
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int VMAX = 32;                        // vectors per chunk
+    constexpr int XJ = VMAX / 4;                    // staging loads (4 vectors each) per lane and slice
+    const int b = blockIdx.x;
+    const int t = (b & 7) * a.bt_per_xcd + (b >> 3);
+    if (t >= a.bt_tiles) return;
+    const int chunk = t / a.bt_row_tiles;
+    const int row_base = (t - chunk * a.bt_row_tiles) * 32;
+    const int vstart = chunk * a.bt_chunk;
+    const int nv = min(a.bt_chunk, a.M - vstart);
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int r = lane & 31;                        // row (A) / vector (B)
+    const int h = lane >> 5;                        // k half of an MFMA step
+    const int U = a.units;
+    const int S = (U + 3) >> 2;                     // 128-weight slices
+    const int KS = S > w ? (S - w + WAVES - 1) / WAVES : 0;   // this wave's slices
+    uint8_t *const ring = lds + w * (kBRing * VMAX * 256);
+
+    f32x16 acc;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes, a.expert_cb);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.scales, a.expert_sb);
+    const int n = row_base + r;
+    const uint32_t oc = n < a.N ? (uint32_t)n * (uint32_t)a.rcb + 16u * h : kBPast;
+    const uint32_t os = n < a.N ? (uint32_t)n * (uint32_t)a.rsb + h : kBPast;
+    // activation staging: lane 16 c + p of load j holds chunk p of vector
+    // 4 j + c of the chunk
+    uint32_t xo[XJ];
+    int xdst[XJ];
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+        const int v = 4 * j + (lane >> 4);
+        xdst[j] = bx_off(v, lane & 15);
+        xo[j] = v < nv ? (uint32_t)(vstart + v) * (uint32_t)a.x_vec_bytes + 16u * (lane & 15) : kBPast;
+    }
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, a.M * a.x_vec_bytes);   // < 2^31
+    const int K = a.K;
+    auto slice = [&](int k) { return w + WAVES * k; };
+    auto load_x = [&](int k, u32x4 (&xr)[XJ]) {
+        const int s = slice(k);
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) {
+            const bool ok = k < KS && 128 * s + 8 * (lane & 15) < K && xo[j] != kBPast;
+            xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? xo[j] + 256u * s : kBPast, 0, 0);
+        }
+    };
+    auto store_x = [&](int k, const u32x4 (&xr)[XJ]) {
+        uint8_t *const buf = ring + (k % kBRing) * (VMAX * 256);
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) *(u32x4 *)(buf + xdst[j]) = xr[j];
+    };
+    auto load_w = [&](int k, u32x4 (&wc)[2], uint8_t (&sb)[2]) {
+        const int s = slice(k);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const bool ok = k < KS && 4 * s + 2 * jb + h < U && oc != kBPast;
+            wc[jb] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? oc + 64u * s + 32u * jb : kBPast, 0, 0);
+            sb[jb] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? os + 4u * s + 2u * jb : kBPast, 0, 0);
+        }
+    };
+    int slow = 0;
+    auto compute = [&](int k, const u32x4 (&wc)[2], const uint8_t (&sbr)[2]) {
+        const int s = slice(k);
+        const uint8_t *const buf = ring + (k % kBRing) * (VMAX * 256);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const bool ok = k < KS && 4 * s + 2 * jb + h < U && oc != kBPast;
+            const uint32_t sb = ok ? (uint32_t)sbr[jb] : 127u;
+            slow |= (sb - 2u) > 250u;
+            const float sc = __uint_as_float(sb << 23);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const bf16x8 Bv = __builtin_bit_cast(bf16x8, lds_read16(buf + bx_off(r, 4 * (2 * jb + h) + tt)));
+                const bf16x8 A = dec8(wc[jb][tt], sc);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bv, acc, 0, 0, 0);
+            }
+        }
+    };
+    // weights three of this wave's slices ahead, activations two; the LDS
+    // ring is this wave's alone (a wave's LDS operations complete in order,
+    // so writing slice k + 1's buffer after slice k - 1's reads of it needs
+    // no barrier); the slice count is padded to a multiple of 6 (the padding
+    // reads past the buffers: zeros)
+    u32x4 wc0[2], wc1[2], wc2[2];
+    uint8_t sb0[2], sb1[2], sb2[2];
+    u32x4 xr0[XJ], xr1[XJ];
+    load_w(0, wc0, sb0);
+    load_x(0, xr0);
+    load_w(1, wc1, sb1);
+    load_x(1, xr1);
+    load_w(2, wc2, sb2);
+    store_x(0, xr0);
+    load_x(2, xr0);
+    auto step = [&](int k, u32x4 (&wc)[2], uint8_t (&sb)[2], u32x4 (&xn)[XJ]) {
+        store_x(k + 1, xn);
+        load_x(k + 3, xn);
+        compute(k, wc, sb);
+        load_w(k + 3, wc, sb);
+    };
+    for (int k = 0; k < KS; k += 6) {
+        step(k, wc0, sb0, xr1);
+        step(k + 1, wc1, sb1, xr0);
+        step(k + 2, wc2, sb2, xr1);
+        step(k + 3, wc0, sb0, xr0);
+        step(k + 4, wc1, sb1, xr1);
+        step(k + 5, wc2, sb2, xr0);
+    }
+    if (__syncthreads_or(slow)) {
+        batched_chunk_exact<0>(a, 0, nullptr, vstart, nv, row_base, min(32, a.N - row_base));
+        return;
+    }
+    // the waves' partial tiles, summed in wave order (every ring is free now)
+    float *const red = (float *)lds;
+    if (w > 0) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) red[((w - 1) * 16 + k) * 64 + lane] = acc[k];
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        for (int ww = 1; ww < WAVES; ++ww) acc[k] += red[((ww - 1) * 16 + k) * 64 + lane];
+    // lane (vector r, half h) holds rows 8 i + 4 h .. + 3 of the tile
+    if (r < nv) {
+        float *const yrow = a.y + (size_t)(vstart + r) * a.N;
+        const bool vec4 = (a.N & 3) == 0 && ((uintptr_t)a.y & 15) == 0;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int n0 = row_base + 8 * ii + 4 * h;
+            if (n0 < a.N) {
+                if (vec4) {
+                    *(float4 *)(yrow + n0) = make_float4(acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (n0 + k < a.N) yrow[n0 + k] = acc[4 * ii + k];
+                }
+            }
+        }
+    }
+}
+
+extern const void *const kTableBatchedKS[2];
+const void *const kTableBatchedKS[2] = {(const void *)&qmv_batched_ks_kernel<4>,
+                                        (const void *)&qmv_batched_ks_kernel<8>};
+
 // Instantiations: (waves per workgroup, 32-row fragments per wave, most
 // vectors per chunk), the chunk capacity as large as the register budget
 // allows without scratch memory.  Gate/up kernels hold a gate and an up

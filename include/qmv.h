@@ -93,7 +93,7 @@
  * a failed check the call returns the status, launches nothing and leaves y
  * untouched.  No check needs a device synchronization.  QMV_EHIP (the
  * runtime refused a launch) can come after earlier launches of the same
- * call have run: a dense (MXFP4, BF16) call with 5 to 20 vectors, and a
+ * call have run: a dense (MXFP4, BF16) call with 5 to 8 vectors, and a
  * gather or gate/up call with 5 to 64 tokens and fewer than two (token,
  * slot) pairs per expert (M * top_k < 2 E), are one launch per group of up
  * to 4 vectors or tokens, so y may then hold the rows of the groups before
@@ -130,9 +130,10 @@ typedef enum {
  *   x, x_scales        M activation vectors ([M][K], [M][K/32])
  *   y                  fp32 [M][N]
  * This is the gather below with one expert, top_k = 1 and ids all 0.
- * With (MXFP4, BF16), 5 <= M <= 20 runs as groups of up to 4 vectors on the
- * 4-vector kernels (one launch per group), and M > 20 on the batched
- * matrix-core kernel described under qmv_gather_moe; 2-bit and 3-bit
+ * With (MXFP4, BF16), 5 <= M <= 8 runs as groups of up to 4 vectors on the
+ * 4-vector kernel (one launch per group), 9 <= M <= 32 in one launch of
+ * 32-row tiles whose K is split over the waves of a workgroup, and M > 32
+ * on the batched matrix-core kernel described under qmv_gather_moe; 2-bit and 3-bit
  * weights with int8 (or in-kernel quantized bf16) activations and M >= 8 on
  * the int8 matrix-core kernel;
  * every other M > 4 call on the grouped kernel.

@@ -13,12 +13,14 @@ ragged N and K (partial 128-weight slices), E8M0 bytes outside [2, 252] and
 Inf activations, the pair and expert limits, and the full-size prefill chunk
 on sampled outputs.
 
-Which kernel a call reaches: dense calls with 5 to 20 vectors run as groups
-of up to 4 vectors on the dense 4-vector kernel (test_dense with M <= 20),
-gathers with fewer than two (token, slot) pairs per expert on the grouped
-decode-MAC kernel (test_gather_few_pairs_*); every other call with more than
-4 vectors runs on the batched kernel, so the special-value cases below use
-dense calls with M >= 21 or gathers with M * top_k >= 2 E.
+Which kernel a call reaches: dense calls with 5 to 8 vectors run as groups
+of up to 4 vectors on the dense 4-vector kernel, dense calls with 9 to 32
+vectors on the K-split tiles (the waves of a workgroup split K, partial tiles
+summed in LDS), gathers with fewer than two (token, slot) pairs per expert
+as token groups on the decode kernels (test_gather_few_pairs_*); every other
+call with more than 4 vectors runs on the batched kernel.  The special-value
+cases below use dense calls with 24 vectors (K-split), dense calls with 40
+vectors (batched) and gathers with M * top_k >= 2 E (batched).
 """
 import numpy as np
 import pytest
@@ -44,8 +46,8 @@ def _check(inp, what, exact=False):
     return assert_parity(y, yr, A, what)
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 37, 32), (8, 45, 96), (16, 130, 544), (64, 301, 2880),
-                                   (129, 64, 160), (200, 257, 1056), (33, 513, 7168)])
+@pytest.mark.parametrize("M,N,K", [(5, 37, 32), (8, 45, 96), (9, 40, 64), (16, 130, 544), (32, 33, 2880),
+                                   (64, 301, 2880), (129, 64, 160), (200, 257, 1056), (33, 513, 7168)])
 def test_dense(M, N, K):
     _check(synth.make(_wl("dense", M, N, K, seed=M + N + K)), f"dense M={M} N={N} K={K}")
 
@@ -120,6 +122,19 @@ def test_e8m0_special_scales():
     inp.scales[39, 0] = 255
     yr = _assert_special(inp, "e8m0 specials, dense")
     assert np.isnan(yr[:, 3]).all() and np.isnan(yr[:, 39]).all()
+
+
+def test_e8m0_special_scales_dense_batched():
+    """The same special scale bytes on a dense call with 40 vectors (the
+    batched kernel's exact path)."""
+    inp = synth.make(_wl("dense", 40, 40, 320, seed=63))
+    inp.scales[0, :] = 0
+    inp.scales[2, :] = 254
+    inp.scales[3, 4] = 255
+    inp.scales[4, :] = [0, 127, 254, 127, 1, 253, 2, 252, 127, 127]
+    inp.scales[39, 9] = 1
+    yr = _assert_special(inp, "e8m0 specials, dense batched")
+    assert np.isnan(yr[:, 3]).all()
 
 
 def test_e8m0_special_scales_gather_chunked():
