@@ -31,7 +31,8 @@ C2c, the 2-bit and 3-bit gathers fed bf16 activations that the kernel
 quantizes while staging them, C3q and C4q, and the gpt-oss gather with MXFP4
 weights and int8 activations (fp16 scale per 32), C2i, and a gpt-oss prefill
 chunk (512 tokens x top-4 of 32 experts) on the expert-batched matrix-core
-path, C6, whose entry also carries its MFMA rate against the dense bf16 peak.
+path, C6, whose entry also carries its MFMA rate against the dense bf16 peak,
+and the same chunk's down projection with the router-weighted combine, C6c.
 """
 from __future__ import annotations
 
@@ -114,7 +115,7 @@ def other_bytes(wl):
 # more than the 256 MB Infinity Cache of other weights is read.
 ROTATION = {"C1": 1, "C2": 32, "C3": 2, "C4": 2, "C5a": 4, "C5b": 40, "C2gu": 4, "C3gu": 1,
             "C4c": 2, "C2c": 32, "C3q": 2, "C4q": 2, "C2i": 32, "C6": 8, "C6gu": 4, "C6d": 40,
-            "C7": 1, "C8": 1}
+            "C7": 1, "C8": 1, "C6c": 8, "C8c": 1}
 
 
 def merge_regions(regions):
@@ -549,7 +550,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c,C3q,C4q,C2i,C6,C7,C8",
+    ap.add_argument("--workloads", default="C1,C3,C4,C5a,C5b,C2gu,C3gu,C4c,C2c,C3q,C4q,C2i,C6,C6c,C7,C8",
                     help="other shapes to measure besides the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")

@@ -1,8 +1,10 @@
 // qmv.hip -- launcher and C ABI of libqmv.so (declared in include/qmv.h).
 //
-// The host side only validates arguments, picks a kernel instantiation from
-// the call's shape, and enqueues one launch on the caller's stream.  It never
-// allocates, synchronizes or touches device memory itself.
+// The host side validates arguments, picks a kernel instantiation from the
+// call's shape, and enqueues the call's launches on the caller's stream.  It
+// never synchronizes or touches device memory itself; the one allocation is
+// the combine's per-slot rows for more than 4 tokens, stream-ordered from a
+// pool of the library's (launch_combine).
 #include "qmv_device.hpp"
 #include "qmv.h"
 
@@ -661,6 +663,116 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
     return QMV_OK;
 }
 
+// The router-weighted sum over each token's slots of the per-slot rows g
+// ([M][top_k][N], fp32): y[t][n] = w[t][0] g[t][0][n] + ... in slot order,
+// each slot one fused multiply-add onto a sum that starts at zero -- the
+// order and rounding of the single-launch combine kernel.  A thread owns
+// four consecutive rows of one token and loads four slots' rows at a time.
+// VEC: N % 4 == 0 and y, g 16-byte aligned (float4 loads and stores).
+template <bool VEC>
+__device__ __forceinline__ float4 slot_rows(const float *p, int n0, int N)
+{
+    if (VEC) return *(const float4 *)p;
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (n0 < N) v.x = p[0];
+    if (n0 + 1 < N) v.y = p[1];
+    if (n0 + 2 < N) v.z = p[2];
+    if (n0 + 3 < N) v.w = p[3];
+    return v;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void qmv_slot_sum_kernel(const float *__restrict__ g,
+                                                           const float *__restrict__ route_w,
+                                                           float *__restrict__ y, int M, int top_k, int N)
+{
+    const int nq = (N + 3) >> 2;
+    const int q = blockIdx.x * 256 + threadIdx.x;    // M * N < 2^31
+    if (q >= M * nq) return;
+    const int t = q / nq;
+    const int n0 = 4 * (q - t * nq);
+    const float *gt = g + (size_t)t * top_k * N + n0;
+    const float *wt = route_w + t * top_k;
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    auto add = [&](float w, float4 v) {
+        s.x = __builtin_fmaf(w, v.x, s.x);
+        s.y = __builtin_fmaf(w, v.y, s.y);
+        s.z = __builtin_fmaf(w, v.z, s.z);
+        s.w = __builtin_fmaf(w, v.w, s.w);
+    };
+    int j = 0;
+    for (; j + 4 <= top_k; j += 4) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = slot_rows<VEC>(gt + (size_t)(j + u) * N, n0, N);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) add(wt[j + u], v[u]);
+    }
+    for (; j < top_k; ++j) add(wt[j], slot_rows<VEC>(gt + (size_t)j * N, n0, N));
+    float *yt = y + (size_t)t * N + n0;
+    if (VEC) {
+        *(float4 *)yt = s;
+    } else {
+        if (n0 < N) yt[0] = s.x;
+        if (n0 + 1 < N) yt[1] = s.y;
+        if (n0 + 2 < N) yt[2] = s.z;
+        if (n0 + 3 < N) yt[3] = s.w;
+    }
+}
+
+// The combine of more than 4 tokens: the gather above (whatever kernel its
+// shape takes) writes every (token, slot) row into g, zeros for ids outside
+// [0, E), and the slot sum reads them back.  g holds M * top_k * N floats,
+// 256-byte aligned; y is written only by the last launch.
+qmv_status_t launch_combine_via(int wfmt, int afmt, const void *codes, const void *scales, int E,
+                                const int32_t *ids, const float *route_w, int M, int top_k, const void *x,
+                                const void *xs, int x_per_slot, float *g, float *y, int N, int K,
+                                hipStream_t stream)
+{
+    const qmv_status_t st = launch(wfmt, afmt, codes, scales, nullptr, nullptr, E, ids, M, top_k, x, xs,
+                                   x_per_slot, g, N, K, stream);
+    if (st != QMV_OK)
+        return st;
+    const long long quads = (long long)M * ((N + 3) / 4);
+    const unsigned blocks = (unsigned)((quads + 255) / 256);
+    if ((N & 3) == 0 && (((uintptr_t)y | (uintptr_t)g) & 15) == 0)
+        hipLaunchKernelGGL(qmv_slot_sum_kernel<true>, dim3(blocks), dim3(256), 0, stream, (const float *)g, route_w,
+                           y, M, top_k, N);
+    else
+        hipLaunchKernelGGL(qmv_slot_sum_kernel<false>, dim3(blocks), dim3(256), 0, stream, (const float *)g,
+                           route_w, y, M, top_k, N);
+    return hipGetLastError() == hipSuccess ? QMV_OK : QMV_EHIP;
+}
+
+// The per-slot rows of a many-token combine come from a memory pool of the
+// library's, one per device, that keeps what it has handed out (release
+// threshold: no limit): a call allocates and frees them in stream order
+// (hipMallocFromPoolAsync / hipFreeAsync on the caller's stream), and calls
+// after the first of their size reuse the pool's memory.
+constexpr int kPoolDevices = 64;
+std::once_flag g_pool_once[kPoolDevices];
+hipMemPool_t g_pool[kPoolDevices];
+hipError_t g_pool_err[kPoolDevices];
+
+hipError_t combine_pool(int dev, hipMemPool_t &pool)
+{
+    std::call_once(g_pool_once[dev], [&] {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipError_t e = hipMemPoolCreate(&g_pool[dev], &props);
+        if (e == hipSuccess) {
+            uint64_t keep = ~0ull;
+            e = hipMemPoolSetAttribute(g_pool[dev], hipMemPoolAttrReleaseThreshold, &keep);
+        }
+        g_pool_err[dev] = e;
+    });
+    pool = g_pool[dev];
+    return g_pool_err[dev];
+}
+
 // Down projection with the router-weighted combine: one launch, grid (row
 // tiles, tokens); each lane carries row n of four of the token's slots.
 qmv_status_t launch_combine(int wfmt, int afmt, const void *codes, const void *scales, int E,
@@ -668,6 +780,24 @@ qmv_status_t launch_combine(int wfmt, int afmt, const void *codes, const void *s
                             const void *x, const void *xs, int x_per_slot, float *y, int N, int K,
                             hipStream_t stream)
 {
+    if (M > kMaxM) {
+        // Many tokens: gather into pool memory, then the slot sum (the
+        // one-launch kernel below re-reads each expert's weights per token).
+        hipDevice_t dev = 0;                         // the stream's device
+        hipMemPool_t pool;
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kPoolDevices ||
+            combine_pool(dev, pool) != hipSuccess)
+            return QMV_EHIP;
+        void *g = nullptr;
+        if (hipMallocFromPoolAsync(&g, (size_t)M * top_k * N * sizeof(float), pool, stream) != hipSuccess)
+            return QMV_EHIP;
+        const qmv_status_t st = launch_combine_via(wfmt, afmt, codes, scales, E, ids, route_w, M, top_k, x, xs,
+                                                   x_per_slot, (float *)g, y, N, K, stream);
+        const hipError_t fe = hipFreeAsync(g, stream);
+        if (st != QMV_OK)
+            return st;
+        return fe == hipSuccess ? QMV_OK : QMV_EHIP;
+    }
     const int kind = kind_of(wfmt, afmt, K);
     Args a = base_args(wfmt, afmt, kind, codes, scales, E, ids, M, top_k, x, xs, x_per_slot, y, N, K);
     a.route_w = route_w;

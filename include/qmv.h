@@ -74,11 +74,15 @@
  * scale / 2) before the activation scale multiplies it.
  *
  * ------------------------------------------------------------- conventions
- * Ownership: every pointer is a device pointer owned by the caller.  The
- * library never allocates, frees, copies to the host or synchronizes; a call
- * only enqueues kernels on `stream` and returns.  It reads only the extents
- * above and writes only y.  It is stateless and may be called concurrently
- * from several host threads.
+ * Ownership: every pointer is a device pointer owned by the caller.  A call
+ * only enqueues work on `stream` and returns: the library never copies to
+ * the host or synchronizes.  It reads only the extents above and writes only
+ * y.  The one device memory it takes for itself is the temporary of a
+ * combine call with more than 4 tokens (qmv_gather_moe_combine), allocated
+ * and freed in stream order on `stream` from a memory pool the library
+ * creates per device at first use and keeps (with the memory it has handed
+ * out) until the process ends.  Calls may be made concurrently from several
+ * host threads and streams.
  *
  * Alignment: codes 16 bytes (8 for CB2 when K % 64 != 0), x 16 bytes,
  * scales, x_scales, expert ids and y 4 bytes.
@@ -97,7 +101,8 @@
  * gather or gate/up call with 5 to 64 tokens and fewer than two (token,
  * slot) pairs per expert (M * top_k < 2 E), are one launch per group of up
  * to 4 vectors or tokens, so y may then hold the rows of the groups before
- * the failing one.  Every other call is one launch.  An expert
+ * the failing one.  A combine call with more than 4 tokens writes y only in
+ * its last launch.  Every other call is one launch.  An expert
  * id outside [0, E) is not an error: that (token, slot) output row is
  * written with zeros (mlxcel issue #2178, Implementation Notes, Edge cases).
  *
@@ -203,7 +208,7 @@ qmv_status_t qmv_gather_moe_swiglu(qmv_wfmt_t wfmt, const void *gate_codes, cons
  *   g(t, j, n) = sum_k w(e, n, k) * x(t, j, k),  e = expert_ids[t][j]
  *   g(t, j, n) = 0                               if e is outside [0, E)
  * The per-slot gather above followed by the weighted sum over each token's
- * slots, in one launch: the result an MoE layer adds to the residual stream.
+ * slots: the result an MoE layer adds to the residual stream.
  * The pages count gate, up and down expert calls per decoded token (mlxcel
  * issue #2178, Problem / Background) and time the down projection's 3-bit
  * matvec on its own (lucebox-hub PR #21, Summary); the combine is the
@@ -213,11 +218,19 @@ qmv_status_t qmv_gather_moe_swiglu(qmv_wfmt_t wfmt, const void *gate_codes, cons
  *                     each (token, slot) -- the usual down-projection input;
  *                  0: x is [M][K] for every slot of a token.
  *   y              fp32 [M][N], overwritten (not accumulated into).
- * The slots of a token are summed in slot order; results are bitwise
+ * The slots of a token are summed in slot order, each slot one fused
+ * multiply-add onto a sum that starts at zero; results are bitwise
  * reproducible.  An out-of-range id contributes route_weights[t][j] * 0.
- * Weights, scales and activations, limits and errors as qmv_gather_moe
- * (any M: a workgroup per token and row tile); route_weights may be signed
- * or sum to zero; a null or misaligned route_weights is QMV_EINVAL.
+ * Up to 4 tokens: one launch, a workgroup per token and row tile, each lane
+ * carrying one row of four of the token's slots.  More than 4 tokens: the
+ * gather of qmv_gather_moe (same kernels and routing) writes every (token,
+ * slot) row to a temporary of M * top_k * N floats from the library's pool
+ * (see Ownership; it can be recorded into a HIP graph as the graph's own
+ * allocation), and a second launch forms the slot sums from it; an
+ * allocation the pool refuses is QMV_EHIP before anything is launched.
+ * Weights, scales and activations, limits and errors as qmv_gather_moe;
+ * route_weights may be signed or sum to zero; a null or misaligned
+ * route_weights is QMV_EINVAL.
  */
 qmv_status_t qmv_gather_moe_combine(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
                                     int E, const int32_t *expert_ids, const float *route_weights,

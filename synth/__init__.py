@@ -171,6 +171,16 @@ BATCHED_WORKLOADS = {
                    x_per_slot=True,
                    desc="DeepSeek-shaped MoE prefill chunk, 3-bit down-proj gather: 512 tokens x "
                         "top-4 of 256, K=2048, N=7168, per-slot int8 x"),
+    # The same chunks' down projections with the router-weighted combine
+    # (y[M][N]): the per-slot gather, then the slot sum.
+    "C6c": Workload("C6c", "combine", "mxfp4", M=512, N=2880, K=2880, seed=18, E=32, top_k=4,
+                    x_per_slot=True,
+                    desc="gpt-oss-20b MoE prefill chunk, down-proj with router-weighted combine: "
+                         "512 tokens x top-4 of 32, K=N=2880, MXFP4 x per-slot bf16"),
+    "C8c": Workload("C8c", "combine", "cb3", M=512, N=7168, K=2048, seed=19, E=256, top_k=4,
+                    x_per_slot=True,
+                    desc="DeepSeek-shaped MoE prefill chunk, 3-bit down-proj with router-weighted "
+                         "combine: 512 tokens x top-4 of 256, K=2048, N=7168, per-slot int8 x"),
 }
 
 

@@ -39,12 +39,14 @@ def gpu_combine(inp, dev=None, y=None, stream=None, weights=None):
                                     x_per_slot=wl.x_per_slot, y=y, stream=stream)
 
 
-def oracle_combine(inp, weights=None):
+def oracle_combine(inp, weights=None, outs=None):
+    """The oracle's combine at every output ([M][N]), or at the flat output
+    indices ``outs`` (1-D)."""
     o = oracle.load()
     wl = inp.wl
     w = inp.extra["weights"] if weights is None else weights
     M = inp.ids.shape[0]
-    sel = np.arange(M * wl.N, dtype=np.int64)
+    sel = np.arange(M * wl.N, dtype=np.int64) if outs is None else np.asarray(outs, np.int64)
     parts = np.array_split(sel, max(1, min(threads(), len(sel) // 64 + 1)))
 
     def run(p):
@@ -53,8 +55,10 @@ def oracle_combine(inp, weights=None):
 
     with ThreadPoolExecutor(len(parts)) as ex:
         res = list(ex.map(run, parts))
-    y = np.concatenate([r[0] for r in res]).reshape(M, wl.N)
-    A = np.concatenate([r[1] for r in res]).reshape(M, wl.N)
+    y = np.concatenate([r[0] for r in res])
+    A = np.concatenate([r[1] for r in res])
+    if outs is None:
+        return y.reshape(M, wl.N), A.reshape(M, wl.N)
     return y, A
 
 
@@ -94,9 +98,12 @@ def test_top_k_groups(wfmt, top_k):
 
 
 @pytest.mark.parametrize("wfmt", FMTS)
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 6, 17])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 17, 40])
 @pytest.mark.parametrize("per_slot", [True, False])
 def test_m_sweep(wfmt, M, per_slot):
+    """Up to 4 tokens on the one-launch combine kernel; more as the gather
+    (40 tokens x 5 slots over 7 experts: the matrix-core kernels) followed
+    by the slot sum."""
     wl = _combine_wl(wfmt, M=M, N=70, K=448, E=7, top_k=5, x_per_slot=per_slot, seed=10 + M)
     _check(synth.make(wl), f"{wfmt} M={M} per_slot={per_slot}")
 
@@ -189,6 +196,64 @@ def test_signed_and_zero_sum_weights(wfmt):
     assert np.array_equal(y[0], y2[0])
 
 
+@pytest.mark.parametrize("wfmt", FMTS)
+def test_many_tokens_one_hot_and_exact(wfmt):
+    """More than 4 tokens: a one-hot weight on slot j gives exactly the per-slot
+    gather's row j of every token (the gather runs the same kernel into the
+    combine's temporary), and at unit scales with power-of-two weights the
+    result is bit-exact against the oracle; invalid ids included."""
+    M, top_k = 24, 4
+    wl = _combine_wl(wfmt, M=M, N=75, K=320, E=6, top_k=top_k, seed=31)
+    inp = _unit_scale(synth.make(wl))
+    inp.ids[3, 1] = -1
+    inp.ids[7, :] = 6
+    dev = to_dev(inp)
+    g = gpu_call(synth.Inputs(wl.scaled(kind="gather"), inp.codes, inp.scales, inp.ids, inp.x,
+                              inp.xs), dev).cpu().numpy()
+    for j in range(top_k):
+        w = np.zeros((M, top_k), np.float32)
+        w[:, j] = 1.0
+        y = gpu_combine(inp, dev, weights=w).cpu().numpy()
+        assert np.array_equal(y.view(np.uint32), g[:, j].view(np.uint32)), j
+    w = np.random.default_rng(32).choice(np.float32([0.125, 0.25, -0.5, 1.0, 2.0, -4.0]),
+                                         size=(M, top_k)).astype(np.float32)
+    y = gpu_combine(inp, dev, weights=w).cpu().numpy()
+    yr, _ = oracle_combine(inp, weights=w)
+    assert_exact(y, yr, f"{wfmt} many tokens, unit scales")
+    assert not y[7].any()
+
+
+@pytest.mark.parametrize("name", ["C6c", "C8c"])
+def test_prefill_combine_full_size_sampled(name):
+    """The prefill chunks' down projections with the combine, as bench.py
+    launches them: sampled outputs and 2 whole rows of y against the oracle."""
+    inp = synth.make(synth.workload(name))
+    y = gpu_combine(inp).cpu().numpy().reshape(-1)
+    wl = inp.wl
+    rng = np.random.default_rng(11)
+    outs = np.concatenate([rng.choice(y.size, size=3000, replace=False),
+                           np.arange(wl.N), 301 * wl.N + np.arange(wl.N)])
+    yr, A = oracle_combine(inp, outs=outs)
+    worst = assert_parity(y[outs], yr, A, f"{name} sampled")
+    print(f"{name}: worst |err| / bound = {worst:.3e}")
+
+
+def test_many_tokens_leaves_nothing_past_y_and_repeats():
+    """The many-token combine writes every row of y, nothing past it, and the
+    same bits on a second call (its temporary comes back from the pool)."""
+    wl = _combine_wl("mxfp4", M=33, N=130, K=256, E=5, top_k=3, seed=41)
+    inp = synth.make(wl)
+    dev = to_dev(inp)
+    n = wl.M * wl.N
+    buf = torch.full((n + 4096,), float("nan"), device="cuda")
+    buf[n:] = 12345.0
+    y1 = gpu_combine(inp, dev, y=buf[:n].view(wl.M, wl.N)).cpu().numpy().copy()
+    assert (buf[n:].cpu().numpy() == 12345.0).all()
+    assert not np.isnan(y1).any()
+    y2 = gpu_combine(inp, dev).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_bitwise_deterministic(name):
     inp = synth.make(synth.COMBINE_WORKLOADS[name].scaled(**SMALL[name]))
@@ -234,6 +299,36 @@ def test_graph_replays_match_eager():
     outs = [torch.empty_like(e) for e in eager]
     wts = [torch.from_numpy(inp.extra["weights"]).cuda() for inp in cases]
     import bit_block_quantized_amd as q
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for inp, dev, out, wt in zip(cases, devs, outs, wts):
+            M, top_k = inp.ids.shape
+            xs = None if dev["xs"] is None else dev["xs"].view(M, top_k, -1)
+            q.qmv_gather_moe_combine(inp.wl.wfmt, dev["codes"], dev["scales"], dev["ids"], wt,
+                                     dev["x"].view(M, top_k, -1), xs, x_per_slot=True, y=out,
+                                     stream=torch.cuda.current_stream())
+    for rep in range(4):
+        for out in outs:
+            out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, out in zip(eager, outs):
+            assert torch.equal(e.view(torch.int32), out.view(torch.int32)), rep
+
+
+def test_many_tokens_graph_replays_match_eager():
+    """A captured many-token combine (its temporary becomes the graph's own
+    allocation) replays to the eager result every time."""
+    import bit_block_quantized_amd as q
+    cases = [synth.make(_combine_wl(f, M=24, N=96, K=320, E=6, top_k=4, seed=51 + i))
+             for i, f in enumerate(FMTS)]
+    devs = [to_dev(inp) for inp in cases]
+    eager = [gpu_combine(inp, dev).clone() for inp, dev in zip(cases, devs)]
+    outs = [torch.empty_like(e) for e in eager]
+    wts = [torch.from_numpy(inp.extra["weights"]).cuda() for inp in cases]
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
