@@ -28,6 +28,7 @@ import os
 import torch  # noqa: F401  -- loads the HIP runtime that libqmv.so binds to
 
 __all__ = ["qmv_dense", "qmv_gather_moe", "qmv_gather_moe_swiglu", "qmv_gather_moe_combine",
+           "qmv_gather_moe_combine_noalloc",
            "qmv_strerror",
            "qmv_probe_stream_read", "lib", "LIB_PATH",
            "W_MXFP4", "W_CB2", "W_CB3", "A_BF16", "A_Q8B32", "A_BF16_Q8", "QmvError"]
@@ -38,7 +39,9 @@ W_MXFP4, W_CB2, W_CB3 = 0, 1, 2
 A_BF16, A_Q8B32, A_BF16_Q8 = 0, 1, 2
 _WFMT = {"mxfp4": W_MXFP4, "cb2": W_CB2, "cb3": W_CB3}
 _AFMT_OF = {W_MXFP4: A_BF16, W_CB2: A_Q8B32, W_CB3: A_Q8B32}
-STATUS = {0: "QMV_OK", 1: "QMV_EINVAL", 2: "QMV_EUNSUPPORTED", 3: "QMV_EHIP"}
+STATUS = {0: "QMV_OK", 1: "QMV_EINVAL", 2: "QMV_EUNSUPPORTED", 3: "QMV_EHIP", 4: "QMV_ESCRATCH"}
+# bytes of the allocation-free combine's fixed temporary per GPU (include/qmv.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class QmvError(RuntimeError):
@@ -68,6 +71,8 @@ def lib():
     L.qmv_gather_moe_swiglu.argtypes = [I, P, P, P, P, I, P, I, I, I, P, P, P, I, I, P]
     L.qmv_gather_moe_combine.restype = I
     L.qmv_gather_moe_combine.argtypes = [I, P, P, I, P, P, I, I, I, P, P, I, P, I, I, P]
+    L.qmv_gather_moe_combine_noalloc.restype = I
+    L.qmv_gather_moe_combine_noalloc.argtypes = [I, P, P, I, P, P, I, I, I, P, P, I, P, I, I, P]
     L.qmv_probe_stream_read.restype = I
     L.qmv_probe_stream_read.argtypes = [I, P, P, I, P, P]
     L.qmv_strerror.restype = ctypes.c_char_p
@@ -298,6 +303,25 @@ def qmv_gather_moe_combine(wfmt, w_codes, w_scales, expert_ids, route_weights, x
     (float32 [M][N]).  ``x`` is [M][top_k][K] per (token, slot) -- the usual
     down-projection input -- or [M][K]; ``x_per_slot`` defaults to
     ``x.dim() == 3``."""
+    return _combine("qmv_gather_moe_combine", wfmt, w_codes, w_scales, expert_ids, route_weights, x,
+                    x_scales, x_per_slot, y, stream)
+
+
+def qmv_gather_moe_combine_noalloc(wfmt, w_codes, w_scales, expert_ids, route_weights, x, y,
+                                   x_scales=None, x_per_slot=None, stream=None):
+    """qmv_gather_moe_combine into the caller's y ([M][N] float32, required)
+    with nothing allocated, by the library or here: a call with more than 4
+    tokens keeps its temporary in the library's fixed per-GPU array of
+    NOALLOC_SCRATCH_BYTES (larger ones raise QMV_ESCRATCH); calls that overlap
+    on one GPU race on that array."""
+    if y is None:
+        raise ValueError("qmv_gather_moe_combine_noalloc needs the output y")
+    return _combine("qmv_gather_moe_combine_noalloc", wfmt, w_codes, w_scales, expert_ids, route_weights,
+                    x, x_scales, x_per_slot, y, stream)
+
+
+def _combine(entry, wfmt, w_codes, w_scales, expert_ids, route_weights, x, x_scales, x_per_slot, y,
+             stream):
     w = _wfmt(wfmt)
     M, top_k = _check_ids(expert_ids)
     E, N = w_codes.shape[0], w_codes.shape[1]
@@ -313,10 +337,10 @@ def qmv_gather_moe_combine(wfmt, w_codes, w_scales, expert_ids, route_weights, x
     if y is not None:
         _check_y(y, (M, N))
     dev = w_codes.device
-    _gpu(dev, "qmv_gather_moe_combine")
+    _gpu(dev, entry)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    s = lib().qmv_gather_moe_combine(
+    s = getattr(lib(), entry)(
         w, _dev_ptr(w_codes, "w_codes", (torch.uint8,), dev),
         _dev_ptr(w_scales, "w_scales", _SCALE_DT, dev), E,
         _dev_ptr(expert_ids, "expert_ids", (torch.int32,), dev),

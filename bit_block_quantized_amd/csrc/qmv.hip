@@ -773,6 +773,38 @@ hipError_t combine_pool(int dev, hipMemPool_t &pool)
     return g_pool_err[dev];
 }
 
+// The allocation-free combine's temporary: one array per GPU in the device
+// code, held from the library's load until the process ends.  In host code
+// `scratch` is only a host-side stand-in, never a device address: the
+// address is looked up once per device (scratch_on) and only that is used.
+static __device__ __align__(256) float scratch[QMV_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+std::once_flag g_scratch_once[kPoolDevices];
+float *g_scratch_ptr[kPoolDevices];
+hipError_t g_scratch_err[kPoolDevices];
+
+// The device address of device dev's `scratch`, looked up at the first call
+// on that device with the device made current for the lookup.
+hipError_t scratch_on(int dev, float *&ptr)
+{
+    std::call_once(g_scratch_once[dev], [&] {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        const bool other = e == hipSuccess && cur != dev;
+        if (other) e = hipSetDevice(dev);
+        void *p = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (other) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        g_scratch_ptr[dev] = (float *)p;
+        g_scratch_err[dev] = e == hipSuccess && p == nullptr ? hipErrorInvalidSymbol : e;
+    });
+    ptr = g_scratch_ptr[dev];
+    return g_scratch_err[dev];
+}
+
 // Down projection with the router-weighted combine: one launch, grid (row
 // tiles, tokens); each lane carries row n of four of the token's slots.
 qmv_status_t launch_combine(int wfmt, int afmt, const void *codes, const void *scales, int E,
@@ -887,6 +919,31 @@ QMV_API qmv_status_t qmv_gather_moe_combine(qmv_wfmt_t wfmt, const void *w_codes
         return s;
     return launch_combine(wfmt, afmt, w_codes, w_scales, E, expert_ids, route_weights, M, top_k, x, xs,
                           x_per_slot ? 1 : 0, y, N, K, stream);
+}
+
+QMV_API qmv_status_t qmv_gather_moe_combine_noalloc(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
+                                            int E, const int32_t *expert_ids, const float *route_weights,
+                                            int M, int top_k, qmv_afmt_t afmt, const void *x,
+                                            const void *x_scales, int x_per_slot, float *y, int N, int K,
+                                            hipStream_t stream)
+{
+    const void *xs = used_xs(afmt, x_scales);
+    const qmv_status_t s = check_combine(wfmt, w_codes, w_scales, E, expert_ids, route_weights, M, top_k, afmt,
+                                         x, x_scales, y, N, K);
+    if (s != QMV_OK)
+        return s;
+    if (M <= kMaxM)                                  // the one-launch kernel: no temporary
+        return launch_combine(wfmt, afmt, w_codes, w_scales, E, expert_ids, route_weights, M, top_k, x, xs,
+                              x_per_slot ? 1 : 0, y, N, K, stream);
+    if ((size_t)M * top_k * N * sizeof(float) > QMV_NOALLOC_SCRATCH_BYTES)
+        return QMV_ESCRATCH;
+    hipDevice_t dev = 0;                             // the stream's device
+    float *g = nullptr;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kPoolDevices ||
+        scratch_on(dev, g) != hipSuccess)
+        return QMV_EHIP;
+    return launch_combine_via(wfmt, afmt, w_codes, w_scales, E, expert_ids, route_weights, M, top_k, x, xs,
+                              x_per_slot ? 1 : 0, g, y, N, K, stream);
 }
 
 QMV_API const char *qmv_strerror(qmv_status_t status)

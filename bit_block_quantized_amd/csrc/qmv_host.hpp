@@ -382,6 +382,8 @@ inline const char *status_text(int status)
                                   "K % 32 == 0 and K <= 16384; "
                                   "pairs MXFP4+BF16, MXFP4+Q8B32, CB2/CB3+Q8B32, CB2/CB3+BF16_Q8)";
     case QMV_EHIP: return "the HIP runtime rejected the kernel launch";
+    case QMV_ESCRATCH: return "the call needs more temporary memory than the allocation-free entry point's "
+                              "fixed 64 MiB per GPU (M * top_k * N * 4 bytes with more than 4 tokens)";
     }
     return "unknown status";
 }

@@ -126,8 +126,13 @@ typedef enum {
     QMV_OK = 0,
     QMV_EINVAL = 1,        /* null or misaligned pointer, size <= 0 */
     QMV_EUNSUPPORTED = 2,  /* M, top_k or K out of range; unsupported format pair */
-    QMV_EHIP = 3           /* the HIP runtime refused the launch */
+    QMV_EHIP = 3,          /* the HIP runtime refused the launch */
+    QMV_ESCRATCH = 4       /* the call needs more than QMV_NOALLOC_SCRATCH_BYTES of
+                              temporary (qmv_gather_moe_combine_noalloc only) */
 } qmv_status_t;
+
+/* The fixed device temporary of qmv_gather_moe_combine_noalloc, per GPU. */
+#define QMV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /*
  * Dense GEMV: y[m][n] = sum_k w(n, k) * x(m, k) for m < M, n < N.
@@ -237,6 +242,31 @@ qmv_status_t qmv_gather_moe_combine(qmv_wfmt_t wfmt, const void *w_codes, const 
                                     int M, int top_k, qmv_afmt_t afmt, const void *x,
                                     const void *x_scales, int x_per_slot, float *y, int N, int K,
                                     hipStream_t stream);
+
+/*
+ * qmv_gather_moe_combine without any allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture that must record no
+ * allocation, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results (bit for bit), limits and errors as
+ * qmv_gather_moe_combine, except where the temporary of a call with more
+ * than 4 tokens lives: in a fixed array inside the library's device code,
+ * QMV_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, which each GPU the library
+ * runs on holds from the library's load until the process ends.  A call with
+ * more than 4 tokens needs M * top_k * N * 4 bytes of it; a larger one
+ * returns QMV_ESCRATCH, launches nothing and leaves y untouched (the
+ * allocating entry point takes it).  Up to 4 tokens use no temporary.
+ * Every call on one GPU uses that GPU's one array, and each call overwrites
+ * what it reads back, so nothing needs clearing between calls; but calls
+ * whose work overlaps on one GPU (other streams, other host threads) race on
+ * it: the caller orders them, e.g. on one stream.  The first call on a device
+ * looks up the array's device address (hipGetSymbolAddress), with that device
+ * made current for the lookup.
+ */
+qmv_status_t qmv_gather_moe_combine_noalloc(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scales,
+                                            int E, const int32_t *expert_ids, const float *route_weights,
+                                            int M, int top_k, qmv_afmt_t afmt, const void *x,
+                                            const void *x_scales, int x_per_slot, float *y, int N, int K,
+                                            hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char *qmv_strerror(qmv_status_t status);

@@ -40,14 +40,15 @@ def declared_functions(header=None):
 
 def test_header_declares_the_boundary():
     assert declared_functions("qmv.h") == ["qmv_dense", "qmv_gather_moe",
-                                           "qmv_gather_moe_combine", "qmv_gather_moe_swiglu",
-                                           "qmv_strerror"]
+                                           "qmv_gather_moe_combine",
+                                           "qmv_gather_moe_combine_noalloc",
+                                           "qmv_gather_moe_swiglu", "qmv_strerror"]
     assert declared_functions("qmv_probe.h") == ["qmv_probe_stream_read"]
 
 
 def test_library_exports_every_declared_symbol(L):
     declared = declared_functions()
-    assert len(declared) == 6
+    assert len(declared) == 7
     for name in declared:
         assert hasattr(L, name), name
     out = os.popen(f"nm -D --defined-only {ROOT}/bit_block_quantized_amd/libqmv.so").read()
@@ -59,7 +60,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_strerror_covers_every_status(L):
-    for s in range(4):
+    for s in range(5):
         txt = L.qmv_strerror(s).decode()
         assert txt and "unknown" not in txt
     assert L.qmv_strerror(99).decode() == "unknown status"
@@ -188,6 +189,26 @@ COMBINE_CASES = [
 @pytest.mark.parametrize("kw,want", COMBINE_CASES)
 def test_combine_validation(L, kw, want):
     assert combine(L, **kw) == want
+
+
+def combine_noalloc(L, wfmt=W_CB3, codes=FAKE, scales=FAKE, E=256, ids=FAKE, rw=FAKE, M=1, top_k=4,
+                    afmt=A_Q8, x=FAKE, xs=FAKE, per_slot=1, y=FAKE, N=7168, K=2048):
+    return L.qmv_gather_moe_combine_noalloc(wfmt, codes, scales, E, ids, rw, M, top_k, afmt, x, xs,
+                                            per_slot, y, N, K, None)
+
+
+@pytest.mark.parametrize("kw,want", COMBINE_CASES + [
+    # more than 4 tokens whose temporary (M * top_k * N * 4 bytes) exceeds the
+    # fixed 64 MiB: refused after the argument checks, before any HIP call
+    (dict(M=512, top_k=8, N=4097, E=1, K=32), 4),
+    (dict(M=2048, top_k=4, N=2049, E=1, K=32), 4),
+    (dict(M=2048, top_k=4, N=2049, E=1, K=32, rw=None), EINVAL),
+    (dict(M=2048, top_k=5, N=2049, E=1, K=32), EUNSUP),
+])
+def test_combine_noalloc_validation(L, kw, want):
+    """The allocation-free combine makes the allocating entry's checks, then
+    the size check of its fixed temporary, all on the host."""
+    assert combine_noalloc(L, **kw) == want
 
 
 def probe(L, n=1, ptrs=(FAKE,), sizes=(4096,), variant=0, sink=FAKE):

@@ -66,11 +66,11 @@ def test_entry_point_checks_under_sanitizers(checker):
 
 
 def test_shape_choice_and_texts_under_sanitizers(checker):
-    lines = ["shapes"] + [f"strerror {s}" for s in (0, 1, 2, 3, 99, -1)]
+    lines = ["shapes"] + [f"strerror {s}" for s in (0, 1, 2, 3, 4, 99, -1)]
     out = _run(checker, lines)
     int(out[0])
-    assert all(t and "unknown" not in t for t in out[1:5])
-    assert out[5] == out[6] == "unknown status"
+    assert all(t and "unknown" not in t for t in out[1:6])
+    assert out[6] == out[7] == "unknown status"
 
 
 def test_library_agrees_with_the_sanitized_build(checker):
