@@ -26,10 +26,14 @@
 // Inside a tile, wave w owns RF fragments of 32 rows, multiplied on the
 // 32x32x16 bf16 MFMA (measured on MI355X: about twice the rate per flop of
 // the 16x16x32 form).  K is walked in 128-weight slices.  Lane (r, h) =
-// lane 32 h + r loads row r's 32-weight blocks h and 2 + h of slice s (16
-// contiguous bytes each).  The MFMA's 16-long k axis is split between the
-// lane halves h: in step (jb, t), half h supplies weights 8t .. 8t + 7 of
-// block 2 jb + h of its row (A) and the same 8 activations of vector r (B).
+// lane 32 h + r loads row r's 32-weight blocks 2 h and 2 h + 1 of slice s
+// (32 contiguous code bytes, and their two scale bytes in one 16-bit load;
+// one byte load per block made the scale loads a large part of the gpt-oss
+// prefill chunk's time: dropping them altogether ran 25% faster, pairing them
+// 4% -- 12% with gate/up).  The MFMA's 16-long k axis is
+// split between the lane halves h: in step (jb, t), half h supplies weights
+// 8t .. 8t + 7 of block 2 h + jb of its row (A) and the same 8 activations
+// of vector r (B).
 // The dot product does not care which physical k sits in which MFMA slot as
 // long as A and B agree, so this layout costs nothing.  An expert's vectors
 // are taken up to VCAP at a time (equal chunks when it has more), and the
@@ -72,6 +76,26 @@ constexpr uint32_t kBPast = 0x80000000u;       // >= every buffer size: reads ze
 __device__ __forceinline__ int bx_off(int v, int pos)
 {
     return v * 256 + 16 * (pos ^ (v & 15));
+}
+
+// The E8M0 bytes of blocks 4 s + 2 h and 4 s + 2 h + 1 of a row (the two
+// blocks lane half h takes in 128-weight slice s) in bits 0-7 and 8-15: one
+// 16-bit load at os = the row's scale offset + 2 h (always even: a row's
+// scales start at an even byte and hold an even count in every slice but the
+// last of an odd count).  A byte past the row's end reads as 0; only the last
+// slice of an odd-length row has a lone block, and there (a wave-uniform
+// branch) the two bytes are loaded one at a time.
+__device__ __forceinline__ uint32_t load_scale_pair(__amdgpu_buffer_rsrc_t rs, uint32_t os, int s, int U, int h,
+                                                    bool valid)
+{
+    const int b0 = 4 * s + 2 * h;
+    const uint32_t o = os + 4u * (uint32_t)s;
+    if ((U & 1) && 4 * s + 4 > U) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b8(rs, valid && b0 < U ? o : kBPast, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b8(rs, valid && b0 + 1 < U ? o + 1u : kBPast, 0, 0);
+        return lo | hi << 8;
+    }
+    return __builtin_amdgcn_raw_buffer_load_b16(rs, valid && b0 < U ? o : kBPast, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 dec8(uint32_t w, float sc)
@@ -152,8 +176,8 @@ __device__ __forceinline__ void batched_chunk(const Args &a, uint8_t *lds, int e
 #pragma unroll
             for (int k = 0; k < 16; ++k) acc[f][g][k] = 0.0f;
 
-    // lane (r, h) streams blocks h and 2 + h of each 128-weight slice of its
-    // fragments' row r
+    // lane (r, h) streams blocks 2 h and 2 h + 1 of each 128-weight slice of
+    // its fragments' row r (32 contiguous code bytes, two adjacent scale bytes)
     __amdgpu_buffer_rsrc_t rc[RF], rs[RF];
     uint32_t oc[RF], os[RF];
 #pragma unroll
@@ -162,8 +186,8 @@ __device__ __forceinline__ void batched_chunk(const Args &a, uint8_t *lds, int e
         rc[f] = buffer_rsrc((up ? a.codes2 : a.codes) + (long long)e * a.expert_cb, a.expert_cb);
         rs[f] = buffer_rsrc((up ? a.scales2 : a.scales) + (long long)e * a.expert_sb, a.expert_sb);
         const int n = row0 + 32 * (MODE == 1 ? f % RH : f) + r;
-        oc[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rcb + 16u * h : kBPast;
-        os[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rsb + h : kBPast;
+        oc[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rcb + 32u * h : kBPast;
+        os[f] = n < a.N ? (uint32_t)n * (uint32_t)a.rsb + 2u * h : kBPast;
     }
     // Activation staging: lane 16 c + p of load j holds chunk p (k = 8 p ..
     // 8 p + 7 of the slice) of ring vector 4 (w + WAVES j) + c, and writes it
@@ -200,17 +224,17 @@ __device__ __forceinline__ void batched_chunk(const Args &a, uint8_t *lds, int e
 #pragma unroll
         for (int j = 0; j < XJ; ++j) *(u32x4 *)(buf + xdst[j]) = xr[j];
     };
-    // (scale bytes one at a time: a row's scales start at any byte, and an
-    // unaligned dword load is far slower than two byte loads)
-    auto load_w = [&](int s, u32x4 (&wc)[RF][2], uint8_t (&sb)[RF][2]) {
+    // (the scales two bytes at a time: a row's scales start at any even
+    // byte, and an unaligned dword load is far slower than 16-bit loads)
+    auto load_w = [&](int s, u32x4 (&wc)[RF][2], uint32_t (&sb)[RF]) {
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb) {
-                const bool okf = s < S && 4 * s + 2 * jb + h < U && oc[f] != kBPast;
-                wc[f][jb] = __builtin_amdgcn_raw_buffer_load_b128(rc[f], okf ? oc[f] + 64u * s + 32u * jb : kBPast, 0, 0);
-                sb[f][jb] = __builtin_amdgcn_raw_buffer_load_b8(rs[f], okf ? os[f] + 4u * s + 2u * jb : kBPast, 0, 0);
+                const bool okf = s < S && 4 * s + 2 * h + jb < U && oc[f] != kBPast;
+                wc[f][jb] = __builtin_amdgcn_raw_buffer_load_b128(rc[f], okf ? oc[f] + 64u * s + 16u * jb : kBPast, 0, 0);
             }
+            sb[f] = load_scale_pair(rs[f], os[f], s, U, h, s < S && oc[f] != kBPast);
         }
     };
     // A slice whose scale bytes are all in [2, 252] (every real weight) is
@@ -218,27 +242,27 @@ __device__ __forceinline__ void batched_chunk(const Args &a, uint8_t *lds, int e
     // the chunk for the exact recomputation below, which keeps this loop free
     // of a second path (and the accumulators out of the VALU).
     int slow = 0;
-    auto compute = [&](int s, const u32x4 (&wc)[RF][2], const uint8_t (&sbr)[RF][2]) {
+    auto compute = [&](int s, const u32x4 (&wc)[RF][2], const uint32_t (&sbr)[RF]) {
         const uint8_t *const buf = lds + (s % kBRing) * (VMAX * 256);
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            const bool ok = 4 * s + 2 * jb + h < U;
+            const bool ok = 4 * s + 2 * h + jb < U;
             float sc[RF];
 #pragma unroll
             for (int f = 0; f < RF; ++f) {
-                const uint32_t sb = (ok && oc[f] != kBPast) ? (uint32_t)sbr[f][jb] : 127u;
+                const uint32_t sb = (ok && oc[f] != kBPast) ? (sbr[f] >> (8 * jb)) & 0xffu : 127u;
                 slow |= (sb - 2u) > 250u;
                 sc[f] = __uint_as_float(sb << 23);
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 // step (jb, t): lane half h supplies weights 8t .. 8t + 7 of
-                // block 2 jb + h of the slice, and the same 8 activations;
+                // block 2 h + jb of the slice, and the same 8 activations;
                 // every fragment's activations are read before the MFMAs
                 bf16x8 Bv[CF];
 #pragma unroll
                 for (int g = 0; g < CF; ++g)
-                    if (g < nf) Bv[g] = __builtin_bit_cast(bf16x8, lds_read16(buf + bx_off(32 * g + r, 4 * (2 * jb + h) + t)));
+                    if (g < nf) Bv[g] = __builtin_bit_cast(bf16x8, lds_read16(buf + bx_off(32 * g + r, 4 * (2 * h + jb) + t)));
                 bf16x8 A[RF];
 #pragma unroll
                 for (int f = 0; f < RF; ++f) A[f] = dec8(wc[f][jb][t], sc[f]);
@@ -262,7 +286,7 @@ __device__ __forceinline__ void batched_chunk(const Args &a, uint8_t *lds, int e
     // slice count is padded to a multiple of 6 (the padding reads past the
     // buffers: zeros).
     u32x4 wc0[RF][2], wc1[RF][2], wc2[RF][2];
-    uint8_t sb0[RF][2], sb1[RF][2], sb2[RF][2];          // widened only where used
+    uint32_t sb0[RF], sb1[RF], sb2[RF];
     u32x4 xr0[XJ], xr1[XJ];
     load_w(0, wc0, sb0);
     load_x(0, xr0);
@@ -273,7 +297,7 @@ __device__ __forceinline__ void batched_chunk(const Args &a, uint8_t *lds, int e
     load_x(2, xr0);
     // step s: x(s + 1) sits in register set (s + 1) % 2 (loaded two slices
     // ago); it is written to LDS and the set refilled with x(s + 3)
-    auto step = [&](int s, u32x4 (&wc)[RF][2], uint8_t (&sb)[RF][2], u32x4 (&xn)[XJ]) {
+    auto step = [&](int s, u32x4 (&wc)[RF][2], uint32_t (&sb)[RF], u32x4 (&xn)[XJ]) {
         __syncthreads();
         store_x(s + 1, xn);
         load_x(s + 3, xn);
@@ -398,7 +422,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void qmv_batched_kernel(const Args a
 // two-slice LDS ring of its own (no workgroup barrier in the loop), and the
 // waves' partial tiles are summed in LDS in wave order at the end, so the
 // result is bitwise reproducible.  The loads, decode and MFMA steps are the
-// batched kernel's (lane (r, h): blocks h and 2 + h of row r per slice).
+// batched kernel's (lane (r, h): blocks 2 h and 2 h + 1 of row r per slice).
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a)
 {
@@ -427,8 +451,8 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes, a.expert_cb);
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.scales, a.expert_sb);
     const int n = row_base + r;
-    const uint32_t oc = n < a.N ? (uint32_t)n * (uint32_t)a.rcb + 16u * h : kBPast;
-    const uint32_t os = n < a.N ? (uint32_t)n * (uint32_t)a.rsb + h : kBPast;
+    const uint32_t oc = n < a.N ? (uint32_t)n * (uint32_t)a.rcb + 32u * h : kBPast;
+    const uint32_t os = n < a.N ? (uint32_t)n * (uint32_t)a.rsb + 2u * h : kBPast;
     // activation staging: lane 16 c + p of load j holds chunk p of vector
     // 4 j + c of the chunk
     uint32_t xo[XJ];
@@ -455,28 +479,28 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a
 #pragma unroll
         for (int j = 0; j < XJ; ++j) *(u32x4 *)(buf + xdst[j]) = xr[j];
     };
-    auto load_w = [&](int k, u32x4 (&wc)[2], uint8_t (&sb)[2]) {
+    auto load_w = [&](int k, u32x4 (&wc)[2], uint32_t &sb) {
         const int s = slice(k);
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            const bool ok = k < KS && 4 * s + 2 * jb + h < U && oc != kBPast;
-            wc[jb] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? oc + 64u * s + 32u * jb : kBPast, 0, 0);
-            sb[jb] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? os + 4u * s + 2u * jb : kBPast, 0, 0);
+            const bool ok = k < KS && 4 * s + 2 * h + jb < U && oc != kBPast;
+            wc[jb] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? oc + 64u * s + 16u * jb : kBPast, 0, 0);
         }
+        sb = load_scale_pair(rs, os, s, U, h, k < KS && oc != kBPast);
     };
     int slow = 0;
-    auto compute = [&](int k, const u32x4 (&wc)[2], const uint8_t (&sbr)[2]) {
+    auto compute = [&](int k, const u32x4 (&wc)[2], uint32_t sbr) {
         const int s = slice(k);
         const uint8_t *const buf = ring + (k % kBRing) * (VMAX * 256);
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            const bool ok = k < KS && 4 * s + 2 * jb + h < U && oc != kBPast;
-            const uint32_t sb = ok ? (uint32_t)sbr[jb] : 127u;
+            const bool ok = k < KS && 4 * s + 2 * h + jb < U && oc != kBPast;
+            const uint32_t sb = ok ? (sbr >> (8 * jb)) & 0xffu : 127u;
             slow |= (sb - 2u) > 250u;
             const float sc = __uint_as_float(sb << 23);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const bf16x8 Bv = __builtin_bit_cast(bf16x8, lds_read16(buf + bx_off(r, 4 * (2 * jb + h) + tt)));
+                const bf16x8 Bv = __builtin_bit_cast(bf16x8, lds_read16(buf + bx_off(r, 4 * (2 * h + jb) + tt)));
                 const bf16x8 A = dec8(wc[jb][tt], sc);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bv, acc, 0, 0, 0);
             }
@@ -488,7 +512,7 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a
     // no barrier); the slice count is padded to a multiple of 6 (the padding
     // reads past the buffers: zeros)
     u32x4 wc0[2], wc1[2], wc2[2];
-    uint8_t sb0[2], sb1[2], sb2[2];
+    uint32_t sb0, sb1, sb2;
     u32x4 xr0[XJ], xr1[XJ];
     load_w(0, wc0, sb0);
     load_x(0, xr0);
@@ -497,7 +521,7 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a
     load_w(2, wc2, sb2);
     store_x(0, xr0);
     load_x(2, xr0);
-    auto step = [&](int k, u32x4 (&wc)[2], uint8_t (&sb)[2], u32x4 (&xn)[XJ]) {
+    auto step = [&](int k, u32x4 (&wc)[2], uint32_t &sb, u32x4 (&xn)[XJ]) {
         store_x(k + 1, xn);
         load_x(k + 3, xn);
         compute(k, wc, sb);
