@@ -11,8 +11,14 @@ HBM.  To measure HBM rather than the 256 MB Infinity Cache, the weights live
 in many layer copies (>= 1 GB in total) that successive calls rotate through,
 and every call draws fresh expert ids.  The K timed calls are captured once
 into a HIP graph (torch.cuda.CUDAGraph) and replayed, so host launch overhead
-is not part of the time; the time is taken with HIP events on the replay
-stream, bracketed by device synchronizations.
+is not part of the time.  The graph also holds a one-thread kernel before the
+first call and after the last that stores the GPU's 100 MHz real-time counter
+(qmv_probe_clock); the time per call is their difference over K, so the graph
+replay's fixed start-up (6-11 us per replay, whatever K) is not spread over
+the calls and a 20-step run reads what a 1000-step run does.  HIP events on
+the replay stream around the whole replay are reported beside it
+(``us_per_call_replay_events``).  The replay is bracketed by device
+synchronizations.
 
 Prints ONE JSON line.  ``value`` is effective weight GB/s (code + scale bytes
 of the experts a call reads / time per call).  ``roofline`` relates the
@@ -311,14 +317,29 @@ class ClockSampler:
         return {"sampled_during_timed_replay": out, "polls": self.n}
 
 
+# The last time_graph call's two measures of the same replay (seconds per call).
+LAST_REPLAY = {}
+_STAMPS = {}
+RTC_HZ = 100e6          # the GPU real-time counter qmv_probe_clock stores
+
+
 def time_graph(fn, first, count, clocks=None):
     """Capture fn(i, stream) for i in [first, first+count) into one graph,
-    replay it untimed for at least 3 ms (graph upload, clocks up), read
-    512 MiB of unrelated memory so no cache holds the weights, then replay
-    it timed.
-    Returns seconds per call.  ``clocks`` (a ClockSampler) polls the clock
-    levels during the timed replay."""
+    with a GPU clock stamp (qmv_probe_clock) before the first call and after
+    the last, replay it untimed for at least 30 ms (graph upload, clocks up),
+    read 512 MiB of unrelated memory so no cache holds the weights, then
+    replay it timed between HIP events.
+    Returns seconds per call between the two stamps: the calls and the gaps
+    between them, on the GPU's own clock.  The HIP events around the replay
+    also hold the replay's fixed start-up (about 6-11 us per replay, which a
+    20-call replay would spread over its calls); LAST_REPLAY keeps both.
+    ``clocks`` (a ClockSampler) polls the clock levels during the timed replay."""
     import torch
+
+    import bit_block_quantized_amd as q
+    if "t" not in _STAMPS:
+        _STAMPS["t"] = torch.zeros(2, dtype=torch.int64, device="cuda")
+    st = _STAMPS["t"]
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
@@ -326,15 +347,17 @@ def time_graph(fn, first, count, clocks=None):
             fn(i, s.cuda_stream)
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=s):
-        h = torch.cuda.current_stream().cuda_stream
+        h = torch.cuda.current_stream()
+        q.qmv_probe_clock(st[0:1], stream=h)
         for i in range(first, first + count):
-            fn(i, h)
+            fn(i, h.cuda_stream)
+        q.qmv_probe_clock(st[1:2], stream=h)
     torch.cuda.synchronize()
-    # untimed replays for at least 3 ms of GPU time: graph upload, and the
-    # clocks ramped up (a short graph replayed once left sclk near its idle
-    # level during the timed replay)
-    t_end = time.perf_counter() + 0.003
-    for _ in range(400):
+    # untimed replays for at least 30 ms of GPU time: graph upload, and the
+    # clocks ramped up (a short graph replayed for only 3 ms still ran its
+    # first timed replay 5% slow)
+    t_end = time.perf_counter() + 0.03
+    for _ in range(2000):
         g.replay()
         torch.cuda.synchronize()
         if time.perf_counter() >= t_end:
@@ -345,9 +368,7 @@ def time_graph(fn, first, count, clocks=None):
         clocks.__enter__()
     with torch.cuda.stream(s):
         # the flush, the start event and the replay are queued back to back:
-        # while the GPU reads the flush buffer the host submits the graph, so
-        # the timed span holds the K calls and not the submission latency
-        # (which a 20-call replay would otherwise spread over its calls)
+        # while the GPU reads the flush buffer the host submits the graph
         flush_caches(s)
         e0.record(s)
         g.replay()
@@ -355,7 +376,12 @@ def time_graph(fn, first, count, clocks=None):
     torch.cuda.synchronize()
     if clocks is not None:
         clocks.__exit__(None, None, None)
-    return e0.elapsed_time(e1) * 1e-3 / count
+    ticks = st.cpu().tolist()
+    gpu = (ticks[1] - ticks[0]) / RTC_HZ / count
+    ev = e0.elapsed_time(e1) * 1e-3 / count
+    LAST_REPLAY.clear()
+    LAST_REPLAY.update(gpu_clock=gpu, events=ev)
+    return gpu
 
 
 def time_eager(p, first, count):
@@ -438,11 +464,13 @@ def measure(name, steps, warmup, hot=True, clocks=None):
     if warmup:
         time_graph(p.call, 0, warmup)
     t = time_graph(p.call, warmup, steps, clocks=clocks)
+    t_events = LAST_REPLAY["events"]
     sel = slice(warmup, warmup + steps)
     wb = float(p.wbytes[sel].mean())
     ab = float(p.abytes[sel].mean())
     res = {
         "us_per_call": t * 1e6,
+        "us_per_call_replay_events": t_events * 1e6,
         "weight_bytes_per_call": wb,
         "algorithmic_bytes_per_call": ab,
         "eff_weight_GBps": wb / t / 1e9,
@@ -603,10 +631,13 @@ def main():
                         "x bf16 -> f32, 4 of 32 experts, 1 token, K=N=2880",
             "E": 32, "top_k": 4, "M": 1, "N": 2880, "K": 2880,
             "layers_rotated": head["layers_rotated"],
-            "timing": "HIP graph of the K calls, HIP events on the replay stream; 512 MiB of "
+            "timing": "HIP graph of the K calls between two GPU real-time-counter stamps "
+                      "(qmv_probe_clock) captured with them; HIP events on the replay stream "
+                      "around the whole replay give us_per_call_replay_events; 512 MiB of "
                       "unrelated memory read just before the timed replay",
         },
         "us_per_call": round(head["us_per_call"], 3),
+        "us_per_call_replay_events": round(head["us_per_call_replay_events"], 3),
         "pct_hbm_peak": round(head["pct_hbm_peak"], 2),
         "us_per_call_eager_launch": round(head["us_per_call_eager_launch"], 3),
         "hot_cache_us_per_call": round(head.get("hot_us_per_call", float("nan")), 3),

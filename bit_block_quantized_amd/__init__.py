@@ -30,7 +30,7 @@ import torch  # noqa: F401  -- loads the HIP runtime that libqmv.so binds to
 __all__ = ["qmv_dense", "qmv_gather_moe", "qmv_gather_moe_swiglu", "qmv_gather_moe_combine",
            "qmv_gather_moe_combine_noalloc",
            "qmv_strerror",
-           "qmv_probe_stream_read", "lib", "LIB_PATH",
+           "qmv_probe_stream_read", "qmv_probe_clock", "lib", "LIB_PATH",
            "W_MXFP4", "W_CB2", "W_CB3", "A_BF16", "A_Q8B32", "A_BF16_Q8", "QmvError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
@@ -75,6 +75,8 @@ def lib():
     L.qmv_gather_moe_combine_noalloc.argtypes = [I, P, P, I, P, P, I, I, I, P, P, I, P, I, I, P]
     L.qmv_probe_stream_read.restype = I
     L.qmv_probe_stream_read.argtypes = [I, P, P, I, P, P]
+    L.qmv_probe_clock.restype = I
+    L.qmv_probe_clock.argtypes = [P, P]
     L.qmv_strerror.restype = ctypes.c_char_p
     L.qmv_strerror.argtypes = [I]
     _lib = L
@@ -365,3 +367,11 @@ def qmv_probe_stream_read(regions, variant, sink, stream=None):
     _check(lib().qmv_probe_stream_read(n, ptrs, sizes, int(variant),
                                        _dev_ptr(sink, "sink", (torch.int32,), dev),
                                        _stream(dev, stream)))
+
+
+def qmv_probe_clock(out, stream=None):
+    """Store the GPU's 100 MHz real-time counter into ``out`` (a 1-element
+    int64 device tensor) from a one-thread kernel on ``stream``
+    (include/qmv_probe.h)."""
+    dev = out.device
+    _check(lib().qmv_probe_clock(_dev_ptr(out, "out", (torch.int64,), dev), _stream(dev, stream)))

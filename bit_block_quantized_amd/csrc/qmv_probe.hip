@@ -54,9 +54,27 @@ const Shape kShapes[QMV_PROBE_VARIANTS] = {
     {(const void *)&stream_read<1024, 4>, 1024, 4},
 };
 
+// One thread stores the GPU's constant-rate real-time counter (100 MHz on
+// this device) with a vector store.
+__global__ __launch_bounds__(64) void clock_stamp(unsigned long long *out)
+{
+    if (threadIdx.x == 0) *out = __builtin_amdgcn_s_memrealtime();
+}
+
 }  // namespace
 
 extern "C" {
+
+__attribute__((visibility("default")))
+qmv_status_t qmv_probe_clock(unsigned long long *out, hipStream_t stream)
+{
+    if (!out || ((uintptr_t)out & 7))
+        return QMV_EINVAL;
+    void *kargs[] = {&out};
+    if (hipLaunchKernel((const void *)&clock_stamp, dim3(1), dim3(64), kargs, 0, stream) != hipSuccess)
+        return QMV_EHIP;
+    return QMV_OK;
+}
 
 __attribute__((visibility("default")))
 qmv_status_t qmv_probe_stream_read(int n_regions, const void *const *ptrs,

@@ -7,7 +7,8 @@
  * separate regions, same 16-byte non-temporal buffer loads), this probe only
  * reads the given regions, with no decode and no dependence on expert ids.
  * Its time per call is the practical read ceiling that a benchmark divides
- * the GEMV's time by.
+ * the GEMV's time by.  A clock stamp (qmv_probe_clock) lets a benchmark time
+ * launches on the GPU's own clock.
  */
 #ifndef QMV_PROBE_H
 #define QMV_PROBE_H
@@ -42,6 +43,16 @@ extern "C" {
 qmv_status_t qmv_probe_stream_read(int n_regions, const void *const *ptrs,
                                    const long long *bytes, int variant, unsigned *sink,
                                    hipStream_t stream);
+
+/*
+ * Enqueue one single-thread kernel on `stream` that stores the GPU's
+ * real-time counter (a constant 100 MHz clock, independent of the shader
+ * clock) to *out, a device word (8-byte aligned) the caller owns.  Two stamps
+ * around a sequence of launches in a HIP graph time that sequence on the GPU
+ * itself, without the graph launch's own start-up.  Returns QMV_EINVAL for a
+ * null or misaligned pointer, QMV_EHIP if the launch is refused.
+ */
+qmv_status_t qmv_probe_clock(unsigned long long *out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

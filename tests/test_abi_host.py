@@ -43,12 +43,12 @@ def test_header_declares_the_boundary():
                                            "qmv_gather_moe_combine",
                                            "qmv_gather_moe_combine_noalloc",
                                            "qmv_gather_moe_swiglu", "qmv_strerror"]
-    assert declared_functions("qmv_probe.h") == ["qmv_probe_stream_read"]
+    assert declared_functions("qmv_probe.h") == ["qmv_probe_clock", "qmv_probe_stream_read"]
 
 
 def test_library_exports_every_declared_symbol(L):
     declared = declared_functions()
-    assert len(declared) == 7
+    assert len(declared) == 8
     for name in declared:
         assert hasattr(L, name), name
     out = os.popen(f"nm -D --defined-only {ROOT}/bit_block_quantized_amd/libqmv.so").read()

@@ -48,3 +48,29 @@ def test_probe_many_regions():
     regions = [(base + r * 16384, 8192) for r in range(64)]
     buf[(63 * 16384 + 8192 - 16) // 4] = KEY
     assert _run(regions, 0) == KEY
+
+
+def test_clock_stamps_advance_at_100_mhz():
+    """Two stamps around a sleep on the host: the counter advances, at the
+    rate bench.py divides by (100 MHz, within 5% of the host's clock over
+    ~0.2 s), and each stamp writes only its own word."""
+    import time
+
+    import bit_block_quantized_amd as q
+    st = torch.full((4,), -1, dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream()
+    q.qmv_probe_clock(st[1:2], stream=s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    time.sleep(0.2)
+    q.qmv_probe_clock(st[2:3], stream=s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    v = st.cpu().tolist()
+    assert v[0] == -1 and v[3] == -1
+    ticks = v[2] - v[1]
+    assert ticks > 0
+    rate = ticks / (t1 - t0)
+    assert 0.95e8 < rate < 1.05e8, rate
+    # a misaligned word is refused on the host, before any launch
+    assert q.lib().qmv_probe_clock(st.data_ptr() + 4, None) == 1
