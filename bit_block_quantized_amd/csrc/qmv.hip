@@ -58,10 +58,11 @@ namespace qmv {
 extern const void *const kTableGmma[2][2][4];
 }
 
-// Dense MXFP4 x bf16 with 9 to 32 vectors: 32-row tiles with K split over
-// the waves of a workgroup (qmv_k_mxfp4b.hip): [4 waves, 8 waves].
+// Dense MXFP4 x bf16 with 9 to 64 vectors: 32-row tiles with K split over
+// the waves of a workgroup (qmv_k_mxfp4b.hip): [4 waves x 32 vectors, 8 waves
+// x 32 vectors, 8 waves x 64 vectors].
 namespace qmv {
-extern const void *const kTableBatchedKS[2];
+extern const void *const kTableBatchedKS[3];
 }
 
 namespace qmv {
@@ -486,30 +487,37 @@ qmv_status_t launch_gmma(int wfmt, int afmt, int kind, const void *codes, const 
     return QMV_OK;
 }
 
-std::once_flag g_ks_once[2];
-hipError_t g_ks_err[2];
-constexpr int kKsVecs = 32;                             // vectors per chunk
-constexpr int kKsMaxM = 32;
+std::once_flag g_ks_once[3];
+hipError_t g_ks_err[3];
+constexpr int kKsMaxM = 64;
 
-// Dense MXFP4 x bf16, 9 to 32 vectors: one launch of K-split tiles (32 rows x
-// a chunk of at most 32 vectors, chunks of equal size); 8 waves per
-// workgroup when K has at least 32 slices of 128 weights, else 4.  LDS: a
-// two-slice activation ring per wave.
+// Dense MXFP4 x bf16, 9 to 64 vectors: one launch of K-split tiles, 32 rows
+// by all the call's vectors.  Up to 32 vectors: 8 waves per workgroup when K
+// has at least 32 slices of 128 weights, else 4, each wave with a two-slice
+// activation ring in LDS; 33 to 64 vectors: two 32-vector column fragments,
+// 8 waves (two per SIMD, which cover each other's latency), a one-slice
+// ring per wave (128 KB of LDS).  Measured on MI355X against the batched
+// kernel (two 32-vector chunks of 64-row tiles): 7168 x 7168 with 64
+// vectors 31.9 -> 23.6 us, 40 vectors 31.9 -> 22.3; 2880 x 2880 with 64
+// vectors 16.7 -> 14.4; 7168 rows x K = 2048, 64 vectors, 12.9 -> 12.3;
+// 2048 rows x K = 7168, 64 vectors, 35.1 -> 22.3 us.  A 4-wave version with
+// a two-slice ring (one wave per SIMD) took 33 us at 7168 x 7168.
 qmv_status_t launch_batched_ks(const void *codes, const void *scales, const void *x, float *y, int M, int N,
                                int K, hipStream_t stream)
 {
     Args a = base_args(QMV_W_MXFP4, QMV_A_BF16, kMXFP4, codes, scales, 1, nullptr, M, 1, x, nullptr, 0, y, N,
                        K);
     const int slices = (K + 127) / 128;
-    const int wi = slices >= 32 ? 1 : 0;
+    const int vecs = M > 32 ? 64 : 32;
+    const int wi = M > 32 ? 2 : slices >= 32 ? 1 : 0;
     const int waves = wi ? 8 : 4;
-    const int nch = (M + kKsVecs - 1) / kKsVecs;
-    a.bt_chunk = (M + nch - 1) / nch;
+    const int ring = vecs == 64 ? 1 : 2;
+    a.bt_chunk = M;
     a.bt_row_tiles = (N + 31) / 32;
-    a.bt_tiles = a.bt_row_tiles * nch;
+    a.bt_tiles = a.bt_row_tiles;
     a.bt_per_xcd = (a.bt_tiles + 7) / 8;
-    a.bt_vmax = kKsVecs;
-    const size_t lds = (size_t)waves * 2 * kKsVecs * 256;
+    a.bt_vmax = vecs;
+    const size_t lds = (size_t)waves * ring * vecs * 256;
     const void *fn = kTableBatchedKS[wi];
     std::call_once(g_ks_once[wi], [&] {
         g_ks_err[wi] = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -557,13 +565,13 @@ qmv_status_t launch(int wfmt, int afmt, const void *codes, const void *scales, c
     const bool gather = ids != nullptr;
     const bool gate_up = codes2 != nullptr;
     const int kind = kind_of(wfmt, afmt, K);
-    // Dense MXFP4 x bf16 with 9 to 32 vectors: K-split tiles, one launch.
+    // Dense MXFP4 x bf16 with 9 to 64 vectors: K-split tiles, one launch.
     // Measured on 7168 x 7168: 16 vectors 34.3 us as four 4-vector launches,
     // 20.8 us here; 24 vectors 34.5 (batched) against 21.0; 5 vectors 16.6
-    // as two launches against 20.7 here; 64 vectors 31 (batched) against 40.
-    // Every tile restages all of x through L2 (32 vectors x K bf16 per
-    // 32-row tile: four times the tile's weight bytes at K = 7168), which
-    // bounds this shape.
+    // as two launches against 20.7 here; 64 vectors 31.9 (batched) against
+    // 23.6.  Every tile restages all of x through L2 (up to 64 vectors x K
+    // bf16 per 32-row tile: eight times the tile's weight bytes at
+    // K = 7168), which bounds this shape.
     if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kDenseGroupsMaxM && M <= kKsMaxM)
         return launch_batched_ks(codes, scales, x, y, M, N, K, stream);
     if (!gather && !gate_up && kind == kMXFP4 && afmt == QMV_A_BF16 && M > kMaxM && M <= kDenseGroupsMaxM) {

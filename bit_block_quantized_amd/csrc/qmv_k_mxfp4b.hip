@@ -418,17 +418,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void qmv_batched_kernel(const Args a
 // a workgroup of waves that each own other rows, and too few tiles fill the
 // GPU.  Here the waves of a workgroup split the tile's K instead: wave w
 // takes the 128-weight slices w, w + WAVES, w + 2 WAVES, ... of the tile
-// (32 rows x a chunk of at most 32 vectors), stages their activations in a
-// two-slice LDS ring of its own (no workgroup barrier in the loop), and the
+// (32 rows x a chunk of at most VMAX vectors: 32, or 64 in 32-vector column
+// fragments), stages their activations in a two-slice LDS ring of its own
+// (no workgroup barrier in the loop), and the
 // waves' partial tiles are summed in LDS in wave order at the end, so the
 // result is bitwise reproducible.  The loads, decode and MFMA steps are the
 // batched kernel's (lane (r, h): blocks 2 h and 2 h + 1 of row r per slice).
-template <int WAVES>
+template <int WAVES, int VMAX>
 __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    constexpr int VMAX = 32;                        // vectors per chunk
     constexpr int XJ = VMAX / 4;                    // staging loads (4 vectors each) per lane and slice
+    constexpr int CF = VMAX / 32;                   // column fragments of 32 vectors
+    // activation slices per wave's LDS ring: two, or one with 64 vectors
+    // (8 waves x 64 vectors x 256 bytes: 128 KB of LDS)
+    constexpr int RING = VMAX == 64 ? 1 : kBRing;
     const int b = blockIdx.x;
     const int t = (b & 7) * a.bt_per_xcd + (b >> 3);
     if (t >= a.bt_tiles) return;
@@ -443,26 +447,24 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a
     const int U = a.units;
     const int S = (U + 3) >> 2;                     // 128-weight slices
     const int KS = S > w ? (S - w + WAVES - 1) / WAVES : 0;   // this wave's slices
-    uint8_t *const ring = lds + w * (kBRing * VMAX * 256);
+    uint8_t *const ring = lds + w * (RING * VMAX * 256);
 
-    f32x16 acc;
+    const int nf = (nv + 31) >> 5;                  // column fragments in use
+    f32x16 acc[CF];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+    for (int g = 0; g < CF; ++g)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) acc[g][k] = 0.0f;
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes, a.expert_cb);
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.scales, a.expert_sb);
     const int n = row_base + r;
     const uint32_t oc = n < a.N ? (uint32_t)n * (uint32_t)a.rcb + 32u * h : kBPast;
     const uint32_t os = n < a.N ? (uint32_t)n * (uint32_t)a.rsb + 2u * h : kBPast;
     // activation staging: lane 16 c + p of load j holds chunk p of vector
-    // 4 j + c of the chunk
-    uint32_t xo[XJ];
-    int xdst[XJ];
-#pragma unroll
-    for (int j = 0; j < XJ; ++j) {
-        const int v = 4 * j + (lane >> 4);
-        xdst[j] = bx_off(v, lane & 15);
-        xo[j] = v < nv ? (uint32_t)(vstart + v) * (uint32_t)a.x_vec_bytes + 16u * (lane & 15) : kBPast;
-    }
+    // 4 j + c of the chunk (offsets formed per load, not kept in registers)
+    const int vl = lane >> 4, pl = lane & 15;
+    const uint32_t xvb = (uint32_t)a.x_vec_bytes;
+    const uint32_t xbase = (uint32_t)(vstart + vl) * xvb + 16u * pl;
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, a.M * a.x_vec_bytes);   // < 2^31
     const int K = a.K;
     auto slice = [&](int k) { return w + WAVES * k; };
@@ -470,14 +472,14 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a
         const int s = slice(k);
 #pragma unroll
         for (int j = 0; j < XJ; ++j) {
-            const bool ok = k < KS && 128 * s + 8 * (lane & 15) < K && xo[j] != kBPast;
-            xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? xo[j] + 256u * s : kBPast, 0, 0);
+            const bool ok = k < KS && 128 * s + 8 * pl < K && 4 * j + vl < nv;
+            xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? xbase + 4u * j * xvb + 256u * s : kBPast, 0, 0);
         }
     };
     auto store_x = [&](int k, const u32x4 (&xr)[XJ]) {
-        uint8_t *const buf = ring + (k % kBRing) * (VMAX * 256);
+        uint8_t *const buf = ring + (k % RING) * (VMAX * 256);
 #pragma unroll
-        for (int j = 0; j < XJ; ++j) *(u32x4 *)(buf + xdst[j]) = xr[j];
+        for (int j = 0; j < XJ; ++j) *(u32x4 *)(buf + bx_off(4 * j + vl, pl)) = xr[j];
     };
     auto load_w = [&](int k, u32x4 (&wc)[2], uint32_t &sb) {
         const int s = slice(k);
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a
     int slow = 0;
     auto compute = [&](int k, const u32x4 (&wc)[2], uint32_t sbr) {
         const int s = slice(k);
-        const uint8_t *const buf = ring + (k % kBRing) * (VMAX * 256);
+        const uint8_t *const buf = ring + (k % RING) * (VMAX * 256);
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
             const bool ok = k < KS && 4 * s + 2 * h + jb < U && oc != kBPast;
@@ -500,40 +502,74 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a
             const float sc = __uint_as_float(sb << 23);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const bf16x8 Bv = __builtin_bit_cast(bf16x8, lds_read16(buf + bx_off(r, 4 * (2 * h + jb) + tt)));
+                bf16x8 Bv[CF];
+#pragma unroll
+                for (int g = 0; g < CF; ++g)
+                    if (g < nf)
+                        Bv[g] = __builtin_bit_cast(bf16x8, lds_read16(buf + bx_off(32 * g + r, 4 * (2 * h + jb) + tt)));
                 const bf16x8 A = dec8(wc[jb][tt], sc);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bv, acc, 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < CF; ++g)
+                    if (g < nf) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bv[g], acc[g], 0, 0, 0);
             }
         }
     };
-    // weights three of this wave's slices ahead, activations two; the LDS
-    // ring is this wave's alone (a wave's LDS operations complete in order,
-    // so writing slice k + 1's buffer after slice k - 1's reads of it needs
-    // no barrier); the slice count is padded to a multiple of 6 (the padding
-    // reads past the buffers: zeros)
     u32x4 wc0[2], wc1[2], wc2[2];
     uint32_t sb0, sb1, sb2;
-    u32x4 xr0[XJ], xr1[XJ];
-    load_w(0, wc0, sb0);
-    load_x(0, xr0);
-    load_w(1, wc1, sb1);
-    load_x(1, xr1);
-    load_w(2, wc2, sb2);
-    store_x(0, xr0);
-    load_x(2, xr0);
-    auto step = [&](int k, u32x4 (&wc)[2], uint32_t &sb, u32x4 (&xn)[XJ]) {
-        store_x(k + 1, xn);
-        load_x(k + 3, xn);
-        compute(k, wc, sb);
-        load_w(k + 3, wc, sb);
-    };
-    for (int k = 0; k < KS; k += 6) {
-        step(k, wc0, sb0, xr1);
-        step(k + 1, wc1, sb1, xr0);
-        step(k + 2, wc2, sb2, xr1);
-        step(k + 3, wc0, sb0, xr0);
-        step(k + 4, wc1, sb1, xr1);
-        step(k + 5, wc2, sb2, xr0);
+    if constexpr (RING == 1) {
+        // two waves per SIMD hide each other's latency, so less is kept in
+        // flight: weights two of this wave's slices ahead, activations one
+        // (one register set, one LDS slice buffer: this wave's reads of slice
+        // k are issued before its writes of slice k + 1, and a wave's LDS
+        // operations complete in order); the slice count is padded to a
+        // multiple of 2 (the padding reads past the buffers: zeros).  Three
+        // weight slices ahead measured slower at 7168 x 7168 (27.7 -> 29.5 us)
+        u32x4 xr[XJ];
+        load_w(0, wc0, sb0);
+        load_x(0, xr);
+        load_w(1, wc1, sb1);
+        store_x(0, xr);
+        load_x(1, xr);
+        auto step = [&](int k, u32x4 (&wc)[2], uint32_t &sb) {
+            compute(k, wc, sb);
+            store_x(k + 1, xr);
+            load_x(k + 2, xr);
+            load_w(k + 2, wc, sb);
+        };
+        for (int k = 0; k < KS; k += 2) {
+            step(k, wc0, sb0);
+            step(k + 1, wc1, sb1);
+        }
+        (void)wc2;
+        (void)sb2;
+    } else {
+        // weights three of this wave's slices ahead, activations two; the
+        // LDS ring is this wave's alone (a wave's LDS operations complete in
+        // order, so writing slice k + 1's buffer after slice k - 1's reads of
+        // it needs no barrier); the slice count is padded to a multiple of 6
+        // (the padding reads past the buffers: zeros)
+        u32x4 xr0[XJ], xr1[XJ];
+        load_w(0, wc0, sb0);
+        load_x(0, xr0);
+        load_w(1, wc1, sb1);
+        load_x(1, xr1);
+        load_w(2, wc2, sb2);
+        store_x(0, xr0);
+        load_x(2, xr0);
+        auto step = [&](int k, u32x4 (&wc)[2], uint32_t &sb, u32x4 (&xn)[XJ]) {
+            store_x(k + 1, xn);
+            load_x(k + 3, xn);
+            compute(k, wc, sb);
+            load_w(k + 3, wc, sb);
+        };
+        for (int k = 0; k < KS; k += 6) {
+            step(k, wc0, sb0, xr1);
+            step(k + 1, wc1, sb1, xr0);
+            step(k + 2, wc2, sb2, xr1);
+            step(k + 3, wc0, sb0, xr0);
+            step(k + 4, wc1, sb1, xr1);
+            step(k + 5, wc2, sb2, xr0);
+        }
     }
     if (__syncthreads_or(slow)) {
         batched_chunk_exact<0>(a, 0, nullptr, vstart, nv, row_base, min(32, a.N - row_base));
@@ -543,36 +579,51 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a
     float *const red = (float *)lds;
     if (w > 0) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) red[((w - 1) * 16 + k) * 64 + lane] = acc[k];
+        for (int g = 0; g < CF; ++g)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) red[(((w - 1) * CF + g) * 16 + k) * 64 + lane] = acc[g][k];
     }
     __syncthreads();
     if (w != 0) return;
+    // (one wave's partial tile at a time: reading every wave's at once
+    // would take more registers than two waves per SIMD leave)
+#pragma unroll 1
+    for (int ww = 1; ww < WAVES; ++ww)
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-        for (int ww = 1; ww < WAVES; ++ww) acc[k] += red[((ww - 1) * 16 + k) * 64 + lane];
-    // lane (vector r, half h) holds rows 8 i + 4 h .. + 3 of the tile
-    if (r < nv) {
-        float *const yrow = a.y + (size_t)(vstart + r) * a.N;
+        for (int g = 0; g < CF; ++g)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) acc[g][k] += red[(((ww - 1) * CF + g) * 16 + k) * 64 + lane];
+    // lane (vector r, half h) of fragment g holds rows 8 i + 4 h .. + 3 of
+    // the tile for vector 32 g + r
+#pragma unroll
+    for (int g = 0; g < CF; ++g) {
+    const int col = 32 * g + r;
+    if (col < nv) {
+        float *const yrow = a.y + (size_t)(vstart + col) * a.N;
         const bool vec4 = (a.N & 3) == 0 && ((uintptr_t)a.y & 15) == 0;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int n0 = row_base + 8 * ii + 4 * h;
             if (n0 < a.N) {
                 if (vec4) {
-                    *(float4 *)(yrow + n0) = make_float4(acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]);
+                    *(float4 *)(yrow + n0) = make_float4(acc[g][4 * ii], acc[g][4 * ii + 1], acc[g][4 * ii + 2],
+                                                         acc[g][4 * ii + 3]);
                 } else {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        if (n0 + k < a.N) yrow[n0 + k] = acc[4 * ii + k];
+                        if (n0 + k < a.N) yrow[n0 + k] = acc[g][4 * ii + k];
                 }
             }
         }
     }
+    }
 }
 
-extern const void *const kTableBatchedKS[2];
-const void *const kTableBatchedKS[2] = {(const void *)&qmv_batched_ks_kernel<4>,
-                                        (const void *)&qmv_batched_ks_kernel<8>};
+// [4 waves x 32 vectors, 8 waves x 32 vectors, 8 waves x 64 vectors]
+extern const void *const kTableBatchedKS[3];
+const void *const kTableBatchedKS[3] = {(const void *)&qmv_batched_ks_kernel<4, 32>,
+                                        (const void *)&qmv_batched_ks_kernel<8, 32>,
+                                        (const void *)&qmv_batched_ks_kernel<8, 64>};
 
 // Instantiations: (waves per workgroup, 32-row fragments per wave, most
 // vectors per chunk), the chunk capacity as large as the register budget

@@ -141,9 +141,10 @@ typedef enum {
  *   y                  fp32 [M][N]
  * This is the gather below with one expert, top_k = 1 and ids all 0.
  * With (MXFP4, BF16), 5 <= M <= 8 runs as groups of up to 4 vectors on the
- * 4-vector kernel (one launch per group), 9 <= M <= 32 in one launch of
- * 32-row tiles whose K is split over the waves of a workgroup, and M > 32
- * on the batched matrix-core kernel described under qmv_gather_moe; 2-bit and 3-bit
+ * 4-vector kernel (one launch per group), 9 <= M <= 64 in one launch of
+ * 32-row tiles whose K is split over the waves of a workgroup (one or two
+ * 32-vector column fragments), and M > 64 on the batched matrix-core kernel
+ * described under qmv_gather_moe; 2-bit and 3-bit
  * weights with int8 (or in-kernel quantized bf16) activations and M >= 8 on
  * the int8 matrix-core kernel;
  * every other M > 4 call on the grouped kernel.

@@ -160,7 +160,7 @@ BATCHED_WORKLOADS = {
                      desc="gpt-oss-20b MoE prefill chunk, fused gate+up with SwiGLU: 512 tokens "
                           "x top-4 of 32 experts, K=N=2880, MXFP4 x bf16, expert-batched"),
     "C6d": Workload("C6d", "dense", "mxfp4", M=64, N=7168, K=7168, seed=15,
-                    desc="dense MXFP4 x bf16, 64 vectors, K=N=7168 (batched matrix-core path)"),
+                    desc="dense MXFP4 x bf16, 64 vectors, K=N=7168 (K-split matrix-core tiles)"),
     # A DeepSeek-shaped prefill chunk on the codebook formats: 512 tokens, each
     # routed to 4 of 256 experts (about 8 (token, slot) pairs per expert),
     # int8 activations with a scale per 32.

@@ -14,13 +14,14 @@ Inf activations, the pair and expert limits, and the full-size prefill chunk
 on sampled outputs.
 
 Which kernel a call reaches: dense calls with 5 to 8 vectors run as groups
-of up to 4 vectors on the dense 4-vector kernel, dense calls with 9 to 32
+of up to 4 vectors on the dense 4-vector kernel, dense calls with 9 to 64
 vectors on the K-split tiles (the waves of a workgroup split K, partial tiles
-summed in LDS), gathers with fewer than two (token, slot) pairs per expert
-as token groups on the decode kernels (test_gather_few_pairs_*); every other
-call with more than 4 vectors runs on the batched kernel.  The special-value
-cases below use dense calls with 24 vectors (K-split), dense calls with 40
-vectors (batched) and gathers with M * top_k >= 2 E (batched).
+summed in LDS; one 32-vector column fragment up to 32 vectors, two above),
+gathers with fewer than two (token, slot) pairs per expert as token groups
+on the decode kernels (test_gather_few_pairs_*); every other call with more
+than 4 vectors runs on the batched kernel.  The special-value cases below use
+dense calls with 24 and 40 vectors (K-split), dense calls with 72 vectors
+(batched) and gathers with M * top_k >= 2 E (batched).
 """
 import numpy as np
 import pytest
@@ -47,7 +48,8 @@ def _check(inp, what, exact=False):
 
 
 @pytest.mark.parametrize("M,N,K", [(5, 37, 32), (8, 45, 96), (9, 40, 64), (16, 130, 544), (32, 33, 2880),
-                                   (64, 301, 2880), (129, 64, 160), (200, 257, 1056), (33, 513, 7168)])
+                                   (64, 301, 2880), (129, 64, 160), (200, 257, 1056), (33, 513, 7168),
+                                   (48, 70, 4160), (65, 97, 2080), (40, 35, 96)])
 def test_dense(M, N, K):
     _check(synth.make(_wl("dense", M, N, K, seed=M + N + K)), f"dense M={M} N={N} K={K}")
 
@@ -124,16 +126,18 @@ def test_e8m0_special_scales():
     assert np.isnan(yr[:, 3]).all() and np.isnan(yr[:, 39]).all()
 
 
-def test_e8m0_special_scales_dense_batched():
-    """The same special scale bytes on a dense call with 40 vectors (the
-    batched kernel's exact path)."""
-    inp = synth.make(_wl("dense", 40, 40, 320, seed=63))
+@pytest.mark.parametrize("M", [40, 72])
+def test_e8m0_special_scales_dense_batched(M):
+    """The same special scale bytes on dense calls with 40 vectors (the
+    K-split tiles with two column fragments) and 72 vectors (the batched
+    kernel), each through its exact path."""
+    inp = synth.make(_wl("dense", M, 40, 320, seed=63))
     inp.scales[0, :] = 0
     inp.scales[2, :] = 254
     inp.scales[3, 4] = 255
     inp.scales[4, :] = [0, 127, 254, 127, 1, 253, 2, 252, 127, 127]
     inp.scales[39, 9] = 1
-    yr = _assert_special(inp, "e8m0 specials, dense batched")
+    yr = _assert_special(inp, f"e8m0 specials, dense M={M}")
     assert np.isnan(yr[:, 3]).all()
 
 
@@ -209,8 +213,8 @@ def test_prefill_chunk_full_size_sampled():
 
 
 def test_dense_wide_full_size_sampled():
-    """Dense 7168 x 7168 MXFP4 against 64 vectors (the batched kernel, vector
-    chunks as tiles) as bench.py launches it: sampled outputs and 2 whole
+    """Dense 7168 x 7168 MXFP4 against 64 vectors (the K-split tiles with two
+    column fragments) as bench.py launches it: sampled outputs and 2 whole
     rows of y."""
     inp = synth.make(synth.workload("C6d"))
     y = gpu_call(inp).cpu().numpy().reshape(-1)
