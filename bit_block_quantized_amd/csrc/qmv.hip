@@ -743,13 +743,11 @@ qmv_status_t launch_combine_via(int wfmt, int afmt, const void *codes, const voi
         return st;
     const long long quads = (long long)M * ((N + 3) / 4);
     const unsigned blocks = (unsigned)((quads + 255) / 256);
-    if ((N & 3) == 0 && (((uintptr_t)y | (uintptr_t)g) & 15) == 0)
-        hipLaunchKernelGGL(qmv_slot_sum_kernel<true>, dim3(blocks), dim3(256), 0, stream, (const float *)g, route_w,
-                           y, M, top_k, N);
-    else
-        hipLaunchKernelGGL(qmv_slot_sum_kernel<false>, dim3(blocks), dim3(256), 0, stream, (const float *)g,
-                           route_w, y, M, top_k, N);
-    return hipGetLastError() == hipSuccess ? QMV_OK : QMV_EHIP;
+    const bool vec = (N & 3) == 0 && (((uintptr_t)y | (uintptr_t)g) & 15) == 0;
+    const void *fn = vec ? (const void *)&qmv_slot_sum_kernel<true> : (const void *)&qmv_slot_sum_kernel<false>;
+    const float *gc = g;
+    void *kargs[] = {&gc, &route_w, &y, &M, &top_k, &N};
+    return hipLaunchKernel(fn, dim3(blocks), dim3(256), kargs, 0, stream) == hipSuccess ? QMV_OK : QMV_EHIP;
 }
 
 // The per-slot rows of a many-token combine come from a memory pool of the
