@@ -49,7 +49,8 @@ def _check(inp, what, exact=False):
 
 @pytest.mark.parametrize("M,N,K", [(5, 37, 32), (8, 45, 96), (9, 40, 64), (16, 130, 544), (32, 33, 2880),
                                    (64, 301, 2880), (129, 64, 160), (200, 257, 1056), (33, 513, 7168),
-                                   (48, 70, 4160), (65, 97, 2080), (40, 35, 96)])
+                                   (48, 70, 4160), (65, 97, 2080), (40, 35, 96), (64, 40, 16384),
+                                   (33, 17, 16384)])
 def test_dense(M, N, K):
     _check(synth.make(_wl("dense", M, N, K, seed=M + N + K)), f"dense M={M} N={N} K={K}")
 

@@ -238,6 +238,20 @@ def test_prefill_combine_full_size_sampled(name):
     print(f"{name}: worst |err| / bound = {worst:.3e}")
 
 
+@pytest.mark.parametrize("wfmt", FMTS)
+def test_many_tokens_at_the_pair_limit(wfmt):
+    """8192 (token, slot) pairs, the most a call with more than 4 tokens may
+    have: 2048 tokens x 4 slots over 24 experts, sampled outputs against the
+    oracle."""
+    inp = synth.make(_combine_wl(wfmt, M=2048, N=40, K=128, E=24, top_k=4, seed=43))
+    y = gpu_combine(inp).cpu().numpy().reshape(-1)
+    rng = np.random.default_rng(44)
+    outs = np.concatenate([rng.choice(y.size, size=3000, replace=False), np.arange(40),
+                           2047 * 40 + np.arange(40)])
+    yr, A = oracle_combine(inp, outs=outs)
+    assert_parity(y[outs], yr, A, f"{wfmt} 8192 pairs")
+
+
 def test_many_tokens_leaves_nothing_past_y_and_repeats():
     """The many-token combine writes every row of y, nothing past it, and the
     same bits on a second call (its temporary comes back from the pool)."""
