@@ -65,14 +65,20 @@ METRIC = "effective weight GB/s and µs/call per expert-gather GEMV; % of HBM pe
 
 
 def kernel_source_hash():
-    """sha256[:16] over the kernel sources (names and bytes, sorted)."""
+    """sha256[:16] over the kernel sources (names and code, sorted), with the
+    comments and blank space taken out, so that an edit of comments alone
+    keeps the hash (and with it the profiled figures) of the same code."""
     import glob
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "bit_block_quantized_amd", "csrc", "*"))):
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)       # the sources hold no "//" or "/*" in strings
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -730,8 +730,9 @@ __global__ __launch_bounds__(256) void qmv_slot_sum_kernel(const float *__restri
 
 // The combine of more than 4 tokens: the gather above (whatever kernel its
 // shape takes) writes every (token, slot) row into g, zeros for ids outside
-// [0, E), and the slot sum reads them back.  g holds M * top_k * N floats,
-// 256-byte aligned; y is written only by the last launch.
+// [0, E), and the slot sum reads them back.  g holds M * top_k * N floats
+// (4-byte aligned at least; float4 accesses only when it and y are 16-byte
+// aligned); y is written only by the last launch.
 qmv_status_t launch_combine_via(int wfmt, int afmt, const void *codes, const void *scales, int E,
                                 const int32_t *ids, const float *route_w, int M, int top_k, const void *x,
                                 const void *xs, int x_per_slot, float *g, float *y, int N, int K,

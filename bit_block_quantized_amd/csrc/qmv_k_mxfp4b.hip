@@ -419,11 +419,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void qmv_batched_kernel(const Args a
 // GPU.  Here the waves of a workgroup split the tile's K instead: wave w
 // takes the 128-weight slices w, w + WAVES, w + 2 WAVES, ... of the tile
 // (32 rows x a chunk of at most VMAX vectors: 32, or 64 in 32-vector column
-// fragments), stages their activations in a two-slice LDS ring of its own
-// (no workgroup barrier in the loop), and the
-// waves' partial tiles are summed in LDS in wave order at the end, so the
-// result is bitwise reproducible.  The loads, decode and MFMA steps are the
-// batched kernel's (lane (r, h): blocks 2 h and 2 h + 1 of row r per slice).
+// fragments), stages their activations in an LDS ring of its own (two
+// slices; one with 64 vectors) with no workgroup barrier in the loop, and
+// the waves' partial tiles are summed in LDS in wave order at the end, so
+// the result is bitwise reproducible.  The loads, decode and MFMA steps are
+// the batched kernel's (lane (r, h): blocks 2 h and 2 h + 1 of row r per
+// slice).
 template <int WAVES, int VMAX>
 __global__ __launch_bounds__(64 * WAVES) void qmv_batched_ks_kernel(const Args a)
 {
