@@ -252,6 +252,27 @@ def test_many_tokens_at_the_pair_limit(wfmt):
     assert_parity(y[outs], yr, A, f"{wfmt} 8192 pairs")
 
 
+def test_many_tokens_on_two_streams_at_once():
+    """Many-token combines queued on two streams without synchronizing
+    between them: each call takes its temporary from the pool in its own
+    stream's order, so the results equal the calls made one at a time."""
+    cases = [synth.make(_combine_wl(f, M=48, N=130, K=320, E=6, top_k=4, seed=61 + i))
+             for i, f in enumerate(["mxfp4", "cb3"])]
+    devs = [to_dev(inp) for inp in cases]
+    ref = [gpu_combine(inp, dev).cpu().numpy() for inp, dev in zip(cases, devs)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty((48, 130), device="cuda") for _ in range(6)] for _ in cases]
+    torch.cuda.synchronize()
+    for rep in range(6):
+        for c, (inp, dev) in enumerate(zip(cases, devs)):
+            with torch.cuda.stream(streams[c]):
+                gpu_combine(inp, dev, y=outs[c][rep], stream=streams[c])
+    torch.cuda.synchronize()
+    for c in range(2):
+        for rep in range(6):
+            assert np.array_equal(outs[c][rep].cpu().numpy().view(np.uint32), ref[c].view(np.uint32)), (c, rep)
+
+
 def test_many_tokens_leaves_nothing_past_y_and_repeats():
     """The many-token combine writes every row of y, nothing past it, and the
     same bits on a second call (its temporary comes back from the pool)."""
