@@ -433,10 +433,11 @@ constexpr int kGmNvg[4] = {1, 2, 3, 4};
 // expert: one launch of the int8 matrix-core kernel.  A workgroup's LDS:
 // the staged vector groups (per group of 4 and unit: the activations in
 // selector order and the per-block side data), the pair scan and bitmap,
-// the pair list.  The groups per chunk cover the average expert's vectors
-// (with room for a few more) as far as the LDS allows; the grid is at most
-// one round of the chip, each workgroup an equal run of (expert, 32-row
-// tile) items, so one staging of a chunk serves many row tiles.
+// the pair list, the per-expert counts.  The groups per chunk cover the
+// average expert's vectors (with room for a few more) as far as the LDS
+// allows; the grid is at most one round of the chip, each workgroup a run of
+// (expert, 32-row tile) items of equal cost with each expert's vector count
+// weighed in, so one staging of a chunk serves many row tiles.
 qmv_status_t launch_gmma(int wfmt, int afmt, int kind, const void *codes, const void *scales, int E,
                          const int32_t *ids, int M, int top_k, const void *x, const void *xs, int x_per_slot,
                          float *y, int N, int K, hipStream_t stream)
@@ -449,11 +450,13 @@ qmv_status_t launch_gmma(int wfmt, int afmt, int kind, const void *codes, const 
     const int U = K / kUnitWeights[kind];
     const int Up = (U + 15) & ~15;
     const size_t group_bytes = (size_t)Up * (fi == 0 ? 256 + 32 : 128 + 16);
-    const size_t tail = kPairCountBytes + kExpertBitmapBytes + (((size_t)2 * (gather ? pairs : 0) + 15) & ~(size_t)15);
-    // groups of 4 for the average expert's vectors and half again (the
-    // counts spread around the average), as far as one workgroup's LDS allows
+    const size_t tail =
+        kPairCountBytes + kExpertBitmapBytes + kExpertCountBytes + (((size_t)2 * (gather ? pairs : 0) + 15) & ~(size_t)15);
+    // groups of 4 for twice the average expert's vectors (the counts spread
+    // around the average, and every further chunk decodes the weights again),
+    // as far as one workgroup's LDS allows
     const int avg = (pairs + busy - 1) / busy;
-    const int want = (avg + avg / 2 + 3) / 4;
+    const int want = (2 * avg + 3) / 4;
     int ni = want < 1 ? 0 : want > 4 ? 3 : want - 1;
     while (ni > 0 && kGmNvg[ni] * group_bytes + tail > (size_t)kLdsPerCU) --ni;
     const size_t lds = kGmNvg[ni] * group_bytes + tail;

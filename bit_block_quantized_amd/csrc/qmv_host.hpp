@@ -41,9 +41,13 @@ constexpr int kMenuCplC[4] = {1, 2, 3, 4};
 // for this many (round, wave) counts plus a total in LDS, ahead of the list.
 constexpr int kPairCounts = 256;
 constexpr int kPairCountBytes = 4 * (kPairCounts + 4);
-// The grouped kernel's bitmap of the experts a call selects (E <= 1024) and
-// the word that hands one of them to every wave.
+// The grouped kernel's bitmap of the experts a call selects (E <= 1024), the
+// word that hands one of them to every wave, the count of them, and two words
+// that hand a workgroup's run of items to every wave.
 constexpr int kExpertBitmapBytes = 4 * 36;
+// The int8 matrix-core kernel's count of pairs per expert (E <= 1024), from
+// which each workgroup finds its share of the call's weighted work.
+constexpr int kExpertCountBytes = 4 * 1024;
 
 }  // namespace qmv_cfg
 

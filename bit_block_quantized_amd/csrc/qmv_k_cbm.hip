@@ -47,8 +47,9 @@
 //
 // Work: (expert slot, row tile) items as in the grouped decode-MAC kernel
 // (qmv_device.hpp): the y-th selected expert from a bitmap of the ids, the
-// expert's (token, slot) pairs listed in index order, equal contiguous runs
-// of items per workgroup.
+// expert's (token, slot) pairs listed in index order, contiguous runs of
+// items per workgroup, of equal cost when the vector counts are weighed in
+// (gm_weighted_run).
 #include "qmv_device.hpp"
 
 namespace qmv {
@@ -364,8 +365,93 @@ __device__ __forceinline__ void gm_run(const Args &a, const uint8_t *lds, const 
     }
 }
 
-// Work items (expert slot, row tile), slot-major, dealt in equal contiguous
-// runs; per slot the pairs are listed and taken in chunks of up to 4 * NVG
+// The cost of one row tile of an expert with c vectors, in units of the step
+// loop's issue slots (from the instruction counts of the step: the decode and
+// the loads cost about 1.5 times one vector group's matrix products and
+// scale epilogue): each chunk of up to 4 * NVG vectors decodes the weights
+// again, each group of 4 vectors adds its own products.
+template <int NVG>
+__device__ __forceinline__ int gm_tile_cost(int c)
+{
+    constexpr int kChunk = 3, kGroup = 2;
+    if (c <= 0) return 0;
+    return kChunk * ((c + 4 * NVG - 1) / (4 * NVG)) + kGroup * ((c + 3) >> 2);
+}
+
+// This workgroup's run of (expert slot, row tile) items, [run[0], run[1]),
+// weighted by gm_tile_cost: the experts a call selects differ in their vector
+// counts, and equal runs of items would leave the workgroups of the busiest
+// experts working long after the rest.  Item i = slot * tiles + t starts at
+// cost tiles * P_slot + t * cost_slot (P the costs of the slots before it);
+// the workgroup takes the items that start in its equal share of the total,
+// [total * b / G, total * (b + 1) / G).  ids are counted per expert into
+// cnt[0..1024) with LDS atomics; one wave scans the counts, 16 experts per
+// lane.  Every workgroup computes the same split.
+template <int THREADS, int NVG>
+__device__ __forceinline__ void gm_weighted_run(const int32_t *ids, int B, int E, int tiles, int *cnt, int *run,
+                                                Ids8 first)
+{
+    const int tid = threadIdx.x;
+    for (int e = tid; e < 1024; e += THREADS) cnt[e] = 0;
+    __syncthreads();
+    const int rounds = (B + THREADS - 1) / THREADS;
+    for (int j0 = 0; j0 < rounds; j0 += 8) {
+        const Ids8 idv = j0 == 0 ? first : load_ids8<THREADS>(ids, B, E, j0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int e = idv.v[j];
+            if (tid + (j0 + j) * THREADS < B && (unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        long long cost = 0;
+        int busy = 0;
+        for (int k = 0; k < 16; ++k) {
+            const int c = cnt[16 * tid + k];
+            cost += gm_tile_cost<NVG>(c);
+            busy += c > 0;
+        }
+        long long cs = cost;                            // inclusive scans over the lanes
+        int bs = busy;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const long long tc = __shfl_up(cs, d);
+            const int tb = __shfl_up(bs, d);
+            if (tid >= d) {
+                cs += tc;
+                bs += tb;
+            }
+        }
+        const long long total = (long long)tiles * __shfl(cs, 63);
+        const int D = __shfl(bs, 63);
+        const long long lo = total * blockIdx.x / gridDim.x;
+        const long long hi = total * (blockIdx.x + 1) / gridDim.x;
+        if (tid == 0) {                                 // a bound at the end: past the last item
+            if (lo >= total) run[0] = D * tiles;
+            if (hi >= total) run[1] = D * tiles;
+        }
+        long long p = (long long)tiles * (cs - cost);   // this lane's first expert's start
+        int s = bs - busy;                              // and its slot
+        for (int k = 0; k < 16; ++k) {
+            const int c = cnt[16 * tid + k];
+            const int w = gm_tile_cost<NVG>(c);
+            if (w > 0) {
+                const long long end = p + (long long)tiles * w;
+                // items of slot s that start before the bound
+                if (lo >= p && lo < end) run[0] = s * tiles + (int)((lo - p + w - 1) / w);
+                if (hi >= p && hi < end) run[1] = s * tiles + (int)((hi - p + w - 1) / w);
+                p = end;
+                ++s;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Work items (expert slot, row tile), slot-major, dealt in contiguous runs of
+// equal weighted cost (gm_weighted_run; equal runs of items for a dense
+// call); per slot the pairs are listed and taken in chunks of up to 4 * NVG
 // vectors, each staged once and streamed against every row tile of the run.
 template <int F, int WAVES, int NVG, int CPL, bool Q>
 __global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
@@ -378,7 +464,8 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
     PairList L;
     L.cnt = (int *)tail;
     uint32_t *bm = (uint32_t *)(tail + kPairCountBytes);
-    L.perm = (uint16_t *)(tail + kPairCountBytes + kExpertBitmapBytes);
+    int *ecnt = (int *)(tail + kPairCountBytes + kExpertBitmapBytes);
+    L.perm = (uint16_t *)(tail + kPairCountBytes + kExpertBitmapBytes + kExpertCountBytes);
     const int tiles = a.gr_tiles, rpt = a.rows_per_tile;
     const int B = a.M * a.top_k;
     Ids8 id0;
@@ -397,9 +484,16 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
             __syncthreads();
         }
     }
-    const long long T = (long long)D * tiles;
-    int i = (int)((long long)blockIdx.x * T / gridDim.x);
-    const int i1 = (int)((long long)(blockIdx.x + 1) * T / gridDim.x);
+    int i, i1;
+    if (gather) {
+        int *run = (int *)(bm + 34);
+        gm_weighted_run<THREADS, NVG>(a.ids, B, a.E, tiles, ecnt, run, id0);
+        i = run[0];
+        i1 = run[1];
+    } else {
+        i = (int)((long long)blockIdx.x * tiles / gridDim.x);
+        i1 = (int)((long long)(blockIdx.x + 1) * tiles / gridDim.x);
+    }
     while (i < i1) {
         const int slot = i / tiles;
         const int iend = min(i1, (slot + 1) * tiles);   // this run's items of the slot
@@ -408,11 +502,10 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
             e = kth_expert(bm, slot);
             c = list_pairs<THREADS>(a.ids, B, a.E, e, L, id0);
         }
-        // chunks of equal size (within one vector) when an expert has more
-        // vectors than one chunk holds
-        const int nchunk = (c + 4 * NVG - 1) / (4 * NVG);
-        for (int k = 0, v0 = 0; k < nchunk; ++k) {
-            const int cc = (c - v0) / (nchunk - k) + ((c - v0) % (nchunk - k) != 0);
+        // full chunks of 4 * NVG vectors and the rest, ceil(c / 4) vector
+        // groups in all
+        for (int v0 = 0; v0 < c;) {
+            const int cc = min(4 * NVG, c - v0);
             const int ng = (cc + 3) >> 2;
             gm_stage<F, THREADS, Q>(a, lds, L.perm, gather, v0, cc, ng, Up);
             __syncthreads();

@@ -248,3 +248,28 @@ def test_int8_matrix_cores_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy().view(np.uint32), y1.view(np.uint32))
+
+
+@pytest.mark.parametrize("wfmt", ["cb2", "cb3"])
+def test_int8_matrix_cores_skewed_routing(wfmt):
+    """Workgroups take runs of (expert, row tile) items of equal weighted cost
+    (each expert's cost per tile grows with its vector count): one expert
+    with most of the pairs (its tiles split over many workgroups, some
+    workgroups left with no item), the rest with 1 to 20 vectors (several
+    light experts in one workgroup's run, chunks of 1 to 16 vectors).  The
+    output starts as NaN so that an item no workgroup takes fails; unit
+    scales make the result bit-exact."""
+    import torch
+    inp = _unit(synth.make(_wl(wfmt, "", "gather", 300, 1000, 512, E=40, top_k=2, seed=195)))
+    rng = np.random.default_rng(196)
+    ids = np.full((300, 2), -1, np.int32)
+    ids[:, 0] = 7
+    spread = np.repeat(np.arange(40), rng.integers(1, 21, size=40))
+    rng.shuffle(spread)
+    ids[:, 1] = np.resize(spread, 300)
+    ids[ids[:, 1] == 7, 1] = 8                      # distinct ids per token
+    inp.ids = ids
+    y = torch.full((300, 2, 1000), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_call(inp, y=y)
+    yr, _ = oracle_call(inp)
+    assert_exact(y.cpu().numpy(), yr, f"{wfmt} skewed routing")
