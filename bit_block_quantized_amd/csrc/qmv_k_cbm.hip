@@ -38,11 +38,12 @@
 //
 // Vectors: an expert's vectors are taken in chunks of up to 4 * NVG (NVG
 // groups of 4); a chunk is staged into LDS once per workgroup and used for
-// every row tile of the workgroup's run of that expert.  LDS per vector
-// group and unit: the four vectors' activations in the order the selectors
-// need (chunk (q, j) at a swizzled place within the unit's record, so the 16
-// lanes of a read quarter hit distinct banks: gm_chunk_off), then the side data
-// xs/2 per 32-block of each vector.
+// every row tile of the workgroup's run of that expert.  LDS per unit: the
+// NVG groups' records one after another (so a group's place is a constant
+// offset from its unit's), each the four vectors' activations in the order
+// the selectors need (chunk (q, j) at a swizzled place within the record, so
+// the 16 lanes of a read quarter hit distinct banks: gm_chunk_off); after all
+// units, the side data xs/2 per 32-block of each vector, in the same order.
 // Units past K and vectors past the chunk are staged as zeros.
 //
 // Work: (expert slot, row tile) items as in the grouped decode-MAC kernel
@@ -79,17 +80,28 @@ __device__ __forceinline__ int gm_group_bytes(int Up)
     return Up * (GmFmt<F>::CH * 64 + 4 * GmFmt<F>::SIDE);
 }
 
-// The 16 lanes of a read quarter take units u .. u + 3 (one chunk q each,
-// four vectors j): the chunk position within a unit's record is xor-ed with
-// the unit's bits above the record's share of a 256-byte bank row, so those
-// 16 chunks fall on 16 distinct 16-byte bank groups (2-bit: 256-byte records,
-// q ^ (u & 3); 3-bit: 128-byte records, q ^ ((u >> 1) & 1)).
-template <int F>
-__device__ __forceinline__ int gm_chunk_off(int u, int q, int j)
+// Activation chunk (q, j) of group g at unit u (units of NVG records).  The
+// 16 lanes of a read quarter take units u .. u + 3 (one chunk q each, four
+// vectors j): the chunk position within a record is xor-ed with the unit's
+// bits above the unit's share of a 256-byte bank row, so those 16 chunks
+// fall on 16 distinct 16-byte bank groups (2-bit: 256-byte records,
+// q ^ (u & 3); 3-bit: 128-byte records, q ^ ((u >> 1) & 1), units 128 or
+// 384 bytes apart for NVG 1 or 3; with NVG 2 two of the four units share
+// a half row, a 2-way conflict).
+template <int F, int NVG>
+__device__ __forceinline__ int gm_chunk_off(int u, int g, int q, int j)
 {
     constexpr int CH = GmFmt<F>::CH;
     const int pos = CH == 4 ? q ^ (u & 3) : q ^ ((u >> 1) & 1);
-    return 16 * ((u * CH + pos) * 4 + j);
+    return 16 * ((u * NVG * CH + pos) * 4 + j) + g * (CH * 64);
+}
+
+// Side data of vector j of group g at unit u (past the Up units' records).
+template <int F, int NVG>
+__device__ __forceinline__ int gm_side_off(int Up, int u, int g, int j)
+{
+    constexpr int CH = GmFmt<F>::CH, SIDE = GmFmt<F>::SIDE;
+    return Up * NVG * CH * 64 + SIDE * ((u * NVG) * 4 + j) + g * (4 * SIDE);
 }
 
 // 3-bit half-block (16 codes: 6 bytes at byte offset OFF of hi:lo) -> four
@@ -119,19 +131,16 @@ __device__ __forceinline__ uint4 cb3_decode_half(uint32_t hi, uint32_t lo)
 // vector indices themselves for a dense call) as ng groups of 4.  Q: the
 // activations are bf16 and each 32-block is quantized here to int8 and an
 // fp16 scale (quant_q8_block, the decode kernels' staging quantizer).
-template <int F, int THREADS, bool Q>
+template <int F, int THREADS, bool Q, int NVG>
 __device__ __forceinline__ void gm_stage(const Args &a, uint8_t *lds, const uint16_t *pairs, bool gather,
                                          int v0, int cc, int ng, int Up)
 {
     constexpr int W = GmFmt<F>::W;
     const int U = a.units;
-    const int gb = gm_group_bytes<F>(Up);
-    const int xbytes = Up * GmFmt<F>::CH * 64;
     const int items = ng * 4 * Up;                   // (vector slot, unit)
     for (int i = threadIdx.x; i < items; i += THREADS) {
         const int m = i / Up, u = i - m * Up;       // vector slot m of the chunk
         const int g = m >> 2, j = m & 3;
-        uint8_t *gbase = lds + g * gb;
         uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0, c2 = c0, c3 = c0;
         float xs0 = 0.0f, xs1 = 0.0f;
         if (m < cc && u < U) {
@@ -163,26 +172,39 @@ __device__ __forceinline__ void gm_stage(const Args &a, uint8_t *lds, const uint
             }
         }
         if constexpr (F == kCB2) {
-            *(uint4 *)(gbase + gm_chunk_off<F>(u, 0, j)) = cb2_xorder(c0);
-            *(uint4 *)(gbase + gm_chunk_off<F>(u, 1, j)) = cb2_xorder(c1);
-            *(uint4 *)(gbase + gm_chunk_off<F>(u, 2, j)) = cb2_xorder(c2);
-            *(uint4 *)(gbase + gm_chunk_off<F>(u, 3, j)) = cb2_xorder(c3);
-            *(uint2 *)(gbase + xbytes + 8 * (u * 4 + j)) = make_uint2(__float_as_uint(xs0), __float_as_uint(xs1));
+            *(uint4 *)(lds + gm_chunk_off<F, NVG>(u, g, 0, j)) = cb2_xorder(c0);
+            *(uint4 *)(lds + gm_chunk_off<F, NVG>(u, g, 1, j)) = cb2_xorder(c1);
+            *(uint4 *)(lds + gm_chunk_off<F, NVG>(u, g, 2, j)) = cb2_xorder(c2);
+            *(uint4 *)(lds + gm_chunk_off<F, NVG>(u, g, 3, j)) = cb2_xorder(c3);
+            *(uint2 *)(lds + gm_side_off<F, NVG>(Up, u, g, j)) = make_uint2(__float_as_uint(xs0), __float_as_uint(xs1));
         } else {
-            *(uint4 *)(gbase + gm_chunk_off<F>(u, 0, j)) = cb3_xorder(c0);
-            *(uint4 *)(gbase + gm_chunk_off<F>(u, 1, j)) = cb3_xorder(c1);
-            *(float *)(gbase + xbytes + 4 * (u * 4 + j)) = xs0;
+            *(uint4 *)(lds + gm_chunk_off<F, NVG>(u, g, 0, j)) = cb3_xorder(c0);
+            *(uint4 *)(lds + gm_chunk_off<F, NVG>(u, g, 1, j)) = cb3_xorder(c1);
+            *(float *)(lds + gm_side_off<F, NVG>(Up, u, g, j)) = xs0;
         }
     }
+}
+
+// fp16 halves of a packed scale pair, widened where they are used: as an
+// operand of a multiply-add the compiler folds the widening into it
+// (v_fma_mix_f32), and a product written as fma(w, x, 0) is the product
+// rounded once, as w * x is (a zero may differ in sign only).
+__device__ __forceinline__ float h16_lo(uint32_t v)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float h16_hi(uint32_t v)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(v >> 16));
 }
 
 // One step (16 units, one per block) of NG vector groups: the int32 tiles
 // of each scale block, scaled into acc[g] (rows 0..3 of the quad, vector j
 // of group g).  The groups' MFMA chains are interleaved, so NG independent
 // accumulators are in flight.
-template <int F, int NG>
-__device__ __forceinline__ void gm_step(const uint8_t *lds, int gb, int xbytes, int u, int j,
-                                        const uint32_t (&A)[16], const float (&wlo)[4], const float (&whi)[4],
+template <int F, int NG, int NVG>
+__device__ __forceinline__ void gm_step(const uint8_t *lds, int Up, int u, int j,
+                                        const uint32_t (&A)[16], const uint32_t (&sw)[4],
                                         float (&acc)[NG][4])
 {
     if constexpr (F == kCB2) {
@@ -191,8 +213,8 @@ __device__ __forceinline__ void gm_step(const uint8_t *lds, int gb, int xbytes, 
             uint32_t xv[NG][8];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                const uint4 x0 = lds_read16(lds + g * gb + gm_chunk_off<F>(u, 2 * b, j));
-                const uint4 x1 = lds_read16(lds + g * gb + gm_chunk_off<F>(u, 2 * b + 1, j));
+                const uint4 x0 = lds_read16(lds + gm_chunk_off<F, NVG>(u, g, 2 * b, j));
+                const uint4 x1 = lds_read16(lds + gm_chunk_off<F, NVG>(u, g, 2 * b + 1, j));
                 xv[g][0] = x0.x; xv[g][1] = x0.y; xv[g][2] = x0.z; xv[g][3] = x0.w;
                 xv[g][4] = x1.x; xv[g][5] = x1.y; xv[g][6] = x1.z; xv[g][7] = x1.w;
             }
@@ -206,11 +228,11 @@ __device__ __forceinline__ void gm_step(const uint8_t *lds, int gb, int xbytes, 
                     d[g] = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A[8 * b + t], (int)xv[g][t], d[g], 0, 0, 0);
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                const float xsh = *(const float *)(lds + g * gb + xbytes + 8 * (u * 4 + j) + 4 * b);
+                const float xsh = *(const float *)(lds + gm_side_off<F, NVG>(Up, u, g, j) + 4 * b);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float ws = b == 0 ? wlo[i] : whi[i];
-                    acc[g][i] = __builtin_fmaf((float)d[g][i], ws * xsh, acc[g][i]);
+                    const float ws = b == 0 ? h16_lo(sw[i]) : h16_hi(sw[i]);
+                    acc[g][i] = __builtin_fmaf((float)d[g][i], __builtin_fmaf(ws, xsh, 0.0f), acc[g][i]);
                 }
             }
         }
@@ -218,8 +240,8 @@ __device__ __forceinline__ void gm_step(const uint8_t *lds, int gb, int xbytes, 
         uint32_t xv[NG][8];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            const uint4 x0 = lds_read16(lds + g * gb + gm_chunk_off<F>(u, 0, j));
-            const uint4 x1 = lds_read16(lds + g * gb + gm_chunk_off<F>(u, 1, j));
+            const uint4 x0 = lds_read16(lds + gm_chunk_off<F, NVG>(u, g, 0, j));
+            const uint4 x1 = lds_read16(lds + gm_chunk_off<F, NVG>(u, g, 1, j));
             xv[g][0] = x0.x; xv[g][1] = x0.y; xv[g][2] = x0.z; xv[g][3] = x0.w;
             xv[g][4] = x1.x; xv[g][5] = x1.y; xv[g][6] = x1.z; xv[g][7] = x1.w;
         }
@@ -235,14 +257,53 @@ __device__ __forceinline__ void gm_step(const uint8_t *lds, int gb, int xbytes, 
             }
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            const float xsh = *(const float *)(lds + g * gb + xbytes + 4 * (u * 4 + j));
+            const float xsh = *(const float *)(lds + gm_side_off<F, NVG>(Up, u, g, j));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float t = __builtin_fmaf(whi[i], (float)d1[g][i], wlo[i] * (float)d0[g][i]);
+                const float t = __builtin_fmaf(h16_hi(sw[i]), (float)d1[g][i],
+                                               __builtin_fmaf(h16_lo(sw[i]), (float)d0[g][i], 0.0f));
                 acc[g][i] = __builtin_fmaf(t, xsh, acc[g][i]);
             }
         }
     }
+}
+
+// v's bits moved under DPP control CTRL into the lanes of the 4-lane banks
+// BANKS of every 16-lane row; the other lanes keep `old`.
+template <int CTRL, int BANKS>
+__device__ __forceinline__ float dpp_into(float old, float v)
+{
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, 0xF, BANKS, false));
+}
+
+// The sum over the wave's 16 blocks (lane bits 2..5) of a block's 4 x 4 tile,
+// v[i] = row i of the lane's vector (lane bits 0..1).  A reduce-scatter over
+// lane bits 3 and 2 -- each lane keeps the rows its side of the pair will
+// own, and adds its partner's copy of them (DPP within the 16-lane row; a
+// row rotation by n hands lane l the value of lane l - n) -- then a sum over
+// bits 4 and 5.  Lane 4 blk + j ends with row blk & 3 of vector j, summed in
+// a fixed order.  Against a 4-level shuffle butterfly over all four rows:
+// about 100 fewer instructions per tile, C8 686-697 -> 646-656 us on MI355X.
+__device__ __forceinline__ float gm_tile_sum(const float (&v)[4])
+{
+    constexpr int kId = 0xE4, kRor4 = 0x124, kRor8 = 0x128, kRor12 = 0x12C;
+    float t[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        // bit 3: banks 0-1 keep row i, banks 2-3 row i + 2; partner l ^ 8
+        const float keep = dpp_into<kId, 0x3>(v[i + 2], v[i]);
+        const float send = dpp_into<kId, 0x3>(v[i], v[i + 2]);
+        t[i] = keep + dpp_into<kRor8, 0xF>(0.0f, send);
+    }
+    // bit 2: banks 0 and 2 keep t[0] (rows 0, 2), banks 1 and 3 t[1]; the
+    // partner is l + 4 (bit 2 clear) or l - 4 (set)
+    const float keep = dpp_into<kId, 0x5>(t[1], t[0]);
+    const float send = dpp_into<kId, 0x5>(t[0], t[1]);
+    float s = keep + dpp_into<kRor4, 0xA>(dpp_into<kRor12, 0x5>(0.0f, send), send);
+    s += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(s), 0x401F));   // lane ^ 16
+    s += __shfl_xor(s, 32);
+    return s;
 }
 
 // Codes and scales of flattened step f = (tile ti, step s): this lane's row
@@ -272,15 +333,13 @@ __device__ __forceinline__ void gm_load(__amdgpu_buffer_rsrc_t rc, __amdgpu_buff
 // vector groups; each wave streams its quad of every tile as one sequence of
 // (tile, step) pairs with CPL steps of loads in flight across tile
 // boundaries, and stores the rows of vectors [v0, v0 + cc) after each tile.
-template <int F, int WAVES, int CPL, int NG>
+template <int F, int WAVES, int CPL, int NG, int NVG>
 __device__ __forceinline__ void gm_run(const Args &a, const uint8_t *lds, const uint16_t *pairs, bool gather,
                                        int expert, int tile0, int ntiles, int v0, int cc, int Up)
 {
     const int lane = threadIdx.x & 63;
     const int blk = lane >> 2, r = lane & 3;
     const int steps = Up >> 4;
-    const int gb = gm_group_bytes<F>(Up);
-    const int xbytes = Up * GmFmt<F>::CH * 64;
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (long long)expert * a.expert_cb, a.expert_cb);
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.scales + (long long)expert * a.expert_sb, a.expert_sb);
     const int wrow = tile0 * a.rows_per_tile + 4 * (int)(threadIdx.x >> 6);   // the wave's quad, first tile
@@ -309,12 +368,6 @@ __device__ __forceinline__ void gm_run(const Args &a, const uint8_t *lds, const 
                 // the quad's four rows' scales for this block's unit
                 const uint32_t sw[4] = {quad_lane<0>(wsd[c]), quad_lane<1>(wsd[c]), quad_lane<2>(wsd[c]),
                                         quad_lane<3>(wsd[c])};
-                float wlo[4], whi[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    wlo[i] = f16_lo(sw[i]);
-                    whi[i] = f16_hi(sw[i]);
-                }
                 uint32_t A[16];
                 if constexpr (F == kCB2) {
                     // codes c -> int8 2c - 3 (a v_perm_b32 LUT), so the MFMA
@@ -333,23 +386,17 @@ __device__ __forceinline__ void gm_run(const Args &a, const uint8_t *lds, const 
 #pragma unroll
                     for (int t = 8; t < 16; ++t) A[t] = 0u;
                 }
-                gm_step<F, NG>(lds, gb, xbytes, u, r, A, wlo, whi, acc);
+                gm_step<F, NG, NVG>(lds, Up, u, r, A, sw, acc);
                 if (cs == steps - 1) {
-                    // tile done: sum the 16 blocks' tiles (butterfly over lane
-                    // bits 2..5), then lane 4 i + j (i < 4) stores row
-                    // 4 quad + i of vector j of each group
-                    const int row = wrow + ct * a.rows_per_tile + blk;
+                    // tile done: sum the 16 blocks' tiles (gm_tile_sum: lane
+                    // 4 blk + j ends with row blk & 3 of vector j), and the
+                    // lanes 16 (g & 3) .. 16 (g & 3) + 15 store group g's 4 x 4
+                    const int row = wrow + ct * a.rows_per_tile + (blk & 3);
 #pragma unroll
                     for (int g = 0; g < NG; ++g) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                            for (int m = 4; m < 64; m <<= 1) acc[g][i] += __shfl_xor(acc[g][i], m);
-                        }
-                        const float val =
-                            blk == 0 ? acc[g][0] : blk == 1 ? acc[g][1] : blk == 2 ? acc[g][2] : acc[g][3];
+                        const float val = gm_tile_sum(acc[g]);
                         const int m = 4 * g + r;
-                        if (blk < 4 && m < cc && row < a.N) {
+                        if ((blk >> 2) == (g & 3) && m < cc && row < a.N) {
                             const int p = gather ? (int)pairs[v0 + m] : v0 + m;
                             a.y[p * a.N + row] = val;       // M * top_k * N < 2^31
                         }
@@ -507,19 +554,19 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
         for (int v0 = 0; v0 < c;) {
             const int cc = min(4 * NVG, c - v0);
             const int ng = (cc + 3) >> 2;
-            gm_stage<F, THREADS, Q>(a, lds, L.perm, gather, v0, cc, ng, Up);
+            gm_stage<F, THREADS, Q, NVG>(a, lds, L.perm, gather, v0, cc, ng, Up);
             __syncthreads();
             const int tile0 = i - slot * tiles, nt = iend - i;
             if constexpr (NVG >= 4) {
-                if (ng == 4) gm_run<F, WAVES, CPL, 4>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
+                if (ng == 4) gm_run<F, WAVES, CPL, 4, NVG>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
             }
             if constexpr (NVG >= 3) {
-                if (ng == 3) gm_run<F, WAVES, CPL, 3>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
+                if (ng == 3) gm_run<F, WAVES, CPL, 3, NVG>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
             }
             if constexpr (NVG >= 2) {
-                if (ng == 2) gm_run<F, WAVES, CPL, 2>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
+                if (ng == 2) gm_run<F, WAVES, CPL, 2, NVG>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
             }
-            if (ng == 1) gm_run<F, WAVES, CPL, 1>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
+            if (ng == 1) gm_run<F, WAVES, CPL, 1, NVG>(a, lds, L.perm, gather, e, tile0, nt, v0, cc, Up);
             __syncthreads();                            // the next chunk or expert restages
             v0 += cc;
         }
