@@ -53,9 +53,9 @@ extern const void *const kTableDense4[2];
 // 2-bit and 3-bit codebook weights x int8 activations with more than 4
 // vectors per expert on the int8 4x4x4 matrix cores (qmv_k_cbm.hip):
 // [int8 x, bf16 x quantized in staging][2-bit, 3-bit][vector groups of 4 per
-// staged chunk: 1, 2, 3]; 12 waves.
+// staged chunk: 1, 2, 3, 4 (2-bit only)]; 12 waves.
 namespace qmv {
-extern const void *const kTableGmma[2][2][3];
+extern const void *const kTableGmma[2][2][4];
 }
 
 // Dense MXFP4 x bf16 with 9 to 64 vectors: 32-row tiles with K split over
@@ -423,15 +423,16 @@ qmv_status_t launch_grouped(int wfmt, int afmt, const void *codes, const void *s
     return QMV_OK;
 }
 
-std::once_flag g_gm_once[2][2][3];
-hipError_t g_gm_err[2][2][3];
-int g_gm_occ[2][2][3];                                  // workgroups per CU by registers
-// 12 waves per workgroup (three per SIMD, which cover each other's latency;
-// the registers of up to 3 vector groups fit 170 per lane).  Measured on
-// MI355X against 8 waves with up to 4 groups: C7 421 -> 408 us, C8 745 ->
-// 667 us; 4 waves: 500-640 and 700-806 us.
+std::once_flag g_gm_once[2][2][4];
+hipError_t g_gm_err[2][2][4];
+int g_gm_occ[2][2][4];                                  // workgroups per CU by registers
+// 12 waves per workgroup: three per SIMD, which cover each other's latency,
+// with up to 168 registers per lane -- enough for 4 vector groups of 2-bit
+// weights, 3 of 3-bit ones.  Measured on MI355X against 8 waves with up to
+// 4 groups: C7 421 -> 408 us, C8 745 -> 667 us; 4 waves: 500-640 and
+// 700-806 us.  2-bit with 4 groups against 3: C7 400 -> 384-391 us.
 constexpr int kGmWaves = 12;
-constexpr int kGmNvg[3] = {1, 2, 3};
+constexpr int kGmNvg[4] = {1, 2, 3, 4};
 
 // Codebook weights x int8 activations, more than 4 vectors, several per
 // expert: one launch of the int8 matrix-core kernel.  A workgroup's LDS:
@@ -461,7 +462,8 @@ qmv_status_t launch_gmma(int wfmt, int afmt, int kind, const void *codes, const 
     // as far as one workgroup's LDS allows
     const int avg = (pairs + busy - 1) / busy;
     const int want = (2 * avg + 3) / 4;
-    int ni = want < 1 ? 0 : want > 3 ? 2 : want - 1;
+    const int nimax = fi == 0 ? 3 : 2;
+    int ni = want < 1 ? 0 : want - 1 > nimax ? nimax : want - 1;
     while (ni > 0 && kGmNvg[ni] * group_bytes + tail > (size_t)kLdsPerCU) --ni;
     const size_t lds = kGmNvg[ni] * group_bytes + tail;
     if (lds > (size_t)kLdsPerCU)
