@@ -464,8 +464,11 @@ qmv_status_t launch_gmma(int wfmt, int afmt, int kind, const void *codes, const 
     const int want = (2 * avg + 3) / 4;
     const int nimax = fi == 0 ? 3 : 2;
     int ni = want < 1 ? 0 : want - 1 > nimax ? nimax : want - 1;
-    while (ni > 0 && kGmNvg[ni] * group_bytes + tail > (size_t)kLdsPerCU) --ni;
-    const size_t lds = kGmNvg[ni] * group_bytes + tail;
+    // the staged groups (2-bit with 4 groups: 32 bytes of padding per unit
+    // in the side data), then the tail
+    auto staged = [&](int k) { return kGmNvg[k] * group_bytes + (fi == 0 && kGmNvg[k] == 4 ? (size_t)Up * 32 : 0); };
+    while (ni > 0 && staged(ni) + tail > (size_t)kLdsPerCU) --ni;
+    const size_t lds = staged(ni) + tail;
     if (lds > (size_t)kLdsPerCU)
         return QMV_EUNSUPPORTED;
     const void *fn = kTableGmma[qi][fi][ni];

@@ -73,11 +73,21 @@ template <int F> struct GmFmt;
 template <> struct GmFmt<kCB2> { static constexpr int W = 64, CH = 4, SIDE = 8, CB = 16; };
 template <> struct GmFmt<kCB3> { static constexpr int W = 32, CH = 2, SIDE = 4, CB = 12; };
 
-// LDS bytes of one vector group (4 vectors) over Up units.
-template <int F>
-__device__ __forceinline__ int gm_group_bytes(int Up)
+// Side-data bytes per unit: NVG groups of 4 vectors, and for 2-bit weights
+// with 4 groups 32 bytes of padding, so that the 4 units a read quarter
+// takes (32 bytes of one group each) start 160 bytes apart and fall on
+// distinct banks (128 bytes apart, units u and u + 2 would share them).
+template <int F, int NVG>
+constexpr int gm_side_stride()
 {
-    return Up * (GmFmt<F>::CH * 64 + 4 * GmFmt<F>::SIDE);
+    return NVG * 4 * GmFmt<F>::SIDE + (F == kCB2 && NVG == 4 ? 32 : 0);
+}
+
+// LDS bytes of the staged vector groups over Up units.
+template <int F, int NVG>
+__device__ __forceinline__ int gm_stage_bytes(int Up)
+{
+    return Up * (NVG * GmFmt<F>::CH * 64 + gm_side_stride<F, NVG>());
 }
 
 // Activation chunk (q, j) of group g at unit u (units of NVG records).  The
@@ -101,7 +111,7 @@ template <int F, int NVG>
 __device__ __forceinline__ int gm_side_off(int Up, int u, int g, int j)
 {
     constexpr int CH = GmFmt<F>::CH, SIDE = GmFmt<F>::SIDE;
-    return Up * NVG * CH * 64 + SIDE * ((u * NVG) * 4 + j) + g * (4 * SIDE);
+    return Up * NVG * CH * 64 + u * gm_side_stride<F, NVG>() + SIDE * j + g * (4 * SIDE);
 }
 
 // 3-bit half-block (16 codes: 6 bytes at byte offset OFF of hi:lo) -> four
@@ -139,8 +149,12 @@ __device__ __forceinline__ void gm_stage(const Args &a, uint8_t *lds, const uint
     const int U = a.units;
     const int items = ng * 4 * Up;                   // (vector slot, unit)
     for (int i = threadIdx.x; i < items; i += THREADS) {
-        const int m = i / Up, u = i - m * Up;       // vector slot m of the chunk
-        const int g = m >> 2, j = m & 3;
+        // vector j of group g at unit u, j fastest and then u: the 16 lanes
+        // of a write quarter store 4 units x 4 vectors, as a read quarter
+        // reads them, on distinct banks
+        const int j = i & 3, t = i >> 2;
+        const int g = t / Up, u = t - g * Up;
+        const int m = 4 * g + j;                    // vector slot m of the chunk
         uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0, c2 = c0, c3 = c0;
         float xs0 = 0.0f, xs1 = 0.0f;
         if (m < cc && u < U) {
@@ -507,7 +521,7 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
     constexpr int THREADS = 64 * WAVES;
     const bool gather = a.ids != nullptr;
     const int Up = (a.units + 15) & ~15;
-    uint8_t *tail = lds + NVG * gm_group_bytes<F>(Up);
+    uint8_t *tail = lds + gm_stage_bytes<F, NVG>(Up);
     PairList L;
     L.cnt = (int *)tail;
     uint32_t *bm = (uint32_t *)(tail + kPairCountBytes);
