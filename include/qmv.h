@@ -174,7 +174,9 @@ qmv_status_t qmv_dense(qmv_wfmt_t wfmt, const void *w_codes, const void *w_scale
  *     its vectors, up to 128 at a time, on the 32x32x16 bf16 matrix cores;
  *   (CB2 with K % 64 == 0 or CB3, Q8B32 or BF16_Q8) with M * top_k >= 2 E:
  *     exact int32 block sums on the int8 4x4x4 matrix cores, up to 16
- *     vectors per staged chunk (bf16 x quantized while staged);
+ *     (2-bit) or 12 (3-bit) vectors per staged chunk (bf16 x quantized
+ *     while staged), each workgroup a run of (expert, row tile) items of
+ *     equal cost with the experts' vector counts weighed in;
  *   at most 64 tokens with fewer than two pairs per expert: groups of up to
  *     4 tokens on the decode kernels, one launch per group;
  *   every other call: the decode kernels' own multiply-adds in one launch,
