@@ -2,20 +2,23 @@
 3-bit codebook weights against int8 blocks (given, or bf16 quantized while
 staged) and MXFP4 weights against int8 blocks (needs an MI355X).
 
-These calls run on the grouped kernel: one launch, a workgroup per (row tile,
-expert); each workgroup lists the (token, slot) pairs of its expert in LDS
-(the pair order of the call) and takes them four at a time through the decode
-kernels' row loop, so an expert's rows are read once per four of its vectors.
-Dense calls are one expert with every vector.  MXFP4 x bf16 gathers with
-fewer than two pairs per expert take the same route (tests in
-test_gpu_batched.py).
+2-bit and 3-bit weights with at least two vectors per expert on average run
+on the int8 matrix-core kernel: each workgroup takes a run of (expert, row
+tile) items of equal weighted cost, lists each expert's (token, slot) pairs in
+LDS and stages them in chunks of up to 16 (2-bit) or 12 (3-bit) vectors.  The
+other calls run on the grouped kernel: one launch, a workgroup per (row tile,
+expert), the pairs taken four at a time through the decode kernels' row loop,
+so an expert's rows are read once per four of its vectors.  Dense calls are
+one expert with every vector.  MXFP4 x bf16 gathers with fewer than two pairs
+per expert take the grouped route too (tests in test_gpu_batched.py).
 
 Against the oracle on the same seeded inputs: every output within
 1e-3 * sum |w x|; bit-exact at unit scales with int8 activations (integer
 block sums, exact in fp32 in any order); zero rows for ids outside [0, E);
-experts with far more than 128 vectors; the 8192-pair and 1023-expert
-limits; and the DeepSeek-shaped prefill chunk at full size on sampled
-outputs.
+experts with far more than 128 vectors; skewed routing that splits one
+expert's tiles over many workgroups (NaN-filled output, bit-exact); the
+8192-pair and 1023-expert limits; and the DeepSeek-shaped prefill chunk at
+full size on sampled outputs.
 """
 import numpy as np
 import pytest
