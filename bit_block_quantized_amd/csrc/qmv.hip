@@ -53,9 +53,9 @@ extern const void *const kTableDense4[2];
 // 2-bit and 3-bit codebook weights x int8 activations with more than 4
 // vectors per expert on the int8 4x4x4 matrix cores (qmv_k_cbm.hip):
 // [int8 x, bf16 x quantized in staging][2-bit, 3-bit][vector groups of 4 per
-// staged chunk: 1, 2, 3, 4 (2-bit only)]; 12 waves.
+// staged chunk: 1, 2, 3, 4]; [8 waves, 12 waves] per workgroup.
 namespace qmv {
-extern const void *const kTableGmma[2][2][4];
+extern const void *const kTableGmma[2][2][2][4];
 }
 
 // Dense MXFP4 x bf16 with 9 to 64 vectors: 32-row tiles with K split over
@@ -423,15 +423,19 @@ qmv_status_t launch_grouped(int wfmt, int afmt, const void *codes, const void *s
     return QMV_OK;
 }
 
-std::once_flag g_gm_once[2][2][4];
-hipError_t g_gm_err[2][2][4];
-int g_gm_occ[2][2][4];                                  // workgroups per CU by registers
-// 12 waves per workgroup: three per SIMD, which cover each other's latency,
-// with up to 168 registers per lane -- enough for 4 vector groups of 2-bit
-// weights, 3 of 3-bit ones.  Measured on MI355X against 8 waves with up to
-// 4 groups: C7 421 -> 408 us, C8 745 -> 667 us; 4 waves: 500-640 and
-// 700-806 us.  2-bit with 4 groups against 3: C7 400 -> 384-391 us.
-constexpr int kGmWaves = 12;
+std::once_flag g_gm_once[2][2][2][4];
+hipError_t g_gm_err[2][2][2][4];
+int g_gm_occ[2][2][2][4];                               // workgroups per CU by registers
+// Workgroups of 12 waves (three per SIMD, which cover each other's latency,
+// with up to 168 registers per lane: 4 vector groups of 2-bit weights, 3 of
+// 3-bit ones) for calls with many (expert, 48-row tile) items, 8 waves
+// (32-row tiles, up to 4 groups) for the others, whose tiles would not fill
+// the chip.  Measured on MI355X, 12 against 8 waves: C7 421 -> 408 us, C8
+// 745 -> 667 us (4 waves: 500-640 and 700-806 us); 2-bit with 4 groups
+// against 3 at 12 waves: C7 400 -> 384-391 us; dense 16 and 64 vectors of
+// 7168 x 7168 2-bit, 16 of 7168 x 2048 3-bit: 15.3, 53 and 10.3 us at 8
+// waves against 17.9, 62 and 14.4 at 12.
+constexpr int kGmWaveMenu[2] = {8, 12};
 constexpr int kGmNvg[4] = {1, 2, 3, 4};
 
 // Codebook weights x int8 activations, more than 4 vectors, several per
@@ -441,7 +445,7 @@ constexpr int kGmNvg[4] = {1, 2, 3, 4};
 // the pair list, the per-expert counts.  The groups per chunk cover the
 // average expert's vectors (with room for a few more) as far as the LDS
 // allows; the grid is at most one round of the chip, each workgroup a run of
-// (expert, 32-row tile) items of equal cost with each expert's vector count
+// (expert, row tile) items of equal cost with each expert's vector count
 // weighed in, so one staging of a chunk serves many row tiles.
 qmv_status_t launch_gmma(int wfmt, int afmt, int kind, const void *codes, const void *scales, int E,
                          const int32_t *ids, int M, int top_k, const void *x, const void *xs, int x_per_slot,
@@ -462,7 +466,10 @@ qmv_status_t launch_gmma(int wfmt, int afmt, int kind, const void *codes, const 
     // as far as one workgroup's LDS allows
     const int avg = (pairs + busy - 1) / busy;
     const int want = (2 * avg + 3) / 4;
-    const int nimax = fi == 0 ? 3 : 2;
+    // 12 waves when the 48-row tiles give at least two items per CU
+    const int wv = (long long)busy * ((N + 47) / 48) >= 2LL * cu_count() ? 1 : 0;
+    const int waves = kGmWaveMenu[wv];
+    const int nimax = wv == 1 && fi == 1 ? 2 : 3;
     int ni = want < 1 ? 0 : want - 1 > nimax ? nimax : want - 1;
     // the staged groups (2-bit with 4 groups: 32 bytes of padding per unit
     // in the side data), then the tail
@@ -471,30 +478,30 @@ qmv_status_t launch_gmma(int wfmt, int afmt, int kind, const void *codes, const 
     const size_t lds = staged(ni) + tail;
     if (lds > (size_t)kLdsPerCU)
         return QMV_EUNSUPPORTED;
-    const void *fn = kTableGmma[qi][fi][ni];
-    std::call_once(g_gm_once[qi][fi][ni], [&] {
+    const void *fn = kTableGmma[wv][qi][fi][ni];
+    std::call_once(g_gm_once[wv][qi][fi][ni], [&] {
         hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCU);
         int n = 0;
         if (err == hipSuccess)
-            err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * kGmWaves, 0);
-        g_gm_err[qi][fi][ni] = err;
-        g_gm_occ[qi][fi][ni] = n > 0 ? n : 1;
+            err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * waves, 0);
+        g_gm_err[wv][qi][fi][ni] = err;
+        g_gm_occ[wv][qi][fi][ni] = n > 0 ? n : 1;
     });
-    if (g_gm_err[qi][fi][ni] != hipSuccess)
+    if (g_gm_err[wv][qi][fi][ni] != hipSuccess)
         return QMV_EHIP;
     Args a = base_args(wfmt, afmt, kind, codes, scales, gather ? E : 1, ids, M, gather ? top_k : 1, x, xs,
                        gather ? x_per_slot : 0, y, N, K);
-    a.rows_per_tile = 4 * kGmWaves;
+    a.rows_per_tile = 4 * waves;
     a.gr_tiles = (N + a.rows_per_tile - 1) / a.rows_per_tile;
     const long long items = (long long)busy * a.gr_tiles;
-    long long per_cu = g_gm_occ[qi][fi][ni];
+    long long per_cu = g_gm_occ[wv][qi][fi][ni];
     const long long by_lds = (long long)kLdsPerCU / (long long)lds;
     if (per_cu > by_lds) per_cu = by_lds;
     if (per_cu < 1) per_cu = 1;
     const long long slots = per_cu * cu_count();
     const unsigned grid = (unsigned)(items < slots ? items : slots);
     void *kargs[] = {&a};
-    if (hipLaunchKernel(fn, dim3(grid), dim3(64 * kGmWaves), kargs, lds, stream) != hipSuccess)
+    if (hipLaunchKernel(fn, dim3(grid), dim3(64 * waves), kargs, lds, stream) != hipSuccess)
         return QMV_EHIP;
     return QMV_OK;
 }

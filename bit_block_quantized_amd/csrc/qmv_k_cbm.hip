@@ -588,17 +588,22 @@ __global__ __launch_bounds__(64 * WAVES) void qmv_gmma_kernel(const Args a)
     }
 }
 
-// [int8 activations, bf16 quantized in staging][format: 2-bit, 3-bit]
-// [vector groups per chunk: 1, 2, 3, 4 (2-bit only: the 3-bit kernel with
-// four groups needs more than the 168 registers per lane that three waves
-// per SIMD leave)]; 12 waves, 3 steps of loads in flight.
-#define QMV_GM(F, N, Q) (const void *)&qmv_gmma_kernel<F, 12, N, 3, Q>
-extern const void *const kTableGmma[2][2][4];
-const void *const kTableGmma[2][2][4] = {
-    {{QMV_GM(kCB2, 1, false), QMV_GM(kCB2, 2, false), QMV_GM(kCB2, 3, false), QMV_GM(kCB2, 4, false)},
-     {QMV_GM(kCB3, 1, false), QMV_GM(kCB3, 2, false), QMV_GM(kCB3, 3, false), nullptr}},
-    {{QMV_GM(kCB2, 1, true), QMV_GM(kCB2, 2, true), QMV_GM(kCB2, 3, true), QMV_GM(kCB2, 4, true)},
-     {QMV_GM(kCB3, 1, true), QMV_GM(kCB3, 2, true), QMV_GM(kCB3, 3, true), nullptr}}};
+// [workgroup: 8 waves, 12 waves][int8 activations, bf16 quantized in
+// staging][format: 2-bit, 3-bit][vector groups per chunk: 1, 2, 3, 4 (at 12
+// waves 2-bit only: the 3-bit kernel with four groups needs more than the 168
+// registers per lane that three waves per SIMD leave)]; 3 steps of loads in
+// flight.
+#define QMV_GM(W, F, N, Q) (const void *)&qmv_gmma_kernel<F, W, N, 3, Q>
+extern const void *const kTableGmma[2][2][2][4];
+const void *const kTableGmma[2][2][2][4] = {
+    {{{QMV_GM(8, kCB2, 1, false), QMV_GM(8, kCB2, 2, false), QMV_GM(8, kCB2, 3, false), QMV_GM(8, kCB2, 4, false)},
+      {QMV_GM(8, kCB3, 1, false), QMV_GM(8, kCB3, 2, false), QMV_GM(8, kCB3, 3, false), QMV_GM(8, kCB3, 4, false)}},
+     {{QMV_GM(8, kCB2, 1, true), QMV_GM(8, kCB2, 2, true), QMV_GM(8, kCB2, 3, true), QMV_GM(8, kCB2, 4, true)},
+      {QMV_GM(8, kCB3, 1, true), QMV_GM(8, kCB3, 2, true), QMV_GM(8, kCB3, 3, true), QMV_GM(8, kCB3, 4, true)}}},
+    {{{QMV_GM(12, kCB2, 1, false), QMV_GM(12, kCB2, 2, false), QMV_GM(12, kCB2, 3, false), QMV_GM(12, kCB2, 4, false)},
+      {QMV_GM(12, kCB3, 1, false), QMV_GM(12, kCB3, 2, false), QMV_GM(12, kCB3, 3, false), nullptr}},
+     {{QMV_GM(12, kCB2, 1, true), QMV_GM(12, kCB2, 2, true), QMV_GM(12, kCB2, 3, true), QMV_GM(12, kCB2, 4, true)},
+      {QMV_GM(12, kCB3, 1, true), QMV_GM(12, kCB3, 2, true), QMV_GM(12, kCB3, 3, true), nullptr}}}};
 #undef QMV_GM
 
 }  // namespace qmv
